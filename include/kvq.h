@@ -1,0 +1,193 @@
+/*
+ * kvq.h -- quantized KV-cache store and compressed-domain attention on MI355X (gfx950).
+ *
+ * C ABI of libkvq.so.  Every pointer argument marked "device" is device memory
+ * owned by the caller; the library never allocates, frees or synchronises.
+ * Every call is asynchronous on the HIP stream passed as `stream` (a
+ * hipStream_t; NULL is the default stream).  Arguments are validated on the
+ * host before anything is enqueued: on error nothing is launched and the
+ * status says why (kvq_last_error() gives a message for the calling thread).
+ * A launch failure maps to KVQ_ERR_HIP.  Device-side values (slots, positions,
+ * lengths, page tables) must be consistent with the shapes passed: the
+ * kernels trust them to stay inside the planes.
+ *
+ * Sources (cited by page title and section):
+ *   [tract-RFC]     "Heads-up / RFC: int4 + Hadamard KV-cache quantization
+ *                   (CPU + Metal)", tract discussion #2402
+ *   [FreeToken-268] "feat(kvcache): sub-byte Q4_0 and Q6_0 KV cache
+ *                   quantization", FreeToken PR #268
+ *   [Open-TQ-Metal] "Open-TQ-Metal: Fused Compressed-Domain Attention for
+ *                   Long-Context LLM Inference on Apple Silicon", arXiv 2604.16957
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Cache encodings.  Codes of element j are packed two per byte, element 2j in
+ * the low nibble ([FreeToken-268] Storage layouts), rows are per token, per kv
+ * head, separately for K and V.
+ *   HAD_INT4  [tract-RFC] What's done (CPU); Architecture > Data flow (decode):
+ *             row rotated by the orthonormal Hadamard (fast transform), then
+ *             per-token symmetric int4 in [-8, 7], scale amax/8 as one f32.
+ *             payload D/2 bytes, record 4 bytes.  D must be a power of two.
+ *   Q4_0      [FreeToken-268] Summary, Storage layouts: 32-element blocks,
+ *             fp16 scale amax/8, codes [-8, 7].  payload D/2, record 2*D/32.
+ *   Q6_0      [FreeToken-268] Storage layouts: per block 16-byte low-nibble
+ *             plane then 8-byte plane of the top two bits (value 4k+i at byte k,
+ *             bits 2i), fp16 scale amax/32, codes [-32, 31].
+ *             payload 24*D/32, record 2*D/32.
+ *   ASYM_INT4_G32 [Open-TQ-Metal] Background (per-group asymmetric int4):
+ *             groups of 32, min-max affine map, fp16 scale (max-min)/15 then
+ *             fp16 zero (= min) per group, unsigned codes [0, 15].
+ *             payload D/2, record 4*D/32. */
+typedef enum kvq_layout {
+  KVQ_LAYOUT_HAD_INT4 = 0,
+  KVQ_LAYOUT_Q4_0 = 1,
+  KVQ_LAYOUT_Q6_0 = 2,
+  KVQ_LAYOUT_ASYM_INT4_G32 = 3
+} kvq_layout;
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent shapes     */
+  KVQ_ERR_UNSUPPORTED = 2, /* (layout, head_dim, gqa) not built into the library */
+  KVQ_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required         */
+  KVQ_ERR_HIP = 4          /* a HIP launch failed                                */
+} kvq_status;
+
+/* Flags of kvq_attend_prefill_causal. */
+#define KVQ_PREFILL_NO_CAUSAL_SKIP 1u /* visit KV tiles wholly past the causal limit too */
+
+/* The paged cache.  All planes are device memory owned by the caller; the
+ * library reads and writes them only inside calls.
+ *   k_payload, v_payload  uint8 [num_pages][num_kv_heads][page_size][payload_bytes]
+ *   k_scale,   v_scale    uint8 [num_pages][num_kv_heads][page_size][scale_bytes]
+ *   k_recent,  v_recent   f32   [max_batch][num_kv_heads][n_recent][head_dim]
+ * The recent window ([tract-RFC] Causality & mixed precision, n_recent) keeps
+ * the newest n_recent positions of each batch row as exact f32 rows (rotated
+ * for HAD_INT4) in a ring indexed by position % n_recent; may be NULL when
+ * n_recent == 0.  page_size is a power of two >= 16; head_dim is 128 or 256. */
+typedef struct kvq_cache {
+  int32_t layout;       /* kvq_layout */
+  int32_t head_dim;
+  int32_t num_kv_heads;
+  int32_t page_size;
+  int32_t num_pages;
+  int32_t n_recent;
+  int32_t max_batch;
+  int32_t reserved;     /* must be 0 */
+  void* k_payload;
+  void* v_payload;
+  void* k_scale;
+  void* v_scale;
+  float* k_recent;
+  float* v_recent;
+} kvq_cache;
+
+/* Bytes of one stored row (per token, per kv head, per tensor); 0 if the
+ * (layout, head_dim) pair is not supported. */
+size_t kvq_payload_bytes(int32_t layout, int32_t head_dim);
+size_t kvq_scale_bytes(int32_t layout, int32_t head_dim);
+
+/* Quantize-on-append.  [tract-RFC] Architecture > Data flow (decode), append
+ * step, and the on-device append kernel asked for under Metal integration;
+ * [FreeToken-268] Changes (store kernel); encodings as documented above.
+ *   k_new, v_new  device f32 [n_tok][num_kv_heads][head_dim]
+ *   slot          device int32 [n_tok]: physical page * page_size + offset
+ *   batch_idx     device int32 [n_tok]: batch row (window ring row)
+ *   pos           device int32 [n_tok]: absolute position of the token
+ *   seq_len       device int32 [max_batch]: row length after this store
+ * Every token is quantised into its slot.  When n_recent > 0 a token whose
+ * pos >= seq_len[row] - n_recent is also written as an f32 row into the ring
+ * slot pos % n_recent (so a multi-token append never writes one ring slot
+ * twice).  n_tok == 0 is a no-op.  Codes and scales are bit-exact functions of
+ * the inputs (ties to even, f32 division, fp16 fields saturate at 65504). */
+kvq_status kvq_store(const kvq_cache* cache, const float* k_new, const float* v_new,
+                     int32_t n_tok, const int32_t* slot, const int32_t* batch_idx,
+                     const int32_t* pos, const int32_t* seq_len, void* stream);
+
+/* Workspace of kvq_attend_decode: split-K partials (o_c, m_c, l_c) per
+ * (batch, query head, chunk), plus the window partial. */
+size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_seq_len, int32_t chunk_tokens);
+
+/* Fused compressed-domain decode attention, one query per batch row.
+ * [Open-TQ-Metal] Algorithm 1 and the split-K paragraphs: the packed cache is
+ * read directly (no dequantised S x d temporary), the sequence is split into
+ * chunks of chunk_tokens tokens that run in parallel, each emitting
+ * (o_c, m_c, l_c), and a reduce merges them with the online-softmax
+ * correction.  Scores are int8(Q) . int4/int6(K) -> i32 per block with the
+ * scales applied outside ([tract-RFC] Architecture > Data flow (decode)); GQA
+ * maps query head h to kv head h / (num_q_heads / num_kv_heads)
+ * ([Open-TQ-Metal] SIMD and threadgroup organization).  For HAD_INT4 the query
+ * is rotated first and the output rotated back.
+ *   q            device f32 [batch][num_q_heads][head_dim]
+ *   out          device f32 [batch][num_q_heads][head_dim]
+ *   block_table  device int32 [batch][max_pages_per_seq]: physical page of each
+ *                logical page of the row
+ *   seq_len      device int32 [batch]: cached tokens of each row (<= max_seq_len);
+ *                the newest min(seq_len, n_recent) are read from the window
+ *   max_seq_len  host bound on seq_len (sizes the grid)
+ *   chunk_tokens split-K chunk, a multiple of 128
+ * num_q_heads / num_kv_heads must be an integer in [1, 16].  A row with
+ * seq_len 0 gets zeros.  alpha is the score scale (1/sqrt(d), or 1.0 for
+ * RMS-normalised Q/K, [Open-TQ-Metal] Section 4). */
+kvq_status kvq_attend_decode(const kvq_cache* cache, const float* q, float* out,
+                             int32_t batch, int32_t num_q_heads, float alpha,
+                             const int32_t* block_table, int32_t max_pages_per_seq,
+                             const int32_t* seq_len, int32_t max_seq_len,
+                             int32_t chunk_tokens, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Workspace of kvq_attend_prefill_causal (0 in this version; pass NULL). */
+size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t num_q_heads,
+                                   int32_t head_dim, int32_t max_seq_len);
+
+/* Causal prefill over the packed cache, called after kvq_store of the chunk.
+ * [tract-RFC] Architecture (prefill appends the chunk, then attends each
+ * position with its causal limit) and Causality & mixed precision (causal
+ * skip is bit-identical to compute-then-mask).  Query i of row b sits at
+ * position q_start[b] + i and, when causal != 0, sees tokens t <= q_start[b] + i;
+ * KV tiles wholly past the limit are skipped unless flags has
+ * KVQ_PREFILL_NO_CAUSAL_SKIP.  The window is the last n_recent positions of
+ * the row, the same for every query.
+ *   q    device f32 [batch][n_q][num_q_heads][head_dim]
+ *   out  device f32 [batch][n_q][num_q_heads][head_dim] */
+kvq_status kvq_attend_prefill_causal(const kvq_cache* cache, const float* q, float* out,
+                                     int32_t batch, int32_t n_q, int32_t num_q_heads,
+                                     float alpha, int32_t causal, const int32_t* q_start,
+                                     const int32_t* block_table, int32_t max_pages_per_seq,
+                                     const int32_t* seq_len, int32_t max_seq_len, uint32_t flags,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Test exports for the bit-exact gates. */
+
+/* Query preparation of the attention kernels: rotation (HAD_INT4 only) and
+ * per-vector int8, sq = amax/127 ([tract-RFC] data flow, int8(Q_rot)).
+ *   q device f32 [n_vec][head_dim]; q8 device int8 [n_vec][head_dim]; sq device f32 [n_vec] */
+kvq_status kvq_debug_quantize_q(int32_t layout, const float* q, int32_t n_vec, int32_t head_dim,
+                                int8_t* q8, float* sq, void* stream);
+
+/* The decode kernel's per-block integer scores I[t][g] = sum_j q8_j * code_tj
+ * over block g (the whole row for HAD_INT4), for quantised tokens
+ * t < seq_len[b] - n_recent; other entries are left untouched.
+ *   scores device int32 [batch][num_q_heads][max_seq_len][n_groups],
+ *   n_groups = 1 for HAD_INT4, head_dim/32 otherwise. */
+kvq_status kvq_debug_qk_i32(const kvq_cache* cache, const float* q, int32_t batch,
+                            int32_t num_q_heads, const int32_t* block_table,
+                            int32_t max_pages_per_seq, const int32_t* seq_len,
+                            int32_t max_seq_len, int32_t* scores, void* stream);
+
+const char* kvq_status_string(kvq_status status);
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

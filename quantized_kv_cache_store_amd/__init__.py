@@ -1,0 +1,12 @@
+"""Quantized KV-cache store and compressed-domain attention for MI355X (gfx950).
+
+A thin binding over libkvq.so, the C-ABI library declared in include/kvq.h.
+PyTorch only supplies device memory and the stream; the store, the split-K
+decode attention and the causal prefill all run in the library's HIP kernels.
+Importing the package does not load the library; the first call does, and
+fails loudly if it is not built.
+"""
+
+from ._lib import LAYOUT_IDS, KvqError, load  # noqa: F401
+from .ops import (KvqCache, attend_decode, attend_prefill_causal, debug_qk_i32,  # noqa: F401
+                  debug_quantize_q, decode_workspace_bytes, prefill_workspace_bytes, store)

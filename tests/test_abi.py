@@ -1,0 +1,84 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, and
+validates arguments before touching the GPU (no compute call runs here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_kv_cache_store_amd as kvq
+from quantized_kv_cache_store_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kvq.load()
+    names = _declared()
+    assert "kvq_store" in names and "kvq_attend_decode" in names and "kvq_attend_prefill_causal" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_sizes():
+    lib = kvq.load()
+    assert lib.kvq_payload_bytes(_lib.Q4_0, 128) == 64
+    assert lib.kvq_scale_bytes(_lib.Q4_0, 128) == 8
+    assert lib.kvq_payload_bytes(_lib.Q6_0, 256) == 192
+    assert lib.kvq_scale_bytes(_lib.Q6_0, 256) == 16
+    assert lib.kvq_payload_bytes(_lib.ASYM_INT4_G32, 128) == 64
+    assert lib.kvq_scale_bytes(_lib.ASYM_INT4_G32, 128) == 16
+    assert lib.kvq_scale_bytes(_lib.HAD_INT4, 128) == 4
+    assert lib.kvq_payload_bytes(_lib.Q4_0, 64) == 0          # unsupported head_dim
+    assert lib.kvq_payload_bytes(7, 128) == 0
+    # partials [B][Hq][chunks + 1][D + 4] f32
+    assert lib.kvq_decode_workspace_bytes(1, 64, 128, 131072, 512) == 64 * 257 * 132 * 4
+    assert lib.kvq_decode_workspace_bytes(1, 64, 128, 1000, 100) == 0  # chunk not a multiple of 128
+
+
+def _desc(**kw):
+    d = dict(layout=1, head_dim=128, num_kv_heads=1, page_size=16, num_pages=4, n_recent=0, max_batch=1,
+             reserved=0, k_payload=16, v_payload=16, k_scale=16, v_scale=16, k_recent=None, v_recent=None)
+    d.update(kw)
+    return _lib.KvqCacheDesc(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=9), 1), (dict(head_dim=96), 2), (dict(page_size=24), 1), (dict(page_size=8), 1),
+    (dict(num_kv_heads=0), 1), (dict(k_payload=None), 1), (dict(n_recent=4), 1), (dict(reserved=3), 1),
+])
+def test_store_validates_cache(kw, status):
+    lib = kvq.load()
+    st = lib.kvq_store(ctypes.byref(_desc(**kw)), 16, 16, 1, 16, 16, 16, 16, None)
+    assert st == status
+    assert lib.kvq_last_error()
+
+
+def test_attend_validates_before_launch():
+    lib = kvq.load()
+    d = ctypes.byref(_desc())
+    # Hq not a multiple of Hkv... (Hkv = 1 here: use a GQA group above 16)
+    assert lib.kvq_attend_decode(d, 16, 16, 1, 17, 1.0, 16, 4, 16, 64, 512, 16, 1 << 20, None) == 2
+    assert lib.kvq_attend_decode(d, 16, 16, 1, 4, 1.0, 16, 4, 16, 64, 100, 16, 1 << 20, None) == 1  # chunk
+    assert lib.kvq_attend_decode(d, 16, 16, 1, 4, 1.0, 16, 4, 16, 64, 512, 16, 10, None) == 3       # workspace
+    assert lib.kvq_attend_decode(d, 16, 16, 1, 4, 1.0, 16, 2, 16, 64, 512, 16, 1 << 20, None) == 1  # pages
+    assert lib.kvq_attend_decode(d, None, 16, 1, 4, 1.0, 16, 4, 16, 64, 512, 16, 1 << 20, None) == 1
+    assert lib.kvq_debug_quantize_q(1, 16, 3, 64, 16, 16, None) == 2
+    assert lib.kvq_store(d, 16, 16, -1, 16, None, None, None, None) == 1
+    assert lib.kvq_store(d, 16, 16, 0, 16, None, None, None, None) == 0   # empty append is a no-op
+    assert kvq.load().kvq_status_string(3) == b"workspace too small"
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libkvq.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load()

@@ -1,0 +1,127 @@
+"""GPU parity of the split-K decode attention against the oracle.
+
+Bit-exact: the kernel's per-block i32 scores.  Outputs: max|diff| <= 2e-3 * max|o_ref|.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_kv_cache_store_amd as kvq
+from oracle import attention, quant, spec
+import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+ALL = [spec.HAD_INT4, spec.Q4_0, spec.Q6_0, spec.ASYM_G32]
+
+
+def _rows(rng, lens, Hkv, D, dist="normal"):
+    if dist == "t3":
+        return [(rng.standard_t(3, size=(n, Hkv, D)) / math.sqrt(3)).astype(np.float32) for n in lens]
+    return [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in lens]
+
+
+def _run_case(layout, D, Hkv, G, lens, n_recent=0, chunk=512, page_size=16, seed=0, alpha=None, dist="normal"):
+    rng = np.random.default_rng(seed)
+    rows_k = _rows(rng, lens, Hkv, D, dist)
+    rows_v = _rows(rng, lens, Hkv, D, dist)
+    B, Hq = len(lens), Hkv * G
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    alpha = alpha if alpha is not None else 1.0 / math.sqrt(D)
+    cache, bt, seq, table = U.build_cache(layout, D, Hkv, rows_k, rows_v, page_size=page_size, n_recent=n_recent)
+    maxs = max(max(lens), 1)
+    out = kvq.attend_decode(cache, torch.from_numpy(q).to(U.DEV), bt, seq, maxs, alpha, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = np.stack([attention.attend_decode(layout, q[b], rows_k[b], rows_v[b], alpha, n_recent=n_recent)
+                    for b in range(B)])
+    return got, ref, (cache, bt, seq, q, rows_k, rows_v)
+
+
+@pytest.mark.parametrize("layout", ALL)
+@pytest.mark.parametrize("D", [128, 256])
+def test_qk_i32_bit_exact(layout, D):
+    U.need_gpu()
+    rng = np.random.default_rng(3 + layout)
+    Hkv, G, lens = 2, 3, [700, 45]
+    rows_k = _rows(rng, lens, Hkv, D)
+    rows_v = _rows(rng, lens, Hkv, D)
+    q = rng.standard_normal((2, Hkv * G, D)).astype(np.float32)
+    cache, bt, seq, table = U.build_cache(layout, D, Hkv, rows_k, rows_v, n_recent=5)
+    got = kvq.debug_qk_i32(cache, torch.from_numpy(q).to(U.DEV), bt, seq, max(lens)).cpu().numpy()
+    for b, n in enumerate(lens):
+        for h in range(Hkv * G):
+            _, q8, _ = attention.prepare_query(layout, q[b, h])
+            codes = quant.encode_rows(layout, rows_k[b][:, h // G, :])["codes"]
+            ref = attention.scores_i32(layout, q8, codes)
+            np.testing.assert_array_equal(got[b, h, :n - 5], ref[:n - 5], err_msg=f"b{b} h{h}")
+
+
+@pytest.mark.parametrize("layout", ALL)
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_decode_matches_oracle(layout, D, G):
+    U.need_gpu()
+    got, ref, _ = _run_case(layout, D, Hkv=2, G=G, lens=[1500, 129, 33], seed=11 * G + D + layout)
+    U.assert_close_rel(got, ref)
+
+
+@pytest.mark.parametrize("layout", ALL)
+@pytest.mark.parametrize("lens", [[1], [5], [16], [127, 128, 129], [513, 1024, 1025], [0, 300]])
+def test_decode_edge_lengths(layout, lens):
+    U.need_gpu()
+    got, ref, _ = _run_case(layout, 128, Hkv=1, G=2, lens=lens, seed=sum(lens) + layout)
+    U.assert_close_rel(got, ref)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert not got[b].any()
+
+
+@pytest.mark.parametrize("layout", ALL)
+@pytest.mark.parametrize("n_recent", [7, 64, 512])
+def test_decode_recent_window(layout, n_recent):
+    """Rows longer than, equal to and shorter than the window (a full window is exact f32)."""
+    U.need_gpu()
+    got, ref, _ = _run_case(layout, 128, Hkv=2, G=2, lens=[1100, 40, 64, 512], n_recent=n_recent,
+                            seed=n_recent + layout)
+    U.assert_close_rel(got, ref)
+
+
+def test_decode_rejects_window_above_cap():
+    U.need_gpu()
+    with pytest.raises(kvq.KvqError, match="unsupported"):
+        _run_case(spec.Q4_0, 128, Hkv=1, G=1, lens=[10], n_recent=513)
+
+
+@pytest.mark.parametrize("G", [2, 16])
+def test_decode_gqa_16_and_t3_values(G):
+    U.need_gpu()
+    got, ref, _ = _run_case(spec.ASYM_G32, 128, Hkv=1, G=G, lens=[900], seed=G, dist="t3")
+    U.assert_close_rel(got, ref)
+
+
+@pytest.mark.parametrize("chunk", [128, 256, 1024, 4096])
+def test_decode_chunk_sweep(chunk):
+    U.need_gpu()
+    got, ref, _ = _run_case(spec.Q4_0, 128, Hkv=2, G=4, lens=[3000, 700], chunk=chunk, seed=chunk)
+    U.assert_close_rel(got, ref)
+
+
+def test_decode_deterministic():
+    U.need_gpu()
+    got, ref, (cache, bt, seq, q, _, _) = _run_case(spec.ASYM_G32, 128, Hkv=2, G=8, lens=[2000, 900], seed=9)
+    qt = torch.from_numpy(q).to(U.DEV)
+    a = kvq.attend_decode(cache, qt, bt, seq, 2000, 1 / math.sqrt(128))
+    b = kvq.attend_decode(cache, qt, bt, seq, 2000, 1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    np.testing.assert_array_equal(a.cpu().numpy(), got)
+
+
+def test_decode_large_page_size():
+    U.need_gpu()
+    got, ref, _ = _run_case(spec.Q6_0, 256, Hkv=1, G=2, lens=[2500, 17], page_size=1024, seed=4)
+    U.assert_close_rel(got, ref)
