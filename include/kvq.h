@@ -145,6 +145,23 @@ kvq_status kvq_attend_decode(const kvq_cache* cache, const float* q, float* out,
                              int32_t chunk_tokens, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* The two phases of kvq_attend_decode as separate calls, for callers that time
+ * or schedule them apart ([Open-TQ-Metal] split-K paragraphs: a partial phase
+ * and a reduce phase ordered by their data dependency; here by stream order).
+ * kvq_attend_decode_partial writes the per-chunk partials (and the window
+ * partial) into the workspace; kvq_attend_decode_reduce merges them into out.
+ * Arguments mean what they mean for kvq_attend_decode and must be identical
+ * between the two calls. */
+kvq_status kvq_attend_decode_partial(const kvq_cache* cache, const float* q, int32_t batch,
+                                     int32_t num_q_heads, float alpha, const int32_t* block_table,
+                                     int32_t max_pages_per_seq, const int32_t* seq_len,
+                                     int32_t max_seq_len, int32_t chunk_tokens, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+kvq_status kvq_attend_decode_reduce(const kvq_cache* cache, float* out, int32_t batch,
+                                    int32_t num_q_heads, const int32_t* seq_len, int32_t max_seq_len,
+                                    int32_t chunk_tokens, const void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /* Workspace of kvq_attend_prefill_causal (0 in this version; pass NULL). */
 size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t num_q_heads,
                                    int32_t head_dim, int32_t max_seq_len);

@@ -32,6 +32,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 #define KVQ_LOG2E 1.4426950408889634f
 
@@ -136,26 +137,295 @@ __device__ void window_partial(const DecodeArgs& a, unsigned char* smem, int b, 
   }
 }
 
-template <int L, int D, bool DBG>
-__global__ __launch_bounds__(256) void decode_partial(DecodeArgs a) {
+// Staging buffer of one 32-token step in a wave's LDS slice:
+//   [K payload rows 32 x PB][V payload rows 32 x PB][K records 32 x SB][V records 32 x SB]
+// filled from registers that were loaded one step ahead with 16-byte loads.
+template <int L, int D>
+struct Step {
   using T = Layout<L, D>;
+  static constexpr int PB = T::PB, SB = T::SB;
+  static constexpr int KP = 0, VP = 32 * PB, KR = 64 * PB, VR = KR + 32 * SB;
+  static constexpr int BYTES = VR + 32 * SB;
+  static constexpr int PAY_SLOTS = (2 * PB + 63) / 64;   // 16-byte chunks of 32 payload rows, per lane
+  static constexpr int REC_SLOTS = (4 * SB + 63) / 64;   // K and V records together
+  static constexpr int SLOTS = 2 * PAY_SLOTS + REC_SLOTS;
+};
+
+// Physical row indices of the two 16-token halves of the step at T (wave-uniform).
+struct HalfRows {
+  size_t r0, r1;
+};
+
+__device__ __forceinline__ HalfRows half_rows(const DecodeArgs& a, int b, int hk, int T, int t_end, size_t row_first) {
+  HalfRows h;
+  h.r0 = T < t_end ? plane_row(a, b, hk, T) : row_first;
+  h.r1 = T + 16 < t_end ? plane_row(a, b, hk, T + 16) : row_first;
+  return h;
+}
+
+// Issue the 16-byte loads of one step into pre[] (no wait).
+template <int L, int D>
+__device__ __forceinline__ void issue_step(const DecodeArgs& a, HalfRows hr, int lane, u32x4* pre) {
+  using ST = Step<L, D>;
+  constexpr int PB = ST::PB, SB = ST::SB;
+#pragma unroll
+  for (int k = 0; k < ST::PAY_SLOTS; ++k) {
+    const int ci = lane + 64 * k;
+    if (ci < 2 * PB) {
+      const size_t row = (ci >= PB) ? hr.r1 : hr.r0;
+      const size_t off = row * PB + (size_t)(ci % PB) * 16;
+      pre[k] = *reinterpret_cast<const u32x4*>(a.kp + off);
+      pre[ST::PAY_SLOTS + k] = *reinterpret_cast<const u32x4*>(a.vp + off);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < ST::REC_SLOTS; ++k) {
+    const int ci = lane + 64 * k;
+    if (ci < 4 * SB) {
+      const int cc = ci % (2 * SB);                 // chunk within the tensor's 32 records
+      const size_t row = (cc >= SB) ? hr.r1 : hr.r0;
+      const uint8_t* base = ci < 2 * SB ? a.ks : a.vs;
+      pre[2 * ST::PAY_SLOTS + k] = *reinterpret_cast<const u32x4*>(base + row * SB + (size_t)(cc % SB) * 16);
+    }
+  }
+}
+
+template <int L, int D>
+__device__ __forceinline__ void stage_step(unsigned char* buf, int lane, const u32x4* pre) {
+  using ST = Step<L, D>;
+  constexpr int PB = ST::PB, SB = ST::SB;
+#pragma unroll
+  for (int k = 0; k < ST::PAY_SLOTS; ++k) {
+    const int ci = lane + 64 * k;
+    if (ci < 2 * PB) {
+      *reinterpret_cast<u32x4*>(buf + ST::KP + ci * 16) = pre[k];
+      *reinterpret_cast<u32x4*>(buf + ST::VP + ci * 16) = pre[ST::PAY_SLOTS + k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < ST::REC_SLOTS; ++k) {
+    const int ci = lane + 64 * k;
+    if (ci < 4 * SB) *reinterpret_cast<u32x4*>(buf + ST::KR + ci * 16) = pre[2 * ST::PAY_SLOTS + k];
+  }
+}
+
+// f16 element idx of a record, as f32
+__device__ __forceinline__ float rec_f16(const unsigned char* p, int idx) {
+  return (float)reinterpret_cast<const _Float16*>(p)[idx];
+}
+
+// Record word idx of a staged record as f16 pairs (scale, or scale|zero for asym).
+__device__ __forceinline__ uint32_t rec_word(const unsigned char* rec, int idx) {
+  return reinterpret_cast<const uint32_t*>(rec)[idx];
+}
+
+// One 32-token step of a wave: Q K^T, online softmax, P V, all from the staged rows in `buf`.
+// FULL: every token of the step is inside the chunk (no masking needed).
+template <int L, int D, bool DBG, bool FULL>
+__device__ __forceinline__ void decode_step(const DecodeArgs& a, const unsigned char* buf, int T0, int t_end, int b,
+                                            int hk, int G, int col, int r, const uint32_t (*qb)[2], const float* qsB,
+                                            const int* qoff, float sqc, uint32_t magic, float& m_run, float& l_run,
+                                            v4f* oacc) {
+  using T = Layout<L, D>;
+  using ST = Step<L, D>;
   constexpr int NG = T::NG;
   constexpr int SG = T::SG;
-  constexpr int NO = D / 128;            // octets per lane: col and col + 16
+  constexpr int PB = T::PB, SB = T::SB;
+  constexpr int NO = D / 128;
+  constexpr int BIAS = CodeBias<L>::value;
+
+  // ---------------- Q K^T on the int8 MFMA, scores of this lane's 8 tokens
+  float xs[8];
+  float vs_had[8];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    const unsigned char* krow = buf + ST::KP + (16 * tau + col) * PB;
+    v4i acc[SG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      uint32_t lo, hi;
+      if (L == Q60) {
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(krow + 24 * g + 4 * r);
+        const uint32_t t2 = *reinterpret_cast<const uint16_t*>(krow + 24 * g + 16 + 2 * r);
+        q6_octet(x, t2, lo, hi);
+      } else {
+        uint32_t x = *reinterpret_cast<const uint32_t*>(krow + 4 * (4 * g + r));
+        if (BIAS) x ^= 0x88888888u;
+        lo = x & 0x0F0F0F0Fu;
+        hi = (x >> 4) & 0x0F0F0F0Fu;
+      }
+      const long A = (long)((uint64_t)lo | ((uint64_t)hi << 32));
+      const long B = (long)((uint64_t)qb[g][0] | ((uint64_t)qb[g][1] << 32));
+      if (L == HAD) {
+        acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[0], 0, 0, 0);
+      } else {
+        acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+      }
+    }
+    // offset term: A[t = col][k = r] from the record of token 16*tau + col
+    v4f xo = v4f{0.f, 0.f, 0.f, 0.f};
+    if (L != HAD) {
+      const unsigned char* orec = buf + ST::KR + (16 * tau + col) * SB;
+#pragma unroll
+      for (int i = 0; i < NG / 4; ++i) {
+        const float av = (L == ASYM) ? rec_f16(orec, 2 * (4 * i + r) + 1) : rec_f16(orec, 4 * i + r);
+        xo = __builtin_amdgcn_mfma_f32_16x16x4f32(av, qsB[i], xo, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tl = 16 * tau + 4 * r + j;       // token within the step
+      const bool ok = FULL || T0 + tl < t_end;
+      const unsigned char* rec = buf + ST::KR + tl * SB;
+      float x;
+      if (L == HAD) {
+        const int I = acc[0][j] - qoff[0];
+        x = *reinterpret_cast<const float*>(rec) * (float)I;
+        if (DBG && ok && col < G) a.dbg[(((size_t)b * a.Hq + hk * G + col) * a.max_seq_len + T0 + tl)] = I;
+        const float vsc = *reinterpret_cast<const float*>(buf + ST::VR + tl * SB);
+        vs_had[tau * 4 + j] = ok ? vsc : 0.0f;
+      } else {
+        x = xo[j];
+#pragma unroll
+        for (int g = 0; g < SG; ++g) {
+          // scale of block g: low half of word g (asym: scale|zero), or half g of the packed fp16 scales
+          const uint32_t w = rec_word(rec, (L == ASYM) ? g : (g >> 1));
+          const float s = (float)as_h2(w)[(L == ASYM) ? 0 : (g & 1)];
+          x = fmaf(s, (float)acc[g][j], x);
+          if (DBG && ok && col < G)
+            a.dbg[(((size_t)b * a.Hq + hk * G + col) * a.max_seq_len + T0 + tl) * SG + g] = acc[g][j] - qoff[g];
+        }
+      }
+      xs[tau * 4 + j] = ok ? x * sqc : -INFINITY;
+    }
+  }
+  if (DBG) return;
+
+  // ---------------- online softmax (base 2), per head = lane column
+  float smax = xs[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) smax = fmaxf(smax, xs[i]);
+  smax = fmaxf(smax, __shfl_xor(smax, 16));
+  smax = fmaxf(smax, __shfl_xor(smax, 32));
+  const float m_new = fmaxf(m_run, smax);
+  const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+  // rescale the running sums only when some lane's maximum moved (rare after the first steps)
+  if (__any(m_new > m_run)) {
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+    l_run *= corr;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) oacc[i] *= corr;
+  }
+  m_run = m_new;
+  float psum = 0.0f;
+  v8h pB;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = __builtin_amdgcn_exp2f(xs[i] - m_use);
+    psum += p;
+    pB[i] = (_Float16)(L == HAD ? p * vs_had[i] : p);
+  }
+  l_run += psum;
+
+  // ---------------- P V on the f16 MFMA, V^T built from the staged rows
+#pragma unroll
+  for (int o = 0; o < NO; ++o) {
+    const int oc = col + 16 * o;       // this lane's octet (elements 8*oc .. 8*oc+7)
+    const int grp = oc >> 2;           // its 32-element block
+    uint32_t ev[8], od[8];
+    uint32_t sz[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int tl = 16 * (k >> 2) + 4 * r + (k & 3);
+      const unsigned char* vrow = buf + ST::VP + tl * PB;
+      if (L == Q60) {
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(vrow + 24 * grp + 4 * (oc & 3));
+        const uint32_t t2 = *reinterpret_cast<const uint16_t*>(vrow + 24 * grp + 16 + 2 * (oc & 3));
+        q6_octet(x, t2, ev[k], od[k]);
+      } else {
+        uint32_t x = *reinterpret_cast<const uint32_t*>(vrow + 4 * oc);
+        if (BIAS) x ^= 0x88888888u;
+        ev[k] = x;
+        od[k] = 0;
+      }
+      const bool ok = FULL || T0 + tl < t_end;   // rows past the end may hold anything: zero their scale
+      const unsigned char* vrec = buf + ST::VR + tl * SB;
+      uint32_t v;
+      if (L == ASYM) v = reinterpret_cast<const uint32_t*>(vrec)[grp];
+      else if (L != HAD) v = (uint32_t)reinterpret_cast<const uint16_t*>(vrec)[grp];
+      else v = 0u;
+      sz[k] = ok ? v : 0u;
+    }
+    h2 s2[4], z2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s2[i] = as_h2(__builtin_amdgcn_perm(sz[2 * i + 1], sz[2 * i], 0x05040100u));
+      z2[i] = as_h2(__builtin_amdgcn_perm(sz[2 * i + 1], sz[2 * i], 0x07060302u));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v8h A;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t bsel = (uint32_t)(e >> 1);
+        const uint32_t sel = bsel | (0x0Cu << 8) | ((4u + bsel) << 16) | (0x0Cu << 24);
+        uint32_t pair;
+        if (L == Q60) {
+          const uint32_t src_a = (e & 1) ? od[2 * i] : ev[2 * i];
+          const uint32_t src_b = (e & 1) ? od[2 * i + 1] : ev[2 * i + 1];
+          pair = __builtin_amdgcn_perm(src_b, src_a, sel) | magic;
+        } else {
+          const uint32_t y = __builtin_amdgcn_perm(ev[2 * i + 1], ev[2 * i], sel);
+          pair = (((e & 1) ? (y >> 4) : y) & 0x000F000Fu) | magic;
+        }
+        h2 v = as_h2(pair) - h2{(_Float16)(1024 + BIAS), (_Float16)(1024 + BIAS)};
+        if (L == ASYM) v = v * s2[i] + z2[i];
+        else if (L != HAD) v = v * s2[i];
+        A[2 * i] = v[0];
+        A[2 * i + 1] = v[1];
+      }
+      oacc[o * 8 + e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pB, oacc[o * 8 + e], 0, 0, 0);
+    }
+  }
+}
+
+// Split-K partial kernel.  Block = four waves = four consecutive chunks of one (batch row,
+// kv head); each wave streams its chunk in 32-token steps with two steps of loads in flight
+// and writes the chunk's partial (o unnormalised, m in base-2 logits, l).
+template <int L, int D, bool DBG>
+__global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
+  using T = Layout<L, D>;
+  using ST = Step<L, D>;
+  constexpr int NB = (D == 128) ? 4 : 1;   // steps of 16-byte loads kept in flight per wave
+  constexpr int NG = T::NG;
+  constexpr int SG = T::SG;
+  constexpr int NO = D / 128;
   constexpr int BIAS = CodeBias<L>::value;
   extern __shared__ __align__(16) unsigned char smem[];
 
-  const int c = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int hk = blockIdx.y, b = blockIdx.z;
   const int S = a.seq_len[b];
   const int Sq = a.n_recent > 0 ? max(0, S - a.n_recent) : S;
-  if (!DBG && a.n_recent > 0 && c == a.nc1 - 1) {
+  if (!DBG && a.n_recent > 0 && (int)blockIdx.x == (int)gridDim.x - 1) {
     if (S > 0) window_partial<L, D>(a, smem, b, hk, S);
     return;
   }
-  const int t_begin = c * a.chunk;
-  if (t_begin >= Sq) return;
-  const int t_end = min(t_begin + a.chunk, Sq);
+  if ((int)blockIdx.x * 4 * a.chunk >= Sq) return;
   const int G = a.G;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = blockIdx.x * 4 + wave;          // this wave's chunk
+  const int t_begin = c * a.chunk;
+  const int t_end = min(t_begin + a.chunk, Sq);
+  const bool active = t_begin < Sq;             // wave-uniform
+  const size_t row_first = active ? plane_row(a, b, hk, t_begin) : 0;
+
+  // the first NB steps' loads go out before the query preparation
+  u32x4 pre[NB][ST::SLOTS];
+#pragma unroll
+  for (int k = 0; k < NB; ++k)
+    if (active && t_begin + 32 * k < t_end)
+      issue_step<L, D>(a, half_rows(a, b, hk, t_begin + 32 * k, t_end, row_first), lane, pre[k]);
 
   // ---- prologue: query preparation for the GQA group of this kv head
   float* qf = reinterpret_cast<float*>(smem);
@@ -169,12 +439,8 @@ __global__ __launch_bounds__(256) void decode_partial(DecodeArgs a) {
   __syncthreads();
   prepare_query_lds<L, D>(qf, q8, sqv, qsum);
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;       // QK: head column; PV: d-row group; V octet
-  const int r = lane >> 4;         // lane group: k-slot block / C rows 4r..4r+3
-
-  // int8 query as the B operand of Q K^T, k-slot order [0,2,4,6,1,3,5,7] per 8
+  const int col = lane & 15;
+  const int r = lane >> 4;
   uint32_t qb[NG][2];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
@@ -183,292 +449,135 @@ __global__ __launch_bounds__(256) void decode_partial(DecodeArgs a) {
     qb[g][0] = __builtin_amdgcn_perm(w1, w0, 0x06040200u);
     qb[g][1] = __builtin_amdgcn_perm(w1, w0, 0x07050301u);
   }
-  int qoff[SG];      // bias * sum(q8) removed from the biased-code dot
-  float qzf[SG];     // sum(q8) per block for the zero-point term
+  // Offset term of the block layouts, sum_g c_g(t) * qsum_g[h], on the f32 MFMA (k = 4 blocks
+  // per product): c_g = zero point (asym), or -bias * scale (codes fed to the int8 MFMA as code + bias).
+  float qsB[NG / 4];
+#pragma unroll
+  for (int i = 0; i < NG / 4; ++i) {
+    const float qs = (float)qsum[col * NG + 4 * i + r];
+    qsB[i] = (L == ASYM) ? qs : -(float)BIAS * qs;
+  }
+  int qoff[SG];      // bias * sum(q8): the Hadamard scores and the score export use it
 #pragma unroll
   for (int g = 0; g < SG; ++g) {
-    int s = 0;
+    int sum = 0;
     if (L == HAD) {
 #pragma unroll
-      for (int gg = 0; gg < NG; ++gg) s += qsum[col * NG + gg];
+      for (int gg = 0; gg < NG; ++gg) sum += qsum[col * NG + gg];
     } else {
-      s = qsum[col * NG + g];
+      sum = qsum[col * NG + g];
     }
-    qoff[g] = BIAS * s;
-    qzf[g] = (float)s;
+    qoff[g] = BIAS * sum;
   }
   const float sqc = sqv[col] * a.alpha * KVQ_LOG2E;
-  __syncthreads();   // the LDS is reused by the merge below
+  __syncthreads();   // the LDS becomes the waves' step buffers
+  if (!active) return;
 
+  unsigned char* buf = smem + wave * ST::BYTES;
   float m_run = -INFINITY, l_run = 0.0f;
   v4f oacc[D / 16];
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) oacc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  const size_t row_first = plane_row(a, b, hk, t_begin);
 
-  for (int T0 = t_begin + 32 * wave; T0 < t_end; T0 += 128) {
-    // ---------------- Q K^T on the int8 MFMA
-    v4i acc[2][SG];
+  uint32_t magic;   // fp16 "1024 + code" exponent bits, kept in a VGPR so v_and_or_b32 can take it
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  for (int T0 = t_begin; T0 < t_end; T0 += 32 * NB) {
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const int ta = T0 + 16 * tau + col;
-      const size_t rk = ta < t_end ? plane_row(a, b, hk, ta) : row_first;
-      const uint8_t* kpr = a.kp + rk * T::PB;
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        uint32_t lo, hi;
-        if (L == Q60) {
-          const uint32_t x = *reinterpret_cast<const uint32_t*>(kpr + 24 * g + 4 * r);
-          const uint32_t t2 = *reinterpret_cast<const uint16_t*>(kpr + 24 * g + 16 + 2 * r);
-          q6_octet(x, t2, lo, hi);
-        } else {
-          uint32_t x = *reinterpret_cast<const uint32_t*>(kpr + 4 * (4 * g + r));
-          if (BIAS) x ^= 0x88888888u;
-          lo = x & 0x0F0F0F0Fu;
-          hi = (x >> 4) & 0x0F0F0F0Fu;
-        }
-        const long A = (long)((uint64_t)lo | ((uint64_t)hi << 32));
-        const long B = (long)((uint64_t)qb[g][0] | ((uint64_t)qb[g][1] << 32));
-        if (L == HAD) {
-          acc[tau][0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[tau][0], 0, 0, 0);
-        } else {
-          acc[tau][g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
-        }
-      }
-    }
-
-    // ---------------- scores of this lane's 8 tokens (C rows 4r+j of both tiles)
-    float xs[8];
-    float vscale_had[8];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const int tb = T0 + 16 * tau + 4 * r;
-      const size_t rb = tb < t_end ? plane_row(a, b, hk, tb) : row_first;
-      const uint8_t* rec = a.ks + rb * T::SB;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = tb + j;
-        float x = 0.0f;
-        if (L == HAD) {
-          const int I = acc[tau][0][j] - qoff[0];
-          x = reinterpret_cast<const float*>(rec)[j] * (float)I;
-          if (DBG && t < t_end && col < G)
-            a.dbg[(((size_t)b * a.Hq + hk * G + col) * a.max_seq_len + t)] = I;
-        } else {
-#pragma unroll
-          for (int g = 0; g < SG; ++g) {
-            const int I = acc[tau][g][j] - qoff[g];
-            if (L == ASYM) {
-              const uint32_t sz = reinterpret_cast<const uint32_t*>(rec + j * T::SB)[g];
-              const float s = (float)as_h2(sz)[0];
-              const float z = (float)as_h2(sz)[1];
-              x += s * (float)I + z * qzf[g];
-            } else {
-              const float s = (float)reinterpret_cast<const _Float16*>(rec + j * T::SB)[g];
-              x += s * (float)I;
-            }
-            if (DBG && t < t_end && col < G)
-              a.dbg[(((size_t)b * a.Hq + hk * G + col) * a.max_seq_len + t) * SG + g] = I;
-          }
-        }
-        xs[tau * 4 + j] = t < t_end ? x * sqc : -INFINITY;
-      }
-      if (L == HAD) {
-        // per-token V scale of the same 8 tokens (folded into the P operand)
-        const uint8_t* vrec = a.vs + rb * T::SB;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vscale_had[tau * 4 + j] = reinterpret_cast<const float*>(vrec)[j];
-      }
-    }
-    if (DBG) continue;
-
-    // ---------------- online softmax (base 2), per head = lane column
-    float smax = xs[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) smax = fmaxf(smax, xs[i]);
-    smax = fmaxf(smax, __shfl_xor(smax, 16));
-    smax = fmaxf(smax, __shfl_xor(smax, 32));
-    const float m_new = fmaxf(m_run, smax);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float corr = exp2f(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.0f;
-    v8h pB;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = exp2f(xs[i] - m_use);
-      psum += p;
-      pB[i] = (_Float16)(L == HAD ? p * vscale_had[i] : p);
-    }
-    l_run = l_run * corr + psum;
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) oacc[i] *= corr;
-
-    // ---------------- P V on the f16 MFMA, V^T built from the packed rows
-#pragma unroll
-    for (int o = 0; o < NO; ++o) {
-      const int oc = col + 16 * o;       // this lane's octet (elements 8*oc .. 8*oc+7)
-      const int grp = oc >> 2;           // its 32-element block
-      uint32_t ev[8], od[8];             // per token (k-slot): even / odd element codes as bytes or raw dword
-      uint32_t sz[8];                    // per token: fp16 scale (| zero << 16 for ASYM)
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        const int tb = T0 + 16 * tau + 4 * r;
-        const size_t rb = tb < t_end ? plane_row(a, b, hk, tb) : row_first;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const size_t rv = (tb + j < t_end) ? rb + j : row_first;
-          const uint8_t* vpr = a.vp + rv * T::PB;
-          const int k = tau * 4 + j;
-          if (L == Q60) {
-            const uint32_t x = *reinterpret_cast<const uint32_t*>(vpr + 24 * grp + 4 * (oc & 3));
-            const uint32_t t2 = *reinterpret_cast<const uint16_t*>(vpr + 24 * grp + 16 + 2 * (oc & 3));
-            q6_octet(x, t2, ev[k], od[k]);
-          } else {
-            uint32_t x = *reinterpret_cast<const uint32_t*>(vpr + 4 * oc);
-            if (BIAS) x ^= 0x88888888u;
-            ev[k] = x;
-            od[k] = 0;
-          }
-          if (L == ASYM) {
-            sz[k] = reinterpret_cast<const uint32_t*>(a.vs + rv * T::SB)[grp];
-          } else if (L != HAD) {
-            sz[k] = reinterpret_cast<const uint16_t*>(a.vs + rv * T::SB)[grp];
-          } else {
-            sz[k] = 0;
-          }
-        }
-      }
-      // f16x2 scale / zero of token pairs (k-slots 2i, 2i+1)
-      h2 s2[4], z2[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s2[i] = as_h2(__builtin_amdgcn_perm(sz[2 * i + 1], sz[2 * i], 0x05040100u));
-        z2[i] = as_h2(__builtin_amdgcn_perm(sz[2 * i + 1], sz[2 * i], 0x07060302u));
-      }
-      // element e of the octet -> d = 8*oc + e -> PV tile (o, e)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        v8h A;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t pair;
-          if (L == Q60) {
-            // byte e/2 of the even/odd code dwords of tokens 2i, 2i+1
-            const uint32_t src_a = (e & 1) ? od[2 * i] : ev[2 * i];
-            const uint32_t src_b = (e & 1) ? od[2 * i + 1] : ev[2 * i + 1];
-            const uint32_t bsel = (uint32_t)(e >> 1);
-            pair = __builtin_amdgcn_perm(src_b, src_a, bsel | (0x0Cu << 8) | ((4u + bsel) << 16) | (0x0Cu << 24)) | 0x64006400u;
-          } else {
-            const uint32_t bsel = (uint32_t)(e >> 1);
-            const uint32_t y = __builtin_amdgcn_perm(ev[2 * i + 1], ev[2 * i], bsel | (0x0Cu << 8) | ((4u + bsel) << 16) | (0x0Cu << 24));
-            pair = ((e & 1) ? (y >> 4) : y) & 0x000F000Fu;
-            pair |= 0x64006400u;
-          }
-          h2 v = as_h2(pair) - h2{(_Float16)(1024 + BIAS), (_Float16)(1024 + BIAS)};
-          if (L == ASYM) v = v * s2[i] + z2[i];
-          else if (L != HAD) v = v * s2[i];
-          A[2 * i] = v[0];
-          A[2 * i + 1] = v[1];
-        }
-        oacc[o * 8 + e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pB, oacc[o * 8 + e], 0, 0, 0);
-      }
+    for (int k = 0; k < NB; ++k) {
+      const int T = T0 + 32 * k;
+      if (T >= t_end) break;
+      stage_step<L, D>(buf, lane, pre[k]);
+      if (T + 32 * NB < t_end) issue_step<L, D>(a, half_rows(a, b, hk, T + 32 * NB, t_end, row_first), lane, pre[k]);
+      if (T + 32 <= t_end)
+        decode_step<L, D, DBG, true>(a, buf, T, t_end, b, hk, G, col, r, qb, qsB, qoff, sqc, magic, m_run, l_run, oacc);
+      else
+        decode_step<L, D, DBG, false>(a, buf, T, t_end, b, hk, G, col, r, qb, qsB, qoff, sqc, magic, m_run, l_run, oacc);
     }
   }
   if (DBG) return;
 
-  // ---------------- merge the four waves of the block (fixed order)
+  // ---------------- this wave's chunk partial
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  float* mbuf = reinterpret_cast<float*>(smem);          // [4][16]
-  float* lbuf = mbuf + 64;                               // [4][16]
-  float* obuf = lbuf + 64;                               // [4][G][D]
-  if (r == 0) {
-    mbuf[wave * 16 + col] = m_run;
-    lbuf[wave * 16 + col] = l_run;
-  }
   if (col < G) {
+    float* dst = a.ws + (((size_t)b * a.Hq + hk * G + col) * a.nc1 + c) * partial_stride(D);
 #pragma unroll
     for (int o = 0; o < NO; ++o)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = 8 * (4 * r + j + 16 * o) + e;
-          obuf[(wave * G + col) * D + d] = oacc[o * 8 + e][j];
-        }
-  }
-  __syncthreads();
-  const int PST = partial_stride(D);
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D, d = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, mbuf[w * 16 + h]);
-    float o = 0.0f, l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = mbuf[w * 16 + h];
-      const float e = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
-      o += e * obuf[(w * G + h) * D + d];
-      l += e * lbuf[w * 16 + h];
-    }
-    float* dst = a.ws + (((size_t)b * a.Hq + hk * G + h) * a.nc1 + c) * PST;
-    dst[d] = o;
-    if (d == 0) {
-      dst[D] = M;
-      dst[D + 1] = l;
+        for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + e] = oacc[o * 8 + e][j];
+    if (r == 0) {
+      dst[D] = m_run;
+      dst[D + 1] = l_run;
     }
   }
 }
 
 // Online-softmax merge of the chunk partials; Hadamard layout: rotate back.
+// Four waves split the chunks; each lane owns D/64 output elements.
 template <int D, bool ROT>
 __global__ __launch_bounds__(256) void decode_reduce(const float* ws, float* out, const int32_t* seq_len,
                                                      int Hq, int nc1, int chunk, int n_recent) {
+  constexpr int E = D / 64;
+  __shared__ float red_o[4][D];
+  __shared__ float red_m[4], red_l[4];
   __shared__ float x[D];
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = seq_len[b];
   const int Sq = n_recent > 0 ? max(0, S - n_recent) : S;
   const int nq = (Sq + chunk - 1) / chunk;
-  const bool has_w = n_recent > 0 && S > 0;
+  const int cnt = nq + ((n_recent > 0 && S > 0) ? 1 : 0);
   const int PST = partial_stride(D);
   const float* base = ws + ((size_t)b * Hq + h) * nc1 * PST;
   float M = -INFINITY;
-  for (int c = 0; c < nq; ++c) M = fmaxf(M, base[(size_t)c * PST + D]);
-  if (has_w) M = fmaxf(M, base[(size_t)(nc1 - 1) * PST + D]);
-  float o = 0.0f, l = 0.0f;
-  for (int c = 0; c < nq + (has_w ? 1 : 0); ++c) {
-    const int cc = c < nq ? c : nc1 - 1;
-    const float* p = base + (size_t)cc * PST;
+  for (int i = tid; i < cnt; i += 256) M = fmaxf(M, base[(size_t)(i < nq ? i : nc1 - 1) * PST + D]);
+  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
+  if (lane == 0) red_m[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  float o[E], l = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.0f;
+#pragma unroll 4
+  for (int i = wave; i < cnt; i += 4) {
+    const float* p = base + (size_t)(i < nq ? i : nc1 - 1) * PST;
     const float mc = p[D];
     const float w = (mc == -INFINITY) ? 0.0f : exp2f(mc - M);
-    o += w * p[d];
     l += w * p[D + 1];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] += w * p[lane * E + e];
   }
-  float res = l > 0.0f ? o / l : 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) red_o[wave][lane * E + e] = o[e];
+  if (lane == 0) red_l[wave] = l;
+  __syncthreads();
+  if (tid < D) {
+    const float lt = red_l[0] + red_l[1] + red_l[2] + red_l[3];
+    const float ot = red_o[0][tid] + red_o[1][tid] + red_o[2][tid] + red_o[3][tid];
+    x[tid] = lt > 0.0f ? ot / lt : 0.0f;
+  }
+  __syncthreads();
   if (ROT) {
     // rotate back with the same butterfly transform (stages h = 1 .. D/2, then 1/sqrt(D))
-    x[d] = res;
-    __syncthreads();
     for (int hh = 1; hh < D; hh <<= 1) {
       int i = 0;
       float p = 0.0f, q = 0.0f;
-      if (d < D / 2) {
-        i = (d / hh) * 2 * hh + (d % hh);
+      if (tid < D / 2) {
+        i = (tid / hh) * 2 * hh + (tid % hh);
         p = x[i];
         q = x[i + hh];
       }
       __syncthreads();
-      if (d < D / 2) {
+      if (tid < D / 2) {
         x[i] = p + q;
         x[i + hh] = p - q;
       }
       __syncthreads();
     }
-    res = x[d] * hadamard_norm<D>();
   }
-  out[((size_t)b * Hq + h) * D + d] = res;
+  if (tid < D) out[((size_t)b * Hq + h) * D + tid] = ROT ? x[tid] * hadamard_norm<D>() : x[tid];
 }
 
 template <int L, int D, bool DBG>
@@ -492,11 +601,16 @@ static partial_fn pick_partial(int layout, int D) {
   return tab[layout][di];
 }
 
-static size_t partial_lds_bytes(int D, int G, int n_recent) {
+static size_t step_bytes(int layout, int D) {
+  return 64 * (payload_bytes_rt(layout, D) + scale_bytes_rt(layout, D));
+}
+
+static size_t partial_lds_bytes(int layout, int D, int G, int n_recent) {
   const size_t pro = (size_t)16 * D * 4 + 16 * D + 16 * 4 + 16 * (D / 32) * 4;
-  const size_t merge = 2 * 64 * 4 + (size_t)4 * G * D * 4;
+  const size_t steps = 4 * step_bytes(layout, D);
+  (void)G;
   const size_t win = n_recent > 0 ? pro + (size_t)16 * n_recent * 4 + 32 * 4 : 0;
-  size_t m = pro > merge ? pro : merge;
+  size_t m = pro > steps ? pro : steps;
   return m > win ? m : win;
 }
 
@@ -530,17 +644,29 @@ extern "C" size_t kvq_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t 
   return (size_t)batch * Hq * nc1 * partial_stride(D) * sizeof(float);
 }
 
-extern "C" kvq_status kvq_attend_decode(const kvq_cache* c, const float* q, float* out, int32_t batch, int32_t Hq,
-                                        float alpha, const int32_t* block_table, int32_t max_pages,
-                                        const int32_t* seq_len, int32_t max_seq_len, int32_t chunk,
-                                        void* workspace, size_t ws_bytes, void* stream) {
+static kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t Hq, const int32_t* seq_len,
+                                int nc1, int32_t chunk, const float* ws, hipStream_t s) {
+  const dim3 rgrid(Hq, batch);
+  const bool rot = c->layout == HAD;
+  if (c->head_dim == 128) {
+    if (rot) hipLaunchKernelGGL((decode_reduce<128, true>), rgrid, dim3(256), 0, s, ws, out, seq_len, Hq, nc1, chunk, c->n_recent);
+    else hipLaunchKernelGGL((decode_reduce<128, false>), rgrid, dim3(256), 0, s, ws, out, seq_len, Hq, nc1, chunk, c->n_recent);
+  } else {
+    if (rot) hipLaunchKernelGGL((decode_reduce<256, true>), rgrid, dim3(256), 0, s, ws, out, seq_len, Hq, nc1, chunk, c->n_recent);
+    else hipLaunchKernelGGL((decode_reduce<256, false>), rgrid, dim3(256), 0, s, ws, out, seq_len, Hq, nc1, chunk, c->n_recent);
+  }
+  return check_launch("decode reduce kernel");
+}
+
+extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
+                                                float alpha, const int32_t* block_table, int32_t max_pages,
+                                                const int32_t* seq_len, int32_t max_seq_len, int32_t chunk,
+                                                void* workspace, size_t ws_bytes, void* stream) {
   kvq_status st = check_attend_args(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len);
   if (st != KVQ_OK) return st;
-  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out must be non-null");
   if (chunk < 128 || chunk % 128) return fail(KVQ_ERR_INVALID_ARG, "chunk_tokens must be a positive multiple of 128");
   const size_t need = kvq_decode_workspace_bytes(batch, Hq, c->head_dim, max_seq_len, chunk);
   if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
-  const int D = c->head_dim;
   DecodeArgs a;
   a.kp = (const uint8_t*)c->k_payload;
   a.vp = (const uint8_t*)c->v_payload;
@@ -564,24 +690,37 @@ extern "C" kvq_status kvq_attend_decode(const kvq_cache* c, const float* q, floa
   a.nc1 = nch + 1;
   a.max_seq_len = max_seq_len;
   a.alpha = alpha;
-  hipStream_t s = (hipStream_t)stream;
-  const int gx = nch + (c->n_recent > 0 ? 1 : 0);
-  if (gx > 0) {
-    const dim3 grid(gx, c->num_kv_heads, batch);
-    pick_partial<false>(c->layout, D)(a, grid, partial_lds_bytes(D, a.G, c->n_recent), s);
-    st = check_launch("decode partial kernel");
-    if (st != KVQ_OK) return st;
-  }
-  const dim3 rgrid(Hq, batch);
-  const bool rot = c->layout == HAD;
-  if (D == 128) {
-    if (rot) hipLaunchKernelGGL((decode_reduce<128, true>), rgrid, dim3(128), 0, s, a.ws, out, seq_len, Hq, a.nc1, chunk, c->n_recent);
-    else hipLaunchKernelGGL((decode_reduce<128, false>), rgrid, dim3(128), 0, s, a.ws, out, seq_len, Hq, a.nc1, chunk, c->n_recent);
-  } else {
-    if (rot) hipLaunchKernelGGL((decode_reduce<256, true>), rgrid, dim3(256), 0, s, a.ws, out, seq_len, Hq, a.nc1, chunk, c->n_recent);
-    else hipLaunchKernelGGL((decode_reduce<256, false>), rgrid, dim3(256), 0, s, a.ws, out, seq_len, Hq, a.nc1, chunk, c->n_recent);
-  }
-  return check_launch("decode reduce kernel");
+  const int gx = (nch + 3) / 4 + (c->n_recent > 0 ? 1 : 0);
+  if (gx == 0) return KVQ_OK;
+  const dim3 grid(gx, c->num_kv_heads, batch);
+  pick_partial<false>(c->layout, c->head_dim)(a, grid, partial_lds_bytes(c->layout, c->head_dim, a.G, c->n_recent), (hipStream_t)stream);
+  return check_launch("decode partial kernel");
+}
+
+extern "C" kvq_status kvq_attend_decode_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t Hq,
+                                               const int32_t* seq_len, int32_t max_seq_len, int32_t chunk,
+                                               const void* workspace, size_t ws_bytes, void* stream) {
+  kvq_status st = validate_cache(c);
+  if (st != KVQ_OK) return st;
+  if (!out || !seq_len) return fail(KVQ_ERR_INVALID_ARG, "out and seq_len must be non-null");
+  if (batch < 1 || Hq < 1 || Hq % c->num_kv_heads) return fail(KVQ_ERR_INVALID_ARG, "bad batch or num_q_heads");
+  if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len must be >= 0");
+  if (chunk < 128 || chunk % 128) return fail(KVQ_ERR_INVALID_ARG, "chunk_tokens must be a positive multiple of 128");
+  const size_t need = kvq_decode_workspace_bytes(batch, Hq, c->head_dim, max_seq_len, chunk);
+  if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  return launch_reduce(c, out, batch, Hq, seq_len, chunks_of(max_seq_len, chunk) + 1, chunk, (const float*)workspace,
+                       (hipStream_t)stream);
+}
+
+extern "C" kvq_status kvq_attend_decode(const kvq_cache* c, const float* q, float* out, int32_t batch, int32_t Hq,
+                                        float alpha, const int32_t* block_table, int32_t max_pages,
+                                        const int32_t* seq_len, int32_t max_seq_len, int32_t chunk,
+                                        void* workspace, size_t ws_bytes, void* stream) {
+  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out must be non-null");
+  kvq_status st = kvq_attend_decode_partial(c, q, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len,
+                                            chunk, workspace, ws_bytes, stream);
+  if (st != KVQ_OK) return st;
+  return kvq_attend_decode_reduce(c, out, batch, Hq, seq_len, max_seq_len, chunk, workspace, ws_bytes, stream);
 }
 
 extern "C" kvq_status kvq_debug_qk_i32(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
@@ -613,7 +752,7 @@ extern "C" kvq_status kvq_debug_qk_i32(const kvq_cache* c, const float* q, int32
   a.nc1 = nch;
   a.max_seq_len = max_seq_len;
   a.alpha = 1.0f;
-  const dim3 grid(nch, c->num_kv_heads, batch);
-  pick_partial<true>(c->layout, c->head_dim)(a, grid, partial_lds_bytes(c->head_dim, a.G, 0), (hipStream_t)stream);
+  const dim3 grid((nch + 3) / 4, c->num_kv_heads, batch);
+  pick_partial<true>(c->layout, c->head_dim)(a, grid, partial_lds_bytes(c->layout, c->head_dim, a.G, 0), (hipStream_t)stream);
   return check_launch("score export kernel");
 }

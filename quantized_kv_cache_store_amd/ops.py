@@ -130,6 +130,25 @@ def attend_decode(cache, q, block_table, seq_len, max_seq_len, alpha, chunk_toke
     return out
 
 
+def attend_decode_partial(cache, q, block_table, seq_len, max_seq_len, alpha, chunk_tokens, workspace):
+    """kvq_attend_decode_partial: the split-K phase; partials go to ``workspace``."""
+    dev = cache.device
+    B, Hq, _ = q.shape
+    st = load().kvq_attend_decode_partial(cache.desc, _ptr(q), B, Hq, float(alpha), _ptr(block_table),
+                                          block_table.shape[1], _ptr(seq_len), int(max_seq_len), int(chunk_tokens),
+                                          _ptr(workspace), workspace.numel(), _stream(dev))
+    check("kvq_attend_decode_partial", st)
+
+
+def attend_decode_reduce(cache, out, seq_len, max_seq_len, chunk_tokens, workspace):
+    """kvq_attend_decode_reduce: merge the partials in ``workspace`` into ``out`` [B, Hq, D]."""
+    dev = cache.device
+    B, Hq, _ = out.shape
+    st = load().kvq_attend_decode_reduce(cache.desc, _ptr(out), B, Hq, _ptr(seq_len), int(max_seq_len),
+                                         int(chunk_tokens), _ptr(workspace), workspace.numel(), _stream(dev))
+    check("kvq_attend_decode_reduce", st)
+
+
 def prefill_workspace_bytes(batch, n_q, num_q_heads, head_dim, max_seq_len):
     return load().kvq_prefill_workspace_bytes(batch, n_q, num_q_heads, head_dim, max_seq_len)
 

@@ -166,3 +166,26 @@ def block_tables(w: Workload, lens, page_size=None, pages_per_row=None):
         table[b, :n] = phys[k:k + n]
         k += n
     return table, total
+
+
+def kv_tokens_device(w: Workload, n, which, generator, device):
+    """Rows of all kv heads for ``n`` tokens drawn on the device: float32 [n, Hkv, D].
+
+    Same distribution, outlier channels and K normalisation as ``kv_tokens``, but
+    a different stream (torch's device generator): for filling multi-GB caches
+    whose values no CPU-side check reads.
+    """
+    import torch
+
+    shape = (n, w.Hkv, w.D)
+    x = torch.randn(shape, generator=generator, device=device, dtype=torch.float32)
+    if w.dist == "t3":
+        chi = torch.randn((3,) + shape, generator=generator, device=device, dtype=torch.float32)
+        x = x / torch.sqrt((chi * chi).sum(0) / 3.0) / math.sqrt(3.0)
+    if w.outliers:
+        for hk in range(w.Hkv):
+            ch = torch.as_tensor(outlier_channels(w, hk), device=device)
+            x[:, hk, ch] *= 10.0
+    if w.rms_norm_qk and which == "k":
+        x = x / torch.sqrt((x * x).mean(-1, keepdim=True) + 1e-6)
+    return x
