@@ -156,26 +156,62 @@ struct HalfRows {
   size_t r0, r1;
 };
 
-__device__ __forceinline__ HalfRows half_rows(const DecodeArgs& a, int b, int hk, int T, int t_end, size_t row_first) {
+// Page entries of a wave's chunk, one per lane (lane l: logical page first_page + l), so that a
+// step's rows come from readlane on the scalar unit instead of a memory round trip.
+struct ChunkPages {
+  int first_page;
+  int lane_page;     // physical page of logical page first_page + lane (or 0)
+  bool in_regs;      // the chunk spans at most 64 pages
+};
+
+__device__ __forceinline__ ChunkPages chunk_pages(const DecodeArgs& a, int b, int t_begin, int t_end, int lane,
+                                                  bool active) {
+  ChunkPages cp;
+  cp.first_page = t_begin >> a.page_shift;
+  const int npages = active ? ((t_end - 1) >> a.page_shift) - cp.first_page + 1 : 0;
+  cp.in_regs = npages <= 64;
+  cp.lane_page = (cp.in_regs && lane < npages) ? a.block_table[(size_t)b * a.max_pages + cp.first_page + lane] : 0;
+  return cp;
+}
+
+__device__ __forceinline__ size_t chunk_row(const DecodeArgs& a, const ChunkPages& cp, int b, int hk, int t) {
+  const int lp = t >> a.page_shift;
+  const int phys = cp.in_regs ? __builtin_amdgcn_readlane(cp.lane_page, lp - cp.first_page)
+                              : a.block_table[(size_t)b * a.max_pages + lp];
+  return (((size_t)phys * a.Hkv + hk) << a.page_shift) + (size_t)(t & ((1 << a.page_shift) - 1));
+}
+
+__device__ __forceinline__ HalfRows half_rows(const DecodeArgs& a, const ChunkPages& cp, int b, int hk, int T, int t_end,
+                                              size_t row_first) {
   HalfRows h;
-  h.r0 = T < t_end ? plane_row(a, b, hk, T) : row_first;
-  h.r1 = T + 16 < t_end ? plane_row(a, b, hk, T + 16) : row_first;
+  h.r0 = T < t_end ? chunk_row(a, cp, b, hk, T) : row_first;
+  h.r1 = T + 16 < t_end ? chunk_row(a, cp, b, hk, T + 16) : row_first;
   return h;
 }
 
-// Issue the 16-byte loads of one step into pre[] (no wait).
+// Issue the 16-byte loads of one step into pre[] (no wait).  Payload chunk ci of the step is
+// row ci / PB (half ci / PB), bytes 16 * (ci % PB); when PB is a multiple of 64 every slot lies in
+// one half, so its base address is wave-uniform and only lane * 16 varies.
 template <int L, int D>
 __device__ __forceinline__ void issue_step(const DecodeArgs& a, HalfRows hr, int lane, u32x4* pre) {
   using ST = Step<L, D>;
   constexpr int PB = ST::PB, SB = ST::SB;
 #pragma unroll
   for (int k = 0; k < ST::PAY_SLOTS; ++k) {
-    const int ci = lane + 64 * k;
-    if (ci < 2 * PB) {
-      const size_t row = (ci >= PB) ? hr.r1 : hr.r0;
-      const size_t off = row * PB + (size_t)(ci % PB) * 16;
+    if (PB % 64 == 0) {
+      const int half = (64 * k) / PB;                     // compile-time
+      const size_t row = half ? hr.r1 : hr.r0;
+      const size_t off = row * PB + (size_t)((64 * k) % PB) * 16 + (size_t)lane * 16;
       pre[k] = *reinterpret_cast<const u32x4*>(a.kp + off);
       pre[ST::PAY_SLOTS + k] = *reinterpret_cast<const u32x4*>(a.vp + off);
+    } else {
+      const int ci = lane + 64 * k;
+      if (ci < 2 * PB) {
+        const size_t row = (ci >= PB) ? hr.r1 : hr.r0;
+        const size_t off = row * PB + (size_t)(ci % PB) * 16;
+        pre[k] = *reinterpret_cast<const u32x4*>(a.kp + off);
+        pre[ST::PAY_SLOTS + k] = *reinterpret_cast<const u32x4*>(a.vp + off);
+      }
     }
   }
 #pragma unroll
@@ -396,7 +432,7 @@ template <int L, int D, bool DBG>
 __global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
   using T = Layout<L, D>;
   using ST = Step<L, D>;
-  constexpr int NB = (D == 128) ? 4 : 1;   // steps of 16-byte loads kept in flight per wave
+  constexpr int NB = (ST::SLOTS <= 5) ? 4 : (D == 128 ? 2 : 1);   // steps of 16-byte loads in flight per wave
   constexpr int NG = T::NG;
   constexpr int SG = T::SG;
   constexpr int NO = D / 128;
@@ -418,14 +454,15 @@ __global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
   const int t_begin = c * a.chunk;
   const int t_end = min(t_begin + a.chunk, Sq);
   const bool active = t_begin < Sq;             // wave-uniform
-  const size_t row_first = active ? plane_row(a, b, hk, t_begin) : 0;
+  const ChunkPages cp = chunk_pages(a, b, t_begin, t_end, lane, active);
+  const size_t row_first = active ? chunk_row(a, cp, b, hk, t_begin) : 0;
 
   // the first NB steps' loads go out before the query preparation
   u32x4 pre[NB][ST::SLOTS];
 #pragma unroll
   for (int k = 0; k < NB; ++k)
     if (active && t_begin + 32 * k < t_end)
-      issue_step<L, D>(a, half_rows(a, b, hk, t_begin + 32 * k, t_end, row_first), lane, pre[k]);
+      issue_step<L, D>(a, half_rows(a, cp, b, hk, t_begin + 32 * k, t_end, row_first), lane, pre[k]);
 
   // ---- prologue: query preparation for the GQA group of this kv head
   float* qf = reinterpret_cast<float*>(smem);
@@ -487,7 +524,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
       const int T = T0 + 32 * k;
       if (T >= t_end) break;
       stage_step<L, D>(buf, lane, pre[k]);
-      if (T + 32 * NB < t_end) issue_step<L, D>(a, half_rows(a, b, hk, T + 32 * NB, t_end, row_first), lane, pre[k]);
+      if (T + 32 * NB < t_end) issue_step<L, D>(a, half_rows(a, cp, b, hk, T + 32 * NB, t_end, row_first), lane, pre[k]);
       if (T + 32 <= t_end)
         decode_step<L, D, DBG, true>(a, buf, T, t_end, b, hk, G, col, r, qb, qsB, qoff, sqc, magic, m_run, l_run, oacc);
       else
