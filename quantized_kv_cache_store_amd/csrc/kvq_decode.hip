@@ -156,12 +156,14 @@ struct HalfRows {
   size_t r0, r1;
 };
 
-// Page entries of a wave's chunk, one per lane (lane l: logical page first_page + l), so that a
-// step's rows come from readlane on the scalar unit instead of a memory round trip.
+// Page entries of a wave's chunk held in registers (entry i in lane i % 64 of register i / 64), so
+// that a step's rows come from readlane on the scalar unit: the streaming loop then issues no
+// memory operation other than its own 16-byte loads, which keeps the load-counter waits exact.
+constexpr int kPageRegs = 4;   // up to 256 pages per chunk
+
 struct ChunkPages {
   int first_page;
-  int lane_page;     // physical page of logical page first_page + lane (or 0)
-  bool in_regs;      // the chunk spans at most 64 pages
+  int lane_page[kPageRegs];
 };
 
 __device__ __forceinline__ ChunkPages chunk_pages(const DecodeArgs& a, int b, int t_begin, int t_end, int lane,
@@ -169,23 +171,28 @@ __device__ __forceinline__ ChunkPages chunk_pages(const DecodeArgs& a, int b, in
   ChunkPages cp;
   cp.first_page = t_begin >> a.page_shift;
   const int npages = active ? ((t_end - 1) >> a.page_shift) - cp.first_page + 1 : 0;
-  cp.in_regs = npages <= 64;
-  cp.lane_page = (cp.in_regs && lane < npages) ? a.block_table[(size_t)b * a.max_pages + cp.first_page + lane] : 0;
+#pragma unroll
+  for (int i = 0; i < kPageRegs; ++i) {
+    const int e = lane + 64 * i;
+    cp.lane_page[i] = e < npages ? a.block_table[(size_t)b * a.max_pages + cp.first_page + e] : 0;
+  }
   return cp;
 }
 
-__device__ __forceinline__ size_t chunk_row(const DecodeArgs& a, const ChunkPages& cp, int b, int hk, int t) {
-  const int lp = t >> a.page_shift;
-  const int phys = cp.in_regs ? __builtin_amdgcn_readlane(cp.lane_page, lp - cp.first_page)
-                              : a.block_table[(size_t)b * a.max_pages + lp];
+__device__ __forceinline__ size_t chunk_row(const DecodeArgs& a, const ChunkPages& cp, int hk, int t) {
+  const int e = (t >> a.page_shift) - cp.first_page;     // wave-uniform
+  int phys = __builtin_amdgcn_readlane(cp.lane_page[0], e & 63);
+#pragma unroll
+  for (int i = 1; i < kPageRegs; ++i)
+    if ((e >> 6) == i) phys = __builtin_amdgcn_readlane(cp.lane_page[i], e & 63);
   return (((size_t)phys * a.Hkv + hk) << a.page_shift) + (size_t)(t & ((1 << a.page_shift) - 1));
 }
 
-__device__ __forceinline__ HalfRows half_rows(const DecodeArgs& a, const ChunkPages& cp, int b, int hk, int T, int t_end,
+__device__ __forceinline__ HalfRows half_rows(const DecodeArgs& a, const ChunkPages& cp, int hk, int T, int t_end,
                                               size_t row_first) {
   HalfRows h;
-  h.r0 = T < t_end ? chunk_row(a, cp, b, hk, T) : row_first;
-  h.r1 = T + 16 < t_end ? chunk_row(a, cp, b, hk, T + 16) : row_first;
+  h.r0 = T < t_end ? chunk_row(a, cp, hk, T) : row_first;
+  h.r1 = T + 16 < t_end ? chunk_row(a, cp, hk, T + 16) : row_first;
   return h;
 }
 
@@ -193,15 +200,16 @@ __device__ __forceinline__ HalfRows half_rows(const DecodeArgs& a, const ChunkPa
 // row ci / PB (half ci / PB), bytes 16 * (ci % PB); when PB is a multiple of 64 every slot lies in
 // one half, so its base address is wave-uniform and only lane * 16 varies.
 template <int L, int D>
-__device__ __forceinline__ void issue_step(const DecodeArgs& a, HalfRows hr, int lane, u32x4* pre) {
+__device__ __forceinline__ void issue_step(const DecodeArgs& a, HalfRows hr, int lane, u32x4* pre, bool dummy = false) {
   using ST = Step<L, D>;
   constexpr int PB = ST::PB, SB = ST::SB;
+  if (dummy) lane = 0;
 #pragma unroll
   for (int k = 0; k < ST::PAY_SLOTS; ++k) {
-    if (PB % 64 == 0) {
+    if (PB % 64 == 0 || dummy) {
       const int half = (64 * k) / PB;                     // compile-time
       const size_t row = half ? hr.r1 : hr.r0;
-      const size_t off = row * PB + (size_t)((64 * k) % PB) * 16 + (size_t)lane * 16;
+      const size_t off = dummy ? hr.r0 * PB : row * PB + (size_t)((64 * k) % PB) * 16 + (size_t)lane * 16;
       pre[k] = *reinterpret_cast<const u32x4*>(a.kp + off);
       pre[ST::PAY_SLOTS + k] = *reinterpret_cast<const u32x4*>(a.vp + off);
     } else {
@@ -216,7 +224,7 @@ __device__ __forceinline__ void issue_step(const DecodeArgs& a, HalfRows hr, int
   }
 #pragma unroll
   for (int k = 0; k < ST::REC_SLOTS; ++k) {
-    const int ci = lane + 64 * k;
+    const int ci = dummy ? 0 : lane + 64 * k;
     if (ci < 4 * SB) {
       const int cc = ci % (2 * SB);                 // chunk within the tensor's 32 records
       const size_t row = (cc >= SB) ? hr.r1 : hr.r0;
@@ -432,7 +440,7 @@ template <int L, int D, bool DBG>
 __global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
   using T = Layout<L, D>;
   using ST = Step<L, D>;
-  constexpr int NB = (ST::SLOTS <= 5) ? 4 : (D == 128 ? 2 : 1);   // steps of 16-byte loads in flight per wave
+  constexpr int NB = (ST::SLOTS <= 5) ? 5 : (D == 128 ? 3 : 2);   // ring slots: NB - 1 steps in flight while one is consumed
   constexpr int NG = T::NG;
   constexpr int SG = T::SG;
   constexpr int NO = D / 128;
@@ -455,23 +463,30 @@ __global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
   const int t_end = min(t_begin + a.chunk, Sq);
   const bool active = t_begin < Sq;             // wave-uniform
   const ChunkPages cp = chunk_pages(a, b, t_begin, t_end, lane, active);
-  const size_t row_first = active ? chunk_row(a, cp, b, hk, t_begin) : 0;
+  const size_t row_first = active ? chunk_row(a, cp, hk, t_begin) : 0;
+  const int nsteps = active ? (t_end - t_begin + 31) / 32 : 0;
 
-  // the first NB steps' loads go out before the query preparation
-  u32x4 pre[NB][ST::SLOTS];
+  // query rows of the GQA group into registers first (all loads in flight together, before the ring)
+  constexpr int QPT = 16 * D / 256;
+  float qv[QPT];
 #pragma unroll
-  for (int k = 0; k < NB; ++k)
-    if (active && t_begin + 32 * k < t_end)
-      issue_step<L, D>(a, half_rows(a, cp, b, hk, t_begin + 32 * k, t_end, row_first), lane, pre[k]);
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    const int row = idx / D;
+    qv[i] = a.q[((size_t)b * a.Hq + hk * G + min(row, G - 1)) * D + idx % D];
+  }
+
+  u32x4 pre[NB][ST::SLOTS];
 
   // ---- prologue: query preparation for the GQA group of this kv head
   float* qf = reinterpret_cast<float*>(smem);
   int8_t* q8 = reinterpret_cast<int8_t*>(qf + 16 * D);
   float* sqv = reinterpret_cast<float*>(q8 + 16 * D);
   int* qsum = reinterpret_cast<int*>(sqv + 16);
-  for (int idx = threadIdx.x; idx < 16 * D; idx += 256) {
-    const int row = idx / D;
-    qf[idx] = row < G ? a.q[((size_t)b * a.Hq + hk * G + row) * D + idx % D] : 0.0f;
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    qf[idx] = (idx / D) < G ? qv[i] : 0.0f;
   }
   __syncthreads();
   prepare_query_lds<L, D>(qf, q8, sqv, qsum);
@@ -518,17 +533,26 @@ __global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
 
   uint32_t magic;   // fp16 "1024 + code" exponent bits, kept in a VGPR so v_and_or_b32 can take it
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
-  for (int T0 = t_begin; T0 < t_end; T0 += 32 * NB) {
+  // Software pipeline over a ring of NB register slots, all loads issued inside the loop (nothing is
+  // in flight at entry, so the compiler's load-counter waits stay exact): iteration i issues step i
+  // into slot i % NB and consumes step i - (NB - 1) from slot (i + 1) % NB.  Issues past the last
+  // step read a few bytes of the chunk's first rows (cache hits) so every iteration issues the same
+  // loads.
+  for (int k0 = 0; k0 < nsteps + NB - 1; k0 += NB) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const int T = T0 + 32 * k;
-      if (T >= t_end) break;
-      stage_step<L, D>(buf, lane, pre[k]);
-      if (T + 32 * NB < t_end) issue_step<L, D>(a, half_rows(a, cp, b, hk, T + 32 * NB, t_end, row_first), lane, pre[k]);
-      if (T + 32 <= t_end)
-        decode_step<L, D, DBG, true>(a, buf, T, t_end, b, hk, G, col, r, qb, qsB, qoff, sqc, magic, m_run, l_run, oacc);
-      else
-        decode_step<L, D, DBG, false>(a, buf, T, t_end, b, hk, G, col, r, qb, qsB, qoff, sqc, magic, m_run, l_run, oacc);
+      const int si = k0 + k;
+      const int Ti = t_begin + 32 * si;
+      issue_step<L, D>(a, half_rows(a, cp, hk, Ti, t_end, row_first), lane, pre[k], si >= nsteps);
+      const int su = si - (NB - 1);
+      if (su >= 0 && su < nsteps) {
+        const int T = t_begin + 32 * su;
+        stage_step<L, D>(buf, lane, pre[(k + 1) % NB]);
+        if (T + 32 <= t_end)
+          decode_step<L, D, DBG, true>(a, buf, T, t_end, b, hk, G, col, r, qb, qsB, qoff, sqc, magic, m_run, l_run, oacc);
+        else
+          decode_step<L, D, DBG, false>(a, buf, T, t_end, b, hk, G, col, r, qb, qsB, qoff, sqc, magic, m_run, l_run, oacc);
+      }
     }
   }
   if (DBG) return;
@@ -702,6 +726,8 @@ extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float*
   kvq_status st = check_attend_args(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len);
   if (st != KVQ_OK) return st;
   if (chunk < 128 || chunk % 128) return fail(KVQ_ERR_INVALID_ARG, "chunk_tokens must be a positive multiple of 128");
+  if ((chunk + c->page_size - 1) / c->page_size + 1 > 64 * kPageRegs)
+    return fail(KVQ_ERR_UNSUPPORTED, "a chunk may span at most %d pages", 64 * kPageRegs - 1);
   const size_t need = kvq_decode_workspace_bytes(batch, Hq, c->head_dim, max_seq_len, chunk);
   if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
   DecodeArgs a;

@@ -106,8 +106,15 @@ def test_decode_gqa_16_and_t3_values(G):
 @pytest.mark.parametrize("chunk", [128, 256, 1024, 4096])
 def test_decode_chunk_sweep(chunk):
     U.need_gpu()
-    got, ref, _ = _run_case(spec.Q4_0, 128, Hkv=2, G=4, lens=[3000, 700], chunk=chunk, seed=chunk)
+    ps = 32 if chunk > 2048 else 16      # a chunk may span at most 255 pages
+    got, ref, _ = _run_case(spec.Q4_0, 128, Hkv=2, G=4, lens=[3000, 700], chunk=chunk, page_size=ps, seed=chunk)
     U.assert_close_rel(got, ref)
+
+
+def test_decode_rejects_chunk_spanning_too_many_pages():
+    U.need_gpu()
+    with pytest.raises(kvq.KvqError, match="at most 255 pages"):
+        _run_case(spec.Q4_0, 128, Hkv=1, G=1, lens=[300], chunk=4096, page_size=16)
 
 
 def test_decode_deterministic():
