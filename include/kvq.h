@@ -135,7 +135,7 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t he
  *                the newest min(seq_len, n_recent) are read from the window
  *   max_seq_len  host bound on seq_len (sizes the grid)
  *   chunk_tokens split-K chunk, a multiple of 128
- * num_q_heads / num_kv_heads must be an integer in [1, 16].  A row with
+ * num_q_heads must be a multiple of num_kv_heads.  A row with
  * seq_len 0 gets zeros.  alpha is the score scale (1/sqrt(d), or 1.0 for
  * RMS-normalised Q/K, [Open-TQ-Metal] Section 4). */
 kvq_status kvq_attend_decode(const kvq_cache* cache, const float* q, float* out,
@@ -162,7 +162,9 @@ kvq_status kvq_attend_decode_reduce(const kvq_cache* cache, float* out, int32_t 
                                     int32_t chunk_tokens, const void* workspace, size_t workspace_bytes,
                                     void* stream);
 
-/* Workspace of kvq_attend_prefill_causal (0 in this version; pass NULL). */
+/* Workspace of kvq_attend_prefill_causal: split-K partials (o_c, m_c, l_c)
+ * per (batch, query, query head, 512-token chunk), plus the window partial.
+ * Returns 0 for invalid arguments. */
 size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t num_q_heads,
                                    int32_t head_dim, int32_t max_seq_len);
 
@@ -172,10 +174,21 @@ size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t num_q_hea
  * skip is bit-identical to compute-then-mask).  Query i of row b sits at
  * position q_start[b] + i and, when causal != 0, sees tokens t <= q_start[b] + i;
  * KV tiles wholly past the limit are skipped unless flags has
- * KVQ_PREFILL_NO_CAUSAL_SKIP.  The window is the last n_recent positions of
- * the row, the same for every query.
- *   q    device f32 [batch][n_q][num_q_heads][head_dim]
- *   out  device f32 [batch][n_q][num_q_heads][head_dim] */
+ * KVQ_PREFILL_NO_CAUSAL_SKIP (same bits, masked tiles streamed).  The window
+ * is the last n_recent positions of the row, the same for every query, masked
+ * per query like the packed tokens.  Scores, scales and the HAD_INT4 rotation
+ * are those of kvq_attend_decode; a query whose limit covers the whole row
+ * gets the decode output exactly.
+ *   q          device f32 [batch][n_q][num_q_heads][head_dim]
+ *   out        device f32 [batch][n_q][num_q_heads][head_dim]
+ *   causal     0 or 1; with 0 every query sees all seq_len[b] tokens
+ *   q_start    device int32 [batch] (may be NULL when causal == 0); the limits
+ *              are meaningful for q_start[b] + n_q <= seq_len[b]; a query
+ *              that sees no token gets zeros
+ *   workspace  at least kvq_prefill_workspace_bytes(...) bytes of device memory
+ * Other arguments as for kvq_attend_decode.  Errors: KVQ_ERR_INVALID_ARG for
+ * null pointers, n_q < 1, causal not 0/1 or unknown flags;
+ * KVQ_ERR_WORKSPACE when the workspace is too small; nothing is launched then. */
 kvq_status kvq_attend_prefill_causal(const kvq_cache* cache, const float* q, float* out,
                                      int32_t batch, int32_t n_q, int32_t num_q_heads,
                                      float alpha, int32_t causal, const int32_t* q_start,

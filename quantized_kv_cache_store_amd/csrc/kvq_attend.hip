@@ -1,5 +1,6 @@
-// Fused compressed-domain decode attention: split-K partial kernel, f32 window
-// partial, and the online-softmax reduce.
+// Fused compressed-domain attention over the packed cache: the split-K partial
+// kernel (decode and causal prefill), the f32 window partial, and the
+// online-softmax reduce.
 //
 // [Open-TQ-Metal] Algorithm 1 (fused single pass over the packed cache, no
 // dequantised S x d temporary) and the split-K paragraphs (chunks in parallel,
@@ -7,22 +8,34 @@
 // integer dot int8(Q) . code(K) per 32-element block with the scales applied
 // outside the reduction ([tract-RFC] Architecture > Data flow (decode)).
 //
+// Rows.  The kernels work on "rows": one query vector of one query head.  A
+// batch entry with n_q queries has n_q * G rows per kv head (G = GQA group),
+// row R = i * G + g for query i and head hk * G + g.  Decode is n_q = 1, so a kv
+// head's rows are its G heads; causal prefill ([tract-RFC] Architecture,
+// prefill) gives row R the limit q_start + i: it sees tokens t <= that limit.
+// Sixteen consecutive rows form a tile, which is the N side of the MFMAs.
+//
 // gfx950 mapping.  One block of four waves handles one (batch row, kv head,
-// chunk); each wave takes 32-token steps of the chunk.  For a step:
+// row tile, four consecutive chunks); each wave takes 32-token steps of its
+// chunk.  For a step:
 //   * Q K^T runs on v_mfma_i32_16x16x32_i8: A = 16 tokens x 32 codes of one
-//     block (unpacked nibbles, one dword per lane), B = the int8 query of up to
-//     16 heads of the kv head's GQA group (kept in registers for the block).
-//     The i32 result per (token, head, block) is scaled by the block's scale.
+//     block (unpacked nibbles, one dword per lane), B = the int8 query of the
+//     tile's 16 rows (kept in registers for the block).  The i32 result per
+//     (token, row, block) is scaled by the block's scale.
 //   * P V runs on v_mfma_f32_16x16x32_f16 with the output transposed,
-//     C[d][head] += V^T[d][t] P^T[t][head]: the P^T operand is exactly the
-//     softmax numerators the lane already holds from Q K^T (lane = head,
+//     C[d][row] += V^T[d][t] P^T[t][row]: the P^T operand is exactly the
+//     softmax numerators the lane already holds from Q K^T (lane = row,
 //     k-slots = its 8 tokens), so no shuffle is needed; the V^T operand is
 //     built from the packed dwords of the same 8 tokens, nibble p of dword c
 //     giving row d = 8c + p (fp16 "1024 + code" then an exact offset and the
 //     block scale).
-//   * the online softmax keeps m and l per head in the lanes that own the
-//     head's column, so the rescale of the accumulators is lane-local.
-// The four waves merge their (m, l, o) in LDS in a fixed order (deterministic).
+//   * the online softmax keeps m and l per row in the lanes that own the
+//     row's column, so the rescale of the accumulators is lane-local.
+// Causal skip ([tract-RFC] Causality & mixed precision): a wave stops at the
+// last token any row of its tile can see, and a chunk wholly past every
+// limit streams nothing and emits the empty partial (m = -inf, l = 0, o = 0).
+// Steps that are partly visible mask per row.  With the skip off, the masked
+// tokens are streamed and contribute exact zeros, so both give the same bits.
 
 #include "kvq_internal.h"
 
@@ -36,7 +49,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 #define KVQ_LOG2E 1.4426950408889634f
 
-struct DecodeArgs {
+struct AttendArgs {
   const uint8_t* kp;
   const uint8_t* vp;
   const uint8_t* ks;
@@ -47,10 +60,28 @@ struct DecodeArgs {
   float* ws;
   const int32_t* block_table;
   const int32_t* seq_len;
+  const int32_t* q_start;   // [batch] position of query 0 (causal prefill), else null
   int32_t* dbg;
   int Hkv, Hq, G, page_shift, n_recent, max_pages, chunk, nc1, max_seq_len;
+  int n_q;       // queries per batch row (1 for decode)
+  int ngroups;   // blocks per row tile along the sequence: chunk groups of four, + 1 for the window
+  int causal;    // rows see t <= q_start + i
+  int skip;      // causal skip: stop streaming past the tile's last visible token
   float alpha;
 };
+
+// Row R of (b, hk) is query i = R / G of head hk * G + R % G; its flat index in
+// [batch][n_q][Hq] addresses q, out and (times the chunk count) the partials.
+__device__ __forceinline__ size_t row_index(const AttendArgs& a, int b, int hk, int R) {
+  const int i = R / a.G;
+  return ((size_t)b * a.n_q + i) * a.Hq + hk * a.G + (R - i * a.G);
+}
+
+// Last visible position of row R (rows past the tile's valid count see nothing).
+__device__ __forceinline__ int row_limit(const AttendArgs& a, int qs0, int R, int nrows) {
+  if (R >= nrows) return -1;
+  return a.causal ? qs0 + R / a.G : 0x7fffffff;
+}
 
 template <int D>
 __host__ __device__ constexpr int prologue_lds_bytes() {
@@ -61,7 +92,7 @@ __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uin
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
 // Physical row of logical token t of (batch b, kv head hk) in the planes.
-__device__ __forceinline__ size_t plane_row(const DecodeArgs& a, int b, int hk, int t) {
+__device__ __forceinline__ size_t plane_row(const AttendArgs& a, int b, int hk, int t) {
   const int phys = a.block_table[(size_t)b * a.max_pages + (t >> a.page_shift)];
   return (((size_t)phys * a.Hkv + hk) << a.page_shift) + (size_t)(t & ((1 << a.page_shift) - 1));
 }
@@ -76,19 +107,21 @@ __device__ __forceinline__ void q6_octet(uint32_t lo, uint32_t hi16, uint32_t& e
   od = (((lo >> 4) & 0x0F0F0F0Fu) | to) ^ 0x20202020u;
 }
 
-// Window partial: exact f32 rows of the newest tokens (HAD: rotated basis).
+// Window partial: exact f32 rows of the newest tokens (HAD: rotated basis), for
+// the rows row0 .. row0 + nvalid - 1 of (b, hk), each masked by its limit.
 template <int L, int D>
-__device__ void window_partial(const DecodeArgs& a, unsigned char* smem, int b, int hk, int S) {
+__device__ __noinline__ void window_partial(const AttendArgs a, unsigned char* smem, int b, int hk, int S, int row0, int nvalid,
+                               int qs0) {
   float* qf = reinterpret_cast<float*>(smem);
   int8_t* q8 = reinterpret_cast<int8_t*>(qf + 16 * D);
   float* sq = reinterpret_cast<float*>(q8 + 16 * D);
   int* qsum = reinterpret_cast<int*>(sq + 16);
-  float* sc = reinterpret_cast<float*>(smem + prologue_lds_bytes<D>());   // [G][W]
+  float* sc = reinterpret_cast<float*>(smem + prologue_lds_bytes<D>());   // [16][W]
   const int tid = threadIdx.x;
-  const int G = a.G;
+  const int nrows = a.n_q * a.G;
   for (int idx = tid; idx < 16 * D; idx += 256) {
     const int row = idx / D;
-    qf[idx] = row < G ? a.q[((size_t)b * a.Hq + hk * G + row) * D + idx % D] : 0.0f;
+    qf[idx] = row < nvalid ? a.q[row_index(a, b, hk, row0 + row) * D + idx % D] : 0.0f;
   }
   __syncthreads();
   prepare_query_lds<L, D>(qf, q8, sq, qsum);
@@ -96,7 +129,7 @@ __device__ void window_partial(const DecodeArgs& a, unsigned char* smem, int b, 
   const int w0 = S - W;
   const size_t ring0 = ((size_t)b * a.Hkv + hk) * a.n_recent;
   const float cl = a.alpha * KVQ_LOG2E;
-  for (int idx = tid; idx < G * W; idx += 256) {
+  for (int idx = tid; idx < nvalid * W; idx += 256) {
     const int h = idx / W, tt = idx % W;
     const float* kr = a.kring + (ring0 + (w0 + tt) % a.n_recent) * D;
     const float* qh = qf + h * D;
@@ -105,17 +138,18 @@ __device__ void window_partial(const DecodeArgs& a, unsigned char* smem, int b, 
       const float4 k4 = *reinterpret_cast<const float4*>(kr + d);
       acc += qh[d] * k4.x + qh[d + 1] * k4.y + qh[d + 2] * k4.z + qh[d + 3] * k4.w;
     }
-    sc[idx] = acc * cl;
+    sc[idx] = w0 + tt <= row_limit(a, qs0, row0 + h, nrows) ? acc * cl : -INFINITY;
   }
   __syncthreads();
   float* mrow = sc + 16 * W;
   float* lrow = mrow + 16;
-  if (tid < G) {
+  if (tid < nvalid) {
     float m = -INFINITY;
     for (int tt = 0; tt < W; ++tt) m = fmaxf(m, sc[tid * W + tt]);
+    const float m_use = m == -INFINITY ? 0.0f : m;   // a row that sees no window token: p = 0, l = 0
     float l = 0.0f;
     for (int tt = 0; tt < W; ++tt) {
-      const float p = exp2f(sc[tid * W + tt] - m);
+      const float p = exp2f(sc[tid * W + tt] - m_use);
       sc[tid * W + tt] = p;
       l += p;
     }
@@ -124,11 +158,11 @@ __device__ void window_partial(const DecodeArgs& a, unsigned char* smem, int b, 
   }
   __syncthreads();
   const int PST = partial_stride(D);
-  for (int idx = tid; idx < G * D; idx += 256) {
+  for (int idx = tid; idx < nvalid * D; idx += 256) {
     const int h = idx / D, d = idx % D;
     float o = 0.0f;
     for (int tt = 0; tt < W; ++tt) o += sc[h * W + tt] * a.vring[(ring0 + (w0 + tt) % a.n_recent) * D + d];
-    float* dst = a.ws + (((size_t)b * a.Hq + hk * G + h) * a.nc1 + (a.nc1 - 1)) * PST;
+    float* dst = a.ws + (row_index(a, b, hk, row0 + h) * a.nc1 + (a.nc1 - 1)) * PST;
     dst[d] = o;
     if (d == 0) {
       dst[D] = mrow[h];
@@ -166,7 +200,7 @@ struct ChunkPages {
   int lane_page[kPageRegs];
 };
 
-__device__ __forceinline__ ChunkPages chunk_pages(const DecodeArgs& a, int b, int t_begin, int t_end, int lane,
+__device__ __forceinline__ ChunkPages chunk_pages(const AttendArgs& a, int b, int t_begin, int t_end, int lane,
                                                   bool active) {
   ChunkPages cp;
   cp.first_page = t_begin >> a.page_shift;
@@ -179,7 +213,7 @@ __device__ __forceinline__ ChunkPages chunk_pages(const DecodeArgs& a, int b, in
   return cp;
 }
 
-__device__ __forceinline__ size_t chunk_row(const DecodeArgs& a, const ChunkPages& cp, int hk, int t) {
+__device__ __forceinline__ size_t chunk_row(const AttendArgs& a, const ChunkPages& cp, int hk, int t) {
   const int e = (t >> a.page_shift) - cp.first_page;     // wave-uniform
   int phys = __builtin_amdgcn_readlane(cp.lane_page[0], e & 63);
 #pragma unroll
@@ -188,7 +222,7 @@ __device__ __forceinline__ size_t chunk_row(const DecodeArgs& a, const ChunkPage
   return (((size_t)phys * a.Hkv + hk) << a.page_shift) + (size_t)(t & ((1 << a.page_shift) - 1));
 }
 
-__device__ __forceinline__ HalfRows half_rows(const DecodeArgs& a, const ChunkPages& cp, int hk, int T, int t_end,
+__device__ __forceinline__ HalfRows half_rows(const AttendArgs& a, const ChunkPages& cp, int hk, int T, int t_end,
                                               size_t row_first) {
   HalfRows h;
   h.r0 = T < t_end ? chunk_row(a, cp, hk, T) : row_first;
@@ -200,7 +234,7 @@ __device__ __forceinline__ HalfRows half_rows(const DecodeArgs& a, const ChunkPa
 // row ci / PB (half ci / PB), bytes 16 * (ci % PB); when PB is a multiple of 64 every slot lies in
 // one half, so its base address is wave-uniform and only lane * 16 varies.
 template <int L, int D>
-__device__ __forceinline__ void issue_step(const DecodeArgs& a, HalfRows hr, int lane, u32x4* pre, bool dummy = false) {
+__device__ __forceinline__ void issue_step(const AttendArgs& a, HalfRows hr, int lane, u32x4* pre, bool dummy = false) {
   using ST = Step<L, D>;
   constexpr int PB = ST::PB, SB = ST::SB;
   if (dummy) lane = 0;
@@ -264,12 +298,15 @@ __device__ __forceinline__ uint32_t rec_word(const unsigned char* rec, int idx) 
 }
 
 // One 32-token step of a wave: Q K^T, online softmax, P V, all from the staged rows in `buf`.
-// FULL: every token of the step is inside the chunk (no masking needed).
+// FULL: every token of the step is inside the chunk and visible to every row (no masking).
+// Otherwise tokens at or past t_end are dropped (their staged rows may hold anything, so their
+// scales are zeroed too) and tokens past `lim`, the limit of this lane's row, get p = 0.
+// drow: flat row index of this lane's row for the score export (DBG), or -1.
 template <int L, int D, bool DBG, bool FULL>
-__device__ __forceinline__ void decode_step(const DecodeArgs& a, const unsigned char* buf, int T0, int t_end, int b,
-                                            int hk, int G, int col, int r, const uint32_t (*qb)[2], const float* qsB,
-                                            const int* qoff, float sqc, uint32_t magic, float& m_run, float& l_run,
-                                            v4f* oacc) {
+__device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned char* buf, int T0, int t_end,
+                                            int lim, long drow, int col, int r, const uint32_t (*qb)[2],
+                                            const float* qsB, const int* qoff, float sqc, uint32_t magic,
+                                            float& m_run, float& l_run, v4f* oacc) {
   using T = Layout<L, D>;
   using ST = Step<L, D>;
   constexpr int NG = T::NG;
@@ -320,12 +357,13 @@ __device__ __forceinline__ void decode_step(const DecodeArgs& a, const unsigned 
     for (int j = 0; j < 4; ++j) {
       const int tl = 16 * tau + 4 * r + j;       // token within the step
       const bool ok = FULL || T0 + tl < t_end;
+      const bool vis = FULL || (ok && T0 + tl <= lim);
       const unsigned char* rec = buf + ST::KR + tl * SB;
       float x;
       if (L == HAD) {
         const int I = acc[0][j] - qoff[0];
         x = *reinterpret_cast<const float*>(rec) * (float)I;
-        if (DBG && ok && col < G) a.dbg[(((size_t)b * a.Hq + hk * G + col) * a.max_seq_len + T0 + tl)] = I;
+        if (DBG && ok && drow >= 0) a.dbg[(size_t)drow * a.max_seq_len + T0 + tl] = I;
         const float vsc = *reinterpret_cast<const float*>(buf + ST::VR + tl * SB);
         vs_had[tau * 4 + j] = ok ? vsc : 0.0f;
       } else {
@@ -336,11 +374,11 @@ __device__ __forceinline__ void decode_step(const DecodeArgs& a, const unsigned 
           const uint32_t w = rec_word(rec, (L == ASYM) ? g : (g >> 1));
           const float s = (float)as_h2(w)[(L == ASYM) ? 0 : (g & 1)];
           x = fmaf(s, (float)acc[g][j], x);
-          if (DBG && ok && col < G)
-            a.dbg[(((size_t)b * a.Hq + hk * G + col) * a.max_seq_len + T0 + tl) * SG + g] = acc[g][j] - qoff[g];
+          if (DBG && ok && drow >= 0)
+            a.dbg[((size_t)drow * a.max_seq_len + T0 + tl) * SG + g] = acc[g][j] - qoff[g];
         }
       }
-      xs[tau * 4 + j] = ok ? x * sqc : -INFINITY;
+      xs[tau * 4 + j] = vis ? x * sqc : -INFINITY;
     }
   }
   if (DBG) return;
@@ -434,10 +472,12 @@ __device__ __forceinline__ void decode_step(const DecodeArgs& a, const unsigned 
 }
 
 // Split-K partial kernel.  Block = four waves = four consecutive chunks of one (batch row,
-// kv head); each wave streams its chunk in 32-token steps with two steps of loads in flight
-// and writes the chunk's partial (o unnormalised, m in base-2 logits, l).
+// kv head, row tile); each wave streams its chunk in 32-token steps with NB - 1 steps of loads
+// in flight and writes the chunk's partial per row (o unnormalised, m in base-2 logits, l).
+// Grid: x = row tile * ngroups + chunk group (the last group is the window when n_recent > 0),
+// y = kv head, z = batch row.
 template <int L, int D, bool DBG>
-__global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void attend_partial(AttendArgs a) {
   using T = Layout<L, D>;
   using ST = Step<L, D>;
   constexpr int NB = (ST::SLOTS <= 5) ? 5 : (D == 128 ? 3 : 2);   // ring slots: NB - 1 steps in flight while one is consumed
@@ -448,37 +488,46 @@ __global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int hk = blockIdx.y, b = blockIdx.z;
+  const int tile = (int)blockIdx.x / a.ngroups;
+  const int cg = (int)blockIdx.x - tile * a.ngroups;
   const int S = a.seq_len[b];
-  const int Sq = a.n_recent > 0 ? max(0, S - a.n_recent) : S;
-  if (!DBG && a.n_recent > 0 && (int)blockIdx.x == (int)gridDim.x - 1) {
-    if (S > 0) window_partial<L, D>(a, smem, b, hk, S);
+  const int Sq = a.n_recent > 0 ? max(0, S - a.n_recent) : S;   // quantised tokens
+  const int nrows = a.n_q * a.G;
+  const int row0 = 16 * tile;
+  const int nvalid = min(16, nrows - row0);
+  const int qs0 = a.causal ? a.q_start[b] : 0;
+  if (!DBG && a.n_recent > 0 && cg == a.ngroups - 1) {
+    if (S > 0) window_partial<L, D>(a, smem, b, hk, S, row0, nvalid, qs0);
     return;
   }
-  if ((int)blockIdx.x * 4 * a.chunk >= Sq) return;
-  const int G = a.G;
+  if (cg * 4 * a.chunk >= Sq) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = blockIdx.x * 4 + wave;          // this wave's chunk
+  const int c = cg * 4 + wave;                  // this wave's chunk
   const int t_begin = c * a.chunk;
-  const int t_end = min(t_begin + a.chunk, Sq);
-  const bool active = t_begin < Sq;             // wave-uniform
+  const int lim_min = row_limit(a, qs0, row0, nrows);               // first row of the tile
+  const int lim_max = row_limit(a, qs0, row0 + nvalid - 1, nrows);  // last row: the tile's farthest limit
+  int t_end = min(t_begin + a.chunk, Sq);
+  if (a.skip && lim_max < t_end - 1) t_end = max(t_begin, lim_max + 1);   // causal skip
+  const bool has_chunk = t_begin < Sq;          // the reduce reads this chunk's partial (wave-uniform)
+  const bool active = t_begin < t_end;          // tokens to stream
   const ChunkPages cp = chunk_pages(a, b, t_begin, t_end, lane, active);
   const size_t row_first = active ? chunk_row(a, cp, hk, t_begin) : 0;
   const int nsteps = active ? (t_end - t_begin + 31) / 32 : 0;
 
-  // query rows of the GQA group into registers first (all loads in flight together, before the ring)
+  // query rows of the tile into registers first (all loads in flight together, before the ring)
   constexpr int QPT = 16 * D / 256;
   float qv[QPT];
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int idx = threadIdx.x + 256 * i;
     const int row = idx / D;
-    qv[i] = a.q[((size_t)b * a.Hq + hk * G + min(row, G - 1)) * D + idx % D];
+    qv[i] = a.q[row_index(a, b, hk, row0 + min(row, nvalid - 1)) * D + idx % D];
   }
 
   u32x4 pre[NB][ST::SLOTS];
 
-  // ---- prologue: query preparation for the GQA group of this kv head
+  // ---- prologue: query preparation for the rows of the tile
   float* qf = reinterpret_cast<float*>(smem);
   int8_t* q8 = reinterpret_cast<int8_t*>(qf + 16 * D);
   float* sqv = reinterpret_cast<float*>(q8 + 16 * D);
@@ -486,7 +535,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int idx = threadIdx.x + 256 * i;
-    qf[idx] = (idx / D) < G ? qv[i] : 0.0f;
+    qf[idx] = (idx / D) < nvalid ? qv[i] : 0.0f;
   }
   __syncthreads();
   prepare_query_lds<L, D>(qf, q8, sqv, qsum);
@@ -522,8 +571,10 @@ __global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
     qoff[g] = BIAS * sum;
   }
   const float sqc = sqv[col] * a.alpha * KVQ_LOG2E;
+  const int lim = row_limit(a, qs0, row0 + col, nrows);
+  const long drow = (DBG && col < nvalid) ? (long)row_index(a, b, hk, row0 + col) : -1;   // score export only
   __syncthreads();   // the LDS becomes the waves' step buffers
-  if (!active) return;
+  if (!has_chunk) return;
 
   unsigned char* buf = smem + wave * ST::BYTES;
   float m_run = -INFINITY, l_run = 0.0f;
@@ -538,7 +589,8 @@ __global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
   // into slot i % NB and consumes step i - (NB - 1) from slot (i + 1) % NB.  Issues past the last
   // step read a few bytes of the chunk's first rows (cache hits) so every iteration issues the same
   // loads.
-  for (int k0 = 0; k0 < nsteps + NB - 1; k0 += NB) {
+  const int kend = nsteps > 0 ? nsteps + NB - 1 : 0;
+  for (int k0 = 0; k0 < kend; k0 += NB) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       const int si = k0 + k;
@@ -548,10 +600,10 @@ __global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
       if (su >= 0 && su < nsteps) {
         const int T = t_begin + 32 * su;
         stage_step<L, D>(buf, lane, pre[(k + 1) % NB]);
-        if (T + 32 <= t_end)
-          decode_step<L, D, DBG, true>(a, buf, T, t_end, b, hk, G, col, r, qb, qsB, qoff, sqc, magic, m_run, l_run, oacc);
+        if (T + 32 <= t_end && T + 31 <= lim_min)
+          attend_step<L, D, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qb, qsB, qoff, sqc, magic, m_run, l_run, oacc);
         else
-          decode_step<L, D, DBG, false>(a, buf, T, t_end, b, hk, G, col, r, qb, qsB, qoff, sqc, magic, m_run, l_run, oacc);
+          attend_step<L, D, DBG, false>(a, buf, T, t_end, lim, drow, col, r, qb, qsB, qoff, sqc, magic, m_run, l_run, oacc);
       }
     }
   }
@@ -560,8 +612,8 @@ __global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
   // ---------------- this wave's chunk partial
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  if (col < G) {
-    float* dst = a.ws + (((size_t)b * a.Hq + hk * G + col) * a.nc1 + c) * partial_stride(D);
+  if (col < nvalid) {
+    float* dst = a.ws + (row_index(a, b, hk, row0 + col) * a.nc1 + c) * partial_stride(D);
 #pragma unroll
     for (int o = 0; o < NO; ++o)
 #pragma unroll
@@ -575,23 +627,25 @@ __global__ __launch_bounds__(256, 2) void decode_partial(DecodeArgs a) {
   }
 }
 
-// Online-softmax merge of the chunk partials; Hadamard layout: rotate back.
-// Four waves split the chunks; each lane owns D/64 output elements.
+// Online-softmax merge of the chunk partials of one row (block x = flat row index
+// (b * n_q + i) * Hq + h); Hadamard layout: rotate back.  Four waves split the
+// chunks; each lane owns D/64 output elements.
 template <int D, bool ROT>
-__global__ __launch_bounds__(256) void decode_reduce(const float* ws, float* out, const int32_t* seq_len,
-                                                     int Hq, int nc1, int chunk, int n_recent) {
+__global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out, const int32_t* seq_len,
+                                                     int rows_per_b, int nc1, int chunk, int n_recent) {
   constexpr int E = D / 64;
   __shared__ float red_o[4][D];
   __shared__ float red_m[4], red_l[4];
   __shared__ float x[D];
-  const int h = blockIdx.x, b = blockIdx.y;
+  const size_t row = blockIdx.x;
+  const int b = (int)(row / (size_t)rows_per_b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = seq_len[b];
   const int Sq = n_recent > 0 ? max(0, S - n_recent) : S;
   const int nq = (Sq + chunk - 1) / chunk;
   const int cnt = nq + ((n_recent > 0 && S > 0) ? 1 : 0);
   const int PST = partial_stride(D);
-  const float* base = ws + ((size_t)b * Hq + h) * nc1 * PST;
+  const float* base = ws + row * nc1 * PST;
   float M = -INFINITY;
   for (int i = tid; i < cnt; i += 256) M = fmaxf(M, base[(size_t)(i < nq ? i : nc1 - 1) * PST + D]);
   for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
@@ -638,17 +692,17 @@ __global__ __launch_bounds__(256) void decode_reduce(const float* ws, float* out
       __syncthreads();
     }
   }
-  if (tid < D) out[((size_t)b * Hq + h) * D + tid] = ROT ? x[tid] * hadamard_norm<D>() : x[tid];
+  if (tid < D) out[row * D + tid] = ROT ? x[tid] * hadamard_norm<D>() : x[tid];
 }
 
 template <int L, int D, bool DBG>
-static void launch_partial(const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+static void launch_partial(const AttendArgs& a, dim3 grid, size_t lds, hipStream_t st) {
   if (lds > 65536)
-    (void)hipFuncSetAttribute((const void*)decode_partial<L, D, DBG>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((decode_partial<L, D, DBG>), grid, dim3(256), lds, st, a);
+    (void)hipFuncSetAttribute((const void*)attend_partial<L, D, DBG>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((attend_partial<L, D, DBG>), grid, dim3(256), lds, st, a);
 }
 
-typedef void (*partial_fn)(const DecodeArgs&, dim3, size_t, hipStream_t);
+typedef void (*partial_fn)(const AttendArgs&, dim3, size_t, hipStream_t);
 
 template <bool DBG>
 static partial_fn pick_partial(int layout, int D) {
@@ -666,16 +720,18 @@ static size_t step_bytes(int layout, int D) {
   return 64 * (payload_bytes_rt(layout, D) + scale_bytes_rt(layout, D));
 }
 
-static size_t partial_lds_bytes(int layout, int D, int G, int n_recent) {
+static size_t partial_lds_bytes(int layout, int D, int n_recent) {
   const size_t pro = (size_t)16 * D * 4 + 16 * D + 16 * 4 + 16 * (D / 32) * 4;
   const size_t steps = 4 * step_bytes(layout, D);
-  (void)G;
   const size_t win = n_recent > 0 ? pro + (size_t)16 * n_recent * 4 + 32 * 4 : 0;
   size_t m = pro > steps ? pro : steps;
   return m > win ? m : win;
 }
 
 static int chunks_of(int max_seq_len, int chunk) { return (max_seq_len + chunk - 1) / chunk; }
+
+// Split-K chunk of the causal prefill (a multiple of 128, like the decode chunk).
+constexpr int kPrefillChunk = 512;
 
 static kvq_status check_attend_args(const kvq_cache* c, const void* q, int32_t batch, int32_t Hq,
                                     const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
@@ -685,12 +741,69 @@ static kvq_status check_attend_args(const kvq_cache* c, const void* q, int32_t b
   if (!q || !block_table || !seq_len) return fail(KVQ_ERR_INVALID_ARG, "q, block_table and seq_len must be non-null");
   if (batch < 1) return fail(KVQ_ERR_INVALID_ARG, "batch must be >= 1");
   if (Hq < 1 || Hq % c->num_kv_heads) return fail(KVQ_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
-  if (Hq / c->num_kv_heads > 16) return fail(KVQ_ERR_UNSUPPORTED, "GQA group larger than 16 heads");
   if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len must be >= 0");
   if (max_pages < 1 || (int64_t)max_pages * c->page_size < max_seq_len)
     return fail(KVQ_ERR_INVALID_ARG, "max_pages_per_seq * page_size must cover max_seq_len");
   if (c->n_recent > 512) return fail(KVQ_ERR_UNSUPPORTED, "n_recent above 512");
   return KVQ_OK;
+}
+
+static kvq_status check_chunk(const kvq_cache* c, int32_t chunk) {
+  if (chunk < 128 || chunk % 128) return fail(KVQ_ERR_INVALID_ARG, "chunk_tokens must be a positive multiple of 128");
+  if ((chunk + c->page_size - 1) / c->page_size + 1 > 64 * kPageRegs)
+    return fail(KVQ_ERR_UNSUPPORTED, "a chunk may span at most %d pages", 64 * kPageRegs - 1);
+  return KVQ_OK;
+}
+
+static AttendArgs make_args(const kvq_cache* c, const float* q, int32_t Hq, int32_t n_q, float alpha,
+                            const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
+                            int32_t max_seq_len, int32_t chunk, void* workspace) {
+  AttendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.kp = (const uint8_t*)c->k_payload;
+  a.vp = (const uint8_t*)c->v_payload;
+  a.ks = (const uint8_t*)c->k_scale;
+  a.vs = (const uint8_t*)c->v_scale;
+  a.kring = c->k_recent;
+  a.vring = c->v_recent;
+  a.q = q;
+  a.ws = (float*)workspace;
+  a.block_table = block_table;
+  a.seq_len = seq_len;
+  a.Hkv = c->num_kv_heads;
+  a.Hq = Hq;
+  a.G = Hq / c->num_kv_heads;
+  a.page_shift = __builtin_ctz((unsigned)c->page_size);
+  a.n_recent = c->n_recent;
+  a.max_pages = max_pages;
+  a.chunk = chunk;
+  const int nch = chunks_of(max_seq_len, chunk);
+  a.nc1 = nch + 1;
+  a.max_seq_len = max_seq_len;
+  a.n_q = n_q;
+  a.ngroups = (nch + 3) / 4 + (c->n_recent > 0 ? 1 : 0);
+  a.alpha = alpha;
+  return a;
+}
+
+// Blocks along x: row tiles times chunk groups (0 when there is nothing to do).
+static int64_t grid_x(const AttendArgs& a) {
+  const int64_t tiles = ((int64_t)a.n_q * a.G + 15) / 16;
+  return tiles * a.ngroups;
+}
+
+static kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b,
+                                const int32_t* seq_len, int nc1, int32_t chunk, const float* ws, hipStream_t s) {
+  const dim3 rgrid((unsigned)((int64_t)batch * rows_per_b));
+  const bool rot = c->layout == HAD;
+  if (c->head_dim == 128) {
+    if (rot) hipLaunchKernelGGL((attend_reduce<128, true>), rgrid, dim3(256), 0, s, ws, out, seq_len, rows_per_b, nc1, chunk, c->n_recent);
+    else hipLaunchKernelGGL((attend_reduce<128, false>), rgrid, dim3(256), 0, s, ws, out, seq_len, rows_per_b, nc1, chunk, c->n_recent);
+  } else {
+    if (rot) hipLaunchKernelGGL((attend_reduce<256, true>), rgrid, dim3(256), 0, s, ws, out, seq_len, rows_per_b, nc1, chunk, c->n_recent);
+    else hipLaunchKernelGGL((attend_reduce<256, false>), rgrid, dim3(256), 0, s, ws, out, seq_len, rows_per_b, nc1, chunk, c->n_recent);
+  }
+  return check_launch("attention reduce kernel");
 }
 
 }  // namespace kvq
@@ -705,58 +818,20 @@ extern "C" size_t kvq_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t 
   return (size_t)batch * Hq * nc1 * partial_stride(D) * sizeof(float);
 }
 
-static kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t Hq, const int32_t* seq_len,
-                                int nc1, int32_t chunk, const float* ws, hipStream_t s) {
-  const dim3 rgrid(Hq, batch);
-  const bool rot = c->layout == HAD;
-  if (c->head_dim == 128) {
-    if (rot) hipLaunchKernelGGL((decode_reduce<128, true>), rgrid, dim3(256), 0, s, ws, out, seq_len, Hq, nc1, chunk, c->n_recent);
-    else hipLaunchKernelGGL((decode_reduce<128, false>), rgrid, dim3(256), 0, s, ws, out, seq_len, Hq, nc1, chunk, c->n_recent);
-  } else {
-    if (rot) hipLaunchKernelGGL((decode_reduce<256, true>), rgrid, dim3(256), 0, s, ws, out, seq_len, Hq, nc1, chunk, c->n_recent);
-    else hipLaunchKernelGGL((decode_reduce<256, false>), rgrid, dim3(256), 0, s, ws, out, seq_len, Hq, nc1, chunk, c->n_recent);
-  }
-  return check_launch("decode reduce kernel");
-}
-
 extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
                                                 float alpha, const int32_t* block_table, int32_t max_pages,
                                                 const int32_t* seq_len, int32_t max_seq_len, int32_t chunk,
                                                 void* workspace, size_t ws_bytes, void* stream) {
   kvq_status st = check_attend_args(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len);
   if (st != KVQ_OK) return st;
-  if (chunk < 128 || chunk % 128) return fail(KVQ_ERR_INVALID_ARG, "chunk_tokens must be a positive multiple of 128");
-  if ((chunk + c->page_size - 1) / c->page_size + 1 > 64 * kPageRegs)
-    return fail(KVQ_ERR_UNSUPPORTED, "a chunk may span at most %d pages", 64 * kPageRegs - 1);
+  if ((st = check_chunk(c, chunk)) != KVQ_OK) return st;
   const size_t need = kvq_decode_workspace_bytes(batch, Hq, c->head_dim, max_seq_len, chunk);
   if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
-  DecodeArgs a;
-  a.kp = (const uint8_t*)c->k_payload;
-  a.vp = (const uint8_t*)c->v_payload;
-  a.ks = (const uint8_t*)c->k_scale;
-  a.vs = (const uint8_t*)c->v_scale;
-  a.kring = c->k_recent;
-  a.vring = c->v_recent;
-  a.q = q;
-  a.ws = (float*)workspace;
-  a.block_table = block_table;
-  a.seq_len = seq_len;
-  a.dbg = nullptr;
-  a.Hkv = c->num_kv_heads;
-  a.Hq = Hq;
-  a.G = Hq / c->num_kv_heads;
-  a.page_shift = __builtin_ctz((unsigned)c->page_size);
-  a.n_recent = c->n_recent;
-  a.max_pages = max_pages;
-  a.chunk = chunk;
-  const int nch = chunks_of(max_seq_len, chunk);
-  a.nc1 = nch + 1;
-  a.max_seq_len = max_seq_len;
-  a.alpha = alpha;
-  const int gx = (nch + 3) / 4 + (c->n_recent > 0 ? 1 : 0);
+  AttendArgs a = make_args(c, q, Hq, 1, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace);
+  const int64_t gx = grid_x(a);
   if (gx == 0) return KVQ_OK;
-  const dim3 grid(gx, c->num_kv_heads, batch);
-  pick_partial<false>(c->layout, c->head_dim)(a, grid, partial_lds_bytes(c->layout, c->head_dim, a.G, c->n_recent), (hipStream_t)stream);
+  const dim3 grid((unsigned)gx, c->num_kv_heads, batch);
+  pick_partial<false>(c->layout, c->head_dim)(a, grid, partial_lds_bytes(c->layout, c->head_dim, c->n_recent), (hipStream_t)stream);
   return check_launch("decode partial kernel");
 }
 
@@ -786,6 +861,45 @@ extern "C" kvq_status kvq_attend_decode(const kvq_cache* c, const float* q, floa
   return kvq_attend_decode_reduce(c, out, batch, Hq, seq_len, max_seq_len, chunk, workspace, ws_bytes, stream);
 }
 
+extern "C" size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t Hq, int32_t D,
+                                              int32_t max_seq_len) {
+  if (batch < 1 || n_q < 1 || Hq < 1 || (D != 128 && D != 256) || max_seq_len < 0) return 0;
+  const size_t nc1 = (size_t)chunks_of(max_seq_len, kPrefillChunk) + 1;
+  return (size_t)batch * n_q * Hq * nc1 * partial_stride(D) * sizeof(float);
+}
+
+extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float* q, float* out, int32_t batch,
+                                                int32_t n_q, int32_t Hq, float alpha, int32_t causal,
+                                                const int32_t* q_start, const int32_t* block_table,
+                                                int32_t max_pages, const int32_t* seq_len, int32_t max_seq_len,
+                                                uint32_t flags, void* workspace, size_t ws_bytes, void* stream) {
+  kvq_status st = check_attend_args(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len);
+  if (st != KVQ_OK) return st;
+  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out must be non-null");
+  if (n_q < 1) return fail(KVQ_ERR_INVALID_ARG, "n_q must be >= 1");
+  if (causal != 0 && causal != 1) return fail(KVQ_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (causal && !q_start) return fail(KVQ_ERR_INVALID_ARG, "q_start must be non-null when causal");
+  if (flags & ~KVQ_PREFILL_NO_CAUSAL_SKIP) return fail(KVQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((st = check_chunk(c, kPrefillChunk)) != KVQ_OK) return st;
+  if ((int64_t)batch * n_q * Hq > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "batch * n_q * num_q_heads above 2^31 - 1");
+  const size_t need = kvq_prefill_workspace_bytes(batch, n_q, Hq, c->head_dim, max_seq_len);
+  if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  AttendArgs a = make_args(c, q, Hq, n_q, alpha, block_table, max_pages, seq_len, max_seq_len, kPrefillChunk,
+                           workspace);
+  a.causal = causal;
+  a.skip = causal && !(flags & KVQ_PREFILL_NO_CAUSAL_SKIP);
+  a.q_start = causal ? q_start : nullptr;
+  const int64_t gx = grid_x(a);
+  if (gx > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
+  if (gx > 0) {
+    const dim3 grid((unsigned)gx, c->num_kv_heads, batch);
+    pick_partial<false>(c->layout, c->head_dim)(a, grid, partial_lds_bytes(c->layout, c->head_dim, c->n_recent), (hipStream_t)stream);
+    if ((st = check_launch("prefill partial kernel")) != KVQ_OK) return st;
+  }
+  return launch_reduce(c, out, batch, n_q * Hq, seq_len, a.nc1, kPrefillChunk, (const float*)workspace,
+                       (hipStream_t)stream);
+}
+
 extern "C" kvq_status kvq_debug_qk_i32(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
                                        const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
                                        int32_t max_seq_len, int32_t* scores, void* stream) {
@@ -793,29 +907,14 @@ extern "C" kvq_status kvq_debug_qk_i32(const kvq_cache* c, const float* q, int32
   if (st != KVQ_OK) return st;
   if (!scores) return fail(KVQ_ERR_INVALID_ARG, "scores must be non-null");
   const int chunk = 512;
-  const int nch = chunks_of(max_seq_len, chunk);
-  if (nch == 0) return KVQ_OK;
-  DecodeArgs a;
-  memset(&a, 0, sizeof(a));
-  a.kp = (const uint8_t*)c->k_payload;
-  a.vp = (const uint8_t*)c->v_payload;
-  a.ks = (const uint8_t*)c->k_scale;
-  a.vs = (const uint8_t*)c->v_scale;
-  a.q = q;
-  a.block_table = block_table;
-  a.seq_len = seq_len;
+  if ((st = check_chunk(c, chunk)) != KVQ_OK) return st;
+  if (chunks_of(max_seq_len, chunk) == 0) return KVQ_OK;
+  AttendArgs a = make_args(c, q, Hq, 1, 1.0f, block_table, max_pages, seq_len, max_seq_len, chunk, nullptr);
   a.dbg = scores;
-  a.Hkv = c->num_kv_heads;
-  a.Hq = Hq;
-  a.G = Hq / c->num_kv_heads;
-  a.page_shift = __builtin_ctz((unsigned)c->page_size);
-  a.n_recent = c->n_recent;
-  a.max_pages = max_pages;
-  a.chunk = chunk;
-  a.nc1 = nch;
-  a.max_seq_len = max_seq_len;
-  a.alpha = 1.0f;
-  const dim3 grid((nch + 3) / 4, c->num_kv_heads, batch);
-  pick_partial<true>(c->layout, c->head_dim)(a, grid, partial_lds_bytes(c->layout, c->head_dim, a.G, 0), (hipStream_t)stream);
+  a.kring = nullptr;
+  a.vring = nullptr;
+  a.ngroups = (chunks_of(max_seq_len, chunk) + 3) / 4;   // no window group: the export covers quantised tokens
+  const dim3 grid((unsigned)grid_x(a), c->num_kv_heads, batch);
+  pick_partial<true>(c->layout, c->head_dim)(a, grid, partial_lds_bytes(c->layout, c->head_dim, 0), (hipStream_t)stream);
   return check_launch("score export kernel");
 }

@@ -155,13 +155,24 @@ def prefill_workspace_bytes(batch, n_q, num_q_heads, head_dim, max_seq_len):
 
 def attend_prefill_causal(cache, q, q_start, block_table, seq_len, max_seq_len, alpha, causal=True,
                           causal_skip=True, out=None, workspace=None):
-    """kvq_attend_prefill_causal: q f32 [B, Sq, Hq, D] -> out f32 [B, Sq, Hq, D]."""
+    """kvq_attend_prefill_causal: q f32 [B, Sq, Hq, D] -> out f32 [B, Sq, Hq, D].
+
+    q_start int32 [B]: position of each row's first query (may be None when not causal).
+    causal_skip=False sets KVQ_PREFILL_NO_CAUSAL_SKIP (same result, masked tiles streamed).
+    """
     dev = cache.device
     _need(q, "q", torch.float32, dev)
-    _need(q_start, "q_start", torch.int32, dev)
+    if q_start is not None or causal:
+        _need(q_start, "q_start", torch.int32, dev)
     _need(block_table, "block_table", torch.int32, dev)
     _need(seq_len, "seq_len", torch.int32, dev)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, Sq, Hq, D]")
     B, Sq, Hq, D = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_len.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_len [B]")
+    if q_start is not None and q_start.shape != (B,):
+        raise ValueError("q_start must be [B]")
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", torch.float32, dev)

@@ -65,8 +65,8 @@ def test_store_validates_cache(kw, status):
 def test_attend_validates_before_launch():
     lib = kvq.load()
     d = ctypes.byref(_desc())
-    # Hq not a multiple of Hkv... (Hkv = 1 here: use a GQA group above 16)
-    assert lib.kvq_attend_decode(d, 16, 16, 1, 17, 1.0, 16, 4, 16, 64, 512, 16, 1 << 20, None) == 2
+    d2 = ctypes.byref(_desc(num_kv_heads=2))
+    assert lib.kvq_attend_decode(d2, 16, 16, 1, 3, 1.0, 16, 4, 16, 64, 512, 16, 1 << 20, None) == 1  # Hq % Hkv
     assert lib.kvq_attend_decode(d, 16, 16, 1, 4, 1.0, 16, 4, 16, 64, 100, 16, 1 << 20, None) == 1  # chunk
     assert lib.kvq_attend_decode(d, 16, 16, 1, 4, 1.0, 16, 4, 16, 64, 512, 16, 10, None) == 3       # workspace
     assert lib.kvq_attend_decode(d, 16, 16, 1, 4, 1.0, 16, 2, 16, 64, 512, 16, 1 << 20, None) == 1  # pages
@@ -75,6 +75,23 @@ def test_attend_validates_before_launch():
     assert lib.kvq_store(d, 16, 16, -1, 16, None, None, None, None) == 1
     assert lib.kvq_store(d, 16, 16, 0, 16, None, None, None, None) == 0   # empty append is a no-op
     assert kvq.load().kvq_status_string(3) == b"workspace too small"
+
+
+def test_prefill_validates_before_launch():
+    lib = kvq.load()
+    d = ctypes.byref(_desc())
+    # partials [B][n_q][Hq][512-token chunks + 1][D + 4] f32
+    assert lib.kvq_prefill_workspace_bytes(1, 512, 16, 128, 8704) == 512 * 16 * 18 * 132 * 4
+    assert lib.kvq_prefill_workspace_bytes(1, 0, 16, 128, 8704) == 0
+    big = 1 << 30
+    pf = lib.kvq_attend_prefill_causal
+    assert pf(d, 16, 16, 1, 0, 1, 1.0, 1, 16, 16, 4, 16, 64, 0, 16, big, None) == 1      # n_q < 1
+    assert pf(d, 16, 16, 1, 4, 1, 1.0, 1, None, 16, 4, 16, 64, 0, 16, big, None) == 1    # causal without q_start
+    assert pf(d, 16, 16, 1, 4, 1, 1.0, 2, 16, 16, 4, 16, 64, 0, 16, big, None) == 1      # causal not 0/1
+    assert pf(d, 16, 16, 1, 4, 1, 1.0, 1, 16, 16, 4, 16, 64, 4, 16, big, None) == 1      # unknown flag
+    assert pf(d, 16, None, 1, 4, 1, 1.0, 1, 16, 16, 4, 16, 64, 0, 16, big, None) == 1    # out
+    assert pf(d, 16, 16, 1, 4, 1, 1.0, 1, 16, 16, 4, 16, 64, 0, 16, 100, None) == 3      # workspace
+    assert b"workspace" in lib.kvq_last_error()
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
