@@ -39,7 +39,133 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-kv-heads", type=int, default=4, help="kv heads of one row timed on the oracle")
     p.add_argument("--batch1", action="store_true", help="also time batch 1 (reported under extra)")
+    p.add_argument("--no-prefill", action="store_true", help="skip the causal prefill timing")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a 1 GiB device-to-device copy 10 times (HBM counter calibration) and exit")
     return p.parse_args()
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attend_partial_asym_int4_g32_llama31_70b_s128k_b8_hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_kv_cache_store_amd", "csrc", f) for f in ("kvq_attend.hip", "kvq_internal.h")]
+
+
+def measured_traffic():
+    """HBM bytes per partial launch from the committed FETCH_SIZE/WRITE_SIZE summary (copy-calibrated),
+    or None when the kernel sources changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    m_sha = re.search(r"^source_sha256: (\w+)", text, re.M)
+    m_val = re.search(r"^traffic_bytes_per_launch: (\S+)", text, re.M)
+    if not m_sha or not m_val or m_sha.group(1) != h.hexdigest():
+        return None
+    return float(m_val.group(1))
+
+
+def copy_calibration():
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch, 10 launches."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 10}), flush=True)
+
+
+def time_prefill(steps, warmup, dev, seed=2):
+    """Causal prefill of the Hadamard workload: 512 queries appended at 8192 (cache of 8704 tokens)."""
+    import torch
+    import quantized_kv_cache_store_amd as kvq
+    import workloads as W
+
+    w = W.WORKLOADS["qwen3_1p7b_had_s8k"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    S0, Sq = w.S, w.prefill_q
+    S1 = S0 + Sq
+    ps = w.page_size
+    npages = (S1 + ps - 1) // ps
+    cache = kvq.KvqCache(w.layout, w.D, w.Hkv, npages, ps, n_recent=w.n_recent, max_batch=1, device=dev)
+    table = torch.arange(npages, dtype=torch.int32, device=dev).reshape(1, npages)
+    seq = torch.full((1,), S1, dtype=torch.int32, device=dev)
+    k = W.kv_tokens_device(w, S1, "k", gen, dev)
+    v = W.kv_tokens_device(w, S1, "v", gen, dev)
+    pos = torch.arange(S1, dtype=torch.int32, device=dev)
+    kvq.store(cache, k, v, pos.clone(), torch.zeros(S1, dtype=torch.int32, device=dev), pos, seq)
+    q = torch.randn((1, Sq, w.Hq, w.D), generator=gen, device=dev, dtype=torch.float32)
+    qs = torch.full((1,), S0, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(kvq.prefill_workspace_bytes(1, Sq, w.Hq, w.D, S1), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        kvq.attend_prefill_causal(cache, q, qs, table, seq, S1, w.alpha, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        kvq.attend_prefill_causal(cache, q, qs, table, seq, S1, w.alpha, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    assert torch.isfinite(out).all(), "non-finite prefill output"
+    # visible (query, token) pairs per query head: query i sees S0 + i + 1 tokens
+    pairs = sum(S0 + i + 1 for i in range(Sq)) * w.Hq
+    ops = 2.0 * pairs * w.D * 2                   # Q K^T (int8 MACs) + P V (f16 MACs), 2 ops per MAC
+    t_min = 2.0 * pairs * w.D / 5.0e15 + 2.0 * pairs * w.D / 2.5e15   # int8 at 5.0 POP/s, f16 at 2.5 PFLOP/s
+    return dict(workload=w.name, n_q=Sq, q_start=S0, seq_len=S1, us=round(us, 2), visible_pairs=pairs,
+                achieved_tops=round(ops / (us * 1e-6) / 1e12, 1), roofline_us=round(t_min * 1e6, 2),
+                frac=round(t_min * 1e6 / us, 4),
+                bound="mfma (int8 Q K^T at 5.0 POP/s + f16 P V at 2.5 PFLOP/s)")
+
+
+def time_store(steps, warmup, dev, seed=1):
+    """kvq_store of one new token per kv head into the Llama-3-8B-shaped q4_0 cache (32768 slots)."""
+    import torch
+    import quantized_kv_cache_store_amd as kvq
+    import workloads as W
+
+    w = W.WORKLOADS["llama3_8b_q4_0_s32k"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    npages = w.S // w.page_size
+    cache = kvq.KvqCache(w.layout, w.D, w.Hkv, npages, w.page_size, device=dev)
+    k = W.kv_tokens_device(w, 1, "k", gen, dev)
+    v = W.kv_tokens_device(w, 1, "v", gen, dev)
+    slot = torch.full((1,), w.S - 1, dtype=torch.int32, device=dev)
+    for _ in range(warmup):
+        kvq.store(cache, k, v, slot)
+    torch.cuda.synchronize()
+    # A one-token store takes a few microseconds on the GPU, less than one host launch through the
+    # binding, so launches are captured into a graph (no memset nodes: the store issues none) and the
+    # graph replays are timed.
+    per_graph = 64
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(per_graph):
+                kvq.store(cache, k, v, slot)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // 4)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return dict(workload=w.name, tokens=1, us=round(e0.elapsed_time(e1) * 1e3 / (reps * per_graph), 2),
+                timing="graph of 64 launches", bytes_in=2 * w.Hkv * w.D * 4, bytes_out=2 * w.Hkv * (64 + 8))
 
 
 def build_layers(w, B, L, dev, gen):
@@ -148,6 +274,9 @@ def cpu_baseline(w, kv_heads):
 
 def main():
     a = parse()
+    if a.copy_calibration:
+        copy_calibration()
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported",
                           "n_gpus": a.gpus}))
@@ -164,6 +293,9 @@ def main():
         extra["batch1"] = dict(us_per_layer=r1["ms_per_step"] * 1e3,
                                packed_gbs=r1["bytes_layer"] / (r1["ms_per_step"] * 1e-3) / 1e9,
                                partial_us=r1["partial_ms_mean"] * 1e3, layers_walked=r1["layers"])
+    if not a.no_prefill:
+        extra["prefill"] = time_prefill(max(a.steps, 20), a.warmup, dev)
+        extra["store"] = time_store(max(a.steps, 20), a.warmup, dev)
     gbs = r["bytes_layer"] / (r["ms_per_step"] * 1e-3) / 1e9
     ach = r["bytes_layer"] / (r["partial_ms_mean"] * 1e-3) / 1e9
     line = {
@@ -186,7 +318,9 @@ def main():
                    "packed_bytes_per_layer": r["bytes_layer"]},
         "roofline": {"bound": "hbm", "kernel": "decode_partial", "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(r["partial_ms_mean"] * 1e3, 2),
+                     "traffic": measured_traffic() if (a.batch, a.chunk) == (8, 512) else None, "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + "
+                     "WRITE_SIZE, copy-calibrated; null if the kernel changed since)",
+                     "avg_launch_us": round(r["partial_ms_mean"] * 1e3, 2),
                      "min_launch_us": round(r["partial_ms_min"] * 1e3, 2)},
     }
     if extra:
