@@ -163,7 +163,7 @@ kvq_status kvq_attend_decode_reduce(const kvq_cache* cache, float* out, int32_t 
                                     void* stream);
 
 /* Workspace of kvq_attend_prefill_causal: split-K partials (o_c, m_c, l_c)
- * per (batch, query, query head, 512-token chunk), plus the window partial.
+ * per (batch, query, query head, 1024-token chunk), plus the window partial.
  * Returns 0 for invalid arguments. */
 size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t num_q_heads,
                                    int32_t head_dim, int32_t max_seq_len);

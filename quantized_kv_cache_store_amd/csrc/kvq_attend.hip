@@ -37,139 +37,9 @@
 // Steps that are partly visible mask per row.  With the skip off, the masked
 // tokens are streamed and contribute exact zeros, so both give the same bits.
 
-#include "kvq_internal.h"
+#include "kvq_attend_common.h"
 
 namespace kvq {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-#define KVQ_LOG2E 1.4426950408889634f
-
-struct AttendArgs {
-  const uint8_t* kp;
-  const uint8_t* vp;
-  const uint8_t* ks;
-  const uint8_t* vs;
-  const float* kring;
-  const float* vring;
-  const float* q;
-  float* ws;
-  const int32_t* block_table;
-  const int32_t* seq_len;
-  const int32_t* q_start;   // [batch] position of query 0 (causal prefill), else null
-  int32_t* dbg;
-  int Hkv, Hq, G, page_shift, n_recent, max_pages, chunk, nc1, max_seq_len;
-  int n_q;       // queries per batch row (1 for decode)
-  int ngroups;   // blocks per row tile along the sequence: chunk groups of four, + 1 for the window
-  int causal;    // rows see t <= q_start + i
-  int skip;      // causal skip: stop streaming past the tile's last visible token
-  float alpha;
-};
-
-// Row R of (b, hk) is query i = R / G of head hk * G + R % G; its flat index in
-// [batch][n_q][Hq] addresses q, out and (times the chunk count) the partials.
-__device__ __forceinline__ size_t row_index(const AttendArgs& a, int b, int hk, int R) {
-  const int i = R / a.G;
-  return ((size_t)b * a.n_q + i) * a.Hq + hk * a.G + (R - i * a.G);
-}
-
-// Last visible position of row R (rows past the tile's valid count see nothing).
-__device__ __forceinline__ int row_limit(const AttendArgs& a, int qs0, int R, int nrows) {
-  if (R >= nrows) return -1;
-  return a.causal ? qs0 + R / a.G : 0x7fffffff;
-}
-
-template <int D>
-__host__ __device__ constexpr int prologue_lds_bytes() {
-  return 16 * D * 4 + 16 * D + 16 * 4 + 16 * (D / 32) * 4;
-}
-
-__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
-__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
-
-// Physical row of logical token t of (batch b, kv head hk) in the planes.
-__device__ __forceinline__ size_t plane_row(const AttendArgs& a, int b, int hk, int t) {
-  const int phys = a.block_table[(size_t)b * a.max_pages + (t >> a.page_shift)];
-  return (((size_t)phys * a.Hkv + hk) << a.page_shift) + (size_t)(t & ((1 << a.page_shift) - 1));
-}
-
-// q6_0 octet (low-nibble dword + 16 bits of top-bit pairs) -> biased 6-bit codes
-// (code + 32) as bytes, even elements [0,2,4,6] in `ev`, odd [1,3,5,7] in `od`.
-__device__ __forceinline__ void q6_octet(uint32_t lo, uint32_t hi16, uint32_t& ev, uint32_t& od) {
-  const uint32_t w = __builtin_amdgcn_perm(hi16, hi16, 0x01010000u);   // bytes [b0, b0, b1, b1]
-  const uint32_t te = ((w << 4) & 0x00300030u) | (w & 0x30003000u);
-  const uint32_t to = ((w << 2) & 0x00300030u) | ((w >> 2) & 0x30003000u);
-  ev = ((lo & 0x0F0F0F0Fu) | te) ^ 0x20202020u;
-  od = (((lo >> 4) & 0x0F0F0F0Fu) | to) ^ 0x20202020u;
-}
-
-// Window partial: exact f32 rows of the newest tokens (HAD: rotated basis), for
-// the rows row0 .. row0 + nvalid - 1 of (b, hk), each masked by its limit.
-template <int L, int D>
-__device__ __noinline__ void window_partial(const AttendArgs a, unsigned char* smem, int b, int hk, int S, int row0, int nvalid,
-                               int qs0) {
-  float* qf = reinterpret_cast<float*>(smem);
-  int8_t* q8 = reinterpret_cast<int8_t*>(qf + 16 * D);
-  float* sq = reinterpret_cast<float*>(q8 + 16 * D);
-  int* qsum = reinterpret_cast<int*>(sq + 16);
-  float* sc = reinterpret_cast<float*>(smem + prologue_lds_bytes<D>());   // [16][W]
-  const int tid = threadIdx.x;
-  const int nrows = a.n_q * a.G;
-  for (int idx = tid; idx < 16 * D; idx += 256) {
-    const int row = idx / D;
-    qf[idx] = row < nvalid ? a.q[row_index(a, b, hk, row0 + row) * D + idx % D] : 0.0f;
-  }
-  __syncthreads();
-  prepare_query_lds<L, D>(qf, q8, sq, qsum);
-  const int W = min(S, a.n_recent);
-  const int w0 = S - W;
-  const size_t ring0 = ((size_t)b * a.Hkv + hk) * a.n_recent;
-  const float cl = a.alpha * KVQ_LOG2E;
-  for (int idx = tid; idx < nvalid * W; idx += 256) {
-    const int h = idx / W, tt = idx % W;
-    const float* kr = a.kring + (ring0 + (w0 + tt) % a.n_recent) * D;
-    const float* qh = qf + h * D;
-    float acc = 0.0f;
-    for (int d = 0; d < D; d += 4) {
-      const float4 k4 = *reinterpret_cast<const float4*>(kr + d);
-      acc += qh[d] * k4.x + qh[d + 1] * k4.y + qh[d + 2] * k4.z + qh[d + 3] * k4.w;
-    }
-    sc[idx] = w0 + tt <= row_limit(a, qs0, row0 + h, nrows) ? acc * cl : -INFINITY;
-  }
-  __syncthreads();
-  float* mrow = sc + 16 * W;
-  float* lrow = mrow + 16;
-  if (tid < nvalid) {
-    float m = -INFINITY;
-    for (int tt = 0; tt < W; ++tt) m = fmaxf(m, sc[tid * W + tt]);
-    const float m_use = m == -INFINITY ? 0.0f : m;   // a row that sees no window token: p = 0, l = 0
-    float l = 0.0f;
-    for (int tt = 0; tt < W; ++tt) {
-      const float p = exp2f(sc[tid * W + tt] - m_use);
-      sc[tid * W + tt] = p;
-      l += p;
-    }
-    mrow[tid] = m;
-    lrow[tid] = l;
-  }
-  __syncthreads();
-  const int PST = partial_stride(D);
-  for (int idx = tid; idx < nvalid * D; idx += 256) {
-    const int h = idx / D, d = idx % D;
-    float o = 0.0f;
-    for (int tt = 0; tt < W; ++tt) o += sc[h * W + tt] * a.vring[(ring0 + (w0 + tt) % a.n_recent) * D + d];
-    float* dst = a.ws + (row_index(a, b, hk, row0 + h) * a.nc1 + (a.nc1 - 1)) * PST;
-    dst[d] = o;
-    if (d == 0) {
-      dst[D] = mrow[h];
-      dst[D + 1] = lrow[h];
-    }
-  }
-}
 
 // Staging buffer of one 32-token step in a wave's LDS slice:
 //   [K payload rows 32 x PB][V payload rows 32 x PB][K records 32 x SB][V records 32 x SB]
@@ -723,29 +593,9 @@ static size_t step_bytes(int layout, int D) {
 static size_t partial_lds_bytes(int layout, int D, int n_recent) {
   const size_t pro = (size_t)16 * D * 4 + 16 * D + 16 * 4 + 16 * (D / 32) * 4;
   const size_t steps = 4 * step_bytes(layout, D);
-  const size_t win = n_recent > 0 ? pro + (size_t)16 * n_recent * 4 + 32 * 4 : 0;
+  const size_t win = n_recent > 0 ? (size_t)(D == 128 ? window_lds_bytes<128>() : window_lds_bytes<256>()) : 0;
   size_t m = pro > steps ? pro : steps;
   return m > win ? m : win;
-}
-
-static int chunks_of(int max_seq_len, int chunk) { return (max_seq_len + chunk - 1) / chunk; }
-
-// Split-K chunk of the causal prefill (a multiple of 128, like the decode chunk).
-constexpr int kPrefillChunk = 512;
-
-static kvq_status check_attend_args(const kvq_cache* c, const void* q, int32_t batch, int32_t Hq,
-                                    const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
-                                    int32_t max_seq_len) {
-  kvq_status st = validate_cache(c);
-  if (st != KVQ_OK) return st;
-  if (!q || !block_table || !seq_len) return fail(KVQ_ERR_INVALID_ARG, "q, block_table and seq_len must be non-null");
-  if (batch < 1) return fail(KVQ_ERR_INVALID_ARG, "batch must be >= 1");
-  if (Hq < 1 || Hq % c->num_kv_heads) return fail(KVQ_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
-  if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len must be >= 0");
-  if (max_pages < 1 || (int64_t)max_pages * c->page_size < max_seq_len)
-    return fail(KVQ_ERR_INVALID_ARG, "max_pages_per_seq * page_size must cover max_seq_len");
-  if (c->n_recent > 512) return fail(KVQ_ERR_UNSUPPORTED, "n_recent above 512");
-  return KVQ_OK;
 }
 
 static kvq_status check_chunk(const kvq_cache* c, int32_t chunk) {
@@ -755,45 +605,8 @@ static kvq_status check_chunk(const kvq_cache* c, int32_t chunk) {
   return KVQ_OK;
 }
 
-static AttendArgs make_args(const kvq_cache* c, const float* q, int32_t Hq, int32_t n_q, float alpha,
-                            const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
-                            int32_t max_seq_len, int32_t chunk, void* workspace) {
-  AttendArgs a;
-  memset(&a, 0, sizeof(a));
-  a.kp = (const uint8_t*)c->k_payload;
-  a.vp = (const uint8_t*)c->v_payload;
-  a.ks = (const uint8_t*)c->k_scale;
-  a.vs = (const uint8_t*)c->v_scale;
-  a.kring = c->k_recent;
-  a.vring = c->v_recent;
-  a.q = q;
-  a.ws = (float*)workspace;
-  a.block_table = block_table;
-  a.seq_len = seq_len;
-  a.Hkv = c->num_kv_heads;
-  a.Hq = Hq;
-  a.G = Hq / c->num_kv_heads;
-  a.page_shift = __builtin_ctz((unsigned)c->page_size);
-  a.n_recent = c->n_recent;
-  a.max_pages = max_pages;
-  a.chunk = chunk;
-  const int nch = chunks_of(max_seq_len, chunk);
-  a.nc1 = nch + 1;
-  a.max_seq_len = max_seq_len;
-  a.n_q = n_q;
-  a.ngroups = (nch + 3) / 4 + (c->n_recent > 0 ? 1 : 0);
-  a.alpha = alpha;
-  return a;
-}
-
-// Blocks along x: row tiles times chunk groups (0 when there is nothing to do).
-static int64_t grid_x(const AttendArgs& a) {
-  const int64_t tiles = ((int64_t)a.n_q * a.G + 15) / 16;
-  return tiles * a.ngroups;
-}
-
-static kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b,
-                                const int32_t* seq_len, int nc1, int32_t chunk, const float* ws, hipStream_t s) {
+kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b, const int32_t* seq_len,
+                         int nc1, int32_t chunk, const float* ws, hipStream_t s) {
   const dim3 rgrid((unsigned)((int64_t)batch * rows_per_b));
   const bool rot = c->layout == HAD;
   if (c->head_dim == 128) {
@@ -859,45 +672,6 @@ extern "C" kvq_status kvq_attend_decode(const kvq_cache* c, const float* q, floa
                                             chunk, workspace, ws_bytes, stream);
   if (st != KVQ_OK) return st;
   return kvq_attend_decode_reduce(c, out, batch, Hq, seq_len, max_seq_len, chunk, workspace, ws_bytes, stream);
-}
-
-extern "C" size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t Hq, int32_t D,
-                                              int32_t max_seq_len) {
-  if (batch < 1 || n_q < 1 || Hq < 1 || (D != 128 && D != 256) || max_seq_len < 0) return 0;
-  const size_t nc1 = (size_t)chunks_of(max_seq_len, kPrefillChunk) + 1;
-  return (size_t)batch * n_q * Hq * nc1 * partial_stride(D) * sizeof(float);
-}
-
-extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float* q, float* out, int32_t batch,
-                                                int32_t n_q, int32_t Hq, float alpha, int32_t causal,
-                                                const int32_t* q_start, const int32_t* block_table,
-                                                int32_t max_pages, const int32_t* seq_len, int32_t max_seq_len,
-                                                uint32_t flags, void* workspace, size_t ws_bytes, void* stream) {
-  kvq_status st = check_attend_args(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len);
-  if (st != KVQ_OK) return st;
-  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out must be non-null");
-  if (n_q < 1) return fail(KVQ_ERR_INVALID_ARG, "n_q must be >= 1");
-  if (causal != 0 && causal != 1) return fail(KVQ_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (causal && !q_start) return fail(KVQ_ERR_INVALID_ARG, "q_start must be non-null when causal");
-  if (flags & ~KVQ_PREFILL_NO_CAUSAL_SKIP) return fail(KVQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
-  if ((st = check_chunk(c, kPrefillChunk)) != KVQ_OK) return st;
-  if ((int64_t)batch * n_q * Hq > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "batch * n_q * num_q_heads above 2^31 - 1");
-  const size_t need = kvq_prefill_workspace_bytes(batch, n_q, Hq, c->head_dim, max_seq_len);
-  if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
-  AttendArgs a = make_args(c, q, Hq, n_q, alpha, block_table, max_pages, seq_len, max_seq_len, kPrefillChunk,
-                           workspace);
-  a.causal = causal;
-  a.skip = causal && !(flags & KVQ_PREFILL_NO_CAUSAL_SKIP);
-  a.q_start = causal ? q_start : nullptr;
-  const int64_t gx = grid_x(a);
-  if (gx > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
-  if (gx > 0) {
-    const dim3 grid((unsigned)gx, c->num_kv_heads, batch);
-    pick_partial<false>(c->layout, c->head_dim)(a, grid, partial_lds_bytes(c->layout, c->head_dim, c->n_recent), (hipStream_t)stream);
-    if ((st = check_launch("prefill partial kernel")) != KVQ_OK) return st;
-  }
-  return launch_reduce(c, out, batch, n_q * Hq, seq_len, a.nc1, kPrefillChunk, (const float*)workspace,
-                       (hipStream_t)stream);
 }
 
 extern "C" kvq_status kvq_debug_qk_i32(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,

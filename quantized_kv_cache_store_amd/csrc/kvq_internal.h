@@ -69,53 +69,73 @@ __device__ __forceinline__ float wave_max16(float v) {
 //   q8    int8 [16][D]: out, per-vector symmetric int8 with sq = amax / 127
 //   sq    f32 [16]
 //   qsum  int32 [16][D/32]: sum of q8 over each 32-element block
-// Rows past n_rows must hold zeros on entry (they give q8 = 0, sq = 0).
-// The rotation is the butterfly transform with stages h = 1, 2, 4, ..., D/2,
-// each butterfly (a, b) -> (a + b, a - b) in f32, then every element times
-// f32(1/sqrt(D)); every value is an IEEE f32 result, so the order in which
-// threads run the independent butterflies does not change it.
+// Rows past n_rows must hold zeros on entry (they give q8 = 0, sq = 0).  The caller
+// synchronises the block after filling qf; this routine ends with a block barrier.
+// Thread (row = tid / 16, j = tid % 16) holds elements j*E .. j*E + E - 1 of its row in
+// registers.  The rotation is the butterfly transform with stages h = 1, 2, 4, ..., D/2, each
+// butterfly (a, b) -> (a + b, a - b) in f32 (stages below E inside the thread, the others
+// between the 16 lanes of the row), then every element times f32(1/sqrt(D)).
 template <int L, int D>
 __device__ void prepare_query_lds(float* qf, int8_t* q8, float* sq, int* qsum) {
 #pragma clang fp contract(off)
+  constexpr int E = D / 16;          // elements per thread
+  constexpr int LPG = 32 / E;        // lanes per 32-element block
   const int tid = threadIdx.x;
-  constexpr int R = 16;
+  const int row = tid >> 4, j = tid & 15;
+  float* xr = qf + row * D + j * E;
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; e += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + e);
+    x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
+  }
   if (L == HAD) {
-    for (int h = 1; h < D; h <<= 1) {
-      for (int idx = tid; idx < R * D / 2; idx += 256) {
-        const int row = idx / (D / 2), k = idx % (D / 2);
-        const int i = (k / h) * 2 * h + (k % h);
-        float* x = qf + row * D;
-        const float a = x[i], b = x[i + h];
-        x[i] = a + b;
-        x[i + h] = a - b;
+#pragma unroll
+    for (int hh = 1; hh < E; hh <<= 1) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        if ((i & hh) == 0) {
+          const float p = x[i], q = x[i + hh];
+          x[i] = p + q;
+          x[i + hh] = p - q;
+        }
       }
-      __syncthreads();
     }
-    for (int idx = tid; idx < R * D; idx += 256) qf[idx] = qf[idx] * hadamard_norm<D>();
-    __syncthreads();
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      const bool upper = (j & m) != 0;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const float y = __shfl_xor(x[i], m);
+        x[i] = upper ? (y - x[i]) : (x[i] + y);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < E; ++i) x[i] = x[i] * hadamard_norm<D>();
+#pragma unroll
+    for (int e = 0; e < E; e += 4) *reinterpret_cast<float4*>(xr + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
   }
-  // amax per row: 16 threads per row
-  {
-    const int row = tid >> 4, sub = tid & 15;
-    float m = 0.0f;
-    for (int d = sub; d < D; d += 16) m = fmaxf(m, fabsf(qf[row * D + d]));
-    m = wave_max16(m);
-    if (sub == 0) sq[row] = m / 127.0f;
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < E; ++i) m = fmaxf(m, fabsf(x[i]));
+  m = wave_max16(m);
+  const float s = m / 127.0f;
+  int gs = 0;
+  uint32_t packed[E / 4];
+#pragma unroll
+  for (int i = 0; i < E / 4; ++i) packed[i] = 0u;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int v = s != 0.0f ? (int)fminf(fmaxf(rintf(x[i] / s), -127.0f), 127.0f) : 0;
+    gs += v;
+    packed[i >> 2] |= (uint32_t)(v & 0xFF) << (8 * (i & 3));
   }
-  __syncthreads();
-  for (int idx = tid; idx < R * D; idx += 256) {
-    const float s = sq[idx / D];
-    int v = 0;
-    if (s != 0.0f) v = (int)fminf(fmaxf(rintf(qf[idx] / s), -127.0f), 127.0f);
-    q8[idx] = (int8_t)v;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < R * (D / 32); idx += 256) {
-    const int row = idx / (D / 32), g = idx % (D / 32);
-    int acc = 0;
-    for (int j = 0; j < 32; ++j) acc += q8[row * D + g * 32 + j];
-    qsum[idx] = acc;
-  }
+#pragma unroll
+  for (int i = 0; i < E / 4; ++i) reinterpret_cast<uint32_t*>(q8 + row * D + j * E)[i] = packed[i];
+#pragma unroll
+  for (int o = 1; o < LPG; o <<= 1) gs += __shfl_xor(gs, o);
+  if (j % LPG == 0) qsum[row * (D / 32) + j / LPG] = gs;
+  if (j == 0) sq[row] = s;
   __syncthreads();
 }
 #endif

@@ -1,0 +1,515 @@
+// Causal prefill over the packed cache.
+//
+// [tract-RFC] Architecture (prefill appends the chunk to the cache, then every
+// query position attends with its own causal limit) and Causality & mixed
+// precision (work wholly past the limit is skipped; the result equals
+// compute-then-mask).  The scores are the same int8(Q) . code(K) -> i32 block
+// dots as decode, and the window and merge are those of decode.
+//
+// Rows and tiles as in the decode kernel: row R of (batch b, kv head hk) is query
+// i = R / G of head hk * G + R % G, with limit q_start + i.  A block of four
+// waves takes 64 consecutive rows (one 16-row tile per wave) and one 1024-token
+// chunk of the quantised region.  Unlike decode, where every wave streams its
+// own chunk, here the block shares each 32-token step:
+//   * the block unpacks the step's K codes once into LDS, already in the A-operand
+//     order of v_mfma_i32_16x16x32_i8 (so a wave's operand is one contiguous
+//     8-byte read per lane), and dequantises the step's V once into LDS as fp16,
+//     already transposed into the A-operand order of v_mfma_f32_16x16x32_f16
+//     (one contiguous 16-byte read per lane);
+//   * each wave then runs Q K^T, the online softmax and P V for its tile from
+//     those operands, so the unpack and dequantisation cost is paid once per
+//     64 rows instead of once per 16.
+// The step's global loads are issued one step ahead into registers; one barrier
+// per step separates the producer writes of step s + 1 from the reads of step s
+// (two LDS buffers).
+//
+// Causal skip: the block stops at the last token its last row can see, and a
+// chunk wholly past every limit streams nothing and emits empty partials.  Steps
+// that are partly visible mask per row.  With the skip off the masked tokens are
+// streamed and contribute exact zeros, so both settings give the same bits.
+
+#include "kvq_attend_common.h"
+
+namespace kvq {
+
+// Split-K chunk of the prefill (tokens); each (64-row block, chunk) is one block of the grid.
+constexpr int kPrefillChunk = 1024;
+static_assert(kPrefillChunk % 32 == 0 && kPrefillChunk / 16 <= 64, "a chunk's pages (>= 16 tokens each) fit one per lane");
+
+// LDS of one 32-token step:
+//   KC  int8 codes (code + bias) in A-operand order: [block g][half tau][lane group r][token
+//       16 tau + i][8 bytes], the bytes being codes 8r, 8r+2, 8r+4, 8r+6, 8r+1, 8r+3, 8r+5, 8r+7
+//       of block g;
+//   VT  dequantised V (fp16) in A-operand order of V^T: [d / 16][lane group r][d % 16][slot k],
+//       slot k holding token 16 (k / 4) + 4r + k % 4 (the same token order as the lane's P);
+//   KR  the raw K records of the 32 tokens.
+template <int L, int D>
+struct PStep {
+  using T = Layout<L, D>;
+  static constexpr int KC = 0;
+  static constexpr int VT = KC + T::NG * 1024;
+  static constexpr int KR = VT + D * 64;
+  static constexpr int BYTES = KR + 32 * T::SB;
+  static constexpr int KU = T::NG / 2;        // K units (token, block, lane group) per thread
+  static constexpr int VU = D / 128;          // V units (element pair, lane group) per thread
+};
+
+// Loaded (not yet unpacked) inputs of one step, per thread.
+template <int L, int D>
+struct PLoad {
+  uint32_t kw[PStep<L, D>::KU];     // K payload dword of each K unit
+  uint32_t kh[PStep<L, D>::KU];     // q6_0: the unit's 16 bits of top-bit pairs
+  uint32_t vb[PStep<L, D>::VU][8];  // V payload byte holding elements (d, d+1) of each of the 8 tokens
+  uint32_t vh[PStep<L, D>::VU][8];  // q6_0: the byte of top-bit pairs of (d, d+1)
+  uint32_t vs[PStep<L, D>::VU][8];  // V record word of the group of d (zeroed past the end)
+  uint32_t kr;                      // one dword of the K records
+};
+
+// Base addresses of the two 16-token halves of a step in the four planes.  A half lies in one
+// page (steps start at multiples of 32 and pages hold a power of two >= 16 tokens), so token
+// 16 h + i of the step is row i past half h's base.  A half wholly past the end reuses half 0's
+// page, so every address stays inside an allocated page; tokens past the end are masked later.
+// Row indices (not pointers, which the compiler would spill to memory when selected per lane).
+struct StepBase {
+  size_t r0, r1;
+};
+
+__device__ __forceinline__ StepBase step_base(const AttendArgs& a, int hk, int T0, int t_end, int first_page,
+                                              int lane_page) {
+  const int mask = (1 << a.page_shift) - 1;
+  const int t1 = T0 + 16 < t_end ? T0 + 16 : T0;
+  const int ph0 = __builtin_amdgcn_readlane(lane_page, (T0 >> a.page_shift) - first_page);
+  const int ph1 = __builtin_amdgcn_readlane(lane_page, (t1 >> a.page_shift) - first_page);
+  StepBase sb;
+  sb.r0 = (((size_t)ph0 * a.Hkv + hk) << a.page_shift) + (size_t)(T0 & mask);
+  sb.r1 = (((size_t)ph1 * a.Hkv + hk) << a.page_shift) + (size_t)(t1 & mask);
+  return sb;
+}
+
+// Issue the global loads of one step (every thread, every load, no condition: the waits the
+// compiler places before the producer then count exactly these loads).
+template <int L, int D>
+__device__ __forceinline__ void prefill_load(const AttendArgs& a, const StepBase& sb, int tid, PLoad<L, D>& ld) {
+  using T = Layout<L, D>;
+  using PS = PStep<L, D>;
+  constexpr int PB = T::PB, SB = T::SB;
+  // K units of a wave all sit in one half (wave-uniform)
+  const uint8_t* kbase = a.kp + (__builtin_amdgcn_readfirstlane((tid >> 6) & 1) ? sb.r1 : sb.r0) * PB;
+#pragma unroll
+  for (int k = 0; k < PS::KU; ++k) {
+    const int u = tid + 256 * k;
+    const int i = u & 15, r = (u >> 4) & 3, g = u >> 7;
+    const uint8_t* row = kbase + i * PB;
+    if (L == Q60) {
+      ld.kw[k] = *reinterpret_cast<const uint32_t*>(row + 24 * g + 4 * r);
+      ld.kh[k] = *reinterpret_cast<const uint16_t*>(row + 24 * g + 16 + 2 * r);
+    } else {
+      ld.kw[k] = *reinterpret_cast<const uint32_t*>(row + 4 * (4 * g + r));
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PS::VU; ++k) {
+    const int u = tid + 256 * k;
+    const int dp8 = u & 7, r = (u >> 3) & 3, dt = u >> 5;
+    const int d = 16 * dt + 2 * dp8;           // even element; the unit covers d and d + 1
+    const int g = d >> 5;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int h = s >> 2, i = 4 * r + (s & 3);   // token 16 h + i
+      const uint8_t* vrow = a.vp + ((h ? sb.r1 : sb.r0) + i) * PB;
+      if (L == Q60) {
+        const int e = d & 31;
+        ld.vb[k][s] = vrow[24 * g + (e >> 1)];
+        ld.vh[k][s] = vrow[24 * g + 16 + (e >> 2)];
+      } else {
+        ld.vb[k][s] = vrow[d >> 1];
+      }
+      const uint8_t* rec = a.vs + ((h ? sb.r1 : sb.r0) + i) * SB;
+      if (L == HAD) ld.vs[k][s] = *reinterpret_cast<const uint32_t*>(rec);
+      else if (L == ASYM) ld.vs[k][s] = *reinterpret_cast<const uint32_t*>(rec + 4 * g);
+      else ld.vs[k][s] = *reinterpret_cast<const uint16_t*>(rec + 2 * g);
+    }
+  }
+  {
+    const int w = tid < 8 * SB ? tid : 0;            // threads past the records reload word 0
+    const int tok = w / (SB / 4), word = w % (SB / 4);
+    const size_t row = (tok < 16 ? sb.r0 : sb.r1) + (tok & 15);
+    ld.kr = *reinterpret_cast<const uint32_t*>(a.ks + row * SB + 4 * word);
+  }
+}
+
+// Unpack and dequantise the loaded step into the LDS buffer.
+// n_tok: tokens of the step inside the chunk; the V scales of the others are zeroed so that their
+// (stale) rows contribute exact zeros.
+template <int L, int D>
+__device__ __forceinline__ void prefill_produce(unsigned char* buf, int tid, const PLoad<L, D>& ld, int n_tok,
+                                                uint32_t magic) {
+  using T = Layout<L, D>;
+  using PS = PStep<L, D>;
+  constexpr int SB = T::SB;
+  constexpr int BIAS = CodeBias<L>::value;
+#pragma unroll
+  for (int k = 0; k < PS::KU; ++k) {
+    const int u = tid + 256 * k;
+    uint32_t lo, hi;
+    if (L == Q60) {
+      q6_octet(ld.kw[k], ld.kh[k], lo, hi);
+    } else {
+      const uint32_t x = BIAS ? (ld.kw[k] ^ 0x88888888u) : ld.kw[k];
+      lo = x & 0x0F0F0F0Fu;
+      hi = (x >> 4) & 0x0F0F0F0Fu;
+    }
+    *reinterpret_cast<uint2*>(buf + PS::KC + 8 * u) = make_uint2(lo, hi);
+  }
+#pragma unroll
+  for (int k = 0; k < PS::VU; ++k) {
+    const int u = tid + 256 * k;
+    const int dp8 = u & 7, r = (u >> 3) & 3, dt = u >> 5;
+    const int d = 16 * dt + 2 * dp8;
+    h2 lowv[4], highv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // tokens of slots 2i and 2i + 1 side by side: [byte(2i), 0, byte(2i + 1), 0]
+      const uint32_t y = __builtin_amdgcn_perm(ld.vb[k][2 * i + 1], ld.vb[k][2 * i], 0x0C040C00u);
+      uint32_t c0, c1;   // element d and d + 1 of both tokens, as code + bias
+      if (L == Q60) {
+        const int sh = 2 * (d & 3);
+        const uint32_t hy = __builtin_amdgcn_perm(ld.vh[k][2 * i + 1], ld.vh[k][2 * i], 0x0C040C00u) >> sh;
+        c0 = ((y & 0x000F000Fu) | ((hy & 0x00030003u) << 4)) ^ 0x00200020u;
+        c1 = (((y >> 4) & 0x000F000Fu) | ((hy & 0x000C000Cu) << 2)) ^ 0x00200020u;
+      } else {
+        const uint32_t yb = BIAS ? (y ^ 0x00880088u) : y;
+        c0 = yb & 0x000F000Fu;
+        c1 = (yb >> 4) & 0x000F000Fu;
+      }
+      const h2 off = h2{(_Float16)(1024 + BIAS), (_Float16)(1024 + BIAS)};
+      h2 v0 = as_h2(c0 | magic) - off;
+      h2 v1 = as_h2(c1 | magic) - off;
+      const int r4 = 4 * ((u >> 3) & 3);
+      const int t0 = 16 * (i >> 1) + r4 + 2 * (i & 1);     // tokens of slots 2i and 2i + 1
+      const uint32_t w0 = t0 < n_tok ? ld.vs[k][2 * i] : 0u;
+      const uint32_t w1 = t0 + 1 < n_tok ? ld.vs[k][2 * i + 1] : 0u;
+      if (L == HAD) {
+        const h2 s2 = h2{(_Float16)__builtin_bit_cast(float, w0), (_Float16)__builtin_bit_cast(float, w1)};
+        v0 = v0 * s2;
+        v1 = v1 * s2;
+      } else {
+        const h2 s2 = as_h2(__builtin_amdgcn_perm(w1, w0, 0x05040100u));
+        if (L == ASYM) {
+          const h2 z2 = as_h2(__builtin_amdgcn_perm(w1, w0, 0x07060302u));
+          v0 = v0 * s2 + z2;
+          v1 = v1 * s2 + z2;
+        } else {
+          v0 = v0 * s2;
+          v1 = v1 * s2;
+        }
+      }
+      lowv[i] = v0;
+      highv[i] = v1;
+    }
+    unsigned char* dst = buf + PS::VT + (((dt * 4 + r) * 16) + (d & 15)) * 16;
+    *reinterpret_cast<u32x4*>(dst) = u32x4{as_u32(lowv[0]), as_u32(lowv[1]), as_u32(lowv[2]), as_u32(lowv[3])};
+    *reinterpret_cast<u32x4*>(dst + 16) =
+        u32x4{as_u32(highv[0]), as_u32(highv[1]), as_u32(highv[2]), as_u32(highv[3])};
+  }
+  if (tid < 8 * SB) *reinterpret_cast<uint32_t*>(buf + PS::KR + 4 * tid) = ld.kr;
+}
+
+// One step of one wave: Q K^T for the wave's 16 rows, online softmax, P V.
+// FULL: all 32 tokens exist and every row of the tile sees them.
+template <int L, int D, bool FULL>
+__device__ __forceinline__ void prefill_consume(const unsigned char* buf, int lane, int T0, int n_tok, int lim,
+                                                const uint32_t (*qb)[2], const float* qsB, int qoff0, float sqc,
+                                                float& m_run, float& l_run, v4f* oacc) {
+  using T = Layout<L, D>;
+  using PS = PStep<L, D>;
+  constexpr int NG = T::NG, SG = T::SG, SB = T::SB;
+  const int col = lane & 15, r = lane >> 4;
+  float xs[8];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    v4i acc[SG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const uint2 w = *reinterpret_cast<const uint2*>(buf + PS::KC + ((g * 2 + tau) * 64 + lane) * 8);
+      const long A = (long)((uint64_t)w.x | ((uint64_t)w.y << 32));
+      const long B = (long)((uint64_t)qb[g][0] | ((uint64_t)qb[g][1] << 32));
+      if (L == HAD)
+        acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[0], 0, 0, 0);
+      else
+        acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+    }
+    v4f xo = v4f{0.f, 0.f, 0.f, 0.f};
+    if (L != HAD) {
+      // offset term sum_g c_g(t) qsum_g: A[t = col][k = r] from the record of token 16 tau + col
+      const unsigned char* orec = buf + PS::KR + (16 * tau + col) * SB;
+#pragma unroll
+      for (int i = 0; i < NG / 4; ++i) {
+        const _Float16* h = reinterpret_cast<const _Float16*>(orec);
+        const float av = (L == ASYM) ? (float)h[2 * (4 * i + r) + 1] : (float)h[4 * i + r];
+        xo = __builtin_amdgcn_mfma_f32_16x16x4f32(av, qsB[i], xo, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tl = 16 * tau + 4 * r + j;
+      const bool vis = FULL || (tl < n_tok && T0 + tl <= lim);
+      const unsigned char* rec = buf + PS::KR + tl * SB;
+      float x;
+      if (L == HAD) {
+        x = (float)(acc[0][j] - qoff0) * *reinterpret_cast<const float*>(rec);
+      } else {
+        x = xo[j];
+#pragma unroll
+        for (int g = 0; g < SG; ++g) {
+          const uint32_t w = reinterpret_cast<const uint32_t*>(rec)[(L == ASYM) ? g : (g >> 1)];
+          const float s = (float)as_h2(w)[(L == ASYM) ? 0 : (g & 1)];
+          x = fmaf(s, (float)acc[g][j], x);
+        }
+      }
+      xs[tau * 4 + j] = vis ? x * sqc : -INFINITY;
+    }
+  }
+
+  float smax = xs[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) smax = fmaxf(smax, xs[i]);
+  smax = fmaxf(smax, __shfl_xor(smax, 16));
+  smax = fmaxf(smax, __shfl_xor(smax, 32));
+  const float m_new = fmaxf(m_run, smax);
+  const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+  if (__any(m_new > m_run)) {
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+    l_run *= corr;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) oacc[i] *= corr;
+  }
+  m_run = m_new;
+  float psum = 0.0f;
+  v8h pB;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = __builtin_amdgcn_exp2f(xs[i] - m_use);
+    psum += p;
+    pB[i] = (_Float16)p;
+  }
+  l_run += psum;
+
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const v8h A = *reinterpret_cast<const v8h*>(buf + PS::VT + (dt * 64 + lane) * 16);
+    oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pB, oacc[dt], 0, 0, 0);
+  }
+}
+
+// Grid: x = 64-row block * ngroups + chunk (the last group is the window when n_recent > 0),
+// y = kv head, z = batch row.
+template <int L, int D>
+__global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
+  using T = Layout<L, D>;
+  using PS = PStep<L, D>;
+  constexpr int NG = T::NG;
+  constexpr int BIAS = CodeBias<L>::value;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int hk = blockIdx.y, b = blockIdx.z;
+  const int rb = (int)blockIdx.x / a.ngroups;
+  const int c = (int)blockIdx.x - rb * a.ngroups;
+  const int S = a.seq_len[b];
+  const int Sq = a.n_recent > 0 ? max(0, S - a.n_recent) : S;
+  const int nrows = a.n_q * a.G;
+  const int row0 = 64 * rb;
+  const int nblk = min(64, nrows - row0);
+  const int qs0 = a.causal ? a.q_start[b] : 0;
+  if (a.n_recent > 0 && c == a.ngroups - 1) {
+    if (S > 0)
+      for (int k = 0; 16 * k < nblk; ++k)
+        window_partial<L, D>(a, smem, b, hk, S, row0 + 16 * k, min(16, nblk - 16 * k), qs0);
+    return;
+  }
+  const int t_begin = c * a.chunk;
+  if (t_begin >= Sq) return;
+  int t_end = min(t_begin + a.chunk, Sq);
+  const int lim_blk = row_limit(a, qs0, row0 + nblk - 1, nrows);
+  if (a.skip && lim_blk < t_end - 1) t_end = max(t_begin, lim_blk + 1);   // causal skip
+  const int nsteps = (t_end - t_begin + 31) / 32;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, r = lane >> 4;
+  const int wrow0 = row0 + 16 * wave;
+  const int nval = min(16, max(0, nblk - 16 * wave));
+
+  // ---- prologue: the four tiles' queries, one pass per tile through the 16-row preparation
+  float* qf = reinterpret_cast<float*>(smem);
+  int8_t* q8 = reinterpret_cast<int8_t*>(qf + 16 * D);
+  float* sqv = reinterpret_cast<float*>(q8 + 16 * D);
+  int* qsum = reinterpret_cast<int*>(sqv + 16);
+  uint32_t qb[NG][2] = {};
+  float qsB[NG / 4] = {};
+  int qoff0 = 0;
+  float sqc = 0.0f;
+  for (int tile = 0; tile < 4; ++tile) {
+    const int trow0 = row0 + 16 * tile;
+    const int tval = min(16, max(0, nblk - 16 * tile));
+    if (tval == 0) break;   // block-uniform
+    for (int idx = tid; idx < 16 * D; idx += 256) {
+      const int row = idx / D;
+      qf[idx] = row < tval ? a.q[row_index(a, b, hk, trow0 + row) * D + idx % D] : 0.0f;
+    }
+    __syncthreads();
+    prepare_query_lds<L, D>(qf, q8, sqv, qsum);
+    if (wave == tile) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(q8 + col * D + 32 * g + 8 * r);
+        const uint32_t w0 = p[0], w1 = p[1];
+        qb[g][0] = __builtin_amdgcn_perm(w1, w0, 0x06040200u);
+        qb[g][1] = __builtin_amdgcn_perm(w1, w0, 0x07050301u);
+      }
+#pragma unroll
+      for (int i = 0; i < NG / 4; ++i) {
+        const float qs = (float)qsum[col * NG + 4 * i + r];
+        qsB[i] = (L == ASYM) ? qs : -(float)BIAS * qs;
+      }
+      int tot = 0;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) tot += qsum[col * NG + g];
+      qoff0 = BIAS * tot;
+      sqc = sqv[col] * a.alpha * KVQ_LOG2E;
+    }
+    __syncthreads();
+  }
+  const int lim = row_limit(a, qs0, wrow0 + col, nrows);
+  const int lim_min = row_limit(a, qs0, wrow0, nrows);   // -1 for a wave without rows
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  v4f oacc[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) oacc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint32_t magic;   // fp16 "1024 + code" exponent bits, in a VGPR so v_and_or_b32 can take it
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+
+  // page entries of the chunk, one per lane (a 1024-token chunk spans at most 64 pages of >= 16 tokens)
+  const int first_page = t_begin >> a.page_shift;
+  const int npages = nsteps > 0 ? ((t_end - 1) >> a.page_shift) - first_page + 1 : 0;
+  const int lane_page = a.block_table[(size_t)b * a.max_pages + first_page + min(lane, max(npages - 1, 0))];
+  {
+    // read the loaded register here, on every path, so that no wait for this load is left to the
+    // streaming loop (a wait there would also drain the step loads in flight)
+    const int first_phys = __builtin_amdgcn_readfirstlane(lane_page);
+    asm volatile("" ::"s"(first_phys));
+  }
+
+  PLoad<L, D> ld;
+  if (nsteps > 0) {
+    prefill_load<L, D>(a, step_base(a, hk, t_begin, t_end, first_page, lane_page), tid, ld);
+    prefill_produce<L, D>(smem, tid, ld, min(32, t_end - t_begin), magic);
+  }
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int T0 = t_begin + 32 * s;
+    const bool more = s + 1 < nsteps;
+    // the next step's loads (the last iteration reloads its own step, unused, so every iteration
+    // issues the same loads)
+    const int Tn = more ? T0 + 32 : T0;
+    prefill_load<L, D>(a, step_base(a, hk, Tn, t_end, first_page, lane_page), tid, ld);
+    const unsigned char* buf = smem + (s & 1) * PS::BYTES;
+    const int n_tok = min(32, t_end - T0);
+    if (nval > 0) {
+      if (n_tok == 32 && T0 + 31 <= lim_min)
+        prefill_consume<L, D, true>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, oacc);
+      else
+        prefill_consume<L, D, false>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, oacc);
+    }
+    if (more) prefill_produce<L, D>(smem + ((s + 1) & 1) * PS::BYTES, tid, ld, min(32, t_end - Tn), magic);
+    __syncthreads();
+  }
+
+  // ---------------- this wave's chunk partial: o[d = 16 dt + 4 r + j] of row col
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (col < nval) {
+    float* dst = a.ws + (row_index(a, b, hk, wrow0 + col) * a.nc1 + c) * partial_stride(D);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<v4f*>(dst + 16 * dt + 4 * r) = oacc[dt];
+    if (r == 0) {
+      dst[D] = m_run;
+      dst[D + 1] = l_run;
+    }
+  }
+}
+
+template <int L, int D>
+static void launch_prefill(const AttendArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+  if (lds > 65536)
+    (void)hipFuncSetAttribute((const void*)prefill_partial<L, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((prefill_partial<L, D>), grid, dim3(256), lds, st, a);
+}
+
+typedef void (*prefill_fn)(const AttendArgs&, dim3, size_t, hipStream_t);
+
+static prefill_fn pick_prefill(int layout, int D) {
+  const int di = D == 256 ? 1 : 0;
+  static const prefill_fn tab[4][2] = {
+      {launch_prefill<HAD, 128>, launch_prefill<HAD, 256>},
+      {launch_prefill<Q40, 128>, launch_prefill<Q40, 256>},
+      {launch_prefill<Q60, 128>, launch_prefill<Q60, 256>},
+      {launch_prefill<ASYM, 128>, launch_prefill<ASYM, 256>},
+  };
+  return tab[layout][di];
+}
+
+static size_t prefill_lds_bytes(int layout, int D, int n_recent) {
+  const size_t pb = (size_t)(D / 32) * 1024 + (size_t)D * 64 + 32 * scale_bytes_rt(layout, D);
+  const size_t pro = (size_t)16 * D * 4 + 16 * D + 16 * 4 + 16 * (D / 32) * 4;
+  const size_t win = n_recent > 0 ? (size_t)(D == 128 ? window_lds_bytes<128>() : window_lds_bytes<256>()) : 0;
+  size_t m = 2 * pb > pro ? 2 * pb : pro;
+  return m > win ? m : win;
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t Hq, int32_t D,
+                                              int32_t max_seq_len) {
+  if (batch < 1 || n_q < 1 || Hq < 1 || (D != 128 && D != 256) || max_seq_len < 0) return 0;
+  const size_t nc1 = (size_t)chunks_of(max_seq_len, kPrefillChunk) + 1;
+  return (size_t)batch * n_q * Hq * nc1 * partial_stride(D) * sizeof(float);
+}
+
+extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float* q, float* out, int32_t batch,
+                                                int32_t n_q, int32_t Hq, float alpha, int32_t causal,
+                                                const int32_t* q_start, const int32_t* block_table,
+                                                int32_t max_pages, const int32_t* seq_len, int32_t max_seq_len,
+                                                uint32_t flags, void* workspace, size_t ws_bytes, void* stream) {
+  kvq_status st = check_attend_args(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len);
+  if (st != KVQ_OK) return st;
+  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out must be non-null");
+  if (n_q < 1) return fail(KVQ_ERR_INVALID_ARG, "n_q must be >= 1");
+  if (causal != 0 && causal != 1) return fail(KVQ_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (causal && !q_start) return fail(KVQ_ERR_INVALID_ARG, "q_start must be non-null when causal");
+  if (flags & ~KVQ_PREFILL_NO_CAUSAL_SKIP) return fail(KVQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((int64_t)batch * n_q * Hq > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "batch * n_q * num_q_heads above 2^31 - 1");
+  const size_t need = kvq_prefill_workspace_bytes(batch, n_q, Hq, c->head_dim, max_seq_len);
+  if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  AttendArgs a = make_args(c, q, Hq, n_q, alpha, block_table, max_pages, seq_len, max_seq_len, kPrefillChunk,
+                           workspace);
+  a.causal = causal;
+  a.skip = causal && !(flags & KVQ_PREFILL_NO_CAUSAL_SKIP);
+  a.q_start = causal ? q_start : nullptr;
+  const int nch = chunks_of(max_seq_len, kPrefillChunk);
+  a.ngroups = nch + (c->n_recent > 0 ? 1 : 0);
+  const int64_t gx = ((int64_t)n_q * a.G + 63) / 64 * a.ngroups;
+  if (gx > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
+  if (gx > 0) {
+    const dim3 grid((unsigned)gx, c->num_kv_heads, batch);
+    pick_prefill(c->layout, c->head_dim)(a, grid, prefill_lds_bytes(c->layout, c->head_dim, c->n_recent),
+                                         (hipStream_t)stream);
+    if ((st = check_launch("prefill partial kernel")) != KVQ_OK) return st;
+  }
+  return launch_reduce(c, out, batch, n_q * Hq, seq_len, a.nc1, kPrefillChunk, (const float*)workspace,
+                       (hipStream_t)stream);
+}

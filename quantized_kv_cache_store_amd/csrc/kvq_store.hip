@@ -191,8 +191,8 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
 // Query preparation export: 16 vectors per block.
 template <int L, int D>
 __global__ __launch_bounds__(256) void quantize_q_kernel(const float* q, int n_vec, int8_t* q8, float* sq) {
-  __shared__ float qf[16 * D];
-  __shared__ int8_t q8s[16 * D];
+  __shared__ __align__(16) float qf[16 * D];
+  __shared__ __align__(16) int8_t q8s[16 * D];
   __shared__ float sqs[16];
   __shared__ int qsum[16 * (D / 32)];
   const int v0 = blockIdx.x * 16;
