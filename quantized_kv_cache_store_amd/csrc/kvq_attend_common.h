@@ -26,6 +26,10 @@ struct AttendArgs {
   const int32_t* block_table;
   const int32_t* seq_len;
   const int32_t* q_start;   // [batch] position of query 0 (causal prefill), else null
+  const float* qrot;        // prepared rows (prefill): f32 query, rotated for HAD, [rows][D], else null
+  const int8_t* q8p;        // prepared rows: int8 query [rows][D]
+  const float* sqp;         // prepared rows: its scale [rows]
+  const int* qsump;         // prepared rows: sum of q8 per 32-element block [rows][D / 32]
   int32_t* dbg;
   int Hkv, Hq, G, page_shift, n_recent, max_pages, chunk, nc1, max_seq_len;
   int n_q;       // queries per batch row (1 for decode)
@@ -79,9 +83,10 @@ __host__ __device__ constexpr int window_lds_bytes() {
 
 template <int L, int D>
 __device__ __forceinline__ void window_partial(const AttendArgs& a, unsigned char* smem, int b, int hk, int S, int row0,
-                                            int nvalid, int qs0) {
+                                               int nvalid, int qs0) {
   constexpr int E = D / 16;
   constexpr int KST = D + 4;
+  constexpr int NL = D / 64;          // float4 of one tile's K (and of its V) per thread
   float* qf = reinterpret_cast<float*>(smem);
   int8_t* q8 = reinterpret_cast<int8_t*>(qf + 16 * D);
   float* sq = reinterpret_cast<float*>(q8 + 16 * D);
@@ -91,12 +96,13 @@ __device__ __forceinline__ void window_partial(const AttendArgs& a, unsigned cha
   float* pt = vt + 16 * D;
   const int tid = threadIdx.x;
   const int nrows = a.n_q * a.G;
+  const float* qsrc = a.qrot ? a.qrot : a.q;     // prepared rows are already rotated
   for (int idx = tid; idx < 16 * D; idx += 256) {
     const int row = idx / D;
-    qf[idx] = row < nvalid ? a.q[row_index(a, b, hk, row0 + row) * D + idx % D] : 0.0f;
+    qf[idx] = row < nvalid ? qsrc[row_index(a, b, hk, row0 + row) * D + idx % D] : 0.0f;
   }
   __syncthreads();
-  prepare_query_lds<L, D>(qf, q8, sq, qsum);
+  if (!a.qrot) prepare_query_lds<L, D>(qf, q8, sq, qsum);
   const int W = min(S, a.n_recent);
   const int w0 = S - W;
   const size_t ring0 = ((size_t)b * a.Hkv + hk) * a.n_recent;
@@ -107,20 +113,35 @@ __device__ __forceinline__ void window_partial(const AttendArgs& a, unsigned cha
   float o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.0f;
-  for (int t0 = 0; t0 < W; t0 += 16) {
-    // stage the tile's K and V rows (rows past the window: zeros)
-    for (int idx = tid; idx < 16 * D / 4; idx += 256) {
+  // tile loads in registers, one tile ahead (rows past the window: zeros)
+  float4 kreg[NL], vreg[NL];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int n = 0; n < NL; ++n) {
+      const int idx = tid + 256 * n;
       const int tt = idx / (D / 4), c4 = idx % (D / 4);
-      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      kreg[n] = make_float4(0.f, 0.f, 0.f, 0.f);
+      vreg[n] = kreg[n];
       if (t0 + tt < W) {
-        const size_t ro = (ring0 + (size_t)((w0 + t0 + tt) % a.n_recent)) * D + 4 * c4;
-        kv = *reinterpret_cast<const float4*>(a.kring + ro);
-        vv = *reinterpret_cast<const float4*>(a.vring + ro);
+        int slot = w0 + t0 + tt;
+        slot -= (slot / a.n_recent) * a.n_recent;
+        const size_t ro = (ring0 + (size_t)slot) * D + 4 * c4;
+        kreg[n] = *reinterpret_cast<const float4*>(a.kring + ro);
+        vreg[n] = *reinterpret_cast<const float4*>(a.vring + ro);
       }
-      *reinterpret_cast<float4*>(kt + tt * KST + 4 * c4) = kv;
-      *reinterpret_cast<float4*>(vt + tt * D + 4 * c4) = vv;
+    }
+  };
+  if (W > 0) load_tile(0);
+  for (int t0 = 0; t0 < W; t0 += 16) {
+#pragma unroll
+    for (int n = 0; n < NL; ++n) {
+      const int idx = tid + 256 * n;
+      const int tt = idx / (D / 4), c4 = idx % (D / 4);
+      *reinterpret_cast<float4*>(kt + tt * KST + 4 * c4) = kreg[n];
+      *reinterpret_cast<float4*>(vt + tt * D + 4 * c4) = vreg[n];
     }
     __syncthreads();
+    if (t0 + 16 < W) load_tile(t0 + 16);
     // score of token t0 + j for this thread's row
     float acc = 0.0f;
     const float* qr = qf + row * D;

@@ -302,8 +302,9 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
   }
 }
 
-// Grid: x = 64-row block * ngroups + chunk (the last group is the window when n_recent > 0),
-// y = kv head, z = batch row.
+// Grid: x = 64-row block * ngroups + group, the groups being the chunks of the quantised region
+// and, when n_recent > 0, four window groups (one per 16-row tile); y = kv head, z = batch row.
+// The rows' int8 queries, scales and block sums come prepared by prepare_rows.
 template <int L, int D>
 __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
   using T = Layout<L, D>;
@@ -321,10 +322,10 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
   const int row0 = 64 * rb;
   const int nblk = min(64, nrows - row0);
   const int qs0 = a.causal ? a.q_start[b] : 0;
-  if (a.n_recent > 0 && c == a.ngroups - 1) {
-    if (S > 0)
-      for (int k = 0; 16 * k < nblk; ++k)
-        window_partial<L, D>(a, smem, b, hk, S, row0 + 16 * k, min(16, nblk - 16 * k), qs0);
+  const int nch = a.n_recent > 0 ? a.ngroups - 4 : a.ngroups;
+  if (c >= nch) {   // window blocks: one per 16-row tile of the 64 rows
+    const int k = c - nch;
+    if (S > 0 && 16 * k < nblk) window_partial<L, D>(a, smem, b, hk, S, row0 + 16 * k, min(16, nblk - 16 * k), qs0);
     return;
   }
   const int t_begin = c * a.chunk;
@@ -341,45 +342,28 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
   const int wrow0 = row0 + 16 * wave;
   const int nval = min(16, max(0, nblk - 16 * wave));
 
-  // ---- prologue: the four tiles' queries, one pass per tile through the 16-row preparation
-  float* qf = reinterpret_cast<float*>(smem);
-  int8_t* q8 = reinterpret_cast<int8_t*>(qf + 16 * D);
-  float* sqv = reinterpret_cast<float*>(q8 + 16 * D);
-  int* qsum = reinterpret_cast<int*>(sqv + 16);
+  // ---- prologue: this wave's 16 rows from the prepared rows (int8 query in the B-operand order,
+  // its scale and block sums); the perms consume the loads here, outside the streaming loop
   uint32_t qb[NG][2] = {};
   float qsB[NG / 4] = {};
   int qoff0 = 0;
   float sqc = 0.0f;
-  for (int tile = 0; tile < 4; ++tile) {
-    const int trow0 = row0 + 16 * tile;
-    const int tval = min(16, max(0, nblk - 16 * tile));
-    if (tval == 0) break;   // block-uniform
-    for (int idx = tid; idx < 16 * D; idx += 256) {
-      const int row = idx / D;
-      qf[idx] = row < tval ? a.q[row_index(a, b, hk, trow0 + row) * D + idx % D] : 0.0f;
+  if (col < nval) {
+    const size_t fr = row_index(a, b, hk, wrow0 + col);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const uint2 w = *reinterpret_cast<const uint2*>(a.q8p + fr * D + 32 * g + 8 * r);
+      qb[g][0] = __builtin_amdgcn_perm(w.y, w.x, 0x06040200u);
+      qb[g][1] = __builtin_amdgcn_perm(w.y, w.x, 0x07050301u);
     }
-    __syncthreads();
-    prepare_query_lds<L, D>(qf, q8, sqv, qsum);
-    if (wave == tile) {
+    const int* qs = a.qsump + fr * NG;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(q8 + col * D + 32 * g + 8 * r);
-        const uint32_t w0 = p[0], w1 = p[1];
-        qb[g][0] = __builtin_amdgcn_perm(w1, w0, 0x06040200u);
-        qb[g][1] = __builtin_amdgcn_perm(w1, w0, 0x07050301u);
-      }
+    for (int i = 0; i < NG / 4; ++i) qsB[i] = (L == ASYM) ? (float)qs[4 * i + r] : -(float)BIAS * (float)qs[4 * i + r];
+    int tot = 0;
 #pragma unroll
-      for (int i = 0; i < NG / 4; ++i) {
-        const float qs = (float)qsum[col * NG + 4 * i + r];
-        qsB[i] = (L == ASYM) ? qs : -(float)BIAS * qs;
-      }
-      int tot = 0;
-#pragma unroll
-      for (int g = 0; g < NG; ++g) tot += qsum[col * NG + g];
-      qoff0 = BIAS * tot;
-      sqc = sqv[col] * a.alpha * KVQ_LOG2E;
-    }
-    __syncthreads();
+    for (int g = 0; g < NG; ++g) tot += qs[g];
+    qoff0 = BIAS * tot;
+    sqc = a.sqp[fr] * a.alpha * KVQ_LOG2E;
   }
   const int lim = row_limit(a, qs0, wrow0 + col, nrows);
   const int lim_min = row_limit(a, qs0, wrow0, nrows);   // -1 for a wave without rows
@@ -441,6 +425,54 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
   }
 }
 
+// Query preparation of every row once (a1), 16 rows per block: int8 query, scale, per-block sums,
+// and for the Hadamard layout the rotated f32 query the window uses.
+template <int L, int D>
+__global__ __launch_bounds__(256) void prepare_rows(const float* q, int n_vec, float* qrot, int8_t* q8, float* sq,
+                                                    int* qsum) {
+  constexpr int NG = D / 32;
+  __shared__ __align__(16) float qf[16 * D];
+  __shared__ __align__(16) int8_t q8s[16 * D];
+  __shared__ float sqs[16];
+  __shared__ int qss[16 * NG];
+  const int tid = threadIdx.x;
+  const int v0 = blockIdx.x * 16;
+  const int nv = min(16, n_vec - v0);
+  for (int idx = tid; idx < 4 * D; idx += 256) {     // float4 of 16 rows
+    const int row = idx / (D / 4);
+    const float4 v = row < nv ? reinterpret_cast<const float4*>(q + (size_t)v0 * D)[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+    reinterpret_cast<float4*>(qf)[idx] = v;
+  }
+  __syncthreads();
+  prepare_query_lds<L, D>(qf, q8s, sqs, qss);
+  if (L == HAD) {
+    for (int idx = tid; idx < 4 * D; idx += 256)
+      if (idx / (D / 4) < nv) reinterpret_cast<float4*>(qrot + (size_t)v0 * D)[idx] = reinterpret_cast<const float4*>(qf)[idx];
+  }
+  for (int idx = tid; idx < D; idx += 256)          // 16-byte pieces of 16 rows
+    if (idx / (D / 16) < nv) reinterpret_cast<u32x4*>(q8 + (size_t)v0 * D)[idx] = reinterpret_cast<const u32x4*>(q8s)[idx];
+  if (tid < 16 * NG && tid / NG < nv) qsum[(size_t)v0 * NG + tid] = qss[tid];
+  if (tid < nv) sq[v0 + tid] = sqs[tid];
+}
+
+template <int L, int D>
+static void launch_prepare(const float* q, int n_vec, float* qrot, int8_t* q8, float* sq, int* qsum, hipStream_t st) {
+  hipLaunchKernelGGL((prepare_rows<L, D>), dim3((n_vec + 15) / 16), dim3(256), 0, st, q, n_vec, qrot, q8, sq, qsum);
+}
+
+typedef void (*prepare_fn)(const float*, int, float*, int8_t*, float*, int*, hipStream_t);
+
+static prepare_fn pick_prepare(int layout, int D) {
+  const int di = D == 256 ? 1 : 0;
+  static const prepare_fn tab[4][2] = {
+      {launch_prepare<HAD, 128>, launch_prepare<HAD, 256>},
+      {launch_prepare<Q40, 128>, launch_prepare<Q40, 256>},
+      {launch_prepare<Q60, 128>, launch_prepare<Q60, 256>},
+      {launch_prepare<ASYM, 128>, launch_prepare<ASYM, 256>},
+  };
+  return tab[layout][di];
+}
+
 template <int L, int D>
 static void launch_prefill(const AttendArgs& a, dim3 grid, size_t lds, hipStream_t st) {
   if (lds > 65536)
@@ -463,10 +495,27 @@ static prefill_fn pick_prefill(int layout, int D) {
 
 static size_t prefill_lds_bytes(int layout, int D, int n_recent) {
   const size_t pb = (size_t)(D / 32) * 1024 + (size_t)D * 64 + 32 * scale_bytes_rt(layout, D);
-  const size_t pro = (size_t)16 * D * 4 + 16 * D + 16 * 4 + 16 * (D / 32) * 4;
   const size_t win = n_recent > 0 ? (size_t)(D == 128 ? window_lds_bytes<128>() : window_lds_bytes<256>()) : 0;
-  size_t m = 2 * pb > pro ? 2 * pb : pro;
-  return m > win ? m : win;
+  return 2 * pb > win ? 2 * pb : win;
+}
+
+static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Workspace of the prefill: [partials f32 rows x (chunks + 1) x (D + 4)] [rotated query f32 rows x D]
+// [int8 query rows x D] [scale f32 rows] [block sums int32 rows x D / 32], each part 16-byte aligned.
+struct PrefillWs {
+  size_t qrot, q8, sq, qsum, total;
+};
+
+static PrefillWs prefill_ws(size_t rows, int D, int max_seq_len) {
+  PrefillWs w;
+  const size_t nc1 = (size_t)chunks_of(max_seq_len, kPrefillChunk) + 1;
+  w.qrot = align16(rows * nc1 * partial_stride(D) * sizeof(float));
+  w.q8 = w.qrot + align16(rows * D * sizeof(float));
+  w.sq = w.q8 + align16(rows * D);
+  w.qsum = w.sq + align16(rows * sizeof(float));
+  w.total = w.qsum + align16(rows * (D / 32) * sizeof(int));
+  return w;
 }
 
 }  // namespace kvq
@@ -476,8 +525,7 @@ using namespace kvq;
 extern "C" size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t Hq, int32_t D,
                                               int32_t max_seq_len) {
   if (batch < 1 || n_q < 1 || Hq < 1 || (D != 128 && D != 256) || max_seq_len < 0) return 0;
-  const size_t nc1 = (size_t)chunks_of(max_seq_len, kPrefillChunk) + 1;
-  return (size_t)batch * n_q * Hq * nc1 * partial_stride(D) * sizeof(float);
+  return prefill_ws((size_t)batch * n_q * Hq, D, max_seq_len).total;
 }
 
 extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float* q, float* out, int32_t batch,
@@ -501,9 +549,19 @@ extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float*
   a.skip = causal && !(flags & KVQ_PREFILL_NO_CAUSAL_SKIP);
   a.q_start = causal ? q_start : nullptr;
   const int nch = chunks_of(max_seq_len, kPrefillChunk);
-  a.ngroups = nch + (c->n_recent > 0 ? 1 : 0);
+  a.ngroups = nch + (c->n_recent > 0 ? 4 : 0);
   const int64_t gx = ((int64_t)n_q * a.G + 63) / 64 * a.ngroups;
   if (gx > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
+  const int rows = batch * n_q * Hq;
+  const PrefillWs w = prefill_ws((size_t)rows, c->head_dim, max_seq_len);
+  unsigned char* wsb = (unsigned char*)workspace;
+  a.qrot = c->layout == HAD ? (const float*)(wsb + w.qrot) : q;   // the window's f32 query
+  a.q8p = (const int8_t*)(wsb + w.q8);
+  a.sqp = (const float*)(wsb + w.sq);
+  a.qsump = (const int*)(wsb + w.qsum);
+  pick_prepare(c->layout, c->head_dim)(q, rows, (float*)(wsb + w.qrot), (int8_t*)(wsb + w.q8), (float*)(wsb + w.sq),
+                                       (int*)(wsb + w.qsum), (hipStream_t)stream);
+  if ((st = check_launch("prefill query preparation kernel")) != KVQ_OK) return st;
   if (gx > 0) {
     const dim3 grid((unsigned)gx, c->num_kv_heads, batch);
     pick_prefill(c->layout, c->head_dim)(a, grid, prefill_lds_bytes(c->layout, c->head_dim, c->n_recent),

@@ -80,8 +80,10 @@ def test_attend_validates_before_launch():
 def test_prefill_validates_before_launch():
     lib = kvq.load()
     d = ctypes.byref(_desc())
-    # partials [B][n_q][Hq][1024-token chunks + 1][D + 4] f32
-    assert lib.kvq_prefill_workspace_bytes(1, 512, 16, 128, 8704) == 512 * 16 * 10 * 132 * 4
+    # partials [B][n_q][Hq][1024-token chunks + 1][D + 4] f32, then the prepared rows:
+    # rotated f32 query, int8 query, f32 scale, int32 block sums
+    rows = 512 * 16
+    assert lib.kvq_prefill_workspace_bytes(1, 512, 16, 128, 8704) == rows * (10 * 132 * 4 + 128 * 4 + 128 + 4 + 4 * 4)
     assert lib.kvq_prefill_workspace_bytes(1, 0, 16, 128, 8704) == 0
     big = 1 << 30
     pf = lib.kvq_attend_prefill_causal
