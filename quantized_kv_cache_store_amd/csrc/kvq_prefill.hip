@@ -306,7 +306,7 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
 // and, when n_recent > 0, four window groups (one per 16-row tile); y = kv head, z = batch row.
 // The rows' int8 queries, scales and block sums come prepared by prepare_rows.
 template <int L, int D>
-__global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
+__global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendArgs a) {
   using T = Layout<L, D>;
   using PS = PStep<L, D>;
   constexpr int NG = T::NG;
