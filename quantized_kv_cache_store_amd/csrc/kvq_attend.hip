@@ -42,13 +42,17 @@
 namespace kvq {
 
 // Staging buffer of one 32-token step in a wave's LDS slice:
-//   [K payload rows 32 x PB][V payload rows 32 x PB][K records 32 x SB][V records 32 x SB]
+//   [K payload rows 32 x RS][V payload rows 32 x RS][K records 32 x SB][V records 32 x SB]
+// with payload rows padded to RS = PB + 16 bytes, which spreads the reads of a 16-row column
+// (K: one dword per lane from 16 rows; V: 16 dwords of one row times four rows 4 apart) over
+// all 64 LDS banks.
 // filled from registers that were loaded one step ahead with 16-byte loads.
 template <int L, int D>
 struct Step {
   using T = Layout<L, D>;
   static constexpr int PB = T::PB, SB = T::SB;
-  static constexpr int KP = 0, VP = 32 * PB, KR = 64 * PB, VR = KR + 32 * SB;
+  static constexpr int RS = PB + 16;
+  static constexpr int KP = 0, VP = 32 * RS, KR = 64 * RS, VR = KR + 32 * SB;
   static constexpr int BYTES = VR + 32 * SB;
   static constexpr int PAY_SLOTS = (2 * PB + 63) / 64;   // 16-byte chunks of 32 payload rows, per lane
   static constexpr int REC_SLOTS = (4 * SB + 63) / 64;   // K and V records together
@@ -146,8 +150,9 @@ __device__ __forceinline__ void stage_step(unsigned char* buf, int lane, const u
   for (int k = 0; k < ST::PAY_SLOTS; ++k) {
     const int ci = lane + 64 * k;
     if (ci < 2 * PB) {
-      *reinterpret_cast<u32x4*>(buf + ST::KP + ci * 16) = pre[k];
-      *reinterpret_cast<u32x4*>(buf + ST::VP + ci * 16) = pre[ST::PAY_SLOTS + k];
+      const int at = (ci / (PB / 16)) * ST::RS + (ci % (PB / 16)) * 16;   // row ci / (PB / 16), padded
+      *reinterpret_cast<u32x4*>(buf + ST::KP + at) = pre[k];
+      *reinterpret_cast<u32x4*>(buf + ST::VP + at) = pre[ST::PAY_SLOTS + k];
     }
   }
 #pragma unroll
@@ -190,7 +195,7 @@ __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned 
   float vs_had[8];
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
-    const unsigned char* krow = buf + ST::KP + (16 * tau + col) * PB;
+    const unsigned char* krow = buf + ST::KP + (16 * tau + col) * ST::RS;
     v4i acc[SG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -257,8 +262,7 @@ __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned 
   float smax = xs[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) smax = fmaxf(smax, xs[i]);
-  smax = fmaxf(smax, __shfl_xor(smax, 16));
-  smax = fmaxf(smax, __shfl_xor(smax, 32));
+  smax = max_over_rows(smax);
   const float m_new = fmaxf(m_run, smax);
   const float m_use = m_new == -INFINITY ? 0.0f : m_new;
   // rescale the running sums only when some lane's maximum moved (rare after the first steps)
@@ -289,7 +293,7 @@ __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned 
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int tl = 16 * (k >> 2) + 4 * r + (k & 3);
-      const unsigned char* vrow = buf + ST::VP + tl * PB;
+      const unsigned char* vrow = buf + ST::VP + tl * ST::RS;
       if (L == Q60) {
         const uint32_t x = *reinterpret_cast<const uint32_t*>(vrow + 24 * grp + 4 * (oc & 3));
         const uint32_t t2 = *reinterpret_cast<const uint16_t*>(vrow + 24 * grp + 16 + 2 * (oc & 3));
@@ -480,8 +484,7 @@ __global__ __launch_bounds__(256, 2) void attend_partial(AttendArgs a) {
   if (DBG) return;
 
   // ---------------- this wave's chunk partial
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_over_rows(l_run);
   if (col < nvalid) {
     float* dst = a.ws + (row_index(a, b, hk, row0 + col) * a.nc1 + c) * partial_stride(D);
 #pragma unroll
@@ -587,7 +590,7 @@ static partial_fn pick_partial(int layout, int D) {
 }
 
 static size_t step_bytes(int layout, int D) {
-  return 64 * (payload_bytes_rt(layout, D) + scale_bytes_rt(layout, D));
+  return 64 * (payload_bytes_rt(layout, D) + 16 + scale_bytes_rt(layout, D));
 }
 
 static size_t partial_lds_bytes(int layout, int D, int n_recent) {

@@ -57,6 +57,36 @@ __host__ __device__ constexpr int prologue_lds_bytes() {
   return 16 * D * 4 + 16 * D + 16 * 4 + 16 * (D / 32) * 4;
 }
 
+// Reductions over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48), on the VALU:
+// v_permlane16_swap / v_permlane32_swap applied to two copies of a value leave in the two
+// registers the value of the lane and of its partner row, in row order, so both lanes of a pair
+// compute the same result.  Written as inline assembly with both registers read-write (the
+// compiler's built-in for it folds its two results into one), with the wait states the swap
+// needs after the VALU writes of its operands.
+__device__ __forceinline__ void row_pair(float v, int swap32, float& lo, float& hi) {
+  float x = v, y = v;
+  if (swap32)
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+  else
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+  lo = x;
+  hi = y;
+}
+
+__device__ __forceinline__ float max_over_rows(float v) {
+  float a, b;
+  row_pair(v, 0, a, b);
+  row_pair(fmaxf(a, b), 1, a, b);
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float sum_over_rows(float v) {
+  float a, b;
+  row_pair(v, 0, a, b);
+  row_pair(a + b, 1, a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 

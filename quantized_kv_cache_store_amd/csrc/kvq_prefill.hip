@@ -274,8 +274,7 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
   float smax = xs[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) smax = fmaxf(smax, xs[i]);
-  smax = fmaxf(smax, __shfl_xor(smax, 16));
-  smax = fmaxf(smax, __shfl_xor(smax, 32));
+  smax = max_over_rows(smax);
   const float m_new = fmaxf(m_run, smax);
   const float m_use = m_new == -INFINITY ? 0.0f : m_new;
   if (__any(m_new > m_run)) {
@@ -412,8 +411,7 @@ __global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendA
   }
 
   // ---------------- this wave's chunk partial: o[d = 16 dt + 4 r + j] of row col
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_over_rows(l_run);
   if (col < nval) {
     float* dst = a.ws + (row_index(a, b, hk, wrow0 + col) * a.nc1 + c) * partial_stride(D);
 #pragma unroll
