@@ -113,7 +113,9 @@ kvq_status kvq_store(const kvq_cache* cache, const float* k_new, const float* v_
                      const int32_t* pos, const int32_t* seq_len, void* stream);
 
 /* Workspace of kvq_attend_decode: split-K partials (o_c, m_c, l_c) per
- * (batch, query head, chunk), plus the window partial. */
+ * (batch, query head, chunk), plus the window partial, then the prepared
+ * queries (int8, scale, block sums, rotated f32 for HAD_INT4) per
+ * (batch, query head).  Returns 0 for invalid arguments. */
 size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_seq_len, int32_t chunk_tokens);
 
@@ -163,8 +165,9 @@ kvq_status kvq_attend_decode_reduce(const kvq_cache* cache, float* out, int32_t 
                                     void* stream);
 
 /* Workspace of kvq_attend_prefill_causal: split-K partials (o_c, m_c, l_c)
- * per (batch, query, query head, 1024-token chunk), plus the window partial.
- * Returns 0 for invalid arguments. */
+ * per (batch, query, query head, 1024-token chunk), plus the window partial,
+ * then the prepared queries per (batch, query, query head).  Returns 0 for
+ * invalid arguments. */
 size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t num_q_heads,
                                    int32_t head_dim, int32_t max_seq_len);
 
@@ -207,12 +210,15 @@ kvq_status kvq_debug_quantize_q(int32_t layout, const float* q, int32_t n_vec, i
 /* The decode kernel's per-block integer scores I[t][g] = sum_j q8_j * code_tj
  * over block g (the whole row for HAD_INT4), for quantised tokens
  * t < seq_len[b] - n_recent; other entries are left untouched.
- *   scores device int32 [batch][num_q_heads][max_seq_len][n_groups],
- *   n_groups = 1 for HAD_INT4, head_dim/32 otherwise. */
+ *   scores     device int32 [batch][num_q_heads][max_seq_len][n_groups],
+ *              n_groups = 1 for HAD_INT4, head_dim/32 otherwise
+ *   workspace  kvq_decode_workspace_bytes(batch, num_q_heads, head_dim,
+ *              max_seq_len, 512) bytes of device memory (the prepared queries) */
 kvq_status kvq_debug_qk_i32(const kvq_cache* cache, const float* q, int32_t batch,
                             int32_t num_q_heads, const int32_t* block_table,
                             int32_t max_pages_per_seq, const int32_t* seq_len,
-                            int32_t max_seq_len, int32_t* scores, void* stream);
+                            int32_t max_seq_len, int32_t* scores, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 const char* kvq_status_string(kvq_status status);
 const char* kvq_last_error(void);

@@ -45,7 +45,7 @@ SIGNATURES = {
     "kvq_attend_prefill_causal": (c_i32, [P, c_vp, c_vp, c_i32, c_i32, c_i32, c_f, c_i32, c_vp, c_vp, c_i32,
                                           c_vp, c_i32, c_u32, c_vp, c_size, c_vp]),
     "kvq_debug_quantize_q": (c_i32, [c_i32, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]),
-    "kvq_debug_qk_i32": (c_i32, [P, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),
+    "kvq_debug_qk_i32": (c_i32, [P, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_size, c_vp]),
     "kvq_status_string": (ctypes.c_char_p, [c_i32]),
     "kvq_last_error": (ctypes.c_char_p, []),
 }

@@ -179,7 +179,7 @@ __device__ __forceinline__ uint32_t rec_word(const unsigned char* rec, int idx) 
 // drow: flat row index of this lane's row for the score export (DBG), or -1.
 template <int L, int D, bool DBG, bool FULL>
 __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned char* buf, int T0, int t_end,
-                                            int lim, long drow, int col, int r, const uint32_t (*qb)[2],
+                                            int lim, long drow, int col, int r, const long* qB,
                                             const float* qsB, const int* qoff, float sqc, uint32_t magic,
                                             float& m_run, float& l_run, v4f* oacc) {
   using T = Layout<L, D>;
@@ -210,8 +210,8 @@ __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned 
         lo = x & 0x0F0F0F0Fu;
         hi = (x >> 4) & 0x0F0F0F0Fu;
       }
-      const long A = (long)((uint64_t)lo | ((uint64_t)hi << 32));
-      const long B = (long)((uint64_t)qb[g][0] | ((uint64_t)qb[g][1] << 32));
+      const long A = __builtin_bit_cast(long, u32x2{lo, hi});
+      const long B = qB[g];
       if (L == HAD) {
         acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[0], 0, 0, 0);
       } else {
@@ -361,6 +361,8 @@ __global__ __launch_bounds__(256, 2) void attend_partial(AttendArgs a) {
   constexpr int BIAS = CodeBias<L>::value;
   extern __shared__ __align__(16) unsigned char smem[];
 
+  // Block numbering: chunk group fastest (measured faster than kv head or batch row fastest: blocks
+  // that run together then stream neighbouring chunks of one (row, kv head)).
   const int hk = blockIdx.y, b = blockIdx.z;
   const int tile = (int)blockIdx.x / a.ngroups;
   const int cg = (int)blockIdx.x - tile * a.ngroups;
@@ -389,65 +391,42 @@ __global__ __launch_bounds__(256, 2) void attend_partial(AttendArgs a) {
   const size_t row_first = active ? chunk_row(a, cp, hk, t_begin) : 0;
   const int nsteps = active ? (t_end - t_begin + 31) / 32 : 0;
 
-  // query rows of the tile into registers first (all loads in flight together, before the ring)
-  constexpr int QPT = 16 * D / 256;
-  float qv[QPT];
-#pragma unroll
-  for (int i = 0; i < QPT; ++i) {
-    const int idx = threadIdx.x + 256 * i;
-    const int row = idx / D;
-    qv[i] = a.q[row_index(a, b, hk, row0 + min(row, nvalid - 1)) * D + idx % D];
-  }
-
   u32x4 pre[NB][ST::SLOTS];
 
-  // ---- prologue: query preparation for the rows of the tile
-  float* qf = reinterpret_cast<float*>(smem);
-  int8_t* q8 = reinterpret_cast<int8_t*>(qf + 16 * D);
-  float* sqv = reinterpret_cast<float*>(q8 + 16 * D);
-  int* qsum = reinterpret_cast<int*>(sqv + 16);
-#pragma unroll
-  for (int i = 0; i < QPT; ++i) {
-    const int idx = threadIdx.x + 256 * i;
-    qf[idx] = (idx / D) < nvalid ? qv[i] : 0.0f;
-  }
-  __syncthreads();
-  prepare_query_lds<L, D>(qf, q8, sqv, qsum);
-
+  // ---- prologue: this lane's row of the tile from the prepared rows (int8 query in the B-operand
+  // order, its scale and block sums); the perms and sums consume the loads here, before the loop
   const int col = lane & 15;
   const int r = lane >> 4;
-  uint32_t qb[NG][2];
+  long qB[NG];   // B operands (int8 query of the tile's rows), one aligned register pair each
+  float qsB[NG / 4];   // offset-term operand: zero point (asym) or -bias * scale times the block sums
+  int qoff[SG];        // bias * sum(q8): the Hadamard scores and the score export use it
+  float sqc = 0.0f;
+  {
+    const size_t fr = row_index(a, b, hk, row0 + min(col, nvalid - 1));
+    const int* qs = a.qsump + fr * NG;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(q8 + col * D + 32 * g + 8 * r);
-    const uint32_t w0 = p[0], w1 = p[1];
-    qb[g][0] = __builtin_amdgcn_perm(w1, w0, 0x06040200u);
-    qb[g][1] = __builtin_amdgcn_perm(w1, w0, 0x07050301u);
-  }
-  // Offset term of the block layouts, sum_g c_g(t) * qsum_g[h], on the f32 MFMA (k = 4 blocks
-  // per product): c_g = zero point (asym), or -bias * scale (codes fed to the int8 MFMA as code + bias).
-  float qsB[NG / 4];
-#pragma unroll
-  for (int i = 0; i < NG / 4; ++i) {
-    const float qs = (float)qsum[col * NG + 4 * i + r];
-    qsB[i] = (L == ASYM) ? qs : -(float)BIAS * qs;
-  }
-  int qoff[SG];      // bias * sum(q8): the Hadamard scores and the score export use it
-#pragma unroll
-  for (int g = 0; g < SG; ++g) {
-    int sum = 0;
-    if (L == HAD) {
-#pragma unroll
-      for (int gg = 0; gg < NG; ++gg) sum += qsum[col * NG + gg];
-    } else {
-      sum = qsum[col * NG + g];
+    for (int g = 0; g < NG; ++g) {
+      const uint2 w = *reinterpret_cast<const uint2*>(a.q8p + fr * D + 32 * g + 8 * r);
+      qB[g] = __builtin_bit_cast(long, u32x2{__builtin_amdgcn_perm(w.y, w.x, 0x06040200u),
+                                             __builtin_amdgcn_perm(w.y, w.x, 0x07050301u)});
     }
-    qoff[g] = BIAS * sum;
+#pragma unroll
+    for (int i = 0; i < NG / 4; ++i) qsB[i] = (L == ASYM) ? (float)qs[4 * i + r] : -(float)BIAS * (float)qs[4 * i + r];
+#pragma unroll
+    for (int g = 0; g < SG; ++g) {
+      int sum = 0;
+      if (L == HAD) {
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) sum += qs[gg];
+      } else {
+        sum = qs[g];
+      }
+      qoff[g] = BIAS * sum;
+    }
+    sqc = a.sqp[fr] * a.alpha * KVQ_LOG2E;
   }
-  const float sqc = sqv[col] * a.alpha * KVQ_LOG2E;
   const int lim = row_limit(a, qs0, row0 + col, nrows);
   const long drow = (DBG && col < nvalid) ? (long)row_index(a, b, hk, row0 + col) : -1;   // score export only
-  __syncthreads();   // the LDS becomes the waves' step buffers
   if (!has_chunk) return;
 
   unsigned char* buf = smem + wave * ST::BYTES;
@@ -475,9 +454,9 @@ __global__ __launch_bounds__(256, 2) void attend_partial(AttendArgs a) {
         const int T = t_begin + 32 * su;
         stage_step<L, D>(buf, lane, pre[(k + 1) % NB]);
         if (T + 32 <= t_end && T + 31 <= lim_min)
-          attend_step<L, D, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qb, qsB, qoff, sqc, magic, m_run, l_run, oacc);
+          attend_step<L, D, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic, m_run, l_run, oacc);
         else
-          attend_step<L, D, DBG, false>(a, buf, T, t_end, lim, drow, col, r, qb, qsB, qoff, sqc, magic, m_run, l_run, oacc);
+          attend_step<L, D, DBG, false>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic, m_run, l_run, oacc);
       }
     }
   }
@@ -594,11 +573,16 @@ static size_t step_bytes(int layout, int D) {
 }
 
 static size_t partial_lds_bytes(int layout, int D, int n_recent) {
-  const size_t pro = (size_t)16 * D * 4 + 16 * D + 16 * 4 + 16 * (D / 32) * 4;
   const size_t steps = 4 * step_bytes(layout, D);
   const size_t win = n_recent > 0 ? (size_t)(D == 128 ? window_lds_bytes<128>() : window_lds_bytes<256>()) : 0;
-  size_t m = pro > steps ? pro : steps;
-  return m > win ? m : win;
+  return steps > win ? steps : win;
+}
+
+// Workspace of the decode: the partials [B x Hq x (chunks + 1) x (D + 4)] f32, then the prepared rows.
+static RowPrep decode_ws(int batch, int Hq, int D, int max_seq_len, int chunk) {
+  const size_t rows = (size_t)batch * Hq;
+  const size_t nc1 = (size_t)chunks_of(max_seq_len, chunk) + 1;
+  return row_prep_layout(rows * nc1 * partial_stride(D) * sizeof(float), rows, D);
 }
 
 static kvq_status check_chunk(const kvq_cache* c, int32_t chunk) {
@@ -629,9 +613,8 @@ using namespace kvq;
 extern "C" size_t kvq_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t D, int32_t max_seq_len,
                                              int32_t chunk) {
   if (batch < 1 || Hq < 1 || (D != 128 && D != 256) || max_seq_len < 0 || chunk < 128 || chunk % 128) return 0;
-  // +1 slot for the window partial (always reserved so the size does not depend on n_recent)
-  const size_t nc1 = (size_t)chunks_of(max_seq_len, chunk) + 1;
-  return (size_t)batch * Hq * nc1 * partial_stride(D) * sizeof(float);
+  // +1 partial slot for the window (always reserved so the size does not depend on n_recent)
+  return decode_ws(batch, Hq, D, max_seq_len, chunk).end;
 }
 
 extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
@@ -646,6 +629,10 @@ extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float*
   AttendArgs a = make_args(c, q, Hq, 1, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace);
   const int64_t gx = grid_x(a);
   if (gx == 0) return KVQ_OK;
+  if ((st = launch_prepare_rows(c, q, batch * Hq, (unsigned char*)workspace,
+                                decode_ws(batch, Hq, c->head_dim, max_seq_len, chunk), a, (hipStream_t)stream)) != KVQ_OK)
+    return st;
+  a.batch = batch;
   const dim3 grid((unsigned)gx, c->num_kv_heads, batch);
   pick_partial<false>(c->layout, c->head_dim)(a, grid, partial_lds_bytes(c->layout, c->head_dim, c->n_recent), (hipStream_t)stream);
   return check_launch("decode partial kernel");
@@ -679,18 +666,25 @@ extern "C" kvq_status kvq_attend_decode(const kvq_cache* c, const float* q, floa
 
 extern "C" kvq_status kvq_debug_qk_i32(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
                                        const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
-                                       int32_t max_seq_len, int32_t* scores, void* stream) {
+                                       int32_t max_seq_len, int32_t* scores, void* workspace, size_t ws_bytes,
+                                       void* stream) {
   kvq_status st = check_attend_args(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len);
   if (st != KVQ_OK) return st;
   if (!scores) return fail(KVQ_ERR_INVALID_ARG, "scores must be non-null");
   const int chunk = 512;
   if ((st = check_chunk(c, chunk)) != KVQ_OK) return st;
   if (chunks_of(max_seq_len, chunk) == 0) return KVQ_OK;
-  AttendArgs a = make_args(c, q, Hq, 1, 1.0f, block_table, max_pages, seq_len, max_seq_len, chunk, nullptr);
+  const size_t need = kvq_decode_workspace_bytes(batch, Hq, c->head_dim, max_seq_len, chunk);
+  if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  AttendArgs a = make_args(c, q, Hq, 1, 1.0f, block_table, max_pages, seq_len, max_seq_len, chunk, workspace);
+  if ((st = launch_prepare_rows(c, q, batch * Hq, (unsigned char*)workspace,
+                                decode_ws(batch, Hq, c->head_dim, max_seq_len, chunk), a, (hipStream_t)stream)) != KVQ_OK)
+    return st;
   a.dbg = scores;
   a.kring = nullptr;
   a.vring = nullptr;
   a.ngroups = (chunks_of(max_seq_len, chunk) + 3) / 4;   // no window group: the export covers quantised tokens
+  a.batch = batch;
   const dim3 grid((unsigned)grid_x(a), c->num_kv_heads, batch);
   pick_partial<true>(c->layout, c->head_dim)(a, grid, partial_lds_bytes(c->layout, c->head_dim, 0), (hipStream_t)stream);
   return check_launch("score export kernel");

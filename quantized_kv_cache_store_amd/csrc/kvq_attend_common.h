@@ -11,6 +11,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 #define KVQ_LOG2E 1.4426950408889634f
 
@@ -33,6 +34,7 @@ struct AttendArgs {
   int32_t* dbg;
   int Hkv, Hq, G, page_shift, n_recent, max_pages, chunk, nc1, max_seq_len;
   int n_q;       // queries per batch row (1 for decode)
+  int batch;     // batch rows (decode: the grid is one-dimensional)
   int ngroups;   // blocks per row tile along the sequence: chunk groups of four, + 1 for the window
   int causal;    // rows see t <= q_start + i
   int skip;      // causal skip: stop streaming past the tile's last visible token
@@ -275,6 +277,29 @@ static inline int64_t grid_x(const AttendArgs& a) {
   const int64_t tiles = ((int64_t)a.n_q * a.G + 15) / 16;
   return tiles * a.ngroups;
 }
+
+static inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Prepared query rows in a workspace, after the partials: [rotated f32 query rows x D] [int8
+// query rows x D] [scale f32 rows] [block sums int32 rows x D / 32], each part 16-byte aligned.
+struct RowPrep {
+  size_t qrot, q8, sq, qsum, end;
+};
+
+static inline RowPrep row_prep_layout(size_t at, size_t rows, int D) {
+  RowPrep w;
+  w.qrot = align16(at);
+  w.q8 = w.qrot + align16(rows * D * sizeof(float));
+  w.sq = w.q8 + align16(rows * D);
+  w.qsum = w.sq + align16(rows * sizeof(float));
+  w.end = w.qsum + align16(rows * (D / 32) * sizeof(int));
+  return w;
+}
+
+// Query preparation of n_vec rows of q (kvq_prefill.hip): int8 query, scale, block sums, and for
+// the Hadamard layout the rotated f32 query.  Points a's prepared-row fields at them.
+kvq_status launch_prepare_rows(const kvq_cache* c, const float* q, int n_vec, unsigned char* ws, const RowPrep& w,
+                               AttendArgs& a, hipStream_t s);
 
 // The online-softmax reduce over the partials of batch * rows_per_b rows (kvq_attend.hip).
 kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b, const int32_t* seq_len,

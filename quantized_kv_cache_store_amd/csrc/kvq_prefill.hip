@@ -497,23 +497,22 @@ static size_t prefill_lds_bytes(int layout, int D, int n_recent) {
   return 2 * pb > win ? 2 * pb : win;
 }
 
-static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
-
-// Workspace of the prefill: [partials f32 rows x (chunks + 1) x (D + 4)] [rotated query f32 rows x D]
-// [int8 query rows x D] [scale f32 rows] [block sums int32 rows x D / 32], each part 16-byte aligned.
-struct PrefillWs {
-  size_t qrot, q8, sq, qsum, total;
-};
-
-static PrefillWs prefill_ws(size_t rows, int D, int max_seq_len) {
-  PrefillWs w;
+// Workspace of the prefill: the partials [rows x (chunks + 1) x (D + 4)] f32, then the prepared rows.
+static RowPrep prefill_ws(size_t rows, int D, int max_seq_len) {
   const size_t nc1 = (size_t)chunks_of(max_seq_len, kPrefillChunk) + 1;
-  w.qrot = align16(rows * nc1 * partial_stride(D) * sizeof(float));
-  w.q8 = w.qrot + align16(rows * D * sizeof(float));
-  w.sq = w.q8 + align16(rows * D);
-  w.qsum = w.sq + align16(rows * sizeof(float));
-  w.total = w.qsum + align16(rows * (D / 32) * sizeof(int));
-  return w;
+  return row_prep_layout(rows * nc1 * partial_stride(D) * sizeof(float), rows, D);
+}
+
+kvq_status launch_prepare_rows(const kvq_cache* c, const float* q, int n_vec, unsigned char* ws, const RowPrep& w,
+                               AttendArgs& a, hipStream_t s) {
+  a.qrot = c->layout == HAD ? (const float*)(ws + w.qrot) : q;   // the window's f32 query
+  a.q8p = (const int8_t*)(ws + w.q8);
+  a.sqp = (const float*)(ws + w.sq);
+  a.qsump = (const int*)(ws + w.qsum);
+  if (n_vec == 0) return KVQ_OK;
+  pick_prepare(c->layout, c->head_dim)(q, n_vec, (float*)(ws + w.qrot), (int8_t*)(ws + w.q8), (float*)(ws + w.sq),
+                                       (int*)(ws + w.qsum), s);
+  return check_launch("query preparation kernel");
 }
 
 }  // namespace kvq
@@ -523,7 +522,7 @@ using namespace kvq;
 extern "C" size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t Hq, int32_t D,
                                               int32_t max_seq_len) {
   if (batch < 1 || n_q < 1 || Hq < 1 || (D != 128 && D != 256) || max_seq_len < 0) return 0;
-  return prefill_ws((size_t)batch * n_q * Hq, D, max_seq_len).total;
+  return prefill_ws((size_t)batch * n_q * Hq, D, max_seq_len).end;
 }
 
 extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float* q, float* out, int32_t batch,
@@ -551,15 +550,8 @@ extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float*
   const int64_t gx = ((int64_t)n_q * a.G + 63) / 64 * a.ngroups;
   if (gx > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
   const int rows = batch * n_q * Hq;
-  const PrefillWs w = prefill_ws((size_t)rows, c->head_dim, max_seq_len);
-  unsigned char* wsb = (unsigned char*)workspace;
-  a.qrot = c->layout == HAD ? (const float*)(wsb + w.qrot) : q;   // the window's f32 query
-  a.q8p = (const int8_t*)(wsb + w.q8);
-  a.sqp = (const float*)(wsb + w.sq);
-  a.qsump = (const int*)(wsb + w.qsum);
-  pick_prepare(c->layout, c->head_dim)(q, rows, (float*)(wsb + w.qrot), (int8_t*)(wsb + w.q8), (float*)(wsb + w.sq),
-                                       (int*)(wsb + w.qsum), (hipStream_t)stream);
-  if ((st = check_launch("prefill query preparation kernel")) != KVQ_OK) return st;
+  const RowPrep w = prefill_ws((size_t)rows, c->head_dim, max_seq_len);
+  if ((st = launch_prepare_rows(c, q, rows, (unsigned char*)workspace, w, a, (hipStream_t)stream)) != KVQ_OK) return st;
   if (gx > 0) {
     const dim3 grid((unsigned)gx, c->num_kv_heads, batch);
     pick_prefill(c->layout, c->head_dim)(a, grid, prefill_lds_bytes(c->layout, c->head_dim, c->n_recent),

@@ -207,7 +207,8 @@ def debug_qk_i32(cache, q, block_table, seq_len, max_seq_len):
     B, Hq, D = q.shape
     ng = 1 if cache.layout == _lib.HAD_INT4 else D // 32
     scores = torch.zeros((B, Hq, max_seq_len, ng), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(decode_workspace_bytes(B, Hq, D, max_seq_len, 512), 1), dtype=torch.uint8, device=dev)
     st = load().kvq_debug_qk_i32(cache.desc, _ptr(q), B, Hq, _ptr(block_table), block_table.shape[1],
-                                 _ptr(seq_len), int(max_seq_len), _ptr(scores), _stream(dev))
+                                 _ptr(seq_len), int(max_seq_len), _ptr(scores), _ptr(ws), ws.numel(), _stream(dev))
     check("kvq_debug_qk_i32", st)
     return scores
