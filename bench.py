@@ -46,7 +46,8 @@ def parse():
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attend_partial_asym_int4_g32_llama31_70b_s128k_b8_hbm_traffic.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "quantized_kv_cache_store_amd", "csrc", f) for f in ("kvq_attend.hip", "kvq_internal.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_kv_cache_store_amd", "csrc", f)
+                  for f in ("kvq_attend.hip", "kvq_attend_common.h", "kvq_internal.h")]
 
 
 def measured_traffic():
