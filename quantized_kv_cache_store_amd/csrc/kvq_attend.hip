@@ -485,36 +485,48 @@ __global__ __launch_bounds__(256, 2) void attend_partial(AttendArgs a) {
   }
 }
 
-// Online-softmax merge of the chunk partials of one row (block x = flat row index
-// (b * n_q + i) * Hq + h); Hadamard layout: rotate back.  Four waves split the
-// chunks; each lane owns D/64 output elements.
-template <int D, bool ROT>
+// Online-softmax merge of the chunk partials of each row (flat index (b * n_q + i) * Hq + h);
+// Hadamard layout: rotate back.  W waves per row (4 / W rows per block): the row's waves split
+// its chunks and, when W > 1, combine through LDS in a fixed order (deterministic).  Lane l owns
+// output elements l * E .. l * E + E - 1; the rotation runs in registers, butterflies inside a
+// lane for strides below E and between lanes above, in the stage order of the encoding
+// (h = 1, 2, ..., D / 2, then 1 / sqrt(D)).
+template <int D, bool ROT, int W>
 __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out, const int32_t* seq_len,
-                                                     int rows_per_b, int nc1, int chunk, int n_recent) {
+                                                     int rows_per_b, int nc1, int chunk, int n_recent,
+                                                     long total_rows) {
+#pragma clang fp contract(off)
   constexpr int E = D / 64;
+  constexpr int RPB = 4 / W;
   __shared__ float red_o[4][D];
   __shared__ float red_m[4], red_l[4];
-  __shared__ float x[D];
-  const size_t row = blockIdx.x;
-  const int b = (int)(row / (size_t)rows_per_b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = wave % W;
+  const long row = (long)blockIdx.x * RPB + wave / W;
+  const bool valid = row < total_rows;              // wave-uniform
+  const long rr = valid ? row : total_rows - 1;
+  const int b = (int)(rr / rows_per_b);
   const int S = seq_len[b];
   const int Sq = n_recent > 0 ? max(0, S - n_recent) : S;
   const int nq = (Sq + chunk - 1) / chunk;
   const int cnt = nq + ((n_recent > 0 && S > 0) ? 1 : 0);
   const int PST = partial_stride(D);
-  const float* base = ws + row * nc1 * PST;
+  const float* base = ws + (size_t)rr * nc1 * PST;
   float M = -INFINITY;
-  for (int i = tid; i < cnt; i += 256) M = fmaxf(M, base[(size_t)(i < nq ? i : nc1 - 1) * PST + D]);
+  for (int i = sub * 64 + lane; i < cnt; i += 64 * W) M = fmaxf(M, base[(size_t)(i < nq ? i : nc1 - 1) * PST + D]);
   for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
-  if (lane == 0) red_m[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  if (W > 1) {
+    if (lane == 0) red_m[wave] = M;
+    __syncthreads();
+    const int w0 = wave - sub;
+    M = red_m[w0];
+    for (int k = 1; k < W; ++k) M = fmaxf(M, red_m[w0 + k]);
+  }
   float o[E], l = 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.0f;
 #pragma unroll 4
-  for (int i = wave; i < cnt; i += 4) {
+  for (int i = sub; i < cnt; i += W) {
     const float* p = base + (size_t)(i < nq ? i : nc1 - 1) * PST;
     const float mc = p[D];
     const float w = (mc == -INFINITY) ? 0.0f : exp2f(mc - M);
@@ -522,35 +534,51 @@ __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] += w * p[lane * E + e];
   }
+  if (W > 1) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) red_o[wave][lane * E + e] = o[e];
-  if (lane == 0) red_l[wave] = l;
-  __syncthreads();
-  if (tid < D) {
-    const float lt = red_l[0] + red_l[1] + red_l[2] + red_l[3];
-    const float ot = red_o[0][tid] + red_o[1][tid] + red_o[2][tid] + red_o[3][tid];
-    x[tid] = lt > 0.0f ? ot / lt : 0.0f;
-  }
-  __syncthreads();
-  if (ROT) {
-    // rotate back with the same butterfly transform (stages h = 1 .. D/2, then 1/sqrt(D))
-    for (int hh = 1; hh < D; hh <<= 1) {
-      int i = 0;
-      float p = 0.0f, q = 0.0f;
-      if (tid < D / 2) {
-        i = (tid / hh) * 2 * hh + (tid % hh);
-        p = x[i];
-        q = x[i + hh];
-      }
-      __syncthreads();
-      if (tid < D / 2) {
-        x[i] = p + q;
-        x[i + hh] = p - q;
-      }
-      __syncthreads();
+    for (int e = 0; e < E; ++e) red_o[wave][lane * E + e] = o[e];
+    if (lane == 0) red_l[wave] = l;
+    __syncthreads();
+    if (sub != 0) return;
+    l = red_l[wave];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = red_o[wave][lane * E + e];
+    for (int k = 1; k < W; ++k) {
+      l += red_l[wave + k];
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] += red_o[wave + k][lane * E + e];
     }
   }
-  if (tid < D) out[row * D + tid] = ROT ? x[tid] * hadamard_norm<D>() : x[tid];
+  if (!valid) return;
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = l > 0.0f ? o[e] / l : 0.0f;
+  if (ROT) {
+#pragma unroll
+    for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if ((e & h) == 0) {
+          const float a = x[e], c = x[e + h];
+          x[e] = a + c;
+          x[e + h] = a - c;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {   // stride m * E: partner lane differs in bit m
+      const bool upper = (lane & m) != 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float y = __shfl_xor(x[e], m);
+        x[e] = upper ? (y - x[e]) : (x[e] + y);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = x[e] * hadamard_norm<D>();
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[(size_t)row * D + lane * E + e] = x[e];
 }
 
 template <int L, int D, bool DBG>
@@ -598,16 +626,31 @@ static kvq_status check_chunk(const kvq_cache* c, int32_t chunk) {
   return KVQ_OK;
 }
 
+template <int D, bool ROT, int W>
+static void launch_reduce_w(float* out, long rows, int rows_per_b, const int32_t* seq_len, int nc1, int chunk,
+                            int n_recent, const float* ws, hipStream_t s) {
+  const long blocks = (rows + (4 / W) - 1) / (4 / W);
+  hipLaunchKernelGGL((attend_reduce<D, ROT, W>), dim3((unsigned)blocks), dim3(256), 0, s, ws, out, seq_len, rows_per_b,
+                     nc1, chunk, n_recent, rows);
+}
+
 kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b, const int32_t* seq_len,
                          int nc1, int32_t chunk, const float* ws, hipStream_t s) {
-  const dim3 rgrid((unsigned)((int64_t)batch * rows_per_b));
+  const long rows = (long)batch * rows_per_b;
+  // one wave per row when there are rows enough to fill the chip, else four waves split each row
+  const bool many = rows >= 4096;
   const bool rot = c->layout == HAD;
+  const int n = c->n_recent;
   if (c->head_dim == 128) {
-    if (rot) hipLaunchKernelGGL((attend_reduce<128, true>), rgrid, dim3(256), 0, s, ws, out, seq_len, rows_per_b, nc1, chunk, c->n_recent);
-    else hipLaunchKernelGGL((attend_reduce<128, false>), rgrid, dim3(256), 0, s, ws, out, seq_len, rows_per_b, nc1, chunk, c->n_recent);
+    if (rot) many ? launch_reduce_w<128, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s)
+                  : launch_reduce_w<128, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s);
+    else many ? launch_reduce_w<128, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s)
+              : launch_reduce_w<128, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s);
   } else {
-    if (rot) hipLaunchKernelGGL((attend_reduce<256, true>), rgrid, dim3(256), 0, s, ws, out, seq_len, rows_per_b, nc1, chunk, c->n_recent);
-    else hipLaunchKernelGGL((attend_reduce<256, false>), rgrid, dim3(256), 0, s, ws, out, seq_len, rows_per_b, nc1, chunk, c->n_recent);
+    if (rot) many ? launch_reduce_w<256, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s)
+                  : launch_reduce_w<256, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s);
+    else many ? launch_reduce_w<256, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s)
+              : launch_reduce_w<256, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s);
   }
   return check_launch("attention reduce kernel");
 }
