@@ -43,20 +43,44 @@ namespace kvq {
 
 // Staging buffer of one 32-token step in a wave's LDS slice:
 //   [K payload rows 32 x RS][V payload rows 32 x RS][K records 32 x SB][V records 32 x SB]
-// with payload rows padded to RS = PB + 16 bytes, which spreads the reads of a 16-row column
-// (K: one dword per lane from 16 rows; V: 16 dwords of one row times four rows 4 apart) over
-// all 64 LDS banks.
-// filled from registers that were loaded one step ahead with 16-byte loads.
-template <int L, int D>
+// Two ways to fill it:
+//   * register ring (DMA = false): 16-byte loads into registers several steps ahead, then one
+//     copy to LDS per step; payload rows are padded to RS = PB + 16 bytes, which spreads the reads
+//     of a 16-row column (K: one dword per lane from 16 rows; V: 16 dwords of one row times four
+//     rows 4 apart) over all 64 LDS banks.
+//   * direct loads (DMA = true): global_load_lds_dwordx4 writes the step straight into one slot
+//     of an LDS ring, 1 KiB per instruction (lane i's 16 bytes at slot offset + 16 i), so no
+//     registers hold data in flight.  Rows cannot be padded then; for 64-byte rows the chunks are
+//     placed instead so that the same reads stay conflict-free: K chunk c of row t goes to chunk
+//     position c ^ ((t >> 2) & 3) of row t, and V row t to row position vperm(t), which swaps the
+//     two 2-bit fields of t within its 16-row half (rows 4 apart then land 16 banks apart).
+template <int L, int D, bool DMA = false>
 struct Step {
   using T = Layout<L, D>;
   static constexpr int PB = T::PB, SB = T::SB;
-  static constexpr int RS = PB + 16;
+  static constexpr int RS = DMA ? PB : PB + 16;
   static constexpr int KP = 0, VP = 32 * RS, KR = 64 * RS, VR = KR + 32 * SB;
   static constexpr int BYTES = VR + 32 * SB;
+  static constexpr bool SWZ = DMA && PB == 64;
+  // register ring
   static constexpr int PAY_SLOTS = (2 * PB + 63) / 64;   // 16-byte chunks of 32 payload rows, per lane
   static constexpr int REC_SLOTS = (4 * SB + 63) / 64;   // K and V records together
   static constexpr int SLOTS = 2 * PAY_SLOTS + REC_SLOTS;
+  // direct loads: instructions per payload tensor, per both record tensors, per step
+  static constexpr int PAY_INSTR = PB / 32;
+  static constexpr int REC_CHUNKS = 4 * SB;
+  static constexpr int REC_INSTR = (REC_CHUNKS + 63) / 64;
+  static constexpr int NINSTR = 2 * PAY_INSTR + REC_INSTR;
+
+  __device__ static int vperm(int t) { return (t & 16) | ((t & 3) << 2) | ((t >> 2) & 3); }
+  // byte offset of dword r of the 16-byte code block g of K row t (layouts with 4-bit codes)
+  __device__ static int kword(int t, int g, int r) {
+    return SWZ ? KP + 16 * (4 * t + (g ^ ((t >> 2) & 3))) + 4 * r : KP + t * RS + 4 * (4 * g + r);
+  }
+  // byte offset of dword oc of V row t (layouts with 4-bit codes)
+  __device__ static int vword(int t, int oc) {
+    return SWZ ? VP + 16 * (4 * vperm(t) + (oc >> 2)) + 4 * (oc & 3) : VP + t * RS + 4 * oc;
+  }
 };
 
 // Physical row indices of the two 16-token halves of the step at T (wave-uniform).
@@ -168,6 +192,58 @@ __device__ __forceinline__ void stage_step(unsigned char* buf, int lane, const u
   }
 }
 
+// One direct load to LDS: lane i's 16 bytes at `src` go to LDS byte address lds + 16 i (lds is
+// wave-uniform and travels in m0).
+__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(lds) : "memory");
+}
+
+// Wait until at most N vector-memory operations of the wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Issue the direct loads of one step into the ring slot at LDS address `slot` (see Step).  Lane i
+// of payload instruction k fills chunk position 64 k + i; the LDS reads of the wave still in
+// flight are waited for first, so a slot is never overwritten under a read.
+template <class ST>
+__device__ __forceinline__ void issue_dma(const AttendArgs& a, HalfRows hr, int lane, uint32_t slot) {
+  constexpr int PB = ST::PB, SB = ST::SB, CPR = PB / 16;
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+#pragma unroll
+  for (int k = 0; k < ST::PAY_INSTR; ++k) {
+    const int p = 64 * k + lane;
+    int tk, ck, tv, cv;   // row and chunk of K, and of V, that position p holds
+    if (ST::SWZ) {
+      tk = p >> 2;
+      ck = (p & 3) ^ ((tk >> 2) & 3);
+      tv = ST::vperm(p >> 2);
+      cv = p & 3;
+    } else {
+      tk = p / CPR;
+      ck = p - tk * CPR;
+      tv = tk;
+      cv = ck;
+    }
+    const size_t rk = (tk < 16 ? hr.r0 : hr.r1) + (size_t)(tk & 15);
+    const size_t rv = (tv < 16 ? hr.r0 : hr.r1) + (size_t)(tv & 15);
+    dma16(a.kp + rk * PB + 16 * ck, slot + ST::KP + 1024 * k);
+    dma16(a.vp + rv * PB + 16 * cv, slot + ST::VP + 1024 * k);
+  }
+#pragma unroll
+  for (int k = 0; k < ST::REC_INSTR; ++k) {
+    const int p = 64 * k + lane;
+    if (ST::REC_CHUNKS % 64 == 0 || p < ST::REC_CHUNKS) {
+      const int isv = p >= 2 * SB;             // K records, then V records
+      const int q = p - isv * 2 * SB;          // 16-byte chunk within the tensor's 32 records
+      const int t = 16 * q / SB, o = 16 * q - t * SB;
+      const size_t row = (t < 16 ? hr.r0 : hr.r1) + (size_t)(t & 15);
+      dma16((isv ? a.vs : a.ks) + row * SB + o, slot + ST::KR + 1024 * k);
+    }
+  }
+}
+
 // f16 element idx of a record, as f32
 __device__ __forceinline__ float rec_f16(const unsigned char* p, int idx) {
   return (float)reinterpret_cast<const _Float16*>(p)[idx];
@@ -178,45 +254,124 @@ __device__ __forceinline__ uint32_t rec_word(const unsigned char* rec, int idx) 
   return reinterpret_cast<const uint32_t*>(rec)[idx];
 }
 
+// A operand of the int8 Q K^T MFMA: codes 32 g + 8 r .. 32 g + 8 r + 7 of staged K row t (even
+// elements in the low dword, odd in the high one, the order the query operand follows).
+template <int L, class ST>
+__device__ __forceinline__ long k_operand(const unsigned char* buf, int t, int g, int r) {
+  constexpr int BIAS = CodeBias<L>::value;
+  uint32_t lo, hi;
+  if (L == Q60) {
+    const unsigned char* krow = buf + ST::KP + t * ST::RS;
+    const uint32_t x = *reinterpret_cast<const uint32_t*>(krow + 24 * g + 4 * r);
+    const uint32_t t2 = *reinterpret_cast<const uint16_t*>(krow + 24 * g + 16 + 2 * r);
+    q6_octet(x, t2, lo, hi);
+  } else {
+    uint32_t x = *reinterpret_cast<const uint32_t*>(buf + ST::kword(t, g, r));
+    if (BIAS) x ^= 0x88888888u;
+    lo = x & 0x0F0F0F0Fu;
+    hi = (x >> 4) & 0x0F0F0F0Fu;
+  }
+  return __builtin_bit_cast(long, u32x2{lo, hi});
+}
+
+// One lane's V source for the P V MFMA: octet oc (elements 8 oc .. 8 oc + 7) of the step's tokens
+// in the lane's eight k-slots (slot k: token 16 (k >> 2) + 4 r + (k & 3)), as biased codes, with
+// the scale (and zero) pairs of consecutive slots.  Rows at or past t_end may hold anything, so
+// their scales are zeroed.
+template <int L>
+struct VOctet {
+  uint32_t ev[8], od[8];
+  h2 s2[4], z2[4];
+};
+
+template <int L, class ST, bool FULL>
+__device__ __forceinline__ void load_voctet(const unsigned char* buf, int T0, int t_end, int oc, int r, VOctet<L>& v) {
+  constexpr int SB = ST::SB;
+  constexpr int BIAS = CodeBias<L>::value;
+  const int grp = oc >> 2;           // its 32-element block
+  uint32_t sz[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int tl = 16 * (k >> 2) + 4 * r + (k & 3);
+    if (L == Q60) {
+      const unsigned char* vrow = buf + ST::VP + tl * ST::RS;
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(vrow + 24 * grp + 4 * (oc & 3));
+      const uint32_t t2 = *reinterpret_cast<const uint16_t*>(vrow + 24 * grp + 16 + 2 * (oc & 3));
+      q6_octet(x, t2, v.ev[k], v.od[k]);
+    } else {
+      uint32_t x = *reinterpret_cast<const uint32_t*>(buf + ST::vword(tl, oc));
+      if (BIAS) x ^= 0x88888888u;
+      v.ev[k] = x;
+      v.od[k] = 0;
+    }
+    const bool ok = FULL || T0 + tl < t_end;
+    const unsigned char* vrec = buf + ST::VR + tl * SB;
+    uint32_t w;
+    if (L == ASYM) w = reinterpret_cast<const uint32_t*>(vrec)[grp];
+    else if (L != HAD) w = (uint32_t)reinterpret_cast<const uint16_t*>(vrec)[grp];
+    else w = 0u;
+    sz[k] = ok ? w : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v.s2[i] = as_h2(__builtin_amdgcn_perm(sz[2 * i + 1], sz[2 * i], 0x05040100u));
+    v.z2[i] = as_h2(__builtin_amdgcn_perm(sz[2 * i + 1], sz[2 * i], 0x07060302u));
+  }
+}
+
+// A operand of the f16 P V MFMA for element e of the octet: V^T[8 oc + e][slot k] as fp16,
+// dequantised ((code | 0x6400) is 1024 + code in fp16, then scale and zero).
+template <int L>
+__device__ __forceinline__ v8h v_operand(const VOctet<L>& v, int e, uint32_t magic) {
+  constexpr int BIAS = CodeBias<L>::value;
+  v8h A;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t bsel = (uint32_t)(e >> 1);
+    const uint32_t sel = bsel | (0x0Cu << 8) | ((4u + bsel) << 16) | (0x0Cu << 24);
+    uint32_t pair;
+    if (L == Q60) {
+      const uint32_t src_a = (e & 1) ? v.od[2 * i] : v.ev[2 * i];
+      const uint32_t src_b = (e & 1) ? v.od[2 * i + 1] : v.ev[2 * i + 1];
+      pair = __builtin_amdgcn_perm(src_b, src_a, sel) | magic;
+    } else {
+      const uint32_t y = __builtin_amdgcn_perm(v.ev[2 * i + 1], v.ev[2 * i], sel);
+      pair = (((e & 1) ? (y >> 4) : y) & 0x000F000Fu) | magic;
+    }
+    h2 x = as_h2(pair) - h2{(_Float16)(1024 + BIAS), (_Float16)(1024 + BIAS)};
+    if (L == ASYM) x = x * v.s2[i] + v.z2[i];
+    else if (L != HAD) x = x * v.s2[i];
+    A[2 * i] = x[0];
+    A[2 * i + 1] = x[1];
+  }
+  return A;
+}
+
 // One 32-token step of a wave: Q K^T, online softmax, P V, all from the staged rows in `buf`.
 // FULL: every token of the step is inside the chunk and visible to every row (no masking).
 // Otherwise tokens at or past t_end are dropped (their staged rows may hold anything, so their
 // scales are zeroed too) and tokens past `lim`, the limit of this lane's row, get p = 0.
 // drow: flat row index of this lane's row for the score export (DBG), or -1.
-template <int L, int D, bool DBG, bool FULL>
+template <int L, int D, class ST, bool DBG, bool FULL>
 __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned char* buf, int T0, int t_end,
                                             int lim, long drow, int col, int r, const long* qB,
                                             const float* qsB, const int* qoff, float sqc, uint32_t magic,
                                             float& m_run, float& l_run, v4f* oacc) {
   using T = Layout<L, D>;
-  using ST = Step<L, D>;
   constexpr int NG = T::NG;
   constexpr int SG = T::SG;
-  constexpr int PB = T::PB, SB = T::SB;
+  constexpr int SB = T::SB;
   constexpr int NO = D / 128;
-  constexpr int BIAS = CodeBias<L>::value;
 
   // ---------------- Q K^T on the int8 MFMA, scores of this lane's 8 tokens
   float xs[8];
   float vs_had[8];
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
-    const unsigned char* krow = buf + ST::KP + (16 * tau + col) * ST::RS;
     v4i acc[SG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      uint32_t lo, hi;
-      if (L == Q60) {
-        const uint32_t x = *reinterpret_cast<const uint32_t*>(krow + 24 * g + 4 * r);
-        const uint32_t t2 = *reinterpret_cast<const uint16_t*>(krow + 24 * g + 16 + 2 * r);
-        q6_octet(x, t2, lo, hi);
-      } else {
-        uint32_t x = *reinterpret_cast<const uint32_t*>(krow + 4 * (4 * g + r));
-        if (BIAS) x ^= 0x88888888u;
-        lo = x & 0x0F0F0F0Fu;
-        hi = (x >> 4) & 0x0F0F0F0Fu;
-      }
-      const long A = __builtin_bit_cast(long, u32x2{lo, hi});
+      const long A = k_operand<L, ST>(buf, 16 * tau + col, g, r);
       const long B = qB[g];
       if (L == HAD) {
         acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[0], 0, 0, 0);
@@ -292,61 +447,137 @@ __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned 
   // ---------------- P V on the f16 MFMA, V^T built from the staged rows
 #pragma unroll
   for (int o = 0; o < NO; ++o) {
-    const int oc = col + 16 * o;       // this lane's octet (elements 8*oc .. 8*oc+7)
-    const int grp = oc >> 2;           // its 32-element block
-    uint32_t ev[8], od[8];
-    uint32_t sz[8];
+    VOctet<L> v;
+    load_voctet<L, ST, FULL>(buf, T0, t_end, col + 16 * o, r, v);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int tl = 16 * (k >> 2) + 4 * r + (k & 3);
-      const unsigned char* vrow = buf + ST::VP + tl * ST::RS;
-      if (L == Q60) {
-        const uint32_t x = *reinterpret_cast<const uint32_t*>(vrow + 24 * grp + 4 * (oc & 3));
-        const uint32_t t2 = *reinterpret_cast<const uint16_t*>(vrow + 24 * grp + 16 + 2 * (oc & 3));
-        q6_octet(x, t2, ev[k], od[k]);
-      } else {
-        uint32_t x = *reinterpret_cast<const uint32_t*>(vrow + 4 * oc);
-        if (BIAS) x ^= 0x88888888u;
-        ev[k] = x;
-        od[k] = 0;
-      }
-      const bool ok = FULL || T0 + tl < t_end;   // rows past the end may hold anything: zero their scale
-      const unsigned char* vrec = buf + ST::VR + tl * SB;
-      uint32_t v;
-      if (L == ASYM) v = reinterpret_cast<const uint32_t*>(vrec)[grp];
-      else if (L != HAD) v = (uint32_t)reinterpret_cast<const uint16_t*>(vrec)[grp];
-      else v = 0u;
-      sz[k] = ok ? v : 0u;
+    for (int e = 0; e < 8; ++e)
+      oacc[o * 8 + e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand<L>(v, e, magic), pB, oacc[o * 8 + e], 0, 0, 0);
+  }
+}
+
+// Lane l and lane l ^ 8 of each 16-lane row exchange a value (DPP row rotation by 8).
+__device__ __forceinline__ uint32_t half_swap_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float half_swap(float v) { return __builtin_bit_cast(float, half_swap_u(__builtin_bit_cast(uint32_t, v))); }
+
+// The same step for a tile of at most 8 rows, which leaves half of a 16 x 16 MFMA tile idle in
+// attend_step.  Here both 16-token halves of the step share one output tile: column n of the
+// Q K^T tile is row n & 7 against the tokens of half n >> 3, obtained by running the int8 MFMA
+// over the two halves with B operands that hold the rows' queries in their own half of the
+// columns and zeros in the other (qB0, qB1).  Lane (col, r) so holds the scores of row col & 7
+// for tokens 16 (col >> 3) + 4 r + j.  P V likewise covers 32 output elements per tile: column n
+// accumulates element 8 m + 2 pt + (n >> 3) of row n & 7 (tile pt), with the numerators of lane
+// n's row in the B operand of its own half and zeros in the other.  Integer scores, the softmax
+// numerators and the accumulated products are the same as in attend_step (the idle half adds
+// exact zeros); only the row sum l is added up in another order.
+template <int L, int D, class ST, bool DBG, bool FULL>
+__device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned char* buf, int T0, int t_end,
+                                             int lim, long drow, int col, int r, const long* qB0, const long* qB1,
+                                             const float* qsB0, const float* qsB1, const int* qoff, float sqc,
+                                             uint32_t magic, float& m_run, float& l_run, v4f* oacc) {
+  using T = Layout<L, D>;
+  constexpr int NG = T::NG;
+  constexpr int SG = T::SG;
+  constexpr int SB = T::SB;
+  constexpr int NO = D / 128;
+  const int hh = col >> 3;
+
+  // ---------------- Q K^T: both halves into one tile
+  v4i acc[SG == 1 ? 2 : SG];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const long A = k_operand<L, ST>(buf, 16 * h + col, g, r);
+      const long B = h ? qB1[g] : qB0[g];
+      if (L == HAD)
+        acc[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[h], 0, 0, 0);
+      else
+        acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, h == 0 ? v4i{0, 0, 0, 0} : acc[g], 0, 0, 0);
     }
-    h2 s2[4], z2[4];
+  }
+  v4f xo = v4f{0.f, 0.f, 0.f, 0.f};
+  if (L != HAD) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s2[i] = as_h2(__builtin_amdgcn_perm(sz[2 * i + 1], sz[2 * i], 0x05040100u));
-      z2[i] = as_h2(__builtin_amdgcn_perm(sz[2 * i + 1], sz[2 * i], 0x07060302u));
-    }
+    for (int h = 0; h < 2; ++h) {
+      const unsigned char* orec = buf + ST::KR + (16 * h + col) * SB;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v8h A;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t bsel = (uint32_t)(e >> 1);
-        const uint32_t sel = bsel | (0x0Cu << 8) | ((4u + bsel) << 16) | (0x0Cu << 24);
-        uint32_t pair;
-        if (L == Q60) {
-          const uint32_t src_a = (e & 1) ? od[2 * i] : ev[2 * i];
-          const uint32_t src_b = (e & 1) ? od[2 * i + 1] : ev[2 * i + 1];
-          pair = __builtin_amdgcn_perm(src_b, src_a, sel) | magic;
-        } else {
-          const uint32_t y = __builtin_amdgcn_perm(ev[2 * i + 1], ev[2 * i], sel);
-          pair = (((e & 1) ? (y >> 4) : y) & 0x000F000Fu) | magic;
-        }
-        h2 v = as_h2(pair) - h2{(_Float16)(1024 + BIAS), (_Float16)(1024 + BIAS)};
-        if (L == ASYM) v = v * s2[i] + z2[i];
-        else if (L != HAD) v = v * s2[i];
-        A[2 * i] = v[0];
-        A[2 * i + 1] = v[1];
+      for (int i = 0; i < NG / 4; ++i) {
+        const float av = (L == ASYM) ? rec_f16(orec, 2 * (4 * i + r) + 1) : rec_f16(orec, 4 * i + r);
+        xo = __builtin_amdgcn_mfma_f32_16x16x4f32(av, h ? qsB1[i] : qsB0[i], xo, 0, 0, 0);
       }
-      oacc[o * 8 + e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pB, oacc[o * 8 + e], 0, 0, 0);
+    }
+  }
+  float xs[4], vs_had[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tl = 16 * hh + 4 * r + j;
+    const bool ok = FULL || T0 + tl < t_end;
+    const bool vis = FULL || (ok && T0 + tl <= lim);
+    const unsigned char* rec = buf + ST::KR + tl * SB;
+    float x;
+    if (L == HAD) {
+      const int I = acc[0][j] + acc[1][j] - qoff[0];
+      x = *reinterpret_cast<const float*>(rec) * (float)I;
+      if (DBG && ok && drow >= 0) a.dbg[(size_t)drow * a.max_seq_len + T0 + tl] = I;
+      const float vsc = *reinterpret_cast<const float*>(buf + ST::VR + tl * SB);
+      vs_had[j] = ok ? vsc : 0.0f;
+    } else {
+      x = xo[j];
+#pragma unroll
+      for (int g = 0; g < SG; ++g) {
+        const uint32_t w = rec_word(rec, (L == ASYM) ? g : (g >> 1));
+        const float s = (float)as_h2(w)[(L == ASYM) ? 0 : (g & 1)];
+        x = fmaf(s, (float)acc[g][j], x);
+        if (DBG && ok && drow >= 0)
+          a.dbg[((size_t)drow * a.max_seq_len + T0 + tl) * SG + g] = acc[g][j] - qoff[g];
+      }
+    }
+    xs[j] = vis ? x * sqc : -INFINITY;
+  }
+  if (DBG) return;
+
+  // ---------------- online softmax (base 2): a row's 32 scores sit in lanes (col, r), (col ^ 8, r)
+  float smax = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
+  smax = max_over_rows(smax);
+  smax = fmaxf(smax, half_swap(smax));
+  const float m_new = fmaxf(m_run, smax);
+  const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+  if (__any(m_new > m_run)) {
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+    l_run *= corr;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[i] *= corr;
+  }
+  m_run = m_new;
+  float psum = 0.0f;
+  _Float16 ph[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float p = __builtin_amdgcn_exp2f(xs[j] - m_use);
+    psum += p;
+    ph[j] = (_Float16)(L == HAD ? p * vs_had[j] : p);
+  }
+  l_run += psum;
+  // B operand of P V: k-slots 0..3 hold half 0's tokens, 4..7 half 1's; the other half's
+  // numerators of this row come from lane col ^ 8
+  const uint32_t own0 = as_u32(h2{ph[0], ph[1]}), own1 = as_u32(h2{ph[2], ph[3]});
+  const uint32_t oth0 = half_swap_u(own0), oth1 = half_swap_u(own1);
+  const u32x4 pr = hh ? u32x4{oth0, oth1, own0, own1} : u32x4{own0, own1, oth0, oth1};
+  const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+  const v8h pB0 = __builtin_bit_cast(v8h, hh ? zero : pr);
+  const v8h pB1 = __builtin_bit_cast(v8h, hh ? pr : zero);
+
+  // ---------------- P V: tile pt of octet group o takes elements 2 pt (columns 0..7) and 2 pt + 1
+#pragma unroll
+  for (int o = 0; o < NO; ++o) {
+    VOctet<L> v;
+    load_voctet<L, ST, FULL>(buf, T0, t_end, col + 16 * o, r, v);
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      oacc[o * 4 + pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand<L>(v, 2 * pt, magic), pB0, oacc[o * 4 + pt], 0, 0, 0);
+      oacc[o * 4 + pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand<L>(v, 2 * pt + 1, magic), pB1, oacc[o * 4 + pt], 0, 0, 0);
     }
   }
 }
@@ -354,13 +585,27 @@ __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned 
 // Split-K partial kernel.  Block = four waves = four consecutive chunks of one (batch row,
 // kv head, row tile); each wave streams its chunk in 32-token steps with NB - 1 steps of loads
 // in flight and writes the chunk's partial per row (o unnormalised, m in base-2 logits, l).
+// TR: rows per tile, 16 (attend_step) or 8 (attend_step8, for groups of at most 8 rows).
 // Grid: x = row tile * ngroups + chunk group (the last group is the window when n_recent > 0),
 // y = kv head, z = batch row.
-template <int L, int D, bool DBG>
-__global__ __launch_bounds__(256, 2) void attend_partial(AttendArgs a) {
+template <int L, int D, int TR>
+struct PartialShape {
+  // 8-row tiles stream through an LDS ring filled by direct loads (two slots: one step in flight
+  // while one is consumed); 16-row tiles through the register ring
+  static constexpr bool DMA = TR == 8;
+  using ST = Step<L, D, DMA>;
+  static constexpr int NB = DMA ? 2 : ((ST::SLOTS <= 5) ? 5 : (D == 128 ? 3 : 2));
+  static constexpr int LDS = 4 * (DMA ? NB : 1) * ST::BYTES;   // per block
+  // waves per SIMD: as many as four blocks' rings in 160 KiB of LDS allow, registers permitting
+  static constexpr int MIN_WAVES = DMA ? (LDS <= 40960 ? 4 : (LDS <= 54613 ? 3 : 2)) : 2;
+};
+
+template <int L, int D, bool DBG, int TR>
+__global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void attend_partial(AttendArgs a) {
   using T = Layout<L, D>;
-  using ST = Step<L, D>;
-  constexpr int NB = (ST::SLOTS <= 5) ? 5 : (D == 128 ? 3 : 2);   // ring slots: NB - 1 steps in flight while one is consumed
+  using PS = PartialShape<L, D, TR>;
+  using ST = typename PS::ST;
+  constexpr int NB = PS::NB;
   constexpr int NG = T::NG;
   constexpr int SG = T::SG;
   constexpr int NO = D / 128;
@@ -375,8 +620,8 @@ __global__ __launch_bounds__(256, 2) void attend_partial(AttendArgs a) {
   const int S = a.seq_len[b];
   const int Sq = a.n_recent > 0 ? max(0, S - a.n_recent) : S;   // quantised tokens
   const int nrows = a.n_q * a.G;
-  const int row0 = 16 * tile;
-  const int nvalid = min(16, nrows - row0);
+  const int row0 = TR * tile;
+  const int nvalid = min(TR, nrows - row0);
   const int qs0 = a.causal ? a.q_start[b] : 0;
   if (!DBG && a.n_recent > 0 && cg == a.ngroups - 1) {
     if (S > 0) window_partial<L, D>(a, smem, b, hk, S, row0, nvalid, qs0);
@@ -397,27 +642,34 @@ __global__ __launch_bounds__(256, 2) void attend_partial(AttendArgs a) {
   const size_t row_first = active ? chunk_row(a, cp, hk, t_begin) : 0;
   const int nsteps = active ? (t_end - t_begin + 31) / 32 : 0;
 
-  u32x4 pre[NB][ST::SLOTS];
-
   // ---- prologue: this lane's row of the tile from the prepared rows (int8 query in the B-operand
-  // order, its scale and block sums); the perms and sums consume the loads here, before the loop
+  // order, its scale and block sums); the perms and sums consume the loads here, before the loop.
+  // With 8-row tiles lane column col serves row col & 7, and its operands are zero outside its half.
   const int col = lane & 15;
   const int r = lane >> 4;
-  long qB[NG];   // B operands (int8 query of the tile's rows), one aligned register pair each
-  float qsB[NG / 4];   // offset-term operand: zero point (asym) or -bias * scale times the block sums
+  const int rsel = TR == 8 ? (col & 7) : col;   // this lane's row within the tile
+  const int hh = col >> 3;
+  long qB0[NG], qB1[NG];   // B operands (int8 query of the tile's rows), one aligned register pair each
+  float qsB0[NG / 4], qsB1[NG / 4];   // offset-term operand: zero point (asym) or -bias * scale times the block sums
   int qoff[SG];        // bias * sum(q8): the Hadamard scores and the score export use it
   float sqc = 0.0f;
   {
-    const size_t fr = row_index(a, b, hk, row0 + min(col, nvalid - 1));
+    const size_t fr = row_index(a, b, hk, row0 + min(rsel, nvalid - 1));
     const int* qs = a.qsump + fr * NG;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const uint2 w = *reinterpret_cast<const uint2*>(a.q8p + fr * D + 32 * g + 8 * r);
-      qB[g] = __builtin_bit_cast(long, u32x2{__builtin_amdgcn_perm(w.y, w.x, 0x06040200u),
-                                             __builtin_amdgcn_perm(w.y, w.x, 0x07050301u)});
+      const long qb = __builtin_bit_cast(long, u32x2{__builtin_amdgcn_perm(w.y, w.x, 0x06040200u),
+                                                     __builtin_amdgcn_perm(w.y, w.x, 0x07050301u)});
+      qB0[g] = (TR == 8 && hh) ? 0 : qb;
+      qB1[g] = hh ? qb : 0;
     }
 #pragma unroll
-    for (int i = 0; i < NG / 4; ++i) qsB[i] = (L == ASYM) ? (float)qs[4 * i + r] : -(float)BIAS * (float)qs[4 * i + r];
+    for (int i = 0; i < NG / 4; ++i) {
+      const float v = (L == ASYM) ? (float)qs[4 * i + r] : -(float)BIAS * (float)qs[4 * i + r];
+      qsB0[i] = (TR == 8 && hh) ? 0.0f : v;
+      qsB1[i] = hh ? v : 0.0f;
+    }
 #pragma unroll
     for (int g = 0; g < SG; ++g) {
       int sum = 0;
@@ -431,38 +683,79 @@ __global__ __launch_bounds__(256, 2) void attend_partial(AttendArgs a) {
     }
     sqc = a.sqp[fr] * a.alpha * KVQ_LOG2E;
   }
-  const int lim = row_limit(a, qs0, row0 + col, nrows);
-  const long drow = (DBG && col < nvalid) ? (long)row_index(a, b, hk, row0 + col) : -1;   // score export only
+  const int lim = row_limit(a, qs0, row0 + rsel, nrows);
+  const long drow = (DBG && rsel < nvalid) ? (long)row_index(a, b, hk, row0 + rsel) : -1;   // score export only
   if (!has_chunk) return;
 
-  unsigned char* buf = smem + wave * ST::BYTES;
   float m_run = -INFINITY, l_run = 0.0f;
-  v4f oacc[D / 16];
+  constexpr int NACC = TR == 8 ? D / 32 : D / 16;
+  v4f oacc[NACC];
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) oacc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NACC; ++i) oacc[i] = v4f{0.f, 0.f, 0.f, 0.f};
 
   uint32_t magic;   // fp16 "1024 + code" exponent bits, kept in a VGPR so v_and_or_b32 can take it
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
-  // Software pipeline over a ring of NB register slots, all loads issued inside the loop (nothing is
-  // in flight at entry, so the compiler's load-counter waits stay exact): iteration i issues step i
-  // into slot i % NB and consumes step i - (NB - 1) from slot (i + 1) % NB.  Issues past the last
-  // step read a few bytes of the chunk's first rows (cache hits) so every iteration issues the same
-  // loads.
-  const int kend = nsteps > 0 ? nsteps + NB - 1 : 0;
-  for (int k0 = 0; k0 < kend; k0 += NB) {
+  auto step = [&](const unsigned char* buf, int T) {
+    const bool full = T + 32 <= t_end && T + 31 <= lim_min;
+    if (TR == 8) {
+      if (full)
+        attend_step8<L, D, ST, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qB0, qB1, qsB0, qsB1, qoff, sqc, magic,
+                                          m_run, l_run, oacc);
+      else
+        attend_step8<L, D, ST, DBG, false>(a, buf, T, t_end, lim, drow, col, r, qB0, qB1, qsB0, qsB1, qoff, sqc, magic,
+                                           m_run, l_run, oacc);
+    } else {
+      if (full)
+        attend_step<L, D, ST, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qB0, qsB0, qoff, sqc, magic, m_run, l_run, oacc);
+      else
+        attend_step<L, D, ST, DBG, false>(a, buf, T, t_end, lim, drow, col, r, qB0, qsB0, qoff, sqc, magic, m_run, l_run, oacc);
+    }
+  };
+
+  if constexpr (PS::DMA) {
+    // LDS ring of NB slots per wave: step s lives in slot s % NB; step s + NB - 1 is issued before
+    // step s is consumed.  The wave's only vector-memory operations in the loop are these loads
+    // (the score export aside, which waits for all), so a count of the loads issued after step s
+    // tells when it has landed.
+    unsigned char* ring = smem + wave * NB * ST::BYTES;
+    const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ring);
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      const int si = k0 + k;
-      const int Ti = t_begin + 32 * si;
-      issue_step<L, D>(a, half_rows(a, cp, hk, Ti, t_end, row_first), lane, pre[k], si >= nsteps);
-      const int su = si - (NB - 1);
-      if (su >= 0 && su < nsteps) {
-        const int T = t_begin + 32 * su;
-        stage_step<L, D>(buf, lane, pre[(k + 1) % NB]);
-        if (T + 32 <= t_end && T + 31 <= lim_min)
-          attend_step<L, D, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic, m_run, l_run, oacc);
-        else
-          attend_step<L, D, DBG, false>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic, m_run, l_run, oacc);
+    for (int i = 0; i < NB - 1; ++i)
+      if (i < nsteps) issue_dma<ST>(a, half_rows(a, cp, hk, t_begin + 32 * i, t_end, row_first), lane, ring_lds + i * ST::BYTES);
+    int slot = 0;
+    for (int s = 0; s < nsteps; ++s) {
+      const int si = s + NB - 1;
+      if (si < nsteps) {
+        const int sl = slot == 0 ? NB - 1 : slot - 1;   // the slot of step s - 1, consumed
+        issue_dma<ST>(a, half_rows(a, cp, hk, t_begin + 32 * si, t_end, row_first), lane, ring_lds + sl * ST::BYTES);
+      }
+      const int after = min(NB - 1, nsteps - 1 - s);   // steps issued after step s
+      if (DBG || after == 0) wait_vm<0>();
+      else if (after == 1) wait_vm<ST::NINSTR>();
+      else wait_vm<2 * ST::NINSTR>();
+      step(ring + slot * ST::BYTES, t_begin + 32 * s);
+      slot = slot == NB - 1 ? 0 : slot + 1;
+    }
+  } else {
+    unsigned char* buf = smem + wave * ST::BYTES;
+    u32x4 pre[NB][ST::SLOTS];
+    // Software pipeline over a ring of NB register slots, all loads issued inside the loop (nothing
+    // is in flight at entry, so the compiler's load-counter waits stay exact): iteration i issues
+    // step i into slot i % NB and consumes step i - (NB - 1) from slot (i + 1) % NB.  Issues past
+    // the last step read a few bytes of the chunk's first rows (cache hits) so every iteration
+    // issues the same loads.
+    const int kend = nsteps > 0 ? nsteps + NB - 1 : 0;
+    for (int k0 = 0; k0 < kend; k0 += NB) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int si = k0 + k;
+        const int Ti = t_begin + 32 * si;
+        issue_step<L, D>(a, half_rows(a, cp, hk, Ti, t_end, row_first), lane, pre[k], si >= nsteps);
+        const int su = si - (NB - 1);
+        if (su >= 0 && su < nsteps) {
+          stage_step<L, D>(buf, lane, pre[(k + 1) % NB]);
+          step(buf, t_begin + 32 * su);
+        }
       }
     }
   }
@@ -470,15 +763,25 @@ __global__ __launch_bounds__(256, 2) void attend_partial(AttendArgs a) {
 
   // ---------------- this wave's chunk partial
   l_run = sum_over_rows(l_run);
-  if (col < nvalid) {
-    float* dst = a.ws + (row_index(a, b, hk, row0 + col) * a.nc1 + c) * partial_stride(D);
+  if (TR == 8) l_run += half_swap(l_run);   // the row's other half of the tokens
+  if (rsel < nvalid) {
+    float* dst = a.ws + (row_index(a, b, hk, row0 + rsel) * a.nc1 + c) * partial_stride(D);
+    if (TR == 8) {
 #pragma unroll
-    for (int o = 0; o < NO; ++o)
+      for (int o = 0; o < NO; ++o)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+        for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + e] = oacc[o * 8 + e][j];
-    if (r == 0) {
+          for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + 2 * pt + hh] = oacc[o * 4 + pt][j];
+    } else {
+#pragma unroll
+      for (int o = 0; o < NO; ++o)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + e] = oacc[o * 8 + e][j];
+    }
+    if (r == 0 && (TR == 16 || hh == 0)) {
       dst[D] = m_run;
       dst[D + 1] = l_run;
     }
@@ -581,35 +884,34 @@ __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out
   for (int e = 0; e < E; ++e) out[(size_t)row * D + lane * E + e] = x[e];
 }
 
-template <int L, int D, bool DBG>
-static void launch_partial(const AttendArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+template <int L, int D, bool DBG, int TR>
+static void launch_partial(const AttendArgs& a, dim3 grid, int n_recent, hipStream_t st) {
+  size_t lds = PartialShape<L, D, TR>::LDS;
+  if (n_recent > 0 && (size_t)window_lds_bytes<D>() > lds) lds = window_lds_bytes<D>();
   if (lds > 65536)
-    (void)hipFuncSetAttribute((const void*)attend_partial<L, D, DBG>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((attend_partial<L, D, DBG>), grid, dim3(256), lds, st, a);
+    (void)hipFuncSetAttribute((const void*)attend_partial<L, D, DBG, TR>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((attend_partial<L, D, DBG, TR>), grid, dim3(256), lds, st, a);
 }
 
-typedef void (*partial_fn)(const AttendArgs&, dim3, size_t, hipStream_t);
+typedef void (*partial_fn)(const AttendArgs&, dim3, int, hipStream_t);
+
+// Rows per tile of the decode kernel: 8 when a (batch row, kv head) has at most 8 query rows.
+static inline int tile_rows(const AttendArgs& a) { return a.n_q * a.G <= 8 ? 8 : 16; }
 
 template <bool DBG>
-static partial_fn pick_partial(int layout, int D) {
-  const int di = D == 256 ? 1 : 0;
-  static const partial_fn tab[4][2] = {
-      {launch_partial<HAD, 128, DBG>, launch_partial<HAD, 256, DBG>},
-      {launch_partial<Q40, 128, DBG>, launch_partial<Q40, 256, DBG>},
-      {launch_partial<Q60, 128, DBG>, launch_partial<Q60, 256, DBG>},
-      {launch_partial<ASYM, 128, DBG>, launch_partial<ASYM, 256, DBG>},
+static partial_fn pick_partial(int layout, int D, int tr) {
+  const int di = (D == 256 ? 1 : 0) + (tr == 8 ? 2 : 0);
+  static const partial_fn tab[4][4] = {
+      {launch_partial<HAD, 128, DBG, 16>, launch_partial<HAD, 256, DBG, 16>, launch_partial<HAD, 128, DBG, 8>,
+       launch_partial<HAD, 256, DBG, 8>},
+      {launch_partial<Q40, 128, DBG, 16>, launch_partial<Q40, 256, DBG, 16>, launch_partial<Q40, 128, DBG, 8>,
+       launch_partial<Q40, 256, DBG, 8>},
+      {launch_partial<Q60, 128, DBG, 16>, launch_partial<Q60, 256, DBG, 16>, launch_partial<Q60, 128, DBG, 8>,
+       launch_partial<Q60, 256, DBG, 8>},
+      {launch_partial<ASYM, 128, DBG, 16>, launch_partial<ASYM, 256, DBG, 16>, launch_partial<ASYM, 128, DBG, 8>,
+       launch_partial<ASYM, 256, DBG, 8>},
   };
   return tab[layout][di];
-}
-
-static size_t step_bytes(int layout, int D) {
-  return 64 * (payload_bytes_rt(layout, D) + 16 + scale_bytes_rt(layout, D));
-}
-
-static size_t partial_lds_bytes(int layout, int D, int n_recent) {
-  const size_t steps = 4 * step_bytes(layout, D);
-  const size_t win = n_recent > 0 ? (size_t)(D == 128 ? window_lds_bytes<128>() : window_lds_bytes<256>()) : 0;
-  return steps > win ? steps : win;
 }
 
 // Workspace of the decode: the partials [B x Hq x (chunks + 1) x (D + 4)] f32, then the prepared rows.
@@ -676,14 +978,15 @@ extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float*
   const size_t need = kvq_decode_workspace_bytes(batch, Hq, c->head_dim, max_seq_len, chunk);
   if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
   AttendArgs a = make_args(c, q, Hq, 1, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace);
-  const int64_t gx = grid_x(a);
+  const int tr = tile_rows(a);
+  const int64_t gx = grid_x(a, tr);
   if (gx == 0) return KVQ_OK;
   if ((st = launch_prepare_rows(c, q, batch * Hq, (unsigned char*)workspace,
                                 decode_ws(batch, Hq, c->head_dim, max_seq_len, chunk), a, (hipStream_t)stream)) != KVQ_OK)
     return st;
   a.batch = batch;
   const dim3 grid((unsigned)gx, c->num_kv_heads, batch);
-  pick_partial<false>(c->layout, c->head_dim)(a, grid, partial_lds_bytes(c->layout, c->head_dim, c->n_recent), (hipStream_t)stream);
+  pick_partial<false>(c->layout, c->head_dim, tr)(a, grid, c->n_recent, (hipStream_t)stream);
   return check_launch("decode partial kernel");
 }
 
@@ -734,7 +1037,8 @@ extern "C" kvq_status kvq_debug_qk_i32(const kvq_cache* c, const float* q, int32
   a.vring = nullptr;
   a.ngroups = (chunks_of(max_seq_len, chunk) + 3) / 4;   // no window group: the export covers quantised tokens
   a.batch = batch;
-  const dim3 grid((unsigned)grid_x(a), c->num_kv_heads, batch);
-  pick_partial<true>(c->layout, c->head_dim)(a, grid, partial_lds_bytes(c->layout, c->head_dim, 0), (hipStream_t)stream);
+  const int tr = tile_rows(a);
+  const dim3 grid((unsigned)grid_x(a, tr), c->num_kv_heads, batch);
+  pick_partial<true>(c->layout, c->head_dim, tr)(a, grid, 0, (hipStream_t)stream);
   return check_launch("score export kernel");
 }

@@ -272,9 +272,10 @@ static inline AttendArgs make_args(const kvq_cache* c, const float* q, int32_t H
   return a;
 }
 
-// Blocks along x of the decode kernel: 16-row tiles times chunk groups (0 when there is nothing to do).
-static inline int64_t grid_x(const AttendArgs& a) {
-  const int64_t tiles = ((int64_t)a.n_q * a.G + 15) / 16;
+// Blocks along x of the decode kernel: row tiles of tr rows times chunk groups (0 when there is
+// nothing to do).
+static inline int64_t grid_x(const AttendArgs& a, int tr) {
+  const int64_t tiles = ((int64_t)a.n_q * a.G + tr - 1) / tr;
   return tiles * a.ngroups;
 }
 
