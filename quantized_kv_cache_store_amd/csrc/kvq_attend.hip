@@ -128,6 +128,23 @@ __device__ __forceinline__ HalfRows half_rows(const AttendArgs& a, const ChunkPa
   return h;
 }
 
+// The same rows from page entries read through the scalar cache (the page index is wave-uniform):
+// no vector registers hold the page list and no vector-memory counter is involved.
+typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
+
+__device__ __forceinline__ size_t page_row(const AttendArgs& a, int b, int hk, int t) {
+  const const_i32_ptr bt = (const_i32_ptr)a.block_table;
+  const int phys = bt[(size_t)b * a.max_pages + (t >> a.page_shift)];
+  return (((size_t)phys * a.Hkv + hk) << a.page_shift) + (size_t)(t & ((1 << a.page_shift) - 1));
+}
+
+__device__ __forceinline__ HalfRows half_rows_s(const AttendArgs& a, int b, int hk, int T, int t_end) {
+  HalfRows h;
+  h.r0 = page_row(a, b, hk, T);   // T < t_end for every issued step
+  h.r1 = T + 16 < t_end ? page_row(a, b, hk, T + 16) : h.r0;
+  return h;
+}
+
 // Issue the 16-byte loads of one step into pre[] (no wait).  Payload chunk ci of the step is
 // row ci / PB (half ci / PB), bytes 16 * (ci % PB); when PB is a multiple of 64 every slot lies in
 // one half, so its base address is wave-uniform and only lane * 16 varies.
@@ -465,7 +482,7 @@ __device__ __forceinline__ float half_swap(float v) { return __builtin_bit_cast(
 // attend_step.  Here both 16-token halves of the step share one output tile: column n of the
 // Q K^T tile is row n & 7 against the tokens of half n >> 3, obtained by running the int8 MFMA
 // over the two halves with B operands that hold the rows' queries in their own half of the
-// columns and zeros in the other (qB0, qB1).  Lane (col, r) so holds the scores of row col & 7
+// columns and zeros in the other.  Lane (col, r) so holds the scores of row col & 7
 // for tokens 16 (col >> 3) + 4 r + j.  P V likewise covers 32 output elements per tile: column n
 // accumulates element 8 m + 2 pt + (n >> 3) of row n & 7 (tile pt), with the numerators of lane
 // n's row in the B operand of its own half and zeros in the other.  Integer scores, the softmax
@@ -473,8 +490,8 @@ __device__ __forceinline__ float half_swap(float v) { return __builtin_bit_cast(
 // exact zeros); only the row sum l is added up in another order.
 template <int L, int D, class ST, bool DBG, bool FULL>
 __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned char* buf, int T0, int t_end,
-                                             int lim, long drow, int col, int r, const long* qB0, const long* qB1,
-                                             const float* qsB0, const float* qsB1, const int* qoff, float sqc,
+                                             int lim, long drow, int col, int r, const long* qB, const float* qsB,
+                                             const int* qoff, float sqc,
                                              uint32_t magic, float& m_run, float& l_run, v4f* oacc) {
   using T = Layout<L, D>;
   constexpr int NG = T::NG;
@@ -490,7 +507,7 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const long A = k_operand<L, ST>(buf, 16 * h + col, g, r);
-      const long B = h ? qB1[g] : qB0[g];
+      const long B = (hh == h) ? qB[g] : 0;   // the rows' queries in the columns of half h
       if (L == HAD)
         acc[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[h], 0, 0, 0);
       else
@@ -505,7 +522,7 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
 #pragma unroll
       for (int i = 0; i < NG / 4; ++i) {
         const float av = (L == ASYM) ? rec_f16(orec, 2 * (4 * i + r) + 1) : rec_f16(orec, 4 * i + r);
-        xo = __builtin_amdgcn_mfma_f32_16x16x4f32(av, h ? qsB1[i] : qsB0[i], xo, 0, 0, 0);
+        xo = __builtin_amdgcn_mfma_f32_16x16x4f32(av, (hh == h) ? qsB[i] : 0.0f, xo, 0, 0, 0);
       }
     }
   }
@@ -595,6 +612,7 @@ struct PartialShape {
   static constexpr bool DMA = TR == 8;
   using ST = Step<L, D, DMA>;
   static constexpr int NB = DMA ? 2 : ((ST::SLOTS <= 5) ? 5 : (D == 128 ? 3 : 2));
+  static_assert(NB <= 4 || !DMA, "the direct-load ring waits for at most three steps in flight");
   static constexpr int LDS = 4 * (DMA ? NB : 1) * ST::BYTES;   // per block
   // waves per SIMD: as many as four blocks' rings in 160 KiB of LDS allow, registers permitting
   static constexpr int MIN_WAVES = DMA ? (LDS <= 40960 ? 4 : (LDS <= 54613 ? 3 : 2)) : 2;
@@ -638,8 +656,12 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
   if (a.skip && lim_max < t_end - 1) t_end = max(t_begin, lim_max + 1);   // causal skip
   const bool has_chunk = t_begin < Sq;          // the reduce reads this chunk's partial (wave-uniform)
   const bool active = t_begin < t_end;          // tokens to stream
-  const ChunkPages cp = chunk_pages(a, b, t_begin, t_end, lane, active);
-  const size_t row_first = active ? chunk_row(a, cp, hk, t_begin) : 0;
+  ChunkPages cp{};
+  size_t row_first = 0;
+  if constexpr (!PS::DMA) {
+    cp = chunk_pages(a, b, t_begin, t_end, lane, active);
+    row_first = active ? chunk_row(a, cp, hk, t_begin) : 0;
+  }
   const int nsteps = active ? (t_end - t_begin + 31) / 32 : 0;
 
   // ---- prologue: this lane's row of the tile from the prepared rows (int8 query in the B-operand
@@ -649,8 +671,8 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
   const int r = lane >> 4;
   const int rsel = TR == 8 ? (col & 7) : col;   // this lane's row within the tile
   const int hh = col >> 3;
-  long qB0[NG], qB1[NG];   // B operands (int8 query of the tile's rows), one aligned register pair each
-  float qsB0[NG / 4], qsB1[NG / 4];   // offset-term operand: zero point (asym) or -bias * scale times the block sums
+  long qB[NG];          // B operands (int8 query of the tile's rows), one aligned register pair each
+  float qsB[NG / 4];    // offset-term operand: zero point (asym) or -bias * scale times the block sums
   int qoff[SG];        // bias * sum(q8): the Hadamard scores and the score export use it
   float sqc = 0.0f;
   {
@@ -659,16 +681,12 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const uint2 w = *reinterpret_cast<const uint2*>(a.q8p + fr * D + 32 * g + 8 * r);
-      const long qb = __builtin_bit_cast(long, u32x2{__builtin_amdgcn_perm(w.y, w.x, 0x06040200u),
-                                                     __builtin_amdgcn_perm(w.y, w.x, 0x07050301u)});
-      qB0[g] = (TR == 8 && hh) ? 0 : qb;
-      qB1[g] = hh ? qb : 0;
+      qB[g] = __builtin_bit_cast(long, u32x2{__builtin_amdgcn_perm(w.y, w.x, 0x06040200u),
+                                             __builtin_amdgcn_perm(w.y, w.x, 0x07050301u)});
     }
 #pragma unroll
     for (int i = 0; i < NG / 4; ++i) {
-      const float v = (L == ASYM) ? (float)qs[4 * i + r] : -(float)BIAS * (float)qs[4 * i + r];
-      qsB0[i] = (TR == 8 && hh) ? 0.0f : v;
-      qsB1[i] = hh ? v : 0.0f;
+      qsB[i] = (L == ASYM) ? (float)qs[4 * i + r] : -(float)BIAS * (float)qs[4 * i + r];
     }
 #pragma unroll
     for (int g = 0; g < SG; ++g) {
@@ -695,44 +713,73 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
 
   uint32_t magic;   // fp16 "1024 + code" exponent bits, kept in a VGPR so v_and_or_b32 can take it
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+
+  // The chunk's partial per row (o unnormalised, m, l).
+  auto write_partial = [&](int ci) {
+    float l = sum_over_rows(l_run);
+    if (TR == 8) l += half_swap(l);   // the row's other half of the tokens
+    if (rsel < nvalid) {
+      float* dst = a.ws + (row_index(a, b, hk, row0 + rsel) * a.nc1 + ci) * partial_stride(D);
+      if (TR == 8) {
+#pragma unroll
+        for (int o = 0; o < NO; ++o)
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + 2 * pt + hh] = oacc[o * 4 + pt][j];
+      } else {
+#pragma unroll
+        for (int o = 0; o < NO; ++o)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + e] = oacc[o * 8 + e][j];
+      }
+      if (r == 0 && (TR == 16 || hh == 0)) {
+        dst[D] = m_run;
+        dst[D + 1] = l;
+      }
+    }
+  };
+
   auto step = [&](const unsigned char* buf, int T) {
     const bool full = T + 32 <= t_end && T + 31 <= lim_min;
     if (TR == 8) {
       if (full)
-        attend_step8<L, D, ST, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qB0, qB1, qsB0, qsB1, qoff, sqc, magic,
+        attend_step8<L, D, ST, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic,
                                           m_run, l_run, oacc);
       else
-        attend_step8<L, D, ST, DBG, false>(a, buf, T, t_end, lim, drow, col, r, qB0, qB1, qsB0, qsB1, qoff, sqc, magic,
+        attend_step8<L, D, ST, DBG, false>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic,
                                            m_run, l_run, oacc);
     } else {
       if (full)
-        attend_step<L, D, ST, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qB0, qsB0, qoff, sqc, magic, m_run, l_run, oacc);
+        attend_step<L, D, ST, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic, m_run, l_run, oacc);
       else
-        attend_step<L, D, ST, DBG, false>(a, buf, T, t_end, lim, drow, col, r, qB0, qsB0, qoff, sqc, magic, m_run, l_run, oacc);
+        attend_step<L, D, ST, DBG, false>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic, m_run, l_run, oacc);
     }
   };
 
   if constexpr (PS::DMA) {
     // LDS ring of NB slots per wave: step s lives in slot s % NB; step s + NB - 1 is issued before
-    // step s is consumed.  The wave's only vector-memory operations in the loop are these loads
-    // (the score export aside, which waits for all), so a count of the loads issued after step s
-    // tells when it has landed.
+    // step s is consumed.  Besides these loads the loop only stores (the score export), and loads
+    // complete in issue order, so a count of the loads issued after step s bounds the wait for it.
     unsigned char* ring = smem + wave * NB * ST::BYTES;
     const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ring);
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i)
-      if (i < nsteps) issue_dma<ST>(a, half_rows(a, cp, hk, t_begin + 32 * i, t_end, row_first), lane, ring_lds + i * ST::BYTES);
+      if (i < nsteps) issue_dma<ST>(a, half_rows_s(a, b, hk, t_begin + 32 * i, t_end), lane, ring_lds + i * ST::BYTES);
     int slot = 0;
     for (int s = 0; s < nsteps; ++s) {
       const int si = s + NB - 1;
       if (si < nsteps) {
         const int sl = slot == 0 ? NB - 1 : slot - 1;   // the slot of step s - 1, consumed
-        issue_dma<ST>(a, half_rows(a, cp, hk, t_begin + 32 * si, t_end, row_first), lane, ring_lds + sl * ST::BYTES);
+        issue_dma<ST>(a, half_rows_s(a, b, hk, t_begin + 32 * si, t_end), lane, ring_lds + sl * ST::BYTES);
       }
-      const int after = min(NB - 1, nsteps - 1 - s);   // steps issued after step s
+      const int after = min(NB - 1, nsteps - 1 - s);   // steps issued after step s (NB <= 4)
       if (DBG || after == 0) wait_vm<0>();
       else if (after == 1) wait_vm<ST::NINSTR>();
-      else wait_vm<2 * ST::NINSTR>();
+      else if (after == 2) wait_vm<2 * ST::NINSTR>();
+      else wait_vm<3 * ST::NINSTR>();
       step(ring + slot * ST::BYTES, t_begin + 32 * s);
       slot = slot == NB - 1 ? 0 : slot + 1;
     }
@@ -759,33 +806,7 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
       }
     }
   }
-  if (DBG) return;
-
-  // ---------------- this wave's chunk partial
-  l_run = sum_over_rows(l_run);
-  if (TR == 8) l_run += half_swap(l_run);   // the row's other half of the tokens
-  if (rsel < nvalid) {
-    float* dst = a.ws + (row_index(a, b, hk, row0 + rsel) * a.nc1 + c) * partial_stride(D);
-    if (TR == 8) {
-#pragma unroll
-      for (int o = 0; o < NO; ++o)
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + 2 * pt + hh] = oacc[o * 4 + pt][j];
-    } else {
-#pragma unroll
-      for (int o = 0; o < NO; ++o)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + e] = oacc[o * 8 + e][j];
-    }
-    if (r == 0 && (TR == 16 || hh == 0)) {
-      dst[D] = m_run;
-      dst[D + 1] = l_run;
-    }
-  }
+  if (!DBG) write_partial(c);
 }
 
 // Online-softmax merge of the chunk partials of each row (flat index (b * n_q + i) * Hq + h);
