@@ -112,7 +112,7 @@ kvq_status kvq_store(const kvq_cache* cache, const float* k_new, const float* v_
                      int32_t n_tok, const int32_t* slot, const int32_t* batch_idx,
                      const int32_t* pos, const int32_t* seq_len, void* stream);
 
-/* Workspace of kvq_attend_decode: split-K partials (o_c, m_c, l_c) per
+/* Workspace of kvq_attend_decode: room for split-K partials (o_c, m_c, l_c) per
  * (batch, query head, chunk), plus the window partial, then the prepared
  * queries (int8, scale, block sums, rotated f32 for HAD_INT4) per
  * (batch, query head).  Returns 0 for invalid arguments. */
@@ -150,8 +150,10 @@ kvq_status kvq_attend_decode(const kvq_cache* cache, const float* q, float* out,
 /* The two phases of kvq_attend_decode as separate calls, for callers that time
  * or schedule them apart ([Open-TQ-Metal] split-K paragraphs: a partial phase
  * and a reduce phase ordered by their data dependency; here by stream order).
- * kvq_attend_decode_partial writes the per-chunk partials (and the window
- * partial) into the workspace; kvq_attend_decode_reduce merges them into out.
+ * kvq_attend_decode_partial computes a partial per chunk, merges each group of
+ * four consecutive chunks' partials at once (the first level of the same
+ * online-softmax merge) and writes one partial per group (and the window
+ * partial) into the workspace; kvq_attend_decode_reduce merges those into out.
  * Arguments mean what they mean for kvq_attend_decode and must be identical
  * between the two calls. */
 kvq_status kvq_attend_decode_partial(const kvq_cache* cache, const float* q, int32_t batch,

@@ -613,7 +613,9 @@ struct PartialShape {
   using ST = Step<L, D, DMA>;
   static constexpr int NB = DMA ? 2 : ((ST::SLOTS <= 5) ? 5 : (D == 128 ? 3 : 2));
   static_assert(NB <= 4 || !DMA, "the direct-load ring waits for at most three steps in flight");
-  static constexpr int LDS = 4 * (DMA ? NB : 1) * ST::BYTES;   // per block
+  static constexpr int RING = 4 * (DMA ? NB : 1) * ST::BYTES;
+  static constexpr int MERGE = 4 * TR * (D + 4) * 4;            // the four waves' chunk partials
+  static constexpr int LDS = RING > MERGE ? RING : MERGE;       // per block
   // waves per SIMD: as many as four blocks' rings in 160 KiB of LDS allow, registers permitting
   static constexpr int MIN_WAVES = DMA ? (LDS <= 40960 ? 4 : (LDS <= 54613 ? 3 : 2)) : 2;
 };
@@ -703,7 +705,7 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
   }
   const int lim = row_limit(a, qs0, row0 + rsel, nrows);
   const long drow = (DBG && rsel < nvalid) ? (long)row_index(a, b, hk, row0 + rsel) : -1;   // score export only
-  if (!has_chunk) return;
+  if (DBG && !has_chunk) return;
 
   float m_run = -INFINITY, l_run = 0.0f;
   constexpr int NACC = TR == 8 ? D / 32 : D / 16;
@@ -714,31 +716,30 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
   uint32_t magic;   // fp16 "1024 + code" exponent bits, kept in a VGPR so v_and_or_b32 can take it
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
-  // The chunk's partial per row (o unnormalised, m, l).
-  auto write_partial = [&](int ci) {
+  // The chunk's partial per row (o unnormalised, m, l) into the block's merge area in LDS, rows
+  // of D + 4 floats per wave.
+  auto write_partial_lds = [&](float* mo) {
     float l = sum_over_rows(l_run);
     if (TR == 8) l += half_swap(l);   // the row's other half of the tokens
-    if (rsel < nvalid) {
-      float* dst = a.ws + (row_index(a, b, hk, row0 + rsel) * a.nc1 + ci) * partial_stride(D);
-      if (TR == 8) {
+    float* dst = mo + rsel * partial_stride(D);
+    if (TR == 8) {
 #pragma unroll
-        for (int o = 0; o < NO; ++o)
+      for (int o = 0; o < NO; ++o)
 #pragma unroll
-          for (int pt = 0; pt < 4; ++pt)
+        for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + 2 * pt + hh] = oacc[o * 4 + pt][j];
-      } else {
+          for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + 2 * pt + hh] = oacc[o * 4 + pt][j];
+    } else {
 #pragma unroll
-        for (int o = 0; o < NO; ++o)
+      for (int o = 0; o < NO; ++o)
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < 8; ++e)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + e] = oacc[o * 8 + e][j];
-      }
-      if (r == 0 && (TR == 16 || hh == 0)) {
-        dst[D] = m_run;
-        dst[D + 1] = l;
-      }
+          for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + e] = oacc[o * 8 + e][j];
+    }
+    if (r == 0 && (TR == 16 || hh == 0)) {
+      dst[D] = m_run;
+      dst[D + 1] = l;
     }
   };
 
@@ -806,7 +807,48 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
       }
     }
   }
-  if (!DBG) write_partial(c);
+  if (DBG) return;
+
+  // ---------------- merge of the block's four chunk partials (the first level of the online-softmax
+  // merge, in a fixed order), written as the partial of the chunk group cg
+  float* merge = reinterpret_cast<float*>(smem);
+  __syncthreads();                                  // every wave is done with its ring
+  write_partial_lds(merge + wave * TR * partial_stride(D));
+  __syncthreads();
+  {
+    constexpr int TPR = 256 / TR;                   // threads per row
+    constexpr int EPT = D / TPR;                    // elements per thread
+    const int tid = threadIdx.x;
+    const int row = tid / TPR, e0 = (tid % TPR) * EPT;
+    if (row < nvalid) {
+      const float* src = merge + row * partial_stride(D);
+      constexpr int WS = TR * partial_stride(D);    // one wave's area
+      float mk[4], M = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        mk[k] = src[k * WS + D];
+        M = fmaxf(M, mk[k]);
+      }
+      float w[4], l = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        w[k] = mk[k] == -INFINITY ? 0.0f : exp2f(mk[k] - M);
+        l += w[k] * src[k * WS + D + 1];
+      }
+      float* dst = a.ws + (row_index(a, b, hk, row0 + row) * a.nc1 + cg) * partial_stride(D);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        float o = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o += w[k] * src[k * WS + e0 + e];
+        dst[e0 + e] = o;
+      }
+      if (tid % TPR == 0) {
+        dst[D] = M;
+        dst[D + 1] = l;
+      }
+    }
+  }
 }
 
 // Online-softmax merge of the chunk partials of each row (flat index (b * n_q + i) * Hq + h);
@@ -1022,7 +1064,8 @@ extern "C" kvq_status kvq_attend_decode_reduce(const kvq_cache* c, float* out, i
   if (chunk < 128 || chunk % 128) return fail(KVQ_ERR_INVALID_ARG, "chunk_tokens must be a positive multiple of 128");
   const size_t need = kvq_decode_workspace_bytes(batch, Hq, c->head_dim, max_seq_len, chunk);
   if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
-  return launch_reduce(c, out, batch, Hq, seq_len, chunks_of(max_seq_len, chunk) + 1, chunk, (const float*)workspace,
+  // each partial slot holds a group of four chunks (merged by the partial kernel's block)
+  return launch_reduce(c, out, batch, Hq, seq_len, chunks_of(max_seq_len, chunk) + 1, 4 * chunk, (const float*)workspace,
                        (hipStream_t)stream);
 }
 
