@@ -66,11 +66,11 @@ struct Step {
   static constexpr int PAY_SLOTS = (2 * PB + 63) / 64;   // 16-byte chunks of 32 payload rows, per lane
   static constexpr int REC_SLOTS = (4 * SB + 63) / 64;   // K and V records together
   static constexpr int SLOTS = 2 * PAY_SLOTS + REC_SLOTS;
-  // direct loads: instructions per payload tensor, per both record tensors, per step
+  // direct loads: K and V issued as separate groups, each the tensor's payload (PB / 32
+  // instructions of 1 KiB) and its 32 records (one instruction)
   static constexpr int PAY_INSTR = PB / 32;
-  static constexpr int REC_CHUNKS = 4 * SB;
-  static constexpr int REC_INSTR = (REC_CHUNKS + 63) / 64;
-  static constexpr int NINSTR = 2 * PAY_INSTR + REC_INSTR;
+  static constexpr int GROUP = PAY_INSTR + 1;
+  static_assert(2 * SB <= 64, "one record instruction per tensor");
 
   __device__ static int vperm(int t) { return (t & 16) | ((t & 3) << 2) | ((t >> 2) & 3); }
   // byte offset of dword r of the 16-byte code block g of K row t (layouts with 4-bit codes)
@@ -221,43 +221,30 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// Issue the direct loads of one step into the ring slot at LDS address `slot` (see Step).  Lane i
-// of payload instruction k fills chunk position 64 k + i; the LDS reads of the wave still in
-// flight are waited for first, so a slot is never overwritten under a read.
-template <class ST>
-__device__ __forceinline__ void issue_dma(const AttendArgs& a, HalfRows hr, int lane, uint32_t slot) {
+// The K half (ISV = false: K payload and records) or the V half of a step's direct loads into
+// the ring slot at LDS address `slot`; ST::GROUP instructions.
+template <class ST, bool ISV>
+__device__ __forceinline__ void issue_dma_half(const AttendArgs& a, HalfRows hr, int lane, uint32_t slot) {
   constexpr int PB = ST::PB, SB = ST::SB, CPR = PB / 16;
   asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
 #pragma unroll
   for (int k = 0; k < ST::PAY_INSTR; ++k) {
     const int p = 64 * k + lane;
-    int tk, ck, tv, cv;   // row and chunk of K, and of V, that position p holds
+    int t, c;   // row and chunk that position p holds
     if (ST::SWZ) {
-      tk = p >> 2;
-      ck = (p & 3) ^ ((tk >> 2) & 3);
-      tv = ST::vperm(p >> 2);
-      cv = p & 3;
+      t = ISV ? ST::vperm(p >> 2) : (p >> 2);
+      c = ISV ? (p & 3) : ((p & 3) ^ ((t >> 2) & 3));
     } else {
-      tk = p / CPR;
-      ck = p - tk * CPR;
-      tv = tk;
-      cv = ck;
+      t = p / CPR;
+      c = p - t * CPR;
     }
-    const size_t rk = (tk < 16 ? hr.r0 : hr.r1) + (size_t)(tk & 15);
-    const size_t rv = (tv < 16 ? hr.r0 : hr.r1) + (size_t)(tv & 15);
-    dma16(a.kp + rk * PB + 16 * ck, slot + ST::KP + 1024 * k);
-    dma16(a.vp + rv * PB + 16 * cv, slot + ST::VP + 1024 * k);
+    const size_t row = (t < 16 ? hr.r0 : hr.r1) + (size_t)(t & 15);
+    dma16((ISV ? a.vp : a.kp) + row * PB + 16 * c, slot + (ISV ? ST::VP : ST::KP) + 1024 * k);
   }
-#pragma unroll
-  for (int k = 0; k < ST::REC_INSTR; ++k) {
-    const int p = 64 * k + lane;
-    if (ST::REC_CHUNKS % 64 == 0 || p < ST::REC_CHUNKS) {
-      const int isv = p >= 2 * SB;             // K records, then V records
-      const int q = p - isv * 2 * SB;          // 16-byte chunk within the tensor's 32 records
-      const int t = 16 * q / SB, o = 16 * q - t * SB;
-      const size_t row = (t < 16 ? hr.r0 : hr.r1) + (size_t)(t & 15);
-      dma16((isv ? a.vs : a.ks) + row * SB + o, slot + ST::KR + 1024 * k);
-    }
+  if (lane < 2 * SB) {
+    const int t = 16 * lane / SB, o = 16 * lane - t * SB;   // 16-byte chunk `lane` of the 32 records
+    const size_t row = (t < 16 ? hr.r0 : hr.r1) + (size_t)(t & 15);
+    dma16((ISV ? a.vs : a.ks) + row * SB + o, slot + (ISV ? ST::VR : ST::KR));
   }
 }
 
@@ -488,11 +475,13 @@ __device__ __forceinline__ float half_swap(float v) { return __builtin_bit_cast(
 // n's row in the B operand of its own half and zeros in the other.  Integer scores, the softmax
 // numerators and the accumulated products are the same as in attend_step (the idle half adds
 // exact zeros); only the row sum l is added up in another order.
-template <int L, int D, class ST, bool DBG, bool FULL>
+// `mid` runs between the K side (Q K^T, scores) and the V side (softmax, P V): the direct-load
+// ring refills the K half of the slot there and waits for the V half.
+template <int L, int D, class ST, bool DBG, bool FULL, class MID>
 __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned char* buf, int T0, int t_end,
                                              int lim, long drow, int col, int r, const long* qB, const float* qsB,
                                              const int* qoff, float sqc,
-                                             uint32_t magic, float& m_run, float& l_run, v4f* oacc) {
+                                             uint32_t magic, float& m_run, float& l_run, v4f* oacc, MID&& mid) {
   using T = Layout<L, D>;
   constexpr int NG = T::NG;
   constexpr int SG = T::SG;
@@ -553,6 +542,7 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
     }
     xs[j] = vis ? x * sqc : -INFINITY;
   }
+  mid();
   if (DBG) return;
 
   // ---------------- online softmax (base 2): a row's 32 scores sit in lanes (col, r), (col ^ 8, r)
@@ -612,7 +602,6 @@ struct PartialShape {
   static constexpr bool DMA = TR == 8;
   using ST = Step<L, D, DMA>;
   static constexpr int NB = DMA ? 2 : ((ST::SLOTS <= 5) ? 5 : (D == 128 ? 3 : 2));
-  static_assert(NB <= 4 || !DMA, "the direct-load ring waits for at most three steps in flight");
   static constexpr int RING = 4 * (DMA ? NB : 1) * ST::BYTES;
   static constexpr int MERGE = 4 * TR * (D + 4) * 4;            // the four waves' chunk partials
   static constexpr int LDS = RING > MERGE ? RING : MERGE;       // per block
@@ -647,14 +636,14 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
     if (S > 0) window_partial<L, D>(a, smem, b, hk, S, row0, nvalid, qs0);
     return;
   }
-  if (cg * 4 * a.chunk >= Sq) return;
+  const int span = a.cpw * a.chunk;             // tokens of each wave: cpw consecutive chunks
+  if (cg * 4 * span >= Sq) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = cg * 4 + wave;                  // this wave's chunk
-  const int t_begin = c * a.chunk;
+  const int t_begin = (cg * 4 + wave) * span;
   const int lim_min = row_limit(a, qs0, row0, nrows);               // first row of the tile
   const int lim_max = row_limit(a, qs0, row0 + nvalid - 1, nrows);  // last row: the tile's farthest limit
-  int t_end = min(t_begin + a.chunk, Sq);
+  int t_end = min(t_begin + span, Sq);
   if (a.skip && lim_max < t_end - 1) t_end = max(t_begin, lim_max + 1);   // causal skip
   const bool has_chunk = t_begin < Sq;          // the reduce reads this chunk's partial (wave-uniform)
   const bool active = t_begin < t_end;          // tokens to stream
@@ -743,15 +732,15 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
     }
   };
 
-  auto step = [&](const unsigned char* buf, int T) {
+  auto step = [&](const unsigned char* buf, int T, auto&& mid) {
     const bool full = T + 32 <= t_end && T + 31 <= lim_min;
     if (TR == 8) {
       if (full)
         attend_step8<L, D, ST, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic,
-                                          m_run, l_run, oacc);
+                                          m_run, l_run, oacc, mid);
       else
         attend_step8<L, D, ST, DBG, false>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic,
-                                           m_run, l_run, oacc);
+                                           m_run, l_run, oacc, mid);
     } else {
       if (full)
         attend_step<L, D, ST, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic, m_run, l_run, oacc);
@@ -761,28 +750,40 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
   };
 
   if constexpr (PS::DMA) {
-    // LDS ring of NB slots per wave: step s lives in slot s % NB; step s + NB - 1 is issued before
-    // step s is consumed.  Besides these loads the loop only stores (the score export), and loads
-    // complete in issue order, so a count of the loads issued after step s bounds the wait for it.
-    unsigned char* ring = smem + wave * NB * ST::BYTES;
+    // LDS ring of two slots per wave, step s in slot s & 1, its K half and V half loaded as separate
+    // groups in the order K0 V0 K1 V1 K2 V2 ...: the K half of step s + 2 is issued as soon as the
+    // K side of step s has read its slot, the V half after the V side, and each half is waited for
+    // only where it is first read.  Loads complete in issue order, so a count of the groups issued
+    // after a half bounds the wait for it (stores in the loop only make such a wait longer).
+    static_assert(NB == 2, "two ring slots");
+    constexpr int G = ST::GROUP;
+    unsigned char* ring = smem + wave * 2 * ST::BYTES;
     const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ring);
 #pragma unroll
-    for (int i = 0; i < NB - 1; ++i)
-      if (i < nsteps) issue_dma<ST>(a, half_rows_s(a, b, hk, t_begin + 32 * i, t_end), lane, ring_lds + i * ST::BYTES);
-    int slot = 0;
-    for (int s = 0; s < nsteps; ++s) {
-      const int si = s + NB - 1;
-      if (si < nsteps) {
-        const int sl = slot == 0 ? NB - 1 : slot - 1;   // the slot of step s - 1, consumed
-        issue_dma<ST>(a, half_rows_s(a, b, hk, t_begin + 32 * si, t_end), lane, ring_lds + sl * ST::BYTES);
+    for (int i = 0; i < 2; ++i)
+      if (i < nsteps) {
+        const HalfRows h = half_rows_s(a, b, hk, t_begin + 32 * i, t_end);
+        issue_dma_half<ST, false>(a, h, lane, ring_lds + i * ST::BYTES);
+        issue_dma_half<ST, true>(a, h, lane, ring_lds + i * ST::BYTES);
       }
-      const int after = min(NB - 1, nsteps - 1 - s);   // steps issued after step s (NB <= 4)
-      if (DBG || after == 0) wait_vm<0>();
-      else if (after == 1) wait_vm<ST::NINSTR>();
-      else if (after == 2) wait_vm<2 * ST::NINSTR>();
-      else wait_vm<3 * ST::NINSTR>();
-      step(ring + slot * ST::BYTES, t_begin + 32 * s);
-      slot = slot == NB - 1 ? 0 : slot + 1;
+    for (int s = 0; s < nsteps; ++s) {
+      const uint32_t sl = ring_lds + (s & 1) * ST::BYTES;
+      const bool more1 = s + 1 < nsteps, more2 = s + 2 < nsteps;
+      HalfRows h2{0, 0};
+      if (more2) h2 = half_rows_s(a, b, hk, t_begin + 32 * (s + 2), t_end);
+      if (more1) wait_vm<3 * G>();   // K of step s: then V(s), K(s + 1), V(s + 1)
+      else wait_vm<G>();
+      step(ring + (s & 1) * ST::BYTES, t_begin + 32 * s, [&]() {
+        if (more2) {
+          issue_dma_half<ST, false>(a, h2, lane, sl);
+          wait_vm<3 * G>();          // V of step s: then K(s + 1), V(s + 1), K(s + 2)
+        } else if (more1) {
+          wait_vm<2 * G>();
+        } else {
+          wait_vm<0>();
+        }
+      });
+      if (more2) issue_dma_half<ST, true>(a, h2, lane, sl);
     }
   } else {
     unsigned char* buf = smem + wave * ST::BYTES;
@@ -802,7 +803,7 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
         const int su = si - (NB - 1);
         if (su >= 0 && su < nsteps) {
           stage_step<L, D>(buf, lane, pre[(k + 1) % NB]);
-          step(buf, t_begin + 32 * su);
+          step(buf, t_begin + 32 * su, [] {});
         }
       }
     }
@@ -977,6 +978,30 @@ static partial_fn pick_partial(int layout, int D, int tr) {
   return tab[layout][di];
 }
 
+// Consecutive chunks per wave of the decode kernel, a function of the call's shape and the device
+// (the partial and the reduce calls agree on it).  A wave streams them as one run, so they merge
+// in its registers by the same online-softmax update, and the grid needs fewer rounds of the chip:
+// each round ends with the blocks' barriers, merges and partial stores, during which their LDS and
+// wave slots stream nothing.  At most four, while one round of resident waves (four per SIMD) still
+// has work for all of them, and while the register-ring kernel's page registers cover the run.
+static int decode_cpw(const kvq_cache* c, int batch, int Hq, int max_seq_len, int chunk) {
+  static int cus_of[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus_of[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    cus_of[dev] = cus;
+  }
+  const int G = Hq / c->num_kv_heads;
+  const int tr = G <= 8 ? 8 : 16;
+  const int64_t waves = (int64_t)batch * c->num_kv_heads * ((G + tr - 1) / tr) * chunks_of(max_seq_len, chunk);
+  int cpw = 1;
+  while (cpw < 4 && waves >= (int64_t)cus_of[dev] * 16 * 2 * cpw && (2 * cpw * chunk) / c->page_size + 1 < 64 * kPageRegs)
+    cpw *= 2;
+  return cpw;
+}
+
 // Workspace of the decode: the partials [B x Hq x (chunks + 1) x (D + 4)] f32, then the prepared rows.
 static RowPrep decode_ws(int batch, int Hq, int D, int max_seq_len, int chunk) {
   const size_t rows = (size_t)batch * Hq;
@@ -1042,6 +1067,8 @@ extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float*
   if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
   AttendArgs a = make_args(c, q, Hq, 1, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace);
   const int tr = tile_rows(a);
+  a.cpw = decode_cpw(c, batch, Hq, max_seq_len, chunk);
+  a.ngroups = (chunks_of(max_seq_len, chunk) + 4 * a.cpw - 1) / (4 * a.cpw) + (c->n_recent > 0 ? 1 : 0);
   const int64_t gx = grid_x(a, tr);
   if (gx == 0) return KVQ_OK;
   if ((st = launch_prepare_rows(c, q, batch * Hq, (unsigned char*)workspace,
@@ -1064,8 +1091,9 @@ extern "C" kvq_status kvq_attend_decode_reduce(const kvq_cache* c, float* out, i
   if (chunk < 128 || chunk % 128) return fail(KVQ_ERR_INVALID_ARG, "chunk_tokens must be a positive multiple of 128");
   const size_t need = kvq_decode_workspace_bytes(batch, Hq, c->head_dim, max_seq_len, chunk);
   if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
-  // each partial slot holds a group of four chunks (merged by the partial kernel's block)
-  return launch_reduce(c, out, batch, Hq, seq_len, chunks_of(max_seq_len, chunk) + 1, 4 * chunk, (const float*)workspace,
+  // each partial slot holds a block's four waves of cpw chunks each (merged by the partial kernel)
+  const int cpw = decode_cpw(c, batch, Hq, max_seq_len, chunk);
+  return launch_reduce(c, out, batch, Hq, seq_len, chunks_of(max_seq_len, chunk) + 1, 4 * cpw * chunk, (const float*)workspace,
                        (hipStream_t)stream);
 }
 
