@@ -67,10 +67,10 @@ struct Step {
   static constexpr int REC_SLOTS = (4 * SB + 63) / 64;   // K and V records together
   static constexpr int SLOTS = 2 * PAY_SLOTS + REC_SLOTS;
   // direct loads: K and V issued as separate groups, each the tensor's payload (PB / 32
-  // instructions of 1 KiB) and its 32 records (one instruction)
+  // instructions of 1 KiB) and its 32 records (one instruction per 16-token half)
   static constexpr int PAY_INSTR = PB / 32;
-  static constexpr int GROUP = PAY_INSTR + 1;
-  static_assert(2 * SB <= 64, "one record instruction per tensor");
+  static constexpr int GROUP = PAY_INSTR + 2;
+  static_assert(SB <= 64, "one record instruction per half");
 
   __device__ static int vperm(int t) { return (t & 16) | ((t & 3) << 2) | ((t >> 2) & 3); }
   // byte offset of dword r of the 16-byte code block g of K row t (layouts with 4-bit codes)
@@ -221,11 +221,19 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// The same with a wave-uniform base address in SGPRs and a 32-bit lane offset.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 nt" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
 // The K half (ISV = false: K payload and records) or the V half of a step's direct loads into
-// the ring slot at LDS address `slot`; ST::GROUP instructions.
+// the ring slot at LDS address `slot`; ST::GROUP instructions.  An instruction whose 64 chunks lie
+// in one 16-token half (rows contiguous in one page) takes that half's row address as a uniform
+// base and a loop-invariant lane offset; the records go as one instruction per half.
 template <class ST, bool ISV>
 __device__ __forceinline__ void issue_dma_half(const AttendArgs& a, HalfRows hr, int lane, uint32_t slot) {
   constexpr int PB = ST::PB, SB = ST::SB, CPR = PB / 16;
+  const uint8_t* const pay = ISV ? a.vp : a.kp;
   asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
 #pragma unroll
   for (int k = 0; k < ST::PAY_INSTR; ++k) {
@@ -238,13 +246,21 @@ __device__ __forceinline__ void issue_dma_half(const AttendArgs& a, HalfRows hr,
       t = p / CPR;
       c = p - t * CPR;
     }
-    const size_t row = (t < 16 ? hr.r0 : hr.r1) + (size_t)(t & 15);
-    dma16((ISV ? a.vp : a.kp) + row * PB + 16 * c, slot + (ISV ? ST::VP : ST::KP) + 1024 * k);
+    const uint32_t lds = slot + (ISV ? ST::VP : ST::KP) + 1024 * k;
+    const bool one_half = (64 * k) / (16 * CPR) == (64 * k + 63) / (16 * CPR);   // folded: k is unrolled
+    if (one_half) {
+      const int half = (64 * k) / (16 * CPR);
+      dma16(pay + (half ? hr.r1 : hr.r0) * PB, (uint32_t)((t & 15) * PB + 16 * c), lds);
+    } else {
+      const size_t row = (t < 16 ? hr.r0 : hr.r1) + (size_t)(t & 15);
+      dma16(pay + row * PB + 16 * c, lds);
+    }
   }
-  if (lane < 2 * SB) {
-    const int t = 16 * lane / SB, o = 16 * lane - t * SB;   // 16-byte chunk `lane` of the 32 records
-    const size_t row = (t < 16 ? hr.r0 : hr.r1) + (size_t)(t & 15);
-    dma16((ISV ? a.vs : a.ks) + row * SB + o, slot + (ISV ? ST::VR : ST::KR));
+  const uint8_t* const rec = ISV ? a.vs : a.ks;
+  if (lane < SB) {   // 16 records of SB bytes per half: SB chunks of 16 bytes
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      dma16(rec + (h ? hr.r1 : hr.r0) * SB, (uint32_t)(16 * lane), slot + (ISV ? ST::VR : ST::KR) + 16 * SB * h);
   }
 }
 
