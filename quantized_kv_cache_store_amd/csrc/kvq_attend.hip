@@ -41,15 +41,15 @@
 
 namespace kvq {
 
-// Staging buffer of one 32-token step in a wave's LDS slice:
-//   [K payload rows 32 x RS][V payload rows 32 x RS][K records 32 x SB][V records 32 x SB]
-// Two ways to fill it:
+// Staging of one 32-token step in a wave's LDS slice.  Two ways to fill it:
 //   * register ring (DMA = false): 16-byte loads into registers several steps ahead, then one
-//     copy to LDS per step; payload rows are padded to RS = PB + 16 bytes, which spreads the reads
+//     copy per step to [K payload rows 32 x RS][V payload rows 32 x RS][K records 32 x SB]
+//     [V records 32 x SB]; payload rows are padded to RS = PB + 16 bytes, which spreads the reads
 //     of a 16-row column (K: one dword per lane from 16 rows; V: 16 dwords of one row times four
 //     rows 4 apart) over all 64 LDS banks.
-//   * direct loads (DMA = true): global_load_lds_dwordx4 writes the step straight into one slot
-//     of an LDS ring, 1 KiB per instruction (lane i's 16 bytes at slot offset + 16 i), so no
+//   * direct loads (DMA = true): global_load_lds_dwordx4 writes the step straight into a K slot
+//     [K payload 32 x PB][K records 32 x SB] and a V slot [V payload][V records] of LDS rings,
+//     1 KiB per instruction (lane i's 16 bytes at slot offset + 16 i), so no
 //     registers hold data in flight.  Rows cannot be padded then; for 64-byte rows the chunks are
 //     placed instead so that the same reads stay conflict-free: K chunk c of row t goes to chunk
 //     position c ^ ((t >> 2) & 3) of row t, and V row t to row position vperm(t), which swaps the
@@ -59,8 +59,12 @@ struct Step {
   using T = Layout<L, D>;
   static constexpr int PB = T::PB, SB = T::SB;
   static constexpr int RS = DMA ? PB : PB + 16;
-  static constexpr int KP = 0, VP = 32 * RS, KR = 64 * RS, VR = KR + 32 * SB;
-  static constexpr int BYTES = VR + 32 * SB;
+  // K side offsets from the K base, V side offsets from the V base.  Register ring: one buffer,
+  // both bases equal.  Direct loads: separate K and V slots of HALF bytes each.
+  static constexpr int KP = 0, KR = DMA ? 32 * PB : 64 * RS;
+  static constexpr int VP = DMA ? 0 : 32 * RS, VR = DMA ? 32 * PB : 64 * RS + 32 * SB;
+  static constexpr int HALF = 32 * (PB + SB);
+  static constexpr int BYTES = 64 * RS + 64 * SB;   // register ring buffer
   static constexpr bool SWZ = DMA && PB == 64;
   // register ring
   static constexpr int PAY_SLOTS = (2 * PB + 63) / 64;   // 16-byte chunks of 32 payload rows, per lane
@@ -227,7 +231,7 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_
 }
 
 // The K half (ISV = false: K payload and records) or the V half of a step's direct loads into
-// the ring slot at LDS address `slot`; ST::GROUP instructions.  An instruction whose 64 chunks lie
+// the K or V slot at LDS address `slot`; ST::GROUP instructions.  An instruction whose 64 chunks lie
 // in one 16-token half (rows contiguous in one page) takes that half's row address as a uniform
 // base and a loop-invariant lane offset; the records go as one instruction per half.
 template <class ST, bool ISV>
@@ -494,7 +498,8 @@ __device__ __forceinline__ float half_swap(float v) { return __builtin_bit_cast(
 // `mid` runs between the K side (Q K^T, scores) and the V side (softmax, P V): the direct-load
 // ring refills the K half of the slot there and waits for the V half.
 template <int L, int D, class ST, bool DBG, bool FULL, class MID>
-__device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned char* buf, int T0, int t_end,
+__device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned char* kbuf, const unsigned char* vbuf,
+                                             int T0, int t_end,
                                              int lim, long drow, int col, int r, const long* qB, const float* qsB,
                                              const int* qoff, float sqc,
                                              uint32_t magic, float& m_run, float& l_run, v4f* oacc, MID&& mid) {
@@ -511,7 +516,7 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const long A = k_operand<L, ST>(buf, 16 * h + col, g, r);
+      const long A = k_operand<L, ST>(kbuf, 16 * h + col, g, r);
       const long B = (hh == h) ? qB[g] : 0;   // the rows' queries in the columns of half h
       if (L == HAD)
         acc[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[h], 0, 0, 0);
@@ -523,7 +528,7 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
   if (L != HAD) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const unsigned char* orec = buf + ST::KR + (16 * h + col) * SB;
+      const unsigned char* orec = kbuf + ST::KR + (16 * h + col) * SB;
 #pragma unroll
       for (int i = 0; i < NG / 4; ++i) {
         const float av = (L == ASYM) ? rec_f16(orec, 2 * (4 * i + r) + 1) : rec_f16(orec, 4 * i + r);
@@ -531,20 +536,18 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
       }
     }
   }
-  float xs[4], vs_had[4];
+  float xs[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tl = 16 * hh + 4 * r + j;
     const bool ok = FULL || T0 + tl < t_end;
     const bool vis = FULL || (ok && T0 + tl <= lim);
-    const unsigned char* rec = buf + ST::KR + tl * SB;
+    const unsigned char* rec = kbuf + ST::KR + tl * SB;
     float x;
     if (L == HAD) {
       const int I = acc[0][j] + acc[1][j] - qoff[0];
       x = *reinterpret_cast<const float*>(rec) * (float)I;
       if (DBG && ok && drow >= 0) a.dbg[(size_t)drow * a.max_seq_len + T0 + tl] = I;
-      const float vsc = *reinterpret_cast<const float*>(buf + ST::VR + tl * SB);
-      vs_had[j] = ok ? vsc : 0.0f;
     } else {
       x = xo[j];
 #pragma unroll
@@ -580,7 +583,13 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
   for (int j = 0; j < 4; ++j) {
     const float p = __builtin_amdgcn_exp2f(xs[j] - m_use);
     psum += p;
-    ph[j] = (_Float16)(L == HAD ? p * vs_had[j] : p);
+    float pv = p;
+    if (L == HAD) {   // the token's V scale (V side: read after the V half has landed)
+      const int tl = 16 * hh + 4 * r + j;
+      const float vsc = *reinterpret_cast<const float*>(vbuf + ST::VR + tl * SB);
+      pv = (FULL || T0 + tl < t_end) ? p * vsc : 0.0f;
+    }
+    ph[j] = (_Float16)pv;
   }
   l_run += psum;
   // B operand of P V: k-slots 0..3 hold half 0's tokens, 4..7 half 1's; the other half's
@@ -596,7 +605,7 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
 #pragma unroll
   for (int o = 0; o < NO; ++o) {
     VOctet<L> v;
-    load_voctet<L, ST, FULL>(buf, T0, t_end, col + 16 * o, r, v);
+    load_voctet<L, ST, FULL>(vbuf, T0, t_end, col + 16 * o, r, v);
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       oacc[o * 4 + pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand<L>(v, 2 * pt, magic), pB0, oacc[o * 4 + pt], 0, 0, 0);
@@ -613,12 +622,14 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
 // y = kv head, z = batch row.
 template <int L, int D, int TR>
 struct PartialShape {
-  // 8-row tiles stream through an LDS ring filled by direct loads (two slots: one step in flight
-  // while one is consumed); 16-row tiles through the register ring
+  // 8-row tiles stream through LDS rings filled by direct loads, one of RK K slots and one of RV V
+  // slots per wave; 16-row tiles through the register ring (NB slots: NB - 1 steps in flight while
+  // one is consumed)
   static constexpr bool DMA = TR == 8;
   using ST = Step<L, D, DMA>;
-  static constexpr int NB = DMA ? 2 : ((ST::SLOTS <= 5) ? 5 : (D == 128 ? 3 : 2));
-  static constexpr int RING = 4 * (DMA ? NB : 1) * ST::BYTES;
+  static constexpr int NB = (ST::SLOTS <= 5) ? 5 : (D == 128 ? 3 : 2);
+  static constexpr int RK = 2, RV = 2;
+  static constexpr int RING = DMA ? 4 * (RK + RV) * ST::HALF : 4 * ST::BYTES;
   static constexpr int MERGE = 4 * TR * (D + 4) * 4;            // the four waves' chunk partials
   static constexpr int LDS = RING > MERGE ? RING : MERGE;       // per block
   // waves per SIMD: as many as four blocks' rings in 160 KiB of LDS allow, registers permitting
@@ -748,58 +759,75 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
     }
   };
 
-  auto step = [&](const unsigned char* buf, int T, auto&& mid) {
+  auto step = [&](const unsigned char* kbuf, const unsigned char* vbuf, int T, auto&& mid) {
     const bool full = T + 32 <= t_end && T + 31 <= lim_min;
     if (TR == 8) {
       if (full)
-        attend_step8<L, D, ST, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic,
+        attend_step8<L, D, ST, DBG, true>(a, kbuf, vbuf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic,
                                           m_run, l_run, oacc, mid);
       else
-        attend_step8<L, D, ST, DBG, false>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic,
+        attend_step8<L, D, ST, DBG, false>(a, kbuf, vbuf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic,
                                            m_run, l_run, oacc, mid);
     } else {
       if (full)
-        attend_step<L, D, ST, DBG, true>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic, m_run, l_run, oacc);
+        attend_step<L, D, ST, DBG, true>(a, kbuf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic, m_run, l_run, oacc);
       else
-        attend_step<L, D, ST, DBG, false>(a, buf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic, m_run, l_run, oacc);
+        attend_step<L, D, ST, DBG, false>(a, kbuf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic, m_run, l_run, oacc);
     }
   };
 
   if constexpr (PS::DMA) {
-    // LDS ring of two slots per wave, step s in slot s & 1, its K half and V half loaded as separate
-    // groups in the order K0 V0 K1 V1 K2 V2 ...: the K half of step s + 2 is issued as soon as the
-    // K side of step s has read its slot, the V half after the V side, and each half is waited for
-    // only where it is first read.  Loads complete in issue order, so a count of the groups issued
-    // after a half bounds the wait for it (stores in the loop only make such a wait longer).
-    static_assert(NB == 2, "two ring slots");
-    constexpr int G = ST::GROUP;
-    unsigned char* ring = smem + wave * 2 * ST::BYTES;
-    const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ring);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (i < nsteps) {
-        const HalfRows h = half_rows_s(a, b, hk, t_begin + 32 * i, t_end);
-        issue_dma_half<ST, false>(a, h, lane, ring_lds + i * ST::BYTES);
-        issue_dma_half<ST, true>(a, h, lane, ring_lds + i * ST::BYTES);
+    // LDS rings of RK K slots and RV V slots per wave (step s in K slot s % RK and V slot s % RV).
+    // The K half of step s + RK is issued as soon as the K side of step s has read its slot, the
+    // V half of step s + RV after the V side, so the issue order is K(j + RK), V(j + RV) for
+    // j = ..., s - 1, s (the prologue issues the same order for negative j), and each half is
+    // waited for only where it is first read.  Loads complete in issue order, so the count of the
+    // groups issued after a half bounds the wait for it (stores in the loop only make such a wait
+    // longer).
+    constexpr int RK = PS::RK, RV = PS::RV, MX = RK > RV ? RK : RV;
+    constexpr int G = ST::GROUP, H = ST::HALF;
+    static_assert((2 * MX) * G <= 63, "load counter range");
+    unsigned char* kring = smem + wave * (RK + RV) * H;
+    unsigned char* vring = kring + RK * H;
+    const uint32_t kr_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)kring);
+    const uint32_t vr_lds = kr_lds + RK * H;
+    auto rows = [&](int st) { return half_rows_s(a, b, hk, t_begin + 32 * st, t_end); };
+    auto wait_groups = [](int n) {
+      switch (n) {
+        case 0: wait_vm<0>(); break;
+        case 1: wait_vm<G>(); break;
+        case 2: wait_vm<2 * G>(); break;
+        case 3: wait_vm<3 * G>(); break;
+        case 4: wait_vm<(4 * G <= 63 ? 4 * G : 63)>(); break;
+        case 5: wait_vm<(5 * G <= 63 ? 5 * G : 63)>(); break;
+        case 6: wait_vm<(6 * G <= 63 ? 6 * G : 63)>(); break;
+        default: wait_vm<(7 * G <= 63 ? 7 * G : 63)>(); break;
       }
+    };
+    auto span_count = [](int lo, int hi) { return hi >= lo ? hi - lo + 1 : 0; };
+#pragma unroll
+    for (int j = -MX; j < 0; ++j) {
+      const int k = j + RK, v = j + RV;
+      if (k >= 0 && k < nsteps) issue_dma_half<ST, false>(a, rows(k), lane, kr_lds + k * H);
+      if (v >= 0 && v < nsteps) issue_dma_half<ST, true>(a, rows(v), lane, vr_lds + v * H);
+    }
+    int ks = 0, vs = 0;   // slots of step s
     for (int s = 0; s < nsteps; ++s) {
-      const uint32_t sl = ring_lds + (s & 1) * ST::BYTES;
-      const bool more1 = s + 1 < nsteps, more2 = s + 2 < nsteps;
-      HalfRows h2{0, 0};
-      if (more2) h2 = half_rows_s(a, b, hk, t_begin + 32 * (s + 2), t_end);
-      if (more1) wait_vm<3 * G>();   // K of step s: then V(s), K(s + 1), V(s + 1)
-      else wait_vm<G>();
-      step(ring + (s & 1) * ST::BYTES, t_begin + 32 * s, [&]() {
-        if (more2) {
-          issue_dma_half<ST, false>(a, h2, lane, sl);
-          wait_vm<3 * G>();          // V of step s: then K(s + 1), V(s + 1), K(s + 2)
-        } else if (more1) {
-          wait_vm<2 * G>();
-        } else {
-          wait_vm<0>();
-        }
+      const bool k_next = s + RK < nsteps, v_next = s + RV < nsteps;
+      const HalfRows hk_next = k_next ? rows(s + RK) : HalfRows{0, 0};
+      const HalfRows hv_next = v_next ? rows(s + RV) : HalfRows{0, 0};
+      // K of step s: then K(s + 1 .. s + RK - 1) and V(s - RK + RV .. s + RV - 1)
+      wait_groups(span_count(s + 1, min(nsteps - 1, s + RK - 1)) +
+                  span_count(max(0, s - RK + RV), min(nsteps - 1, s + RV - 1)));
+      step(kring + ks * H, vring + vs * H, t_begin + 32 * s, [&]() {
+        if (k_next) issue_dma_half<ST, false>(a, hk_next, lane, kr_lds + ks * H);
+        // V of step s: then K(s - RV + 1 + RK .. s + RK) and V(s + 1 .. s + RV - 1)
+        wait_groups(span_count(max(0, s - RV + 1 + RK), min(nsteps - 1, s + RK)) +
+                    span_count(s + 1, min(nsteps - 1, s + RV - 1)));
       });
-      if (more2) issue_dma_half<ST, true>(a, h2, lane, sl);
+      if (v_next) issue_dma_half<ST, true>(a, hv_next, lane, vr_lds + vs * H);
+      ks = ks + 1 == RK ? 0 : ks + 1;
+      vs = vs + 1 == RV ? 0 : vs + 1;
     }
   } else {
     unsigned char* buf = smem + wave * ST::BYTES;
@@ -819,7 +847,7 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
         const int su = si - (NB - 1);
         if (su >= 0 && su < nsteps) {
           stage_step<L, D>(buf, lane, pre[(k + 1) % NB]);
-          step(buf, t_begin + 32 * su, [] {});
+          step(buf, buf, t_begin + 32 * su, [] {});
         }
       }
     }
