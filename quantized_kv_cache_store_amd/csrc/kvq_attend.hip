@@ -41,57 +41,6 @@
 
 namespace kvq {
 
-// Staging of one 32-token step in a wave's LDS slice.  Two ways to fill it:
-//   * register ring (DMA = false): 16-byte loads into registers several steps ahead, then one
-//     copy per step to [K payload rows 32 x RS][V payload rows 32 x RS][K records 32 x SB]
-//     [V records 32 x SB]; payload rows are padded to RS = PB + 16 bytes, which spreads the reads
-//     of a 16-row column (K: one dword per lane from 16 rows; V: 16 dwords of one row times four
-//     rows 4 apart) over all 64 LDS banks.
-//   * direct loads (DMA = true): global_load_lds_dwordx4 writes the step straight into a K slot
-//     [K payload 32 x PB][K records 32 x SB] and a V slot [V payload][V records] of LDS rings,
-//     1 KiB per instruction (lane i's 16 bytes at slot offset + 16 i), so no
-//     registers hold data in flight.  Rows cannot be padded then; for 64-byte rows the chunks are
-//     placed instead so that the same reads stay conflict-free: K chunk c of row t goes to chunk
-//     position c ^ ((t >> 2) & 3) of row t, and V row t to row position vperm(t), which swaps the
-//     two 2-bit fields of t within its 16-row half (rows 4 apart then land 16 banks apart).
-template <int L, int D, bool DMA = false>
-struct Step {
-  using T = Layout<L, D>;
-  static constexpr int PB = T::PB, SB = T::SB;
-  static constexpr int RS = DMA ? PB : PB + 16;
-  // K side offsets from the K base, V side offsets from the V base.  Register ring: one buffer,
-  // both bases equal.  Direct loads: separate K and V slots of HALF bytes each.
-  static constexpr int KP = 0, KR = DMA ? 32 * PB : 64 * RS;
-  static constexpr int VP = DMA ? 0 : 32 * RS, VR = DMA ? 32 * PB : 64 * RS + 32 * SB;
-  static constexpr int HALF = 32 * (PB + SB);
-  static constexpr int BYTES = 64 * RS + 64 * SB;   // register ring buffer
-  static constexpr bool SWZ = DMA && PB == 64;
-  // register ring
-  static constexpr int PAY_SLOTS = (2 * PB + 63) / 64;   // 16-byte chunks of 32 payload rows, per lane
-  static constexpr int REC_SLOTS = (4 * SB + 63) / 64;   // K and V records together
-  static constexpr int SLOTS = 2 * PAY_SLOTS + REC_SLOTS;
-  // direct loads: K and V issued as separate groups, each the tensor's payload (PB / 32
-  // instructions of 1 KiB) and its 32 records (one instruction per 16-token half)
-  static constexpr int PAY_INSTR = PB / 32;
-  static constexpr int GROUP = PAY_INSTR + 2;
-  static_assert(SB <= 64, "one record instruction per half");
-
-  __device__ static int vperm(int t) { return (t & 16) | ((t & 3) << 2) | ((t >> 2) & 3); }
-  // byte offset of dword r of the 16-byte code block g of K row t (layouts with 4-bit codes)
-  __device__ static int kword(int t, int g, int r) {
-    return SWZ ? KP + 16 * (4 * t + (g ^ ((t >> 2) & 3))) + 4 * r : KP + t * RS + 4 * (4 * g + r);
-  }
-  // byte offset of dword oc of V row t (layouts with 4-bit codes)
-  __device__ static int vword(int t, int oc) {
-    return SWZ ? VP + 16 * (4 * vperm(t) + (oc >> 2)) + 4 * (oc & 3) : VP + t * RS + 4 * oc;
-  }
-};
-
-// Physical row indices of the two 16-token halves of the step at T (wave-uniform).
-struct HalfRows {
-  size_t r0, r1;
-};
-
 // Page entries of a wave's chunk held in registers (entry i in lane i % 64 of register i / 64), so
 // that a step's rows come from readlane on the scalar unit: the streaming loop then issues no
 // memory operation other than its own 16-byte loads, which keeps the load-counter waits exact.
@@ -129,23 +78,6 @@ __device__ __forceinline__ HalfRows half_rows(const AttendArgs& a, const ChunkPa
   HalfRows h;
   h.r0 = T < t_end ? chunk_row(a, cp, hk, T) : row_first;
   h.r1 = T + 16 < t_end ? chunk_row(a, cp, hk, T + 16) : row_first;
-  return h;
-}
-
-// The same rows from page entries read through the scalar cache (the page index is wave-uniform):
-// no vector registers hold the page list and no vector-memory counter is involved.
-typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
-
-__device__ __forceinline__ size_t page_row(const AttendArgs& a, int b, int hk, int t) {
-  const const_i32_ptr bt = (const_i32_ptr)a.block_table;
-  const int phys = bt[(size_t)b * a.max_pages + (t >> a.page_shift)];
-  return (((size_t)phys * a.Hkv + hk) << a.page_shift) + (size_t)(t & ((1 << a.page_shift) - 1));
-}
-
-__device__ __forceinline__ HalfRows half_rows_s(const AttendArgs& a, int b, int hk, int T, int t_end) {
-  HalfRows h;
-  h.r0 = page_row(a, b, hk, T);   // T < t_end for every issued step
-  h.r1 = T + 16 < t_end ? page_row(a, b, hk, T + 16) : h.r0;
   return h;
 }
 
@@ -210,61 +142,6 @@ __device__ __forceinline__ void stage_step(unsigned char* buf, int lane, const u
   for (int k = 0; k < ST::REC_SLOTS; ++k) {
     const int ci = lane + 64 * k;
     if (ci < 4 * SB) *reinterpret_cast<u32x4*>(buf + ST::KR + ci * 16) = pre[2 * ST::PAY_SLOTS + k];
-  }
-}
-
-// One direct load to LDS: lane i's 16 bytes at `src` go to LDS byte address lds + 16 i (lds is
-// wave-uniform and travels in m0).
-__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(lds) : "memory");
-}
-
-// Wait until at most N vector-memory operations of the wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-// The same with a wave-uniform base address in SGPRs and a 32-bit lane offset.
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, %1 nt" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
-}
-
-// The K half (ISV = false: K payload and records) or the V half of a step's direct loads into
-// the K or V slot at LDS address `slot`; ST::GROUP instructions.  An instruction whose 64 chunks lie
-// in one 16-token half (rows contiguous in one page) takes that half's row address as a uniform
-// base and a loop-invariant lane offset; the records go as one instruction per half.
-template <class ST, bool ISV>
-__device__ __forceinline__ void issue_dma_half(const AttendArgs& a, HalfRows hr, int lane, uint32_t slot) {
-  constexpr int PB = ST::PB, SB = ST::SB, CPR = PB / 16;
-  const uint8_t* const pay = ISV ? a.vp : a.kp;
-  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-#pragma unroll
-  for (int k = 0; k < ST::PAY_INSTR; ++k) {
-    const int p = 64 * k + lane;
-    int t, c;   // row and chunk that position p holds
-    if (ST::SWZ) {
-      t = ISV ? ST::vperm(p >> 2) : (p >> 2);
-      c = ISV ? (p & 3) : ((p & 3) ^ ((t >> 2) & 3));
-    } else {
-      t = p / CPR;
-      c = p - t * CPR;
-    }
-    const uint32_t lds = slot + (ISV ? ST::VP : ST::KP) + 1024 * k;
-    const bool one_half = (64 * k) / (16 * CPR) == (64 * k + 63) / (16 * CPR);   // folded: k is unrolled
-    if (one_half) {
-      const int half = (64 * k) / (16 * CPR);
-      dma16(pay + (half ? hr.r1 : hr.r0) * PB, (uint32_t)((t & 15) * PB + 16 * c), lds);
-    } else {
-      const size_t row = (t < 16 ? hr.r0 : hr.r1) + (size_t)(t & 15);
-      dma16(pay + row * PB + 16 * c, lds);
-    }
-  }
-  const uint8_t* const rec = ISV ? a.vs : a.ks;
-  if (lane < SB) {   // 16 records of SB bytes per half: SB chunks of 16 bytes
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      dma16(rec + (h ? hr.r1 : hr.r0) * SB, (uint32_t)(16 * lane), slot + (ISV ? ST::VR : ST::KR) + 16 * SB * h);
   }
 }
 
@@ -660,7 +537,7 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
   const int nvalid = min(TR, nrows - row0);
   const int qs0 = a.causal ? a.q_start[b] : 0;
   if (!DBG && a.n_recent > 0 && cg == a.ngroups - 1) {
-    if (S > 0) window_partial<L, D>(a, smem, b, hk, S, row0, nvalid, qs0);
+    if (S > 0) window_tile_block<L, D>(a, smem, b, hk, S, row0, nvalid, qs0);
     return;
   }
   const int span = a.cpw * a.chunk;             // tokens of each wave: cpw consecutive chunks

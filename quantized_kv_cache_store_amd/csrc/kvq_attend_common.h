@@ -55,11 +55,6 @@ __device__ __forceinline__ int row_limit(const AttendArgs& a, int qs0, int R, in
   return a.causal ? qs0 + R / a.G : 0x7fffffff;
 }
 
-template <int D>
-__host__ __device__ constexpr int prologue_lds_bytes() {
-  return 16 * D * 4 + 16 * D + 16 * 4 + 16 * (D / 32) * 4;
-}
-
 // Reductions over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48), on the VALU:
 // v_permlane16_swap / v_permlane32_swap applied to two copies of a value leave in the two
 // registers the value of the lane and of its partner row, in row order, so both lanes of a pair
@@ -103,121 +98,345 @@ __device__ __forceinline__ void q6_octet(uint32_t lo, uint32_t hi16, uint32_t& e
   od = (((lo >> 4) & 0x0F0F0F0Fu) | to) ^ 0x20202020u;
 }
 
-// Window partial: exact f32 rows of the newest tokens (HAD: rotated basis), for the rows
-// row0 .. row0 + nvalid - 1 of (b, hk), each masked by its limit.  The window is walked in
-// tiles of 16 tokens staged in LDS with an online softmax: thread (row = tid / 16, j = tid % 16)
-// scores token j of the tile for its row and accumulates output elements d = j + 16 e.
-// LDS: the query preparation area, then K tile [16][D + 4] (padded rows: conflict-free float4
-// reads), V tile [16][D], P tile [16][16].
-template <int D>
-__host__ __device__ constexpr int window_lds_bytes() {
-  return prologue_lds_bytes<D>() + 16 * (D + 4) * 4 + 16 * D * 4 + 16 * 16 * 4;
+// Reductions over the 16 lanes of a row of the wave (lanes 16 k .. 16 k + 15): DPP rotations
+// within the row by 1, 2, 4, 8 leave every lane with the reduction of all 16.
+__device__ __forceinline__ float row16_rot(float v, int n) {
+  const int x = __builtin_bit_cast(int, v);
+  int y;
+  switch (n) {
+    case 1: y = __builtin_amdgcn_update_dpp(0, x, 0x121, 0xF, 0xF, false); break;
+    case 2: y = __builtin_amdgcn_update_dpp(0, x, 0x122, 0xF, 0xF, false); break;
+    case 4: y = __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false); break;
+    default: y = __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false); break;
+  }
+  return __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, row16_rot(v, 1));
+  v = fmaxf(v, row16_rot(v, 2));
+  v = fmaxf(v, row16_rot(v, 4));
+  return fmaxf(v, row16_rot(v, 8));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += row16_rot(v, 1);
+  v += row16_rot(v, 2);
+  v += row16_rot(v, 4);
+  return v + row16_rot(v, 8);
 }
 
+// Window partial: exact f32 rows of the newest W = min(S, n_recent) tokens (HAD: rotated basis),
+// each row masked by its limit, on the f32 MFMA (v_mfma_f32_16x16x4f32).  One wave takes a tile
+// of 16 rows and walks 16-token tiles k = k0, k0 + kstep, ... of the window with an online
+// softmax:
+//   * Q K^T as C[row][token] = sum_d Q[row][d] K[token][d]: lane (col, r) holds the query of row
+//     col and K of token col for d = 32 r + i in MFMA i (i < D / 4), both from registers; C gives
+//     lane (col, r) the scores of rows 4 r + j, token col (a row's 16 tokens are a 16-lane row);
+//   * P V as C[row][d] += sum_t P[row][t] V[t][d], four tokens per MFMA: the A operand (lane
+//     (col, r): P[row col][token 4 q + r]) is P transposed through LDS, the B operand (lane
+//     (col, r): V[token 4 q + r][d]) comes from the V tile staged in LDS.  The output rows 4 r + j
+//     are the rows of the lane's scores, so the online rescale is lane-local.
+// The wave's LDS: the V tile [16][D + 16] f32, rows padded (conflict-free B reads), P in the
+// padding of its rows ([row][D .. D + 15]).
+template <int D>
+__host__ __device__ constexpr int window_wave_lds() { return 16 * (D + 16) * 4; }
+template <int D>
+__host__ __device__ constexpr int window_lds_bytes() { return 4 * window_wave_lds<D>(); }
+
+template <int D>
+struct WinState {
+  v4f o[D / 16];     // rows 4 r + j, d = 16 dt + col
+  float m[4], l[4];  // per row 4 r + j (l: this lane's part, summed over the row at the end)
+};
+
 template <int L, int D>
-__device__ __forceinline__ void window_partial(const AttendArgs& a, unsigned char* smem, int b, int hk, int S, int row0,
-                                               int nvalid, int qs0) {
-  constexpr int E = D / 16;
-  constexpr int KST = D + 4;
-  constexpr int NL = D / 64;          // float4 of one tile's K (and of its V) per thread
-  float* qf = reinterpret_cast<float*>(smem);
-  int8_t* q8 = reinterpret_cast<int8_t*>(qf + 16 * D);
-  float* sq = reinterpret_cast<float*>(q8 + 16 * D);
-  int* qsum = reinterpret_cast<int*>(sq + 16);
-  float* kt = reinterpret_cast<float*>(smem + prologue_lds_bytes<D>());
-  float* vt = kt + 16 * KST;
-  float* pt = vt + 16 * D;
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int b, int hk, int S, int row0, int nvalid,
+                                            int qs0, int k0, int kstep, int lane, WinState<D>& st) {
+  constexpr int NI = D / 4;           // MFMAs of Q K^T (d = 32 r + i... four lanes groups of D / 4)
+  constexpr int VS = D + 16;          // V tile row stride (floats)
+  const int col = lane & 15, r = lane >> 4;
   const int nrows = a.n_q * a.G;
-  const float* qsrc = a.qrot ? a.qrot : a.q;     // prepared rows are already rotated
-  for (int idx = tid; idx < 16 * D; idx += 256) {
-    const int row = idx / D;
-    qf[idx] = row < nvalid ? qsrc[row_index(a, b, hk, row0 + row) * D + idx % D] : 0.0f;
-  }
-  __syncthreads();
-  if (!a.qrot) prepare_query_lds<L, D>(qf, q8, sq, qsum);
   const int W = min(S, a.n_recent);
   const int w0 = S - W;
   const size_t ring0 = ((size_t)b * a.Hkv + hk) * a.n_recent;
   const float cl = a.alpha * KVQ_LOG2E;
-  const int row = tid >> 4, j = tid & 15;
-  const int lim = row < nvalid ? row_limit(a, qs0, row0 + row, nrows) : -1;
-  float m = -INFINITY, l = 0.0f;
-  float o[E];
+  // the query of row col (prepared rows: rotated for HAD), elements NI r .. NI r + NI - 1
+  float q[NI];
+  {
+    const float* qsrc = a.qrot ? a.qrot : a.q;
+    const bool ok = col < nvalid;
+    const float* qr = qsrc + (ok ? row_index(a, b, hk, row0 + col) * D : 0) + NI * r;
 #pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.0f;
-  // tile loads in registers, one tile ahead (rows past the window: zeros)
-  float4 kreg[NL], vreg[NL];
-  auto load_tile = [&](int t0) {
-#pragma unroll
-    for (int n = 0; n < NL; ++n) {
-      const int idx = tid + 256 * n;
-      const int tt = idx / (D / 4), c4 = idx % (D / 4);
-      kreg[n] = make_float4(0.f, 0.f, 0.f, 0.f);
-      vreg[n] = kreg[n];
-      if (t0 + tt < W) {
-        int slot = w0 + t0 + tt;
-        slot -= (slot / a.n_recent) * a.n_recent;
-        const size_t ro = (ring0 + (size_t)slot) * D + 4 * c4;
-        kreg[n] = *reinterpret_cast<const float4*>(a.kring + ro);
-        vreg[n] = *reinterpret_cast<const float4*>(a.vring + ro);
-      }
+    for (int i = 0; i < NI; i += 4) {
+      const float4 v = ok ? *reinterpret_cast<const float4*>(qr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      q[i] = v.x;
+      q[i + 1] = v.y;
+      q[i + 2] = v.z;
+      q[i + 3] = v.w;
     }
-  };
-  if (W > 0) load_tile(0);
-  for (int t0 = 0; t0 < W; t0 += 16) {
-#pragma unroll
-    for (int n = 0; n < NL; ++n) {
-      const int idx = tid + 256 * n;
-      const int tt = idx / (D / 4), c4 = idx % (D / 4);
-      *reinterpret_cast<float4*>(kt + tt * KST + 4 * c4) = kreg[n];
-      *reinterpret_cast<float4*>(vt + tt * D + 4 * c4) = vreg[n];
-    }
-    __syncthreads();
-    if (t0 + 16 < W) load_tile(t0 + 16);
-    // score of token t0 + j for this thread's row
-    float acc = 0.0f;
-    const float* qr = qf + row * D;
-    const float* kr = kt + j * KST;
-#pragma unroll 8
-    for (int d = 0; d < D; d += 4) {
-      const float4 k4 = *reinterpret_cast<const float4*>(kr + d);
-      const float4 q4 = *reinterpret_cast<const float4*>(qr + d);
-      acc += q4.x * k4.x + q4.y * k4.y + q4.z * k4.z + q4.w * k4.w;
-    }
-    const int t = t0 + j;
-    const float x = (t < W && w0 + t <= lim) ? acc * cl : -INFINITY;
-    float tmax = x;
-#pragma unroll
-    for (int k = 1; k < 16; k <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, k));
-    const float m_new = fmaxf(m, tmax);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // a row that sees nothing yet: p = 0
-    const float corr = exp2f(m - m_use);
-    const float p = exp2f(x - m_use);
-    float ps = p;
-#pragma unroll
-    for (int k = 1; k < 16; k <<= 1) ps += __shfl_xor(ps, k);
-    l = l * corr + ps;
-    m = m_new;
-    pt[row * 16 + j] = p;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float acc_o = o[e] * corr;
-#pragma unroll
-      for (int tt = 0; tt < 16; ++tt) acc_o += pt[row * 16 + tt] * vt[tt * D + j + 16 * e];
-      o[e] = acc_o;
-    }
-    __syncthreads();
   }
+  int lim[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lim[j] = 4 * r + j < nvalid ? row_limit(a, qs0, row0 + 4 * r + j, nrows) : -1;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) st.o[i] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    st.m[j] = -INFINITY;
+    st.l[j] = 0.0f;
+  }
+  const int ntiles = (W + 15) / 16;
+  for (int k = k0; k < ntiles; k += kstep) {
+    const int t0 = 16 * k;
+    const bool tok_ok = t0 + col < W;
+    int slot = w0 + t0 + col;
+    slot -= (slot / a.n_recent) * a.n_recent;
+    const size_t ro = (ring0 + (size_t)(tok_ok ? slot : 0)) * D + NI * r;
+    // ---- Q K^T
+    v4f c = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NI; i += 4) {
+      const float4 kv = tok_ok ? *reinterpret_cast<const float4*>(a.kring + ro + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i], kv.x, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 1], kv.y, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 2], kv.z, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 3], kv.w, c, 0, 0, 0);
+    }
+    // ---- V tile to LDS (token col, elements NI r ..), zeros past the window
+#pragma unroll
+    for (int i = 0; i < NI; i += 4) {
+      const float4 vv = tok_ok ? *reinterpret_cast<const float4*>(a.vring + ro + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(vt + col * VS + NI * r + i) = vv;
+    }
+    // ---- online softmax of rows 4 r + j over the tile's 16 tokens (lanes of the 16-lane row)
+    float p[4], corr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x = (tok_ok && w0 + t0 + col <= lim[j]) ? c[j] * cl : -INFINITY;
+      const float m_new = fmaxf(st.m[j], row16_max(x));
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // a row that sees nothing yet: p = 0
+      corr[j] = exp2f(st.m[j] - m_use);
+      p[j] = exp2f(x - m_use);
+      st.l[j] = st.l[j] * corr[j] + p[j];
+      st.m[j] = m_new;
+      vt[(4 * r + j) * VS + D + col] = p[j];   // P[row][token col] in the row's padding
+    }
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      v4f o = st.o[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] *= corr[j];
+      st.o[i] = o;
+    }
+    // ---- P V
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const float pa = vt[col * VS + D + 4 * qq + r];   // P[row col][token 4 qq + r]
+      const float* vrow = vt + (4 * qq + r) * VS + col;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vrow[16 * dt], st.o[dt], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) st.l[j] = row16_sum(st.l[j]);
+}
+
+// Write a window state as the partial of rows row0 + 4 r + j (< nvalid) in the window slot.
+template <int D>
+__device__ __forceinline__ void window_store(const AttendArgs& a, const WinState<D>& st, int b, int hk, int row0, int nvalid,
+                                             int lane) {
+  const int col = lane & 15, r = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (4 * r + j >= nvalid) continue;
+    float* dst = a.ws + (row_index(a, b, hk, row0 + 4 * r + j) * a.nc1 + (a.nc1 - 1)) * partial_stride(D);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) dst[16 * dt + col] = st.o[dt][j];
+    if (col == 0) {
+      dst[D] = st.m[j];
+      dst[D + 1] = st.l[j];
+    }
+  }
+}
+
+// Window partial of one tile of at most 16 rows by the block's four waves, which split the
+// window's 16-token tiles (wave w: tiles w, w + 4, ...) and merge their states through LDS in a
+// fixed order (decode).
+template <int L, int D>
+__device__ __forceinline__ void window_tile_block(const AttendArgs& a, unsigned char* smem, int b, int hk, int S, int row0,
+                                                  int nvalid, int qs0) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  WinState<D> st;
+  window_wave<L, D>(a, reinterpret_cast<float*>(smem + wave * window_wave_lds<D>()), b, hk, S, row0, nvalid, qs0, wave, 4,
+                    lane, st);
+  __syncthreads();
+  // each wave's state as [16 rows][D + 4] (o, m, l)
+  constexpr int PST = D + 4;
+  float* mo = reinterpret_cast<float*>(smem) + wave * 16 * PST;
+  const int col = lane & 15, r = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float* dst = mo + (4 * r + j) * PST;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) dst[16 * dt + col] = st.o[dt][j];
+    if (col == 0) {
+      dst[D] = st.m[j];
+      dst[D + 1] = st.l[j];
+    }
+  }
+  __syncthreads();
+  const int row = tid >> 4, e0 = (tid & 15) * (D / 16);   // 16 threads per row
   if (row < nvalid) {
+    const float* src = reinterpret_cast<const float*>(smem) + row * PST;
+    float mk[4], M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      mk[k] = src[k * 16 * PST + D];
+      M = fmaxf(M, mk[k]);
+    }
+    float w[4], l = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      w[k] = mk[k] == -INFINITY ? 0.0f : exp2f(mk[k] - M);
+      l += w[k] * src[k * 16 * PST + D + 1];
+    }
     float* dst = a.ws + (row_index(a, b, hk, row0 + row) * a.nc1 + (a.nc1 - 1)) * partial_stride(D);
 #pragma unroll
-    for (int e = 0; e < E; ++e) dst[j + 16 * e] = o[e];
-    if (j == 0) {
-      dst[D] = m;
+    for (int e = 0; e < D / 16; ++e) {
+      float o = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o += w[k] * src[k * 16 * PST + e0 + e];
+      dst[e0 + e] = o;
+    }
+    if ((tid & 15) == 0) {
+      dst[D] = M;
       dst[D + 1] = l;
     }
+  }
+}
+
+// ----------------------------------------------------------------------------- staging of 32-token steps
+
+// Staging of one 32-token step in a wave's LDS slice.  Two ways to fill it:
+//   * register ring (DMA = false): 16-byte loads into registers several steps ahead, then one
+//     copy per step to [K payload rows 32 x RS][V payload rows 32 x RS][K records 32 x SB]
+//     [V records 32 x SB]; payload rows are padded to RS = PB + 16 bytes, which spreads the reads
+//     of a 16-row column (K: one dword per lane from 16 rows; V: 16 dwords of one row times four
+//     rows 4 apart) over all 64 LDS banks.
+//   * direct loads (DMA = true): global_load_lds_dwordx4 writes the step straight into a K slot
+//     [K payload 32 x PB][K records 32 x SB] and a V slot [V payload][V records] of LDS rings,
+//     1 KiB per instruction (lane i's 16 bytes at slot offset + 16 i), so no
+//     registers hold data in flight.  Rows cannot be padded then; for 64-byte rows the chunks are
+//     placed instead so that the same reads stay conflict-free: K chunk c of row t goes to chunk
+//     position c ^ ((t >> 2) & 3) of row t, and V row t to row position vperm(t), which swaps the
+//     two 2-bit fields of t within its 16-row half (rows 4 apart then land 16 banks apart).
+template <int L, int D, bool DMA = false>
+struct Step {
+  using T = Layout<L, D>;
+  static constexpr int PB = T::PB, SB = T::SB;
+  static constexpr int RS = DMA ? PB : PB + 16;
+  // K side offsets from the K base, V side offsets from the V base.  Register ring: one buffer,
+  // both bases equal.  Direct loads: separate K and V slots of HALF bytes each.
+  static constexpr int KP = 0, KR = DMA ? 32 * PB : 64 * RS;
+  static constexpr int VP = DMA ? 0 : 32 * RS, VR = DMA ? 32 * PB : 64 * RS + 32 * SB;
+  static constexpr int HALF = 32 * (PB + SB);
+  static constexpr int BYTES = 64 * RS + 64 * SB;   // register ring buffer
+  static constexpr bool SWZ = DMA && PB == 64;
+  // register ring
+  static constexpr int PAY_SLOTS = (2 * PB + 63) / 64;   // 16-byte chunks of 32 payload rows, per lane
+  static constexpr int REC_SLOTS = (4 * SB + 63) / 64;   // K and V records together
+  static constexpr int SLOTS = 2 * PAY_SLOTS + REC_SLOTS;
+  // direct loads: K and V issued as separate groups, each the tensor's payload (PB / 32
+  // instructions of 1 KiB) and its 32 records (one instruction per 16-token half)
+  static constexpr int PAY_INSTR = PB / 32;
+  static constexpr int GROUP = PAY_INSTR + 2;
+  static_assert(SB <= 64, "one record instruction per half");
+
+  __device__ static int vperm(int t) { return (t & 16) | ((t & 3) << 2) | ((t >> 2) & 3); }
+  // byte offset of dword r of the 16-byte code block g of K row t (layouts with 4-bit codes)
+  __device__ static int kword(int t, int g, int r) {
+    return SWZ ? KP + 16 * (4 * t + (g ^ ((t >> 2) & 3))) + 4 * r : KP + t * RS + 4 * (4 * g + r);
+  }
+  // byte offset of dword oc of V row t (layouts with 4-bit codes)
+  __device__ static int vword(int t, int oc) {
+    return SWZ ? VP + 16 * (4 * vperm(t) + (oc >> 2)) + 4 * (oc & 3) : VP + t * RS + 4 * oc;
+  }
+};
+
+// Physical row indices of the two 16-token halves of the step at T (wave-uniform).
+struct HalfRows {
+  size_t r0, r1;
+};
+
+// The same rows from page entries read through the scalar cache (the page index is wave-uniform):
+// no vector registers hold the page list and no vector-memory counter is involved.
+typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
+
+__device__ __forceinline__ size_t page_row(const AttendArgs& a, int b, int hk, int t) {
+  const const_i32_ptr bt = (const_i32_ptr)a.block_table;
+  const int phys = bt[(size_t)b * a.max_pages + (t >> a.page_shift)];
+  return (((size_t)phys * a.Hkv + hk) << a.page_shift) + (size_t)(t & ((1 << a.page_shift) - 1));
+}
+
+__device__ __forceinline__ HalfRows half_rows_s(const AttendArgs& a, int b, int hk, int T, int t_end) {
+  HalfRows h;
+  h.r0 = page_row(a, b, hk, T);   // T < t_end for every issued step
+  h.r1 = T + 16 < t_end ? page_row(a, b, hk, T + 16) : h.r0;
+  return h;
+}
+
+// One direct load to LDS: lane i's 16 bytes at `src` go to LDS byte address lds + 16 i (lds is
+// wave-uniform and travels in m0).
+__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(lds) : "memory");
+}
+
+// Wait until at most N vector-memory operations of the wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// The same with a wave-uniform base address in SGPRs and a 32-bit lane offset.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 nt" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+// The K half (ISV = false: K payload and records) or the V half of a step's direct loads into
+// the K or V slot at LDS address `slot`; ST::GROUP instructions.  An instruction whose 64 chunks lie
+// in one 16-token half (rows contiguous in one page) takes that half's row address as a uniform
+// base and a loop-invariant lane offset; the records go as one instruction per half.
+template <class ST, bool ISV>
+__device__ __forceinline__ void issue_dma_half(const AttendArgs& a, HalfRows hr, int lane, uint32_t slot) {
+  constexpr int PB = ST::PB, SB = ST::SB, CPR = PB / 16;
+  const uint8_t* const pay = ISV ? a.vp : a.kp;
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+#pragma unroll
+  for (int k = 0; k < ST::PAY_INSTR; ++k) {
+    const int p = 64 * k + lane;
+    int t, c;   // row and chunk that position p holds
+    if (ST::SWZ) {
+      t = ISV ? ST::vperm(p >> 2) : (p >> 2);
+      c = ISV ? (p & 3) : ((p & 3) ^ ((t >> 2) & 3));
+    } else {
+      t = p / CPR;
+      c = p - t * CPR;
+    }
+    const uint32_t lds = slot + (ISV ? ST::VP : ST::KP) + 1024 * k;
+    const bool one_half = (64 * k) / (16 * CPR) == (64 * k + 63) / (16 * CPR);   // folded: k is unrolled
+    if (one_half) {
+      const int half = (64 * k) / (16 * CPR);
+      dma16(pay + (half ? hr.r1 : hr.r0) * PB, (uint32_t)((t & 15) * PB + 16 * c), lds);
+    } else {
+      const size_t row = (t < 16 ? hr.r0 : hr.r1) + (size_t)(t & 15);
+      dma16(pay + row * PB + 16 * c, lds);
+    }
+  }
+  const uint8_t* const rec = ISV ? a.vs : a.ks;
+  if (lane < SB) {   // 16 records of SB bytes per half: SB chunks of 16 bytes
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      dma16(rec + (h ? hr.r1 : hr.r0) * SB, (uint32_t)(16 * lane), slot + (ISV ? ST::VR : ST::KR) + 16 * SB * h);
   }
 }
 

@@ -65,46 +65,38 @@ struct PLoad {
   uint32_t kr;                      // one dword of the K records
 };
 
-// Base addresses of the two 16-token halves of a step in the four planes.  A half lies in one
-// page (steps start at multiples of 32 and pages hold a power of two >= 16 tokens), so token
-// 16 h + i of the step is row i past half h's base.  A half wholly past the end reuses half 0's
-// page, so every address stays inside an allocated page; tokens past the end are masked later.
-// Row indices (not pointers, which the compiler would spill to memory when selected per lane).
-struct StepBase {
-  size_t r0, r1;
+// Raw steps reach LDS by direct loads (the decode's staging layout: a K slot and a V slot per
+// step, see Step), NR steps ahead; the block then reads each step's inputs from LDS.
+template <int L, int D>
+struct PrefillShape {
+  using ST = Step<L, D, true>;
+  static constexpr int OPS = 2 * PStep<L, D>::BYTES;        // the two operand buffers
+  static constexpr int BUDGET = D == 128 ? 54613 : 81920;     // three (two) blocks per CU
+  static constexpr int NR_FIT = (BUDGET - OPS) / (2 * ST::HALF);
+  static constexpr int NR = NR_FIT < 2 ? 2 : (NR_FIT > 6 ? 6 : NR_FIT);
+  static constexpr int LDS = OPS + NR * 2 * ST::HALF;
 };
 
-__device__ __forceinline__ StepBase step_base(const AttendArgs& a, int hk, int T0, int t_end, int first_page,
-                                              int lane_page) {
-  const int mask = (1 << a.page_shift) - 1;
-  const int t1 = T0 + 16 < t_end ? T0 + 16 : T0;
-  const int ph0 = __builtin_amdgcn_readlane(lane_page, (T0 >> a.page_shift) - first_page);
-  const int ph1 = __builtin_amdgcn_readlane(lane_page, (t1 >> a.page_shift) - first_page);
-  StepBase sb;
-  sb.r0 = (((size_t)ph0 * a.Hkv + hk) << a.page_shift) + (size_t)(T0 & mask);
-  sb.r1 = (((size_t)ph1 * a.Hkv + hk) << a.page_shift) + (size_t)(t1 & mask);
-  return sb;
-}
-
-// Issue the global loads of one step (every thread, every load, no condition: the waits the
-// compiler places before the producer then count exactly these loads).
+// One step's inputs for this thread from its raw slot (K slot, V slot), in the units the
+// producer works on.
 template <int L, int D>
-__device__ __forceinline__ void prefill_load(const AttendArgs& a, const StepBase& sb, int tid, PLoad<L, D>& ld) {
+__device__ __forceinline__ void prefill_fetch(const unsigned char* kslot, const unsigned char* vslot, int tid,
+                                              PLoad<L, D>& ld) {
   using T = Layout<L, D>;
   using PS = PStep<L, D>;
+  using ST = Step<L, D, true>;
   constexpr int PB = T::PB, SB = T::SB;
-  // K units of a wave all sit in one half (wave-uniform)
-  const uint8_t* kbase = a.kp + (__builtin_amdgcn_readfirstlane((tid >> 6) & 1) ? sb.r1 : sb.r0) * PB;
 #pragma unroll
   for (int k = 0; k < PS::KU; ++k) {
     const int u = tid + 256 * k;
-    const int i = u & 15, r = (u >> 4) & 3, g = u >> 7;
-    const uint8_t* row = kbase + i * PB;
+    const int i = u & 15, r = (u >> 4) & 3, h = (u >> 6) & 1, g = u >> 7;
+    const int t = 16 * h + i;
     if (L == Q60) {
+      const unsigned char* row = kslot + ST::KP + t * PB;
       ld.kw[k] = *reinterpret_cast<const uint32_t*>(row + 24 * g + 4 * r);
       ld.kh[k] = *reinterpret_cast<const uint16_t*>(row + 24 * g + 16 + 2 * r);
     } else {
-      ld.kw[k] = *reinterpret_cast<const uint32_t*>(row + 4 * (4 * g + r));
+      ld.kw[k] = *reinterpret_cast<const uint32_t*>(kslot + ST::kword(t, g, r));
     }
   }
 #pragma unroll
@@ -115,27 +107,23 @@ __device__ __forceinline__ void prefill_load(const AttendArgs& a, const StepBase
     const int g = d >> 5;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int h = s >> 2, i = 4 * r + (s & 3);   // token 16 h + i
-      const uint8_t* vrow = a.vp + ((h ? sb.r1 : sb.r0) + i) * PB;
+      const int t = 16 * (s >> 2) + 4 * r + (s & 3);
       if (L == Q60) {
+        const unsigned char* vrow = vslot + ST::VP + t * PB;
         const int e = d & 31;
         ld.vb[k][s] = vrow[24 * g + (e >> 1)];
         ld.vh[k][s] = vrow[24 * g + 16 + (e >> 2)];
       } else {
-        ld.vb[k][s] = vrow[d >> 1];
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(vslot + ST::vword(t, d >> 3));
+        ld.vb[k][s] = (w >> (8 * ((d >> 1) & 3))) & 0xFFu;
       }
-      const uint8_t* rec = a.vs + ((h ? sb.r1 : sb.r0) + i) * SB;
+      const unsigned char* rec = vslot + ST::VR + t * SB;
       if (L == HAD) ld.vs[k][s] = *reinterpret_cast<const uint32_t*>(rec);
       else if (L == ASYM) ld.vs[k][s] = *reinterpret_cast<const uint32_t*>(rec + 4 * g);
       else ld.vs[k][s] = *reinterpret_cast<const uint16_t*>(rec + 2 * g);
     }
   }
-  {
-    const int w = tid < 8 * SB ? tid : 0;            // threads past the records reload word 0
-    const int tok = w / (SB / 4), word = w % (SB / 4);
-    const size_t row = (tok < 16 ? sb.r0 : sb.r1) + (tok & 15);
-    ld.kr = *reinterpret_cast<const uint32_t*>(a.ks + row * SB + 4 * word);
-  }
+  ld.kr = *reinterpret_cast<const uint32_t*>(kslot + ST::KR + 4 * (tid < 8 * SB ? tid : 0));
 }
 
 // Unpack and dequantise the loaded step into the LDS buffer.
@@ -301,8 +289,8 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
   }
 }
 
-// Grid: x = 64-row block * ngroups + group, the groups being the chunks of the quantised region
-// and, when n_recent > 0, four window groups (one per 16-row tile); y = kv head, z = batch row.
+// Grid: one block per (batch row, kv head, group, 64-row block), the groups being the chunks of
+// the quantised region and, when n_recent > 0, the window.
 // The rows' int8 queries, scales and block sums come prepared by prepare_rows.
 template <int L, int D>
 __global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendArgs a) {
@@ -312,19 +300,32 @@ __global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendA
   constexpr int BIAS = CodeBias<L>::value;
   extern __shared__ __align__(16) unsigned char smem[];
 
-  const int hk = blockIdx.y, b = blockIdx.z;
-  const int rb = (int)blockIdx.x / a.ngroups;
-  const int c = (int)blockIdx.x - rb * a.ngroups;
+  // One-dimensional grid in an XCD-aware order: the chip hands consecutive blocks round robin to
+  // its 8 XCDs (block id runs on XCD id % 8), so virtual index v gives each XCD a contiguous
+  // range, and v puts the 64-row blocks of one (batch row, kv head, chunk) next to each other:
+  // they read the same K/V, which their XCD's L2 then holds for all of them.
+  const int nrb = (a.n_q * a.G + 63) / 64;
+  const int id = (int)blockIdx.x, nblocks = (int)gridDim.x;
+  const int v = (nblocks % 8 == 0) ? (id % 8) * (nblocks / 8) + id / 8 : id;
+  const int rb = v % nrb;
+  const int rest = v / nrb;
+  const int c = rest % a.ngroups;
+  const int hk = (rest / a.ngroups) % a.Hkv, b = rest / a.ngroups / a.Hkv;
   const int S = a.seq_len[b];
   const int Sq = a.n_recent > 0 ? max(0, S - a.n_recent) : S;
   const int nrows = a.n_q * a.G;
   const int row0 = 64 * rb;
   const int nblk = min(64, nrows - row0);
   const int qs0 = a.causal ? a.q_start[b] : 0;
-  const int nch = a.n_recent > 0 ? a.ngroups - 4 : a.ngroups;
-  if (c >= nch) {   // window blocks: one per 16-row tile of the 64 rows
-    const int k = c - nch;
-    if (S > 0 && 16 * k < nblk) window_partial<L, D>(a, smem, b, hk, S, row0 + 16 * k, min(16, nblk - 16 * k), qs0);
+  const int nch = a.n_recent > 0 ? a.ngroups - 1 : a.ngroups;
+  if (c >= nch) {   // window block: wave w takes the 16-row tile 16 w of the 64 rows
+    const int w = threadIdx.x >> 6, nv = min(16, nblk - 16 * w);
+    if (S > 0 && nv > 0) {
+      WinState<D> st;
+      window_wave<L, D>(a, reinterpret_cast<float*>(smem + w * window_wave_lds<D>()), b, hk, S, row0 + 16 * w, nv, qs0, 0, 1,
+                        threadIdx.x & 63, st);
+      window_store<D>(a, st, b, hk, row0 + 16 * w, nv, threadIdx.x & 63);
+    }
     return;
   }
   const int t_begin = c * a.chunk;
@@ -374,30 +375,61 @@ __global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendA
   uint32_t magic;   // fp16 "1024 + code" exponent bits, in a VGPR so v_and_or_b32 can take it
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
-  // page entries of the chunk, one per lane (a 1024-token chunk spans at most 64 pages of >= 16 tokens)
-  const int first_page = t_begin >> a.page_shift;
-  const int npages = nsteps > 0 ? ((t_end - 1) >> a.page_shift) - first_page + 1 : 0;
-  const int lane_page = a.block_table[(size_t)b * a.max_pages + first_page + min(lane, max(npages - 1, 0))];
-  {
-    // read the loaded register here, on every path, so that no wait for this load is left to the
-    // streaming loop (a wait there would also drain the step loads in flight)
-    const int first_phys = __builtin_amdgcn_readfirstlane(lane_page);
-    asm volatile("" ::"s"(first_phys));
-  }
+  // Raw steps in a ring of NR slots after the two operand buffers, NR - 1 steps ahead: wave 0 loads
+  // each step's K half, wave 1 its V half.  Iteration s: issue step s + NR - 1 (into the slot step
+  // s - 1 left, read two iterations ago), wait for step s + 1, barrier, produce step s + 1 into
+  // operand buffer (s + 1) & 1 (read by consume at s - 1, before this barrier), consume step s
+  // (produced before it).  The raw loads complete in issue order, so a wave's count of the steps
+  // it issued after s + 1 bounds its wait; the barrier then publishes the slot to every wave.
+  using PSh = PrefillShape<L, D>;
+  using ST = Step<L, D, true>;
+  constexpr int NR = PSh::NR, H = ST::HALF, G = ST::GROUP;
+  unsigned char* raw = smem + PSh::OPS;
+  const uint32_t raw_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)raw);
+  auto issue = [&](int st) {
+    const uint32_t slot = raw_lds + (st % NR) * 2 * H;
+    if (wave == 0) issue_dma_half<ST, false>(a, half_rows_s(a, b, hk, t_begin + 32 * st, t_end), lane, slot);
+    else if (wave == 1) issue_dma_half<ST, true>(a, half_rows_s(a, b, hk, t_begin + 32 * st, t_end), lane, slot + H);
+  };
+  auto wait_steps = [&](int n) {   // this wave's loads of all but the newest n steps have landed
+    if (wave < 2) {
+      switch (n) {
+        case 0: wait_vm<0>(); break;
+        case 1: wait_vm<G>(); break;
+        case 2: wait_vm<2 * G>(); break;
+        case 3: wait_vm<3 * G>(); break;
+        default: wait_vm<4 * G>(); break;
+      }
+    }
+  };
+  static_assert(NR - 2 <= 4 && 4 * G <= 63, "load counter range");
+  auto raw_k = [&](int st) { return raw + (st % NR) * 2 * H; };
+  auto barrier = [] {
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");   // this wave's LDS writes are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" : : : "memory");
+  };
 
   PLoad<L, D> ld;
+#pragma unroll
+  for (int i = 0; i < NR - 1; ++i)
+    if (i < nsteps) issue(i);
   if (nsteps > 0) {
-    prefill_load<L, D>(a, step_base(a, hk, t_begin, t_end, first_page, lane_page), tid, ld);
+    wait_steps(min(nsteps - 1, NR - 2));
+    barrier();
+    prefill_fetch<L, D>(raw_k(0), raw_k(0) + H, tid, ld);
     prefill_produce<L, D>(smem, tid, ld, min(32, t_end - t_begin), magic);
   }
-  __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
     const int T0 = t_begin + 32 * s;
     const bool more = s + 1 < nsteps;
-    // the next step's loads (the last iteration reloads its own step, unused, so every iteration
-    // issues the same loads)
-    const int Tn = more ? T0 + 32 : T0;
-    prefill_load<L, D>(a, step_base(a, hk, Tn, t_end, first_page, lane_page), tid, ld);
+    if (s + NR - 1 < nsteps) issue(s + NR - 1);
+    if (more) wait_steps(min(nsteps - 1, s + NR - 1) - (s + 1));
+    barrier();
+    if (more) {
+      prefill_fetch<L, D>(raw_k(s + 1), raw_k(s + 1) + H, tid, ld);
+      prefill_produce<L, D>(smem + ((s + 1) & 1) * PS::BYTES, tid, ld, min(32, t_end - T0 - 32), magic);
+    }
     const unsigned char* buf = smem + (s & 1) * PS::BYTES;
     const int n_tok = min(32, t_end - T0);
     if (nval > 0) {
@@ -406,8 +438,6 @@ __global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendA
       else
         prefill_consume<L, D, false>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, oacc);
     }
-    if (more) prefill_produce<L, D>(smem + ((s + 1) & 1) * PS::BYTES, tid, ld, min(32, t_end - Tn), magic);
-    __syncthreads();
   }
 
   // ---------------- this wave's chunk partial: o[d = 16 dt + 4 r + j] of row col
@@ -472,13 +502,15 @@ static prepare_fn pick_prepare(int layout, int D) {
 }
 
 template <int L, int D>
-static void launch_prefill(const AttendArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+static void launch_prefill(const AttendArgs& a, dim3 grid, int n_recent, hipStream_t st) {
+  size_t lds = PrefillShape<L, D>::LDS;
+  if (n_recent > 0 && (size_t)window_lds_bytes<D>() > lds) lds = window_lds_bytes<D>();
   if (lds > 65536)
     (void)hipFuncSetAttribute((const void*)prefill_partial<L, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL((prefill_partial<L, D>), grid, dim3(256), lds, st, a);
 }
 
-typedef void (*prefill_fn)(const AttendArgs&, dim3, size_t, hipStream_t);
+typedef void (*prefill_fn)(const AttendArgs&, dim3, int, hipStream_t);
 
 static prefill_fn pick_prefill(int layout, int D) {
   const int di = D == 256 ? 1 : 0;
@@ -491,11 +523,6 @@ static prefill_fn pick_prefill(int layout, int D) {
   return tab[layout][di];
 }
 
-static size_t prefill_lds_bytes(int layout, int D, int n_recent) {
-  const size_t pb = (size_t)(D / 32) * 1024 + (size_t)D * 64 + 32 * scale_bytes_rt(layout, D);
-  const size_t win = n_recent > 0 ? (size_t)(D == 128 ? window_lds_bytes<128>() : window_lds_bytes<256>()) : 0;
-  return 2 * pb > win ? 2 * pb : win;
-}
 
 // Workspace of the prefill: the partials [rows x (chunks + 1) x (D + 4)] f32, then the prepared rows.
 static RowPrep prefill_ws(size_t rows, int D, int max_seq_len) {
@@ -546,16 +573,15 @@ extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float*
   a.skip = causal && !(flags & KVQ_PREFILL_NO_CAUSAL_SKIP);
   a.q_start = causal ? q_start : nullptr;
   const int nch = chunks_of(max_seq_len, kPrefillChunk);
-  a.ngroups = nch + (c->n_recent > 0 ? 4 : 0);
-  const int64_t gx = ((int64_t)n_q * a.G + 63) / 64 * a.ngroups;
+  a.ngroups = nch + (c->n_recent > 0 ? 1 : 0);
+  const int64_t gx = ((int64_t)n_q * a.G + 63) / 64 * a.ngroups * c->num_kv_heads * batch;
   if (gx > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
   const int rows = batch * n_q * Hq;
   const RowPrep w = prefill_ws((size_t)rows, c->head_dim, max_seq_len);
   if ((st = launch_prepare_rows(c, q, rows, (unsigned char*)workspace, w, a, (hipStream_t)stream)) != KVQ_OK) return st;
   if (gx > 0) {
-    const dim3 grid((unsigned)gx, c->num_kv_heads, batch);
-    pick_prefill(c->layout, c->head_dim)(a, grid, prefill_lds_bytes(c->layout, c->head_dim, c->n_recent),
-                                         (hipStream_t)stream);
+    const dim3 grid((unsigned)gx);
+    pick_prefill(c->layout, c->head_dim)(a, grid, c->n_recent, (hipStream_t)stream);
     if ((st = check_launch("prefill partial kernel")) != KVQ_OK) return st;
   }
   return launch_reduce(c, out, batch, n_q * Hq, seq_len, a.nc1, kPrefillChunk, (const float*)workspace,
