@@ -540,7 +540,7 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
     if (S > 0) window_tile_block<L, D>(a, smem, b, hk, S, row0, nvalid, qs0);
     return;
   }
-  const int span = a.cpw * a.chunk;             // tokens of each wave: cpw consecutive chunks
+  const int span = a.span;                      // tokens of each wave
   if (cg * 4 * span >= Sq) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -899,13 +899,15 @@ static partial_fn pick_partial(int layout, int D, int tr) {
   return tab[layout][di];
 }
 
-// Consecutive chunks per wave of the decode kernel, a function of the call's shape and the device
-// (the partial and the reduce calls agree on it).  A wave streams them as one run, so they merge
-// in its registers by the same online-softmax update, and the grid needs fewer rounds of the chip:
-// each round ends with the blocks' barriers, merges and partial stores, during which their LDS and
-// wave slots stream nothing.  At most four, while one round of resident waves (four per SIMD) still
-// has work for all of them, and while the register-ring kernel's page registers cover the run.
-static int decode_cpw(const kvq_cache* c, int batch, int Hq, int max_seq_len, int chunk) {
+// Tokens per wave of the decode kernel, a function of the call's shape and the device (the partial
+// and the reduce calls agree on it).  Every level of the split-K merge is the same online-softmax
+// update, so a wave can take up to four consecutive chunks as one run, merged in its registers,
+// while one round of resident waves (four per SIMD) still has work for all of them: the grid then
+// needs fewer rounds of the chip, each of which ends with the blocks' barriers, merges and partial
+// stores, during which their LDS and wave slots stream nothing (the register-ring kernel also
+// needs the run's pages to fit its page registers).  Half a chunk per wave for small batches,
+// which would fill more wave slots, measured slower (batch 1 at 128K: 42 us against 39).
+static int decode_span(const kvq_cache* c, int batch, int Hq, int max_seq_len, int chunk) {
   static int cus_of[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -917,10 +919,10 @@ static int decode_cpw(const kvq_cache* c, int batch, int Hq, int max_seq_len, in
   const int G = Hq / c->num_kv_heads;
   const int tr = G <= 8 ? 8 : 16;
   const int64_t waves = (int64_t)batch * c->num_kv_heads * ((G + tr - 1) / tr) * chunks_of(max_seq_len, chunk);
+  const int64_t resident = (int64_t)cus_of[dev] * 16;
   int cpw = 1;
-  while (cpw < 4 && waves >= (int64_t)cus_of[dev] * 16 * 2 * cpw && (2 * cpw * chunk) / c->page_size + 1 < 64 * kPageRegs)
-    cpw *= 2;
-  return cpw;
+  while (cpw < 4 && waves >= resident * 2 * cpw && (2 * cpw * chunk) / c->page_size + 1 < 64 * kPageRegs) cpw *= 2;
+  return cpw * chunk;
 }
 
 // Workspace of the decode: the partials [B x Hq x (chunks + 1) x (D + 4)] f32, then the prepared rows.
@@ -988,8 +990,8 @@ extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float*
   if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
   AttendArgs a = make_args(c, q, Hq, 1, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace);
   const int tr = tile_rows(a);
-  a.cpw = decode_cpw(c, batch, Hq, max_seq_len, chunk);
-  a.ngroups = (chunks_of(max_seq_len, chunk) + 4 * a.cpw - 1) / (4 * a.cpw) + (c->n_recent > 0 ? 1 : 0);
+  a.span = decode_span(c, batch, Hq, max_seq_len, chunk);
+  a.ngroups = chunks_of(max_seq_len, 4 * a.span) + (c->n_recent > 0 ? 1 : 0);
   const int64_t gx = grid_x(a, tr);
   if (gx == 0) return KVQ_OK;
   if ((st = launch_prepare_rows(c, q, batch * Hq, (unsigned char*)workspace,
@@ -1012,9 +1014,9 @@ extern "C" kvq_status kvq_attend_decode_reduce(const kvq_cache* c, float* out, i
   if (chunk < 128 || chunk % 128) return fail(KVQ_ERR_INVALID_ARG, "chunk_tokens must be a positive multiple of 128");
   const size_t need = kvq_decode_workspace_bytes(batch, Hq, c->head_dim, max_seq_len, chunk);
   if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
-  // each partial slot holds a block's four waves of cpw chunks each (merged by the partial kernel)
-  const int cpw = decode_cpw(c, batch, Hq, max_seq_len, chunk);
-  return launch_reduce(c, out, batch, Hq, seq_len, chunks_of(max_seq_len, chunk) + 1, 4 * cpw * chunk, (const float*)workspace,
+  // each partial slot holds a block's four waves of `span` tokens each (merged by the partial kernel)
+  const int span = decode_span(c, batch, Hq, max_seq_len, chunk);
+  return launch_reduce(c, out, batch, Hq, seq_len, chunks_of(max_seq_len, chunk) + 1, 4 * span, (const float*)workspace,
                        (hipStream_t)stream);
 }
 

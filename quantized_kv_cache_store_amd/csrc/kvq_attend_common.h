@@ -36,7 +36,7 @@ struct AttendArgs {
   int n_q;       // queries per batch row (1 for decode)
   int batch;     // batch rows (decode: the grid is one-dimensional)
   int ngroups;   // blocks per row tile along the sequence: chunk groups of four, + 1 for the window
-  int cpw;       // consecutive chunks each wave of the decode kernel streams (1 elsewhere)
+  int span;      // tokens each wave of the decode kernel streams (a multiple of 32; chunk elsewhere)
   int causal;    // rows see t <= q_start + i
   int skip;      // causal skip: stop streaming past the tile's last visible token
   float alpha;
@@ -488,7 +488,7 @@ static inline AttendArgs make_args(const kvq_cache* c, const float* q, int32_t H
   a.max_seq_len = max_seq_len;
   a.n_q = n_q;
   a.ngroups = (nch + 3) / 4 + (c->n_recent > 0 ? 1 : 0);
-  a.cpw = 1;
+  a.span = chunk;
   a.alpha = alpha;
   return a;
 }
