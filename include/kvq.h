@@ -113,9 +113,8 @@ kvq_status kvq_store(const kvq_cache* cache, const float* k_new, const float* v_
                      const int32_t* pos, const int32_t* seq_len, void* stream);
 
 /* Workspace of kvq_attend_decode: room for split-K partials (o_c, m_c, l_c) per
- * (batch, query head, chunk), plus the window partial, then the prepared
- * queries (int8, scale, block sums, rotated f32 for HAD_INT4) per
- * (batch, query head).  Returns 0 for invalid arguments. */
+ * (batch, query head, chunk), plus the window partial.  (The decode kernel
+ * prepares its int8 queries itself.)  Returns 0 for invalid arguments. */
 size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_seq_len, int32_t chunk_tokens);
 

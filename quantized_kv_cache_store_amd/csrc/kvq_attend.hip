@@ -559,9 +559,9 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
   }
   const int nsteps = active ? (t_end - t_begin + 31) / 32 : 0;
 
-  // ---- prologue: this lane's row of the tile from the prepared rows (int8 query in the B-operand
-  // order, its scale and block sums); the perms and sums consume the loads here, before the loop.
-  // With 8-row tiles lane column col serves row col & 7, and its operands are zero outside its half.
+  // ---- prologue: this lane's row of the tile, prepared in the wave (int8 query in the B-operand
+  // order, its scale and block sums).  With 8-row tiles lane column col serves row col & 7, and
+  // its operands are zero outside its half.
   const int col = lane & 15;
   const int r = lane >> 4;
   const int rsel = TR == 8 ? (col & 7) : col;   // this lane's row within the tile
@@ -571,30 +571,27 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
   int qoff[SG];        // bias * sum(q8): the Hadamard scores and the score export use it
   float sqc = 0.0f;
   {
-    const size_t fr = row_index(a, b, hk, row0 + min(rsel, nvalid - 1));
-    const int* qs = a.qsump + fr * NG;
+    RowQ<D> rq;
+    prepare_row_lanes<L, D>(a.q + row_index(a, b, hk, row0 + min(rsel, nvalid - 1)) * D, r, rq);
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const uint2 w = *reinterpret_cast<const uint2*>(a.q8p + fr * D + 32 * g + 8 * r);
-      qB[g] = __builtin_bit_cast(long, u32x2{__builtin_amdgcn_perm(w.y, w.x, 0x06040200u),
-                                             __builtin_amdgcn_perm(w.y, w.x, 0x07050301u)});
-    }
+    for (int g = 0; g < NG; ++g) qB[g] = rq.qB[g];
 #pragma unroll
     for (int i = 0; i < NG / 4; ++i) {
-      qsB[i] = (L == ASYM) ? (float)qs[4 * i + r] : -(float)BIAS * (float)qs[4 * i + r];
+      const int qs = r == 0 ? rq.qsum[4 * i] : r == 1 ? rq.qsum[4 * i + 1] : r == 2 ? rq.qsum[4 * i + 2] : rq.qsum[4 * i + 3];
+      qsB[i] = (L == ASYM) ? (float)qs : -(float)BIAS * (float)qs;
     }
 #pragma unroll
     for (int g = 0; g < SG; ++g) {
       int sum = 0;
       if (L == HAD) {
 #pragma unroll
-        for (int gg = 0; gg < NG; ++gg) sum += qs[gg];
+        for (int gg = 0; gg < NG; ++gg) sum += rq.qsum[gg];
       } else {
-        sum = qs[g];
+        sum = rq.qsum[g];
       }
       qoff[g] = BIAS * sum;
     }
-    sqc = a.sqp[fr] * a.alpha * KVQ_LOG2E;
+    sqc = rq.sq * a.alpha * KVQ_LOG2E;
   }
   const int lim = row_limit(a, qs0, row0 + rsel, nrows);
   const long drow = (DBG && rsel < nvalid) ? (long)row_index(a, b, hk, row0 + rsel) : -1;   // score export only
@@ -925,11 +922,12 @@ static int decode_span(const kvq_cache* c, int batch, int Hq, int max_seq_len, i
   return cpw * chunk;
 }
 
-// Workspace of the decode: the partials [B x Hq x (chunks + 1) x (D + 4)] f32, then the prepared rows.
-static RowPrep decode_ws(int batch, int Hq, int D, int max_seq_len, int chunk) {
+// Workspace of the decode: room for the partials [B x Hq x (chunks + 1) x (D + 4)] f32 (the decode
+// kernel prepares its query rows itself).
+static size_t decode_ws_bytes(int batch, int Hq, int D, int max_seq_len, int chunk) {
   const size_t rows = (size_t)batch * Hq;
   const size_t nc1 = (size_t)chunks_of(max_seq_len, chunk) + 1;
-  return row_prep_layout(rows * nc1 * partial_stride(D) * sizeof(float), rows, D);
+  return rows * nc1 * partial_stride(D) * sizeof(float);
 }
 
 static kvq_status check_chunk(const kvq_cache* c, int32_t chunk) {
@@ -976,7 +974,7 @@ extern "C" size_t kvq_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t 
                                              int32_t chunk) {
   if (batch < 1 || Hq < 1 || (D != 128 && D != 256) || max_seq_len < 0 || chunk < 128 || chunk % 128) return 0;
   // +1 partial slot for the window (always reserved so the size does not depend on n_recent)
-  return decode_ws(batch, Hq, D, max_seq_len, chunk).end;
+  return decode_ws_bytes(batch, Hq, D, max_seq_len, chunk);
 }
 
 extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
@@ -994,9 +992,6 @@ extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float*
   a.ngroups = chunks_of(max_seq_len, 4 * a.span) + (c->n_recent > 0 ? 1 : 0);
   const int64_t gx = grid_x(a, tr);
   if (gx == 0) return KVQ_OK;
-  if ((st = launch_prepare_rows(c, q, batch * Hq, (unsigned char*)workspace,
-                                decode_ws(batch, Hq, c->head_dim, max_seq_len, chunk), a, (hipStream_t)stream)) != KVQ_OK)
-    return st;
   a.batch = batch;
   const dim3 grid((unsigned)gx, c->num_kv_heads, batch);
   pick_partial<false>(c->layout, c->head_dim, tr)(a, grid, c->n_recent, (hipStream_t)stream);
@@ -1044,9 +1039,6 @@ extern "C" kvq_status kvq_debug_qk_i32(const kvq_cache* c, const float* q, int32
   const size_t need = kvq_decode_workspace_bytes(batch, Hq, c->head_dim, max_seq_len, chunk);
   if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
   AttendArgs a = make_args(c, q, Hq, 1, 1.0f, block_table, max_pages, seq_len, max_seq_len, chunk, workspace);
-  if ((st = launch_prepare_rows(c, q, batch * Hq, (unsigned char*)workspace,
-                                decode_ws(batch, Hq, c->head_dim, max_seq_len, chunk), a, (hipStream_t)stream)) != KVQ_OK)
-    return st;
   a.dbg = scores;
   a.kring = nullptr;
   a.vring = nullptr;

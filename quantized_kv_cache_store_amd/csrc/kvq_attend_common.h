@@ -124,6 +124,127 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + row16_rot(v, 8);
 }
 
+// Butterflies between partner lane rows (lanes l and l ^ 16, or l and l ^ 32): row_pair leaves the
+// lower row's value in lo and the upper row's in hi, so the lower lane takes lo + hi and the upper
+// lo - hi, the (a, b) -> (a + b, a - b) of the transform with a the lower-index element.
+__device__ __forceinline__ float butterfly_rows(float v, int swap32, bool upper) {
+  float lo, hi;
+  row_pair(v, swap32, lo, hi);
+  return upper ? lo - hi : lo + hi;
+}
+
+// Query preparation of one row inside a wave, in the order the int8 MFMA's B operand takes: lane
+// row r (lanes 16 r .. 16 r + 15 all hold the same row in their column) keeps elements
+// 32 g + 8 r + i (i < 8) of every 32-element block g.  The arithmetic is that of the query
+// preparation kernel, step for step: the Hadamard layout's butterflies with strides 1, 2, 4 inside
+// the lane, 8 and 16 between lane rows, 32, 64, ... inside the lane again (the ascending stage order
+// of the encoding), each in f32, then f32(1/sqrt(D)); amax over the row, sq = amax / 127 (IEEE
+// division), q8 = rint(x / sq) clamped to [-127, 127]; per-block sums of q8.
+template <int D>
+struct RowQ {
+  long qB[D / 32];     // B operand of block g: codes [0, 2, 4, 6, 1, 3, 5, 7] of the lane's 8 (the order
+                       // in which the A operand unpacks even and odd nibbles)
+  int qsum[D / 32];    // sum of q8 over block g (every lane)
+  float sq;
+};
+
+template <int L, int D>
+__device__ __forceinline__ void prepare_row_lanes(const float* qrow, int r, RowQ<D>& out) {
+#pragma clang fp contract(off)
+  constexpr int NG = D / 32;
+  float x[NG][8];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const float4 u = *reinterpret_cast<const float4*>(qrow + 32 * g + 8 * r);
+    const float4 w = *reinterpret_cast<const float4*>(qrow + 32 * g + 8 * r + 4);
+    x[g][0] = u.x; x[g][1] = u.y; x[g][2] = u.z; x[g][3] = u.w;
+    x[g][4] = w.x; x[g][5] = w.y; x[g][6] = w.z; x[g][7] = w.w;
+  }
+  if (L == HAD) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if ((i & h) == 0) {
+            const float p = x[g][i], q = x[g][i + h];
+            x[g][i] = p + q;
+            x[g][i + h] = p - q;
+          }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)   // strides 8, 16: lane rows r ^ 1, r ^ 2
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[g][i] = butterfly_rows(x[g][i], m, (r >> m) & 1);
+#pragma unroll
+    for (int hg = 1; hg < NG; hg <<= 1)
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        if ((g & hg) == 0)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float p = x[g][i], q = x[g + hg][i];
+            x[g][i] = p + q;
+            x[g + hg][i] = p - q;
+          }
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[g][i] = x[g][i] * hadamard_norm<D>();
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[g][i]));
+  m = max_over_rows(m);
+  const float s = m / 127.0f;
+  out.sq = s;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    int c[8], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      c[i] = s != 0.0f ? (int)fminf(fmaxf(rintf(x[g][i] / s), -127.0f), 127.0f) : 0;
+      sum += c[i];
+    }
+    const uint32_t lo = (uint32_t)(c[0] & 0xFF) | ((uint32_t)(c[2] & 0xFF) << 8) | ((uint32_t)(c[4] & 0xFF) << 16) |
+                        ((uint32_t)(c[6] & 0xFF) << 24);
+    const uint32_t hi = (uint32_t)(c[1] & 0xFF) | ((uint32_t)(c[3] & 0xFF) << 8) | ((uint32_t)(c[5] & 0xFF) << 16) |
+                        ((uint32_t)(c[7] & 0xFF) << 24);
+    out.qB[g] = __builtin_bit_cast(long, u32x2{lo, hi});
+    sum += __shfl_xor(sum, 16);
+    sum += __shfl_xor(sum, 32);
+    out.qsum[g] = sum;
+  }
+}
+
+// The f32 query of a row rotated in a wave, for the window: lane row r holds the contiguous
+// elements N r .. N r + N - 1 (N = D / 4): butterflies with strides below N inside the lane,
+// N and 2 N between lane rows, then f32(1/sqrt(D)).
+template <int D>
+__device__ __forceinline__ void rotate_quarters(float* x, int r) {
+#pragma clang fp contract(off)
+  constexpr int N = D / 4;
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((i & h) == 0) {
+        const float p = x[i], q = x[i + h];
+        x[i] = p + q;
+        x[i + h] = p - q;
+      }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = butterfly_rows(x[i], m, (r >> m) & 1);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = x[i] * hadamard_norm<D>();
+}
+
 // Window partial: exact f32 rows of the newest W = min(S, n_recent) tokens (HAD: rotated basis),
 // each row masked by its limit, on the f32 MFMA (v_mfma_f32_16x16x4f32).  One wave takes a tile
 // of 16 rows and walks 16-token tiles k = k0, k0 + kstep, ... of the window with an online
@@ -162,7 +283,7 @@ __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int 
   // the query of row col (prepared rows: rotated for HAD), elements NI r .. NI r + NI - 1
   float q[NI];
   {
-    const float* qsrc = a.qrot ? a.qrot : a.q;
+    const float* qsrc = a.qrot ? a.qrot : a.q;   // prepared rows (prefill: rotated for HAD) or the raw query
     const bool ok = col < nvalid;
     const float* qr = qsrc + (ok ? row_index(a, b, hk, row0 + col) * D : 0) + NI * r;
 #pragma unroll
@@ -173,6 +294,7 @@ __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int 
       q[i + 2] = v.z;
       q[i + 3] = v.w;
     }
+    if (L == HAD && !a.qrot) rotate_quarters<D>(q, r);
   }
   int lim[4];
 #pragma unroll

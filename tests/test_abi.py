@@ -39,9 +39,8 @@ def test_sizes():
     assert lib.kvq_scale_bytes(_lib.HAD_INT4, 128) == 4
     assert lib.kvq_payload_bytes(_lib.Q4_0, 64) == 0          # unsupported head_dim
     assert lib.kvq_payload_bytes(7, 128) == 0
-    # partials [B][Hq][chunks + 1][D + 4] f32, then the prepared queries of the B * Hq rows:
-    # rotated f32 query, int8 query, f32 scale, int32 block sums
-    assert lib.kvq_decode_workspace_bytes(1, 64, 128, 131072, 512) == 64 * (257 * 132 * 4 + 128 * 4 + 128 + 4 + 4 * 4)
+    # room for the partials [B][Hq][chunks + 1][D + 4] f32
+    assert lib.kvq_decode_workspace_bytes(1, 64, 128, 131072, 512) == 64 * 257 * 132 * 4
     assert lib.kvq_decode_workspace_bytes(1, 64, 128, 1000, 100) == 0  # chunk not a multiple of 128
 
 
