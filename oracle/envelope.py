@@ -118,8 +118,9 @@ def _sample(w, S, kv_heads):
 def main(S=2048, kv_heads=2):
     import workloads as W
 
-    names = {spec.HAD_INT4: "HAD int4", spec.Q4_0: "q4_0", spec.Q6_0: "q6_0", spec.ASYM_G32: "asym int4 g32"}
-    layouts = [spec.HAD_INT4, spec.Q4_0, spec.Q6_0, spec.ASYM_G32]
+    names = {spec.HAD_INT4: "HAD int4", spec.Q4_0: "q4_0", spec.Q6_0: "q6_0", spec.ASYM_G32: "asym int4 g32",
+             spec.Q8_0: "q8_0"}
+    layouts = [spec.HAD_INT4, spec.Q4_0, spec.Q6_0, spec.ASYM_G32, spec.Q8_0]
     print(f"relative L2 error vs exact attention, one batch row, {kv_heads} kv heads, S = {S}, no window\n")
     print("| values (workload) | layout | K and V | K only | V only | K and V, f32 query |")
     print("|---|---|---|---|---|---|")

@@ -71,11 +71,12 @@ def _blocks(x):
 
 # --------------------------------------------------------------------- symmetric block layouts
 def quantize_symmetric_blocks(x, layout):
-    """q4_0 / q6_0 encoding of rows ``x`` [..., D].
+    """q4_0 / q6_0 / q8_0 encoding of rows ``x`` [..., D].
 
     [FreeToken-268] Summary and Storage layouts: per 32 values along head_dim,
     d = amax / max_magnitude stored as fp16 (8 for q4_0, so codes span
-    [-8, 7]); the code is the value divided by the stored scale, rounded.
+    [-8, 7]; 32 for q6_0, 128 for q8_0); the code is the value divided by the
+    stored scale, rounded.
 
     Returns (codes int64 [..., D], d float64 [..., D/32] holding the fp16 values).
     """
@@ -204,6 +205,17 @@ def unpack_q6(packed):
     return v.reshape(b.shape[:-1] + (nb * 32,))
 
 
+def pack_bytes(codes):
+    """q8_0 payload: code j of a row in byte j, as its two's-complement byte."""
+    return (np.asarray(codes, dtype=np.int64) & 0xFF).astype(np.uint8)
+
+
+def unpack_bytes(packed):
+    """Inverse of pack_bytes: signed codes from bytes (v ^ 0x80) - 0x80."""
+    v = np.asarray(packed, dtype=np.int64)
+    return (v ^ 0x80) - 0x80
+
+
 # --------------------------------------------------------------------- whole rows
 def encode_rows(layout, x):
     """Encode rows ``x`` [..., D] into the stored cache bytes of ``layout``.
@@ -226,9 +238,14 @@ def encode_rows(layout, x):
         scales = s[..., None]
         payload = pack_nibbles(codes)
         record = np.ascontiguousarray(f32_bits(s)[..., None]).view(np.uint8)
-    elif layout in (spec.Q4_0, spec.Q6_0):
+    elif layout in (spec.Q4_0, spec.Q6_0, spec.Q8_0):
         codes, scales = quantize_symmetric_blocks(x, layout)
-        payload = pack_nibbles(codes) if layout == spec.Q4_0 else pack_q6(codes)
+        if layout == spec.Q4_0:
+            payload = pack_nibbles(codes)
+        elif layout == spec.Q6_0:
+            payload = pack_q6(codes)
+        else:
+            payload = pack_bytes(codes)
         record = np.ascontiguousarray(f16_bits(scales)).view(np.uint8)
     else:
         codes, scales, zeros = quantize_asym_g32(x)
@@ -244,6 +261,8 @@ def decode_codes(layout, payload):
     """Codes of stored payload bytes [..., P] (sign rules of the layout)."""
     if layout == spec.Q6_0:
         return unpack_q6(payload)
+    if layout == spec.Q8_0:
+        return unpack_bytes(payload)
     return unpack_nibbles(payload, signed=(layout != spec.ASYM_G32))
 
 

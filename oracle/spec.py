@@ -15,15 +15,19 @@ Q6_0       [FreeToken-268] Storage layouts: 32 values, 16-byte low-nibble plane
 ASYM_G32   [Open-TQ-Metal] Background, per-group asymmetric int4: groups of 32
            consecutive elements, per-group scale and zero point, two values
            per byte.  The scale and zero are stored as fp16 each.
+Q8_0       [FreeToken-268] Summary and the memory table: the 8-bit block
+           scheme at 1.0625 bytes per element, i.e. 32 one-byte codes plus one
+           fp16 scale per 32 values along head_dim.
 """
 
 HAD_INT4 = 0
 Q4_0 = 1
 Q6_0 = 2
 ASYM_G32 = 3
+Q8_0 = 4
 
-LAYOUTS = (HAD_INT4, Q4_0, Q6_0, ASYM_G32)
-NAMES = {HAD_INT4: "had_int4", Q4_0: "q4_0", Q6_0: "q6_0", ASYM_G32: "asym_int4_g32"}
+LAYOUTS = (HAD_INT4, Q4_0, Q6_0, ASYM_G32, Q8_0)
+NAMES = {HAD_INT4: "had_int4", Q4_0: "q4_0", Q6_0: "q6_0", ASYM_G32: "asym_int4_g32", Q8_0: "q8_0"}
 
 BLOCK = 32  # elements per block / group for the block layouts
 
@@ -49,6 +53,8 @@ def payload_bytes(layout, D):
     check_head_dim(layout, D)
     if layout == Q6_0:
         return (D // BLOCK) * 24
+    if layout == Q8_0:
+        return D
     return D // 2
 
 
@@ -71,6 +77,8 @@ def code_range(layout):
     """Inclusive (lo, hi) range of the integer codes of a layout."""
     if layout == Q6_0:
         return (-32, 31)
+    if layout == Q8_0:
+        return (-128, 127)
     if layout == ASYM_G32:
         return (0, 15)
     return (-8, 7)
@@ -81,10 +89,13 @@ def max_magnitude(layout):
 
     [FreeToken-268] Storage layouts: the 4-bit layout uses 8 (not 7), so the
     symmetric range is [-8, 7].  The 6-bit layout takes 2^(bits-1) = 32 by the
-    same rule; the Hadamard int4 layout is symmetric int4 and takes 8.
+    same rule, the 8-bit layout 128 (range [-128, 127]); the Hadamard int4
+    layout is symmetric int4 and takes 8.
     """
     if layout == Q6_0:
         return 32
+    if layout == Q8_0:
+        return 128
     if layout in (Q4_0, HAD_INT4):
         return 8
     raise ValueError("asymmetric layout has no max magnitude")

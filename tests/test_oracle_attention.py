@@ -8,7 +8,7 @@ import pytest
 from oracle import attention, quant, spec
 from oracle.fwht import fwht_f32, hadamard_f64
 
-ALL = [spec.HAD_INT4, spec.Q4_0, spec.Q6_0, spec.ASYM_G32]
+ALL = [spec.HAD_INT4, spec.Q4_0, spec.Q6_0, spec.ASYM_G32, spec.Q8_0]
 
 
 def _inputs(rng, S, Hq, Hkv, D, scale=1.0):

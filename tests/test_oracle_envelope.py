@@ -17,7 +17,7 @@ from oracle.envelope import exact_attention, quantized_attention, rel_error
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
-ALL = [spec.HAD_INT4, spec.Q4_0, spec.Q6_0, spec.ASYM_G32]
+ALL = [spec.HAD_INT4, spec.Q4_0, spec.Q6_0, spec.ASYM_G32, spec.Q8_0]
 
 
 def _data(name, S=512, kv_heads=2):
@@ -71,8 +71,9 @@ def test_full_options_equal_the_hot_path_definition():
 def test_six_bits_beat_four(name):
     """q6_0 lands closer to exact than q4_0 on the same values ([FreeToken-268] Validation ordering)."""
     q, k, v, alpha = _data(name)
-    rows = {r["layout"]: r for r in envelope.envelope_rows(q, k, v, alpha, [spec.Q4_0, spec.Q6_0])}
+    rows = {r["layout"]: r for r in envelope.envelope_rows(q, k, v, alpha, [spec.Q4_0, spec.Q6_0, spec.Q8_0])}
     assert rows[spec.Q6_0]["kv"] < rows[spec.Q4_0]["kv"]
+    assert rows[spec.Q8_0]["kv"] < rows[spec.Q6_0]["kv"]
     for r in rows.values():
         assert 0.0 < r["kv"] < 1.0 and 0.0 < r["k_only"] < 1.0 and 0.0 < r["v_only"] < 1.0
 

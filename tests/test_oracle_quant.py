@@ -106,7 +106,7 @@ def test_int8_query_extremes():
 
 def test_zero_blocks_give_zero_scale_and_codes():
     x = np.zeros((2, 64), dtype=np.float32)
-    for layout in (spec.Q4_0, spec.Q6_0):
+    for layout in (spec.Q4_0, spec.Q6_0, spec.Q8_0):
         codes, d = quant.quantize_symmetric_blocks(x, layout)
         assert not codes.any() and not d.any()
     codes, s, z = quant.quantize_asym_g32(x)
@@ -144,7 +144,7 @@ def test_asym_min_max_affine_map_by_hand():
 
 
 # ------------------------------------------------------------------ error bounds
-@pytest.mark.parametrize("layout", [spec.Q4_0, spec.Q6_0])
+@pytest.mark.parametrize("layout", [spec.Q4_0, spec.Q6_0, spec.Q8_0])
 def test_symmetric_error_bound(layout, rng):
     x = (rng.standard_normal((200, 128)) * rng.uniform(0.01, 50, size=(200, 1))).astype(np.float32)
     codes, d = quant.quantize_symmetric_blocks(x, layout)
@@ -187,7 +187,7 @@ def test_had_roundtrip_error_bound(rng):
 
 # ------------------------------------------------------------------ stored bytes
 @pytest.mark.parametrize("layout,D", [(spec.HAD_INT4, 128), (spec.Q4_0, 128), (spec.Q6_0, 256),
-                                      (spec.ASYM_G32, 128), (spec.Q4_0, 64)])
+                                      (spec.ASYM_G32, 128), (spec.Q4_0, 64), (spec.Q8_0, 128), (spec.Q8_0, 256)])
 def test_encode_decode_bytes_roundtrip(layout, D, rng):
     x = rng.standard_normal((9, D)).astype(np.float32)
     e = quant.encode_rows(layout, x)
@@ -226,3 +226,21 @@ def test_asym_codes_use_the_stored_fp16_zero():
     codes, s, z = quant.quantize_asym_g32(x)
     assert z[0] == 1.0 and s[0] == 1.0
     assert codes[0] == 0 and codes[1] == 1 and codes[2] == 15
+
+
+def test_q8_0_byte_codes_exhaustive():
+    """Every code -128..127 packs into its two's-complement byte and back."""
+    codes = np.arange(-128, 128, dtype=np.int64).reshape(8, 32)
+    b = quant.pack_bytes(codes)
+    assert b.dtype == np.uint8
+    np.testing.assert_array_equal(b.astype(np.int64), codes & 0xFF)
+    np.testing.assert_array_equal(quant.unpack_bytes(b), codes)
+
+
+def test_q8_0_range_ends():
+    """amax maps to 127 on the positive side (128 is out of range) and -128 on the negative side."""
+    x = np.zeros(32, dtype=np.float32)
+    x[0], x[1], x[2] = 2.0, -2.0, 1.0
+    codes, d = quant.quantize_symmetric_blocks(x, spec.Q8_0)
+    assert d[0] == float(np.float16(2.0 / 128.0))
+    assert codes[0] == 127 and codes[1] == -128 and codes[2] == 64

@@ -15,10 +15,12 @@ def test_block_densities_match_printed_values():
     d = GOLD["densities_bytes_per_element"]
     assert spec.bytes_per_element(spec.Q4_0, 128) == d["q4_0"]
     assert spec.bytes_per_element(spec.Q6_0, 256) == d["q6_0"]
+    assert spec.bytes_per_element(spec.Q8_0, 128) == d["q8_0"]
     # density is a per-block property: the same for every multiple of 32
     for D in (32, 64, 96, 128, 256, 512):
         assert spec.bytes_per_element(spec.Q4_0, D) == d["q4_0"]
         assert spec.bytes_per_element(spec.Q6_0, D) == d["q6_0"]
+        assert spec.bytes_per_element(spec.Q8_0, D) == d["q8_0"]
 
 
 def test_bytes_per_token_table_is_density_over_bf16():
@@ -28,6 +30,7 @@ def test_bytes_per_token_table_is_density_over_bf16():
     assert elems * spec.bytes_per_element(spec.Q4_0, 128) == t["q4_0"]
     assert elems * spec.bytes_per_element(spec.Q6_0, 128) == t["q6_0"]
     assert elems * d["q8_0"] == t["q8_0"]
+    assert elems * spec.bytes_per_element(spec.Q8_0, 128) == t["q8_0"]
     for n_tok, gib in GOLD["gib_at_context"]["q4_0"]:
         assert round(n_tok * t["q4_0"] / 2**30, 2) == gib
 
@@ -66,6 +69,9 @@ def test_code_ranges_and_magnitudes():
     assert spec.code_range(spec.Q6_0) == (-32, 31)
     assert spec.max_magnitude(spec.Q6_0) == 32
     assert spec.code_range(spec.ASYM_G32) == (0, 15)
+    # q8_0: 2^(bits-1) by the same rule as q6_0
+    assert spec.code_range(spec.Q8_0) == (-128, 127)
+    assert spec.max_magnitude(spec.Q8_0) == 128
 
 
 def test_group_counts_and_head_dim_checks():
@@ -73,6 +79,8 @@ def test_group_counts_and_head_dim_checks():
     assert spec.n_groups(spec.Q4_0, 128) == 4
     assert spec.n_groups(spec.Q6_0, 256) == 8
     assert spec.scale_bytes(spec.ASYM_G32, 128) == 16
+    assert spec.n_groups(spec.Q8_0, 128) == 4
+    assert spec.payload_bytes(spec.Q8_0, 128) == 128 and spec.scale_bytes(spec.Q8_0, 128) == 8
     with pytest.raises(ValueError):
         spec.payload_bytes(spec.Q4_0, 48)
     with pytest.raises(ValueError):
