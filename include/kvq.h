@@ -29,9 +29,9 @@
 extern "C" {
 #endif
 
-/* Cache encodings.  Codes of element j are packed two per byte, element 2j in
- * the low nibble ([FreeToken-268] Storage layouts), rows are per token, per kv
- * head, separately for K and V.
+/* Cache encodings.  4-bit codes of element j are packed two per byte, element
+ * 2j in the low nibble ([FreeToken-268] Storage layouts); rows are per token,
+ * per kv head, separately for K and V.
  *   HAD_INT4  [tract-RFC] What's done (CPU); Architecture > Data flow (decode):
  *             row rotated by the orthonormal Hadamard (fast transform), then
  *             per-token symmetric int4 in [-8, 7], scale amax/8 as one f32.
@@ -45,12 +45,17 @@ extern "C" {
  *   ASYM_INT4_G32 [Open-TQ-Metal] Background (per-group asymmetric int4):
  *             groups of 32, min-max affine map, fp16 scale (max-min)/15 then
  *             fp16 zero (= min) per group, unsigned codes [0, 15].
- *             payload D/2, record 4*D/32. */
+ *             payload D/2, record 4*D/32.
+ *   Q8_0      [FreeToken-268] Summary and memory table (8-bit block scheme,
+ *             1.0625 bytes per element): 32-element blocks, fp16 scale amax/128,
+ *             codes [-128, 127] stored one per byte as two's complement, in
+ *             element order.  payload D, record 2*D/32. */
 typedef enum kvq_layout {
   KVQ_LAYOUT_HAD_INT4 = 0,
   KVQ_LAYOUT_Q4_0 = 1,
   KVQ_LAYOUT_Q6_0 = 2,
-  KVQ_LAYOUT_ASYM_INT4_G32 = 3
+  KVQ_LAYOUT_ASYM_INT4_G32 = 3,
+  KVQ_LAYOUT_Q8_0 = 4
 } kvq_layout;
 
 typedef enum kvq_status {

@@ -12,8 +12,8 @@ c_size = ctypes.c_size_t
 c_vp = ctypes.c_void_p
 c_f = ctypes.c_float
 
-HAD_INT4, Q4_0, Q6_0, ASYM_INT4_G32 = 0, 1, 2, 3
-LAYOUT_IDS = {"had_int4": HAD_INT4, "q4_0": Q4_0, "q6_0": Q6_0, "asym_int4_g32": ASYM_INT4_G32}
+HAD_INT4, Q4_0, Q6_0, ASYM_INT4_G32, Q8_0 = 0, 1, 2, 3, 4
+LAYOUT_IDS = {"had_int4": HAD_INT4, "q4_0": Q4_0, "q6_0": Q6_0, "asym_int4_g32": ASYM_INT4_G32, "q8_0": Q8_0}
 PREFILL_NO_CAUSAL_SKIP = 1
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP launch failure"}

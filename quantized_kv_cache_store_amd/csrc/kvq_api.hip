@@ -24,7 +24,7 @@ kvq_status check_launch(const char* what) {
 
 kvq_status validate_cache(const kvq_cache* c) {
   if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache descriptor is null");
-  if (c->layout < 0 || c->layout > 3) return fail(KVQ_ERR_INVALID_ARG, "unknown layout %d", c->layout);
+  if (c->layout < 0 || c->layout >= kNumLayouts) return fail(KVQ_ERR_INVALID_ARG, "unknown layout %d", c->layout);
   if (c->head_dim != 128 && c->head_dim != 256)
     return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d (supported: 128, 256)", c->head_dim);
   if (c->num_kv_heads < 1) return fail(KVQ_ERR_INVALID_ARG, "num_kv_heads must be >= 1");

@@ -156,10 +156,12 @@ __device__ __forceinline__ uint32_t rec_word(const unsigned char* rec, int idx) 
 }
 
 // A operand of the int8 Q K^T MFMA: codes 32 g + 8 r .. 32 g + 8 r + 7 of staged K row t (even
-// elements in the low dword, odd in the high one, the order the query operand follows).
+// elements in the low dword, odd in the high one, the order the query operand follows; the 8-bit
+// layout's stored bytes as they are, in element order).
 template <int L, class ST>
 __device__ __forceinline__ long k_operand(const unsigned char* buf, int t, int g, int r) {
   constexpr int BIAS = CodeBias<L>::value;
+  if (L == Q80) return *reinterpret_cast<const long*>(buf + ST::kbytes8(t, g, r));
   uint32_t lo, hi;
   if (L == Q60) {
     const unsigned char* krow = buf + ST::KP + t * ST::RS;
@@ -178,7 +180,8 @@ __device__ __forceinline__ long k_operand(const unsigned char* buf, int t, int g
 // One lane's V source for the P V MFMA: octet oc (elements 8 oc .. 8 oc + 7) of the step's tokens
 // in the lane's eight k-slots (slot k: token 16 (k >> 2) + 4 r + (k & 3)), as biased codes, with
 // the scale (and zero) pairs of consecutive slots.  Rows at or past t_end may hold anything, so
-// their scales are zeroed.
+// their scales are zeroed.  Codes as bytes: q6_0 even elements in ev, odd in od; q8_0 elements
+// 0..3 in ev, 4..7 in od; the 4-bit layouts the octet's nibbles in ev.
 template <int L>
 struct VOctet {
   uint32_t ev[8], od[8];
@@ -199,6 +202,10 @@ __device__ __forceinline__ void load_voctet(const unsigned char* buf, int T0, in
       const uint32_t x = *reinterpret_cast<const uint32_t*>(vrow + 24 * grp + 4 * (oc & 3));
       const uint32_t t2 = *reinterpret_cast<const uint16_t*>(vrow + 24 * grp + 16 + 2 * (oc & 3));
       q6_octet(x, t2, v.ev[k], v.od[k]);
+    } else if (L == Q80) {
+      const uint2 x = *reinterpret_cast<const uint2*>(buf + ST::vbytes8(tl, oc));
+      v.ev[k] = x.x ^ 0x80808080u;
+      v.od[k] = x.y ^ 0x80808080u;
     } else {
       uint32_t x = *reinterpret_cast<const uint32_t*>(buf + ST::vword(tl, oc));
       if (BIAS) x ^= 0x88888888u;
@@ -228,12 +235,13 @@ __device__ __forceinline__ v8h v_operand(const VOctet<L>& v, int e, uint32_t mag
   v8h A;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t bsel = (uint32_t)(e >> 1);
+    const uint32_t bsel = (uint32_t)(L == Q80 ? (e & 3) : (e >> 1));
     const uint32_t sel = bsel | (0x0Cu << 8) | ((4u + bsel) << 16) | (0x0Cu << 24);
     uint32_t pair;
-    if (L == Q60) {
-      const uint32_t src_a = (e & 1) ? v.od[2 * i] : v.ev[2 * i];
-      const uint32_t src_b = (e & 1) ? v.od[2 * i + 1] : v.ev[2 * i + 1];
+    if (L == Q60 || L == Q80) {
+      const bool hi = L == Q80 ? (e >> 2) != 0 : (e & 1) != 0;
+      const uint32_t src_a = hi ? v.od[2 * i] : v.ev[2 * i];
+      const uint32_t src_b = hi ? v.od[2 * i + 1] : v.ev[2 * i + 1];
       pair = __builtin_amdgcn_perm(src_b, src_a, sel) | magic;
     } else {
       const uint32_t y = __builtin_amdgcn_perm(v.ev[2 * i + 1], v.ev[2 * i], sel);
@@ -282,7 +290,7 @@ __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned 
     }
     // offset term: A[t = col][k = r] from the record of token 16*tau + col
     v4f xo = v4f{0.f, 0.f, 0.f, 0.f};
-    if (L != HAD) {
+    if (L != HAD && L != Q80) {
       const unsigned char* orec = buf + ST::KR + (16 * tau + col) * SB;
 #pragma unroll
       for (int i = 0; i < NG / 4; ++i) {
@@ -402,7 +410,7 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
     }
   }
   v4f xo = v4f{0.f, 0.f, 0.f, 0.f};
-  if (L != HAD) {
+  if (L != HAD && L != Q80) {   // the 8-bit K codes carry no offset
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const unsigned char* orec = kbuf + ST::KR + (16 * h + col) * SB;
@@ -522,7 +530,7 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
   constexpr int NG = T::NG;
   constexpr int SG = T::SG;
   constexpr int NO = D / 128;
-  constexpr int BIAS = CodeBias<L>::value;
+  constexpr int BIAS = CodeBias<L>::k_side;
   extern __shared__ __align__(16) unsigned char smem[];
 
   // Block numbering: chunk group fastest (measured faster than kv head or batch row fastest: blocks
@@ -883,7 +891,7 @@ static inline int tile_rows(const AttendArgs& a) { return a.n_q * a.G <= 8 ? 8 :
 template <bool DBG>
 static partial_fn pick_partial(int layout, int D, int tr) {
   const int di = (D == 256 ? 1 : 0) + (tr == 8 ? 2 : 0);
-  static const partial_fn tab[4][4] = {
+  static const partial_fn tab[kNumLayouts][4] = {
       {launch_partial<HAD, 128, DBG, 16>, launch_partial<HAD, 256, DBG, 16>, launch_partial<HAD, 128, DBG, 8>,
        launch_partial<HAD, 256, DBG, 8>},
       {launch_partial<Q40, 128, DBG, 16>, launch_partial<Q40, 256, DBG, 16>, launch_partial<Q40, 128, DBG, 8>,
@@ -892,6 +900,8 @@ static partial_fn pick_partial(int layout, int D, int tr) {
        launch_partial<Q60, 256, DBG, 8>},
       {launch_partial<ASYM, 128, DBG, 16>, launch_partial<ASYM, 256, DBG, 16>, launch_partial<ASYM, 128, DBG, 8>,
        launch_partial<ASYM, 256, DBG, 8>},
+      {launch_partial<Q80, 128, DBG, 16>, launch_partial<Q80, 256, DBG, 16>, launch_partial<Q80, 128, DBG, 8>,
+       launch_partial<Q80, 256, DBG, 8>},
   };
   return tab[layout][di];
 }

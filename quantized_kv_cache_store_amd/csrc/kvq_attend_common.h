@@ -143,7 +143,8 @@ __device__ __forceinline__ float butterfly_rows(float v, int swap32, bool upper)
 template <int D>
 struct RowQ {
   long qB[D / 32];     // B operand of block g: codes [0, 2, 4, 6, 1, 3, 5, 7] of the lane's 8 (the order
-                       // in which the A operand unpacks even and odd nibbles)
+                       // in which the A operand unpacks even and odd nibbles); the 8-bit layout, whose
+                       // A operand is 8 stored bytes, takes them in element order [0 .. 7]
   int qsum[D / 32];    // sum of q8 over block g (every lane)
   float sq;
 };
@@ -210,10 +211,11 @@ __device__ __forceinline__ void prepare_row_lanes(const float* qrow, int r, RowQ
       c[i] = s != 0.0f ? (int)fminf(fmaxf(rintf(x[g][i] / s), -127.0f), 127.0f) : 0;
       sum += c[i];
     }
-    const uint32_t lo = (uint32_t)(c[0] & 0xFF) | ((uint32_t)(c[2] & 0xFF) << 8) | ((uint32_t)(c[4] & 0xFF) << 16) |
-                        ((uint32_t)(c[6] & 0xFF) << 24);
-    const uint32_t hi = (uint32_t)(c[1] & 0xFF) | ((uint32_t)(c[3] & 0xFF) << 8) | ((uint32_t)(c[5] & 0xFF) << 16) |
-                        ((uint32_t)(c[7] & 0xFF) << 24);
+    const int s1 = L == Q80 ? 1 : 2, s2 = L == Q80 ? 4 : 1;   // element of byte k of lo / hi: s1 * k (+ s2)
+    const uint32_t lo = (uint32_t)(c[0] & 0xFF) | ((uint32_t)(c[s1] & 0xFF) << 8) |
+                        ((uint32_t)(c[2 * s1] & 0xFF) << 16) | ((uint32_t)(c[3 * s1] & 0xFF) << 24);
+    const uint32_t hi = (uint32_t)(c[s2] & 0xFF) | ((uint32_t)(c[s2 + s1] & 0xFF) << 8) |
+                        ((uint32_t)(c[s2 + 2 * s1] & 0xFF) << 16) | ((uint32_t)(c[s2 + 3 * s1] & 0xFF) << 24);
     out.qB[g] = __builtin_bit_cast(long, u32x2{lo, hi});
     sum += __shfl_xor(sum, 16);
     sum += __shfl_xor(sum, 32);
@@ -452,6 +454,10 @@ __device__ __forceinline__ void window_tile_block(const AttendArgs& a, unsigned 
 //     placed instead so that the same reads stay conflict-free: K chunk c of row t goes to chunk
 //     position c ^ ((t >> 2) & 3) of row t, and V row t to row position vperm(t), which swaps the
 //     two 2-bit fields of t within its 16-row half (rows 4 apart then land 16 banks apart).
+//     The 8-bit layout's rows (D bytes, CPR = D / 16 chunks) are read 8 bytes per lane: K chunk c
+//     of row t goes to position c ^ kswz8(t) of its row (the 16 rows of an operand then fill every
+//     bank twice), and V chunk j of the slot (j = CPR t + c) to j ^ (8 ((t >> 2) & 1)) (rows 4
+//     apart, read together, alternate between the two halves of the banks).
 template <int L, int D, bool DMA = false>
 struct Step {
   using T = Layout<L, D>;
@@ -464,6 +470,8 @@ struct Step {
   static constexpr int HALF = 32 * (PB + SB);
   static constexpr int BYTES = 64 * RS + 64 * SB;   // register ring buffer
   static constexpr bool SWZ = DMA && PB == 64;
+  static constexpr bool SWZ8 = DMA && L == Q80;
+  static constexpr int CPR = PB / 16;   // 16-byte chunks per row
   // register ring
   static constexpr int PAY_SLOTS = (2 * PB + 63) / 64;   // 16-byte chunks of 32 payload rows, per lane
   static constexpr int REC_SLOTS = (4 * SB + 63) / 64;   // K and V records together
@@ -482,6 +490,18 @@ struct Step {
   // byte offset of dword oc of V row t (layouts with 4-bit codes)
   __device__ static int vword(int t, int oc) {
     return SWZ ? VP + 16 * (4 * vperm(t) + (oc >> 2)) + 4 * (oc & 3) : VP + t * RS + 4 * oc;
+  }
+  // 8-bit layout: chunk placement (both maps are their own inverses)
+  __device__ static int kswz8(int t) { return 2 * ((t >> 1) & (CPR / 2 - 1)); }
+  __device__ static int vlin8(int j) { return j ^ (8 * (((j / CPR) >> 2) & 1)); }
+  // byte offset of the 8 codes 32 g + 8 r .. 32 g + 8 r + 7 of K row t (8-bit layout)
+  __device__ static int kbytes8(int t, int g, int r) {
+    const int c = 2 * g + (r >> 1);
+    return SWZ8 ? KP + t * PB + 16 * (c ^ kswz8(t)) + 8 * (r & 1) : KP + t * RS + 32 * g + 8 * r;
+  }
+  // byte offset of the 8 codes of octet oc (elements 8 oc .. 8 oc + 7) of V row t (8-bit layout)
+  __device__ static int vbytes8(int t, int oc) {
+    return SWZ8 ? VP + 16 * vlin8(t * CPR + (oc >> 1)) + 8 * (oc & 1) : VP + t * RS + 8 * oc;
   }
 };
 
@@ -540,6 +560,10 @@ __device__ __forceinline__ void issue_dma_half(const AttendArgs& a, HalfRows hr,
     if (ST::SWZ) {
       t = ISV ? ST::vperm(p >> 2) : (p >> 2);
       c = ISV ? (p & 3) : ((p & 3) ^ ((t >> 2) & 3));
+    } else if (ST::SWZ8) {
+      const int j = ISV ? ST::vlin8(p) : p;
+      t = j / CPR;
+      c = ISV ? j - t * CPR : ((j - t * CPR) ^ ST::kswz8(t));
     } else {
       t = p / CPR;
       c = p - t * CPR;

@@ -9,31 +9,42 @@
 
 namespace kvq {
 
-enum : int { HAD = KVQ_LAYOUT_HAD_INT4, Q40 = KVQ_LAYOUT_Q4_0, Q60 = KVQ_LAYOUT_Q6_0, ASYM = KVQ_LAYOUT_ASYM_INT4_G32 };
+enum : int {
+  HAD = KVQ_LAYOUT_HAD_INT4,
+  Q40 = KVQ_LAYOUT_Q4_0,
+  Q60 = KVQ_LAYOUT_Q6_0,
+  ASYM = KVQ_LAYOUT_ASYM_INT4_G32,
+  Q80 = KVQ_LAYOUT_Q8_0
+};
+constexpr int kNumLayouts = 5;
 
 // Per-(layout, head_dim) constants of one stored row.
 template <int L, int D>
 struct Layout {
   static_assert(D == 128 || D == 256, "head_dim 128 or 256");
   static constexpr int NG = D / 32;                                   // 32-element blocks
-  static constexpr int PB = (L == Q60) ? NG * 24 : D / 2;             // payload bytes
+  static constexpr int PB = (L == Q60) ? NG * 24 : (L == Q80 ? D : D / 2);   // payload bytes
   static constexpr int SB = (L == HAD) ? 4 : (L == ASYM ? NG * 4 : NG * 2);  // record bytes
   static constexpr int SG = (L == HAD) ? 1 : NG;                      // scale groups
   static constexpr int OCT = D / 8;                                   // 8-element octets
 };
 
-// Offset added to a signed code to make it non-negative (n + OFF = code ^ OFF).
+// Offset added to a signed code to make it non-negative (n + OFF = code ^ OFF), the form in which
+// the V side turns codes into fp16.  The K side's int8 MFMA takes the 8-bit codes as they are
+// (signed), so that layout's K codes carry no offset (k_side).
 template <int L>
 struct CodeBias {
-  static constexpr int value = (L == Q60) ? 32 : (L == ASYM ? 0 : 8);
+  static constexpr int value = (L == Q60) ? 32 : (L == ASYM ? 0 : (L == Q80 ? 128 : 8));
+  static constexpr int k_side = (L == Q80) ? 0 : value;
 };
 
 static inline size_t payload_bytes_rt(int layout, int D) {
-  if ((D != 128 && D != 256) || layout < 0 || layout > 3) return 0;
+  if ((D != 128 && D != 256) || layout < 0 || layout >= kNumLayouts) return 0;
+  if (layout == Q80) return (size_t)D;
   return layout == Q60 ? (size_t)(D / 32) * 24 : (size_t)D / 2;
 }
 static inline size_t scale_bytes_rt(int layout, int D) {
-  if ((D != 128 && D != 256) || layout < 0 || layout > 3) return 0;
+  if ((D != 128 && D != 256) || layout < 0 || layout >= kNumLayouts) return 0;
   if (layout == HAD) return 4;
   return layout == ASYM ? (size_t)(D / 32) * 4 : (size_t)(D / 32) * 2;
 }

@@ -39,7 +39,7 @@ static_assert(kPrefillChunk % 32 == 0 && kPrefillChunk / 16 <= 64, "a chunk's pa
 // LDS of one 32-token step:
 //   KC  int8 codes (code + bias) in A-operand order: [block g][half tau][lane group r][token
 //       16 tau + i][8 bytes], the bytes being codes 8r, 8r+2, 8r+4, 8r+6, 8r+1, 8r+3, 8r+5, 8r+7
-//       of block g;
+//       of block g (8-bit layout: the signed codes 8r .. 8r+7 in order);
 //   VT  dequantised V (fp16) in A-operand order of V^T: [d / 16][lane group r][d % 16][slot k],
 //       slot k holding token 16 (k / 4) + 4r + k % 4 (the same token order as the lane's P);
 //   KR  the raw K records of the 32 tokens.
@@ -58,8 +58,8 @@ struct PStep {
 template <int L, int D>
 struct PLoad {
   uint32_t kw[PStep<L, D>::KU];     // K payload dword of each K unit
-  uint32_t kh[PStep<L, D>::KU];     // q6_0: the unit's 16 bits of top-bit pairs
-  uint32_t vb[PStep<L, D>::VU][8];  // V payload byte holding elements (d, d+1) of each of the 8 tokens
+  uint32_t kh[PStep<L, D>::KU];     // q6_0: the unit's 16 bits of top-bit pairs; q8_0: its second dword
+  uint32_t vb[PStep<L, D>::VU][8];  // V payload byte (q8_0: the two bytes) of elements (d, d+1) of each token
   uint32_t vh[PStep<L, D>::VU][8];  // q6_0: the byte of top-bit pairs of (d, d+1)
   uint32_t vs[PStep<L, D>::VU][8];  // V record word of the group of d (zeroed past the end)
   uint32_t kr;                      // one dword of the K records
@@ -95,6 +95,10 @@ __device__ __forceinline__ void prefill_fetch(const unsigned char* kslot, const 
       const unsigned char* row = kslot + ST::KP + t * PB;
       ld.kw[k] = *reinterpret_cast<const uint32_t*>(row + 24 * g + 4 * r);
       ld.kh[k] = *reinterpret_cast<const uint16_t*>(row + 24 * g + 16 + 2 * r);
+    } else if (L == Q80) {
+      const uint2 w = *reinterpret_cast<const uint2*>(kslot + ST::kbytes8(t, g, r));
+      ld.kw[k] = w.x;
+      ld.kh[k] = w.y;
     } else {
       ld.kw[k] = *reinterpret_cast<const uint32_t*>(kslot + ST::kword(t, g, r));
     }
@@ -113,6 +117,8 @@ __device__ __forceinline__ void prefill_fetch(const unsigned char* kslot, const 
         const int e = d & 31;
         ld.vb[k][s] = vrow[24 * g + (e >> 1)];
         ld.vh[k][s] = vrow[24 * g + 16 + (e >> 2)];
+      } else if (L == Q80) {
+        ld.vb[k][s] = *reinterpret_cast<const uint16_t*>(vslot + ST::vbytes8(t, d >> 3) + (d & 7));
       } else {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(vslot + ST::vword(t, d >> 3));
         ld.vb[k][s] = (w >> (8 * ((d >> 1) & 3))) & 0xFFu;
@@ -142,6 +148,9 @@ __device__ __forceinline__ void prefill_produce(unsigned char* buf, int tid, con
     uint32_t lo, hi;
     if (L == Q60) {
       q6_octet(ld.kw[k], ld.kh[k], lo, hi);
+    } else if (L == Q80) {
+      lo = ld.kw[k];
+      hi = ld.kh[k];
     } else {
       const uint32_t x = BIAS ? (ld.kw[k] ^ 0x88888888u) : ld.kw[k];
       lo = x & 0x0F0F0F0Fu;
@@ -160,7 +169,10 @@ __device__ __forceinline__ void prefill_produce(unsigned char* buf, int tid, con
       // tokens of slots 2i and 2i + 1 side by side: [byte(2i), 0, byte(2i + 1), 0]
       const uint32_t y = __builtin_amdgcn_perm(ld.vb[k][2 * i + 1], ld.vb[k][2 * i], 0x0C040C00u);
       uint32_t c0, c1;   // element d and d + 1 of both tokens, as code + bias
-      if (L == Q60) {
+      if (L == Q80) {
+        c0 = y ^ 0x00800080u;
+        c1 = __builtin_amdgcn_perm(ld.vb[k][2 * i + 1], ld.vb[k][2 * i], 0x0C050C01u) ^ 0x00800080u;
+      } else if (L == Q60) {
         const int sh = 2 * (d & 3);
         const uint32_t hy = __builtin_amdgcn_perm(ld.vh[k][2 * i + 1], ld.vh[k][2 * i], 0x0C040C00u) >> sh;
         c0 = ((y & 0x000F000Fu) | ((hy & 0x00030003u) << 4)) ^ 0x00200020u;
@@ -228,7 +240,7 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
         acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
     }
     v4f xo = v4f{0.f, 0.f, 0.f, 0.f};
-    if (L != HAD) {
+    if (L != HAD && L != Q80) {   // the 8-bit K codes carry no offset
       // offset term sum_g c_g(t) qsum_g: A[t = col][k = r] from the record of token 16 tau + col
       const unsigned char* orec = buf + PS::KR + (16 * tau + col) * SB;
 #pragma unroll
@@ -297,7 +309,7 @@ __global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendA
   using T = Layout<L, D>;
   using PS = PStep<L, D>;
   constexpr int NG = T::NG;
-  constexpr int BIAS = CodeBias<L>::value;
+  constexpr int BIAS = CodeBias<L>::k_side;
   extern __shared__ __align__(16) unsigned char smem[];
 
   // One-dimensional grid in an XCD-aware order: the chip hands consecutive blocks round robin to
@@ -353,8 +365,8 @@ __global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendA
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const uint2 w = *reinterpret_cast<const uint2*>(a.q8p + fr * D + 32 * g + 8 * r);
-      qb[g][0] = __builtin_amdgcn_perm(w.y, w.x, 0x06040200u);
-      qb[g][1] = __builtin_amdgcn_perm(w.y, w.x, 0x07050301u);
+      qb[g][0] = L == Q80 ? w.x : __builtin_amdgcn_perm(w.y, w.x, 0x06040200u);
+      qb[g][1] = L == Q80 ? w.y : __builtin_amdgcn_perm(w.y, w.x, 0x07050301u);
     }
     const int* qs = a.qsump + fr * NG;
 #pragma unroll
@@ -491,14 +503,9 @@ static void launch_prepare(const float* q, int n_vec, float* qrot, int8_t* q8, f
 typedef void (*prepare_fn)(const float*, int, float*, int8_t*, float*, int*, hipStream_t);
 
 static prepare_fn pick_prepare(int layout, int D) {
-  const int di = D == 256 ? 1 : 0;
-  static const prepare_fn tab[4][2] = {
-      {launch_prepare<HAD, 128>, launch_prepare<HAD, 256>},
-      {launch_prepare<Q40, 128>, launch_prepare<Q40, 256>},
-      {launch_prepare<Q60, 128>, launch_prepare<Q60, 256>},
-      {launch_prepare<ASYM, 128>, launch_prepare<ASYM, 256>},
-  };
-  return tab[layout][di];
+  // the preparation differs only by the rotation
+  return layout == HAD ? (D == 256 ? launch_prepare<HAD, 256> : launch_prepare<HAD, 128>)
+                       : (D == 256 ? launch_prepare<Q40, 256> : launch_prepare<Q40, 128>);
 }
 
 template <int L, int D>
@@ -514,11 +521,12 @@ typedef void (*prefill_fn)(const AttendArgs&, dim3, int, hipStream_t);
 
 static prefill_fn pick_prefill(int layout, int D) {
   const int di = D == 256 ? 1 : 0;
-  static const prefill_fn tab[4][2] = {
+  static const prefill_fn tab[kNumLayouts][2] = {
       {launch_prefill<HAD, 128>, launch_prefill<HAD, 256>},
       {launch_prefill<Q40, 128>, launch_prefill<Q40, 256>},
       {launch_prefill<Q60, 128>, launch_prefill<Q60, 256>},
       {launch_prefill<ASYM, 128>, launch_prefill<ASYM, 256>},
+      {launch_prefill<Q80, 128>, launch_prefill<Q80, 256>},
   };
   return tab[layout][di];
 }

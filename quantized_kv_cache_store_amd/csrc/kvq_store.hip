@@ -4,7 +4,8 @@
 // Walsh-Hadamard), per-token symmetric int4, pack -- or keep the newest tokens
 // as exact f32 rows (n_recent); the on-device append kernel is the piece the
 // Metal integration section leaves unwritten.  [FreeToken-268] Storage layouts
-// give the q4_0 / q6_0 block encodings; [Open-TQ-Metal] Background gives the
+// give the q4_0 / q6_0 block encodings (and its Summary the 8-bit q8_0 block
+// at 1.0625 bytes per element); [Open-TQ-Metal] Background gives the
 // per-group asymmetric int4.  Every stored value is a bit-exact function of
 // the f32 inputs: IEEE f32 add/sub/mul/div, round-half-even to integers, fp16
 // fields rounded to nearest even after clamping to +-65504.
@@ -131,8 +132,8 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
 #pragma unroll
     for (int i = 0; i < E; ++i) n[i] = sc == 0.0f ? 0 : (int)fminf(fmaxf(rintf(x[i] / sc), -8.0f), 7.0f);
     if (active && sub == 0) *reinterpret_cast<float*>(rec) = sc;
-  } else if (L == Q40 || L == Q60) {
-    constexpr float M = (L == Q40) ? 8.0f : 32.0f;
+  } else if (L == Q40 || L == Q60 || L == Q80) {
+    constexpr float M = (L == Q40) ? 8.0f : (L == Q60 ? 32.0f : 128.0f);
     constexpr float lo = -M, hi = M - 1.0f;
     float m = 0.0f;
 #pragma unroll
@@ -168,7 +169,16 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
 
   if (!active) return;
   uint8_t* pay = a.payload[kv] + prow * T::PB;
-  if (L != Q60) {
+  if (L == Q80) {
+    // one two's-complement byte per code, element order: the lane's E codes at byte sub * E
+    uint32_t w[E / 4];
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i)
+      w[i] = (uint32_t)(n[4 * i] & 0xFF) | ((uint32_t)(n[4 * i + 1] & 0xFF) << 8) |
+             ((uint32_t)(n[4 * i + 2] & 0xFF) << 16) | ((uint32_t)(n[4 * i + 3] & 0xFF) << 24);
+    if constexpr (E == 8) reinterpret_cast<uint2*>(pay)[sub] = make_uint2(w[0], w[1]);
+    else reinterpret_cast<uint4*>(pay)[sub] = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if (L != Q60) {
     if (E == 8) {
       reinterpret_cast<uint32_t*>(pay)[sub] = pack8(n);
     } else {
@@ -219,11 +229,12 @@ typedef void (*store_fn)(const StoreArgs&, hipStream_t);
 
 static store_fn pick_store(int layout, int D) {
   const int di = D == 256 ? 1 : 0;
-  static const store_fn tab[4][2] = {
+  static const store_fn tab[kNumLayouts][2] = {
       {launch_store<HAD, 128>, launch_store<HAD, 256>},
       {launch_store<Q40, 128>, launch_store<Q40, 256>},
       {launch_store<Q60, 128>, launch_store<Q60, 256>},
       {launch_store<ASYM, 128>, launch_store<ASYM, 256>},
+      {launch_store<Q80, 128>, launch_store<Q80, 256>},
   };
   return tab[layout][di];
 }

@@ -10,7 +10,7 @@ import torch
 
 import quantized_kv_cache_store_amd as kvq
 
-LAYOUT_NAMES = {0: "had_int4", 1: "q4_0", 2: "q6_0", 3: "asym_int4_g32"}
+LAYOUT_NAMES = {0: "had_int4", 1: "q4_0", 2: "q6_0", 3: "asym_int4_g32", 4: "q8_0"}
 DEV = torch.device("cuda:0")
 
 

@@ -37,6 +37,8 @@ def test_sizes():
     assert lib.kvq_payload_bytes(_lib.ASYM_INT4_G32, 128) == 64
     assert lib.kvq_scale_bytes(_lib.ASYM_INT4_G32, 128) == 16
     assert lib.kvq_scale_bytes(_lib.HAD_INT4, 128) == 4
+    assert lib.kvq_payload_bytes(_lib.Q8_0, 128) == 128
+    assert lib.kvq_scale_bytes(_lib.Q8_0, 256) == 16
     assert lib.kvq_payload_bytes(_lib.Q4_0, 64) == 0          # unsupported head_dim
     assert lib.kvq_payload_bytes(7, 128) == 0
     # room for the partials [B][Hq][chunks + 1][D + 4] f32

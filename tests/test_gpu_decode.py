@@ -15,7 +15,7 @@ import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-ALL = [spec.HAD_INT4, spec.Q4_0, spec.Q6_0, spec.ASYM_G32]
+ALL = [spec.HAD_INT4, spec.Q4_0, spec.Q6_0, spec.ASYM_G32, spec.Q8_0]
 
 
 def _rows(rng, lens, Hkv, D, dist="normal"):

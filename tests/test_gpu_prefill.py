@@ -19,7 +19,7 @@ import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-ALL = [spec.HAD_INT4, spec.Q4_0, spec.Q6_0, spec.ASYM_G32]
+ALL = [spec.HAD_INT4, spec.Q4_0, spec.Q6_0, spec.ASYM_G32, spec.Q8_0]
 
 
 def _case(layout, D, Hkv, G, lens, n_q, q_starts, n_recent=0, page_size=16, seed=0, alpha=None):

@@ -12,7 +12,8 @@ import gpu_util as U
 pytestmark = pytest.mark.gpu
 
 CASES = [(spec.HAD_INT4, 128), (spec.HAD_INT4, 256), (spec.Q4_0, 128), (spec.Q4_0, 256),
-         (spec.Q6_0, 128), (spec.Q6_0, 256), (spec.ASYM_G32, 128), (spec.ASYM_G32, 256)]
+         (spec.Q6_0, 128), (spec.Q6_0, 256), (spec.ASYM_G32, 128), (spec.ASYM_G32, 256),
+         (spec.Q8_0, 128), (spec.Q8_0, 256)]
 
 
 def _special_rows(rng, n, D):

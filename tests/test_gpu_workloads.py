@@ -20,7 +20,7 @@ import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-LAYOUT = {"had_int4": spec.HAD_INT4, "q4_0": spec.Q4_0, "q6_0": spec.Q6_0, "asym_int4_g32": spec.ASYM_G32}
+LAYOUT = {"had_int4": spec.HAD_INT4, "q4_0": spec.Q4_0, "q6_0": spec.Q6_0, "asym_int4_g32": spec.ASYM_G32, "q8_0": spec.Q8_0}
 BLOCK = 16384
 
 
