@@ -204,7 +204,8 @@ def time_decode(w, B, chunk, steps, warmup, layers, dev, seed):
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
     S = w.S
-    bytes_layer = B * w.Hkv * S * 2 * (kvq.load().kvq_payload_bytes(3, w.D) + kvq.load().kvq_scale_bytes(3, w.D))
+    lay = kvq.LAYOUT_IDS[w.layout]
+    bytes_layer = B * w.Hkv * S * 2 * (kvq.load().kvq_payload_bytes(lay, w.D) + kvq.load().kvq_scale_bytes(lay, w.D))
     L = layers or max(2, math.ceil(2.5e9 / bytes_layer))
     caches, table, seq = build_layers(w, B, L, dev, gen)
     q = torch.randn((B, w.Hq, w.D), generator=gen, device=dev, dtype=torch.float32)
