@@ -24,6 +24,14 @@ organization: kv_head = head_idx / gqa_factor):
 * Hadamard layout: the output is rotated back, o <- H o ([tract-RFC] data
   flow, un-rotate step).
 
+Float-query mode (``float_q``): the quantised tokens are scored with the f32
+query (rotated for the Hadamard layout) instead of its int8 form, q_tilde = q
+everywhere.  This is how the other two pages read the cache: [FreeToken-268]
+Changes (the attention kernel's K/V load gains unpack paths, i.e. the codes
+become floats inside a standard attention) and [Open-TQ-Metal]'s fused kernel
+(its nibble-extraction step multiplies the packed codes by a pre-divided
+floating-point query).
+
 The integer path that the kernels take is an exact re-association of the same
 scores; ``scores_i32`` gives its i32 intermediates for the bit-exact gates, and
 ``scores_from_i32`` rebuilds the float score from them so that the two forms
@@ -119,11 +127,11 @@ def _query_rows(layout, q):
 
 
 # --------------------------------------------------------------------- decode
-def attend_decode(layout, q, k, v, alpha, n_recent=0):
+def attend_decode(layout, q, k, v, alpha, n_recent=0, float_q=False):
     """Single-query decode attention of one batch row.
 
     q [Hq, D] f32; k, v [S, Hkv, D] f32 (every cached token, in position order);
-    returns o [Hq, D] float64.
+    returns o [Hq, D] float64.  float_q: the float-query mode (module docstring).
     """
     q = np.asarray(q)
     Hq, D = q.shape
@@ -139,6 +147,8 @@ def attend_decode(layout, q, k, v, alpha, n_recent=0):
         K, V, w0 = _effective_rows(cache, S, n_recent)
         for h in range(hk * G, (hk + 1) * G):
             q_quant, q_f = _query_rows(layout, q[h])
+            if float_q:
+                q_quant = q_f
             s = np.empty(S, dtype=np.float64)
             s[:w0] = K[:w0] @ q_quant
             s[w0:] = K[w0:] @ q_f
@@ -217,7 +227,7 @@ def merge_partials(parts):
     return num / den
 
 
-def attend_decode_split(layout, q, k, v, alpha, chunk, n_recent=0):
+def attend_decode_split(layout, q, k, v, alpha, chunk, n_recent=0, float_q=False):
     """Decode attention computed as split-K chunks of ``chunk`` tokens plus the merge.
 
     Same inputs and result as ``attend_decode`` up to float re-association.
@@ -234,6 +244,8 @@ def attend_decode_split(layout, q, k, v, alpha, chunk, n_recent=0):
         K, V, w0 = _effective_rows(cache, S, n_recent)
         for h in range(hk * G, (hk + 1) * G):
             q_quant, q_f = _query_rows(layout, q[h])
+            if float_q:
+                q_quant = q_f
             s = np.empty(S, dtype=np.float64)
             s[:w0] = K[:w0] @ q_quant
             s[w0:] = K[w0:] @ q_f

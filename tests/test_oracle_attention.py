@@ -26,8 +26,9 @@ def _plain_attention(q, K, V, alpha):
 
 
 # ------------------------------------------------------------------ brute force (explicit loops)
-def _brute_decode(layout, q, k, v, alpha, n_recent):
-    """Decode from the integer formulation with explicit Python loops over tokens and elements."""
+def _brute_decode(layout, q, k, v, alpha, n_recent, float_q=False):
+    """Decode from the integer formulation with explicit Python loops over tokens and elements
+    (float_q: each block's dot taken with the f32 query instead of the int8 codes)."""
     Hq, D = q.shape
     S, Hkv, _ = k.shape
     G = Hq // Hkv
@@ -56,12 +57,16 @@ def _brute_decode(layout, q, k, v, alpha, n_recent):
                 I = 0
                 qs = 0
                 for j in range(g * gsz, (g + 1) * gsz):
-                    I += int(q8[j]) * int(ek["codes"][j])
-                    qs += int(q8[j])
+                    if float_q:
+                        I += float(qr[j]) * int(ek["codes"][j])
+                        qs += float(qr[j])
+                    else:
+                        I += int(q8[j]) * int(ek["codes"][j])
+                        qs += int(q8[j])
                 acc += float(ek["scales"][g]) * I
                 if layout == spec.ASYM_G32:
                     acc += float(ek["zeros"][g]) * qs
-            scores.append(alpha * float(sq) * acc)
+            scores.append(alpha * (1.0 if float_q else float(sq)) * acc)
             vrow = np.empty(D)
             for j in range(D):
                 g = j // gsz
@@ -84,9 +89,10 @@ def test_decode_matches_brute_force(layout, S):
     q, k, v = _inputs(rng, S, Hq=2, Hkv=1, D=D)
     alpha = 1.0 / math.sqrt(D)
     for n_recent in ((0, 5) if S < 100 else (0,)):
-        got = attention.attend_decode(layout, q, k, v, alpha, n_recent=n_recent)
-        ref = _brute_decode(layout, q, k, v, alpha, n_recent)
-        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+        for float_q in (False, True):
+            got = attention.attend_decode(layout, q, k, v, alpha, n_recent=n_recent, float_q=float_q)
+            ref = _brute_decode(layout, q, k, v, alpha, n_recent, float_q)
+            np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
 
 
 # ------------------------------------------------------------------ integer scores
@@ -160,7 +166,7 @@ def _exact_block_rows(rng, S, D, layout):
     return (d * n).reshape(S, D).astype(np.float32)
 
 
-@pytest.mark.parametrize("layout", [spec.Q4_0, spec.Q6_0, spec.ASYM_G32])
+@pytest.mark.parametrize("layout", [spec.Q4_0, spec.Q6_0, spec.ASYM_G32, spec.Q8_0])
 def test_exactly_encodable_inputs_give_textbook_attention(layout, rng):
     S, D = 70, 128
     k = _exact_block_rows(rng, S, D, layout)[:, None, :]
@@ -174,6 +180,46 @@ def test_exactly_encodable_inputs_give_textbook_attention(layout, rng):
     alpha = 1.0 / math.sqrt(D)
     o = attention.attend_decode(layout, q, k, v, alpha)
     np.testing.assert_allclose(o[0], _plain_attention(q[0], k[:, 0], v[:, 0], alpha), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("layout", [spec.Q4_0, spec.Q6_0, spec.ASYM_G32, spec.Q8_0])
+def test_float_q_on_exact_rows_is_textbook_attention_for_any_query(layout, rng):
+    """Float-query mode: with rows the layout encodes exactly, only the query could differ from the
+    f32 inputs, and in this mode it does not, whatever the query; the int8 mode does differ."""
+    S, D = 70, 128
+    k = _exact_block_rows(rng, S, D, layout)[:, None, :]
+    v = _exact_block_rows(rng, S, D, layout)[:, None, :]
+    q = rng.standard_normal((2, D)).astype(np.float32)
+    alpha = 2.0 / (math.sqrt(D) * float(np.abs(k).max()))   # logits of order one (no one-hot softmax)
+    o = attention.attend_decode(layout, q, k, v, alpha, float_q=True)
+    o8 = attention.attend_decode(layout, q, k, v, alpha)
+    for h in range(2):
+        ref = _plain_attention(q[h], k[:, 0], v[:, 0], alpha)
+        np.testing.assert_allclose(o[h], ref, rtol=1e-12, atol=1e-12)
+        assert np.abs(o8[h] - ref).max() > 1e-6
+
+
+@pytest.mark.parametrize("layout", ALL)
+def test_float_q_equals_int8_mode_for_a_query_on_the_int8_grid(layout, rng):
+    """A query whose (rotated) form int8 encodes exactly gives both modes the same scores.  For the
+    Hadamard layout at D = 256, q = 16 * 127 * 2^-3 e_j rotates exactly to +-127 * 2^-3 (1/sqrt(D) =
+    1/16), whose int8 scale is 2^-3."""
+    S, D = 90, 256
+    _, k, v = _inputs(rng, S, 2, 1, D)
+    if layout == spec.HAD_INT4:
+        q = np.zeros((2, D), dtype=np.float32)
+        q[0, 5] = 16 * 127 * 2.0 ** -3
+        q[1, 200] = -16 * 127 * 2.0 ** -3
+    else:
+        q8 = rng.integers(-127, 128, size=(2, D))
+        q8[:, 0] = 127
+        q = (q8 * 2.0 ** -4).astype(np.float32)
+    qr, q8r, sq = attention.prepare_query(layout, q)
+    np.testing.assert_array_equal(sq[:, None] * q8r, qr)   # the grid case really holds
+    for n_recent in (0, 9):
+        a = attention.attend_decode(layout, q, k, v, 0.2, n_recent=n_recent, float_q=True)
+        b = attention.attend_decode(layout, q, k, v, 0.2, n_recent=n_recent)
+        np.testing.assert_array_equal(a, b)
 
 
 @pytest.mark.parametrize("layout", ALL)
@@ -211,9 +257,10 @@ def test_window_boundary_token(rng):
 def test_split_k_merge_equals_single_pass(layout, chunk, rng):
     S = 600
     q, k, v = _inputs(rng, S, 4, 2, 128, scale=2.0)
-    a = attention.attend_decode(layout, q, k, v, 0.2, n_recent=9)
-    b = attention.attend_decode_split(layout, q, k, v, 0.2, chunk, n_recent=9)
-    np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-13)
+    for float_q in (False, True):
+        a = attention.attend_decode(layout, q, k, v, 0.2, n_recent=9, float_q=float_q)
+        b = attention.attend_decode_split(layout, q, k, v, 0.2, chunk, n_recent=9, float_q=float_q)
+        np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-13)
 
 
 def test_merge_ignores_empty_chunks():

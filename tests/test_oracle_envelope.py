@@ -65,6 +65,8 @@ def test_full_options_equal_the_hot_path_definition():
     for layout in ALL:
         np.testing.assert_array_equal(quantized_attention(layout, q, k, v, alpha, n_recent=32),
                                       attention.attend_decode(layout, q, k, v, alpha, n_recent=32))
+        np.testing.assert_array_equal(quantized_attention(layout, q, k, v, alpha, int8_q=False, n_recent=32),
+                                      attention.attend_decode(layout, q, k, v, alpha, n_recent=32, float_q=True))
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_q4_0_s32k", "llama31_70b_asym_s128k", "gemma_q6_0_ragged_b16"])
