@@ -151,6 +151,23 @@ kvq_status kvq_attend_decode(const kvq_cache* cache, const float* q, float* out,
                              int32_t chunk_tokens, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Decode in the float-query mode: the quantised tokens are scored with the f32
+ * query (rotated for HAD_INT4) instead of its int8 form, the way
+ * [FreeToken-268] Changes (the attention kernel's K/V load unpacks the codes
+ * into a standard attention) and [Open-TQ-Metal]'s fused kernel (a
+ * pre-divided floating-point query against the packed nibbles) read the
+ * cache.  The integer dots run on the same packed codes with the query
+ * expanded to two int8 terms, sq * (q8 + r8 / 254) with sq = amax|q| / 127,
+ * which holds the f32 query to within half a step of sq / 254 (amax|q| / 64516)
+ * per element; V, the window, the merge and every argument are those of
+ * kvq_attend_decode (same workspace size and errors). */
+kvq_status kvq_attend_decode_float_q(const kvq_cache* cache, const float* q, float* out,
+                                     int32_t batch, int32_t num_q_heads, float alpha,
+                                     const int32_t* block_table, int32_t max_pages_per_seq,
+                                     const int32_t* seq_len, int32_t max_seq_len,
+                                     int32_t chunk_tokens, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
 /* The two phases of kvq_attend_decode as separate calls, for callers that time
  * or schedule them apart ([Open-TQ-Metal] split-K paragraphs: a partial phase
  * and a reduce phase ordered by their data dependency; here by stream order).

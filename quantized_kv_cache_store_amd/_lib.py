@@ -38,6 +38,8 @@ SIGNATURES = {
     "kvq_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "kvq_attend_decode": (c_i32, [P, c_vp, c_vp, c_i32, c_i32, c_f, c_vp, c_i32, c_vp, c_i32, c_i32,
                                   c_vp, c_size, c_vp]),
+    "kvq_attend_decode_float_q": (c_i32, [P, c_vp, c_vp, c_i32, c_i32, c_f, c_vp, c_i32, c_vp, c_i32, c_i32,
+                                          c_vp, c_size, c_vp]),
     "kvq_attend_decode_partial": (c_i32, [P, c_vp, c_i32, c_i32, c_f, c_vp, c_i32, c_vp, c_i32, c_i32,
                                           c_vp, c_size, c_vp]),
     "kvq_attend_decode_reduce": (c_i32, [P, c_vp, c_i32, c_i32, c_vp, c_i32, c_i32, c_vp, c_size, c_vp]),

@@ -261,9 +261,11 @@ __device__ __forceinline__ v8h v_operand(const VOctet<L>& v, int e, uint32_t mag
 // Otherwise tokens at or past t_end are dropped (their staged rows may hold anything, so their
 // scales are zeroed too) and tokens past `lim`, the limit of this lane's row, get p = 0.
 // drow: flat row index of this lane's row for the score export (DBG), or -1.
-template <int L, int D, class ST, bool DBG, bool FULL>
+// FQ: float-query mode; qBl holds the query's residual term, and every block dot becomes
+// 254 I(q8) + I(residual) (qsB, qoff and sqc come scaled to match).
+template <int L, int D, class ST, bool DBG, bool FULL, bool FQ>
 __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned char* buf, int T0, int t_end,
-                                            int lim, long drow, int col, int r, const long* qB,
+                                            int lim, long drow, int col, int r, const long* qB, const long* qBl,
                                             const float* qsB, const int* qoff, float sqc, uint32_t magic,
                                             float& m_run, float& l_run, v4f* oacc) {
   using T = Layout<L, D>;
@@ -277,16 +279,24 @@ __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned 
   float vs_had[8];
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
-    v4i acc[SG];
+    v4i acc[SG], accl[SG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const long A = k_operand<L, ST>(buf, 16 * tau + col, g, r);
       const long B = qB[g];
       if (L == HAD) {
         acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[0], 0, 0, 0);
+        if (FQ) accl[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, qBl[g], g == 0 ? v4i{0, 0, 0, 0} : accl[0], 0, 0, 0);
       } else {
         acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+        if (FQ) accl[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, qBl[g], v4i{0, 0, 0, 0}, 0, 0, 0);
       }
+    }
+    if (FQ) {
+#pragma unroll
+      for (int g = 0; g < SG; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[g][j] = 254 * acc[g][j] + accl[g][j];
     }
     // offset term: A[t = col][k = r] from the record of token 16*tau + col
     v4f xo = v4f{0.f, 0.f, 0.f, 0.f};
@@ -382,11 +392,11 @@ __device__ __forceinline__ float half_swap(float v) { return __builtin_bit_cast(
 // exact zeros); only the row sum l is added up in another order.
 // `mid` runs between the K side (Q K^T, scores) and the V side (softmax, P V): the direct-load
 // ring refills the K half of the slot there and waits for the V half.
-template <int L, int D, class ST, bool DBG, bool FULL, class MID>
+template <int L, int D, class ST, bool DBG, bool FULL, bool FQ, class MID>
 __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned char* kbuf, const unsigned char* vbuf,
                                              int T0, int t_end,
-                                             int lim, long drow, int col, int r, const long* qB, const float* qsB,
-                                             const int* qoff, float sqc,
+                                             int lim, long drow, int col, int r, const long* qB, const long* qBl,
+                                             const float* qsB, const int* qoff, float sqc,
                                              uint32_t magic, float& m_run, float& l_run, v4f* oacc, MID&& mid) {
   using T = Layout<L, D>;
   constexpr int NG = T::NG;
@@ -396,18 +406,29 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
   const int hh = col >> 3;
 
   // ---------------- Q K^T: both halves into one tile
-  v4i acc[SG == 1 ? 2 : SG];
+  constexpr int NACC = SG == 1 ? 2 : SG;
+  v4i acc[NACC], accl[NACC];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const long A = k_operand<L, ST>(kbuf, 16 * h + col, g, r);
       const long B = (hh == h) ? qB[g] : 0;   // the rows' queries in the columns of half h
-      if (L == HAD)
+      const long Bl = FQ && hh == h ? qBl[g] : 0;
+      if (L == HAD) {
         acc[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[h], 0, 0, 0);
-      else
+        if (FQ) accl[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, Bl, g == 0 ? v4i{0, 0, 0, 0} : accl[h], 0, 0, 0);
+      } else {
         acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, h == 0 ? v4i{0, 0, 0, 0} : acc[g], 0, 0, 0);
+        if (FQ) accl[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, Bl, h == 0 ? v4i{0, 0, 0, 0} : accl[g], 0, 0, 0);
+      }
     }
+  }
+  if (FQ) {
+#pragma unroll
+    for (int i = 0; i < NACC; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 254 * acc[i][j] + accl[i][j];
   }
   v4f xo = v4f{0.f, 0.f, 0.f, 0.f};
   if (L != HAD && L != Q80) {   // the 8-bit K codes carry no offset
@@ -505,7 +526,7 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
 // TR: rows per tile, 16 (attend_step) or 8 (attend_step8, for groups of at most 8 rows).
 // Grid: x = row tile * ngroups + chunk group (the last group is the window when n_recent > 0),
 // y = kv head, z = batch row.
-template <int L, int D, int TR>
+template <int L, int D, int TR, bool FQ = false>
 struct PartialShape {
   // 8-row tiles stream through LDS rings filled by direct loads, one of RK K slots and one of RV V
   // slots per wave; 16-row tiles through the register ring (NB slots: NB - 1 steps in flight while
@@ -517,14 +538,17 @@ struct PartialShape {
   static constexpr int RING = DMA ? 4 * (RK + RV) * ST::HALF : 4 * ST::BYTES;
   static constexpr int MERGE = 4 * TR * (D + 4) * 4;            // the four waves' chunk partials
   static constexpr int LDS = RING > MERGE ? RING : MERGE;       // per block
-  // waves per SIMD: as many as four blocks' rings in 160 KiB of LDS allow, registers permitting
-  static constexpr int MIN_WAVES = DMA ? (LDS <= 40960 ? 4 : (LDS <= 54613 ? 3 : 2)) : 2;
+  // waves per SIMD: as many as four blocks' rings in 160 KiB of LDS allow, registers permitting (the
+  // float-query mode's second query term and accumulators need the registers of three)
+  static constexpr int LDS_WAVES = LDS <= 40960 ? 4 : (LDS <= 54613 ? 3 : 2);
+  static constexpr int MIN_WAVES = DMA ? (FQ && LDS_WAVES > 3 ? 3 : LDS_WAVES) : 2;
 };
 
-template <int L, int D, bool DBG, int TR>
-__global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void attend_partial(AttendArgs a) {
+template <int L, int D, bool DBG, int TR, bool FQ>
+__global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void attend_partial(AttendArgs a) {
+  static_assert(!(DBG && FQ), "the score export has no float-query form");
   using T = Layout<L, D>;
-  using PS = PartialShape<L, D, TR>;
+  using PS = PartialShape<L, D, TR, FQ>;
   using ST = typename PS::ST;
   constexpr int NB = PS::NB;
   constexpr int NG = T::NG;
@@ -568,24 +592,31 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
   const int nsteps = active ? (t_end - t_begin + 31) / 32 : 0;
 
   // ---- prologue: this lane's row of the tile, prepared in the wave (int8 query in the B-operand
-  // order, its scale and block sums).  With 8-row tiles lane column col serves row col & 7, and
-  // its operands are zero outside its half.
+  // order, its scale and block sums; float-query mode: also the residual term, with the block sums
+  // and the scale taken for 254 I(q8) + I(residual)).  With 8-row tiles lane column col serves row
+  // col & 7, and its operands are zero outside its half.
   const int col = lane & 15;
   const int r = lane >> 4;
   const int rsel = TR == 8 ? (col & 7) : col;   // this lane's row within the tile
   const int hh = col >> 3;
   long qB[NG];          // B operands (int8 query of the tile's rows), one aligned register pair each
+  long qBl[NG];         // float-query mode: the residual term's B operands
   float qsB[NG / 4];    // offset-term operand: zero point (asym) or -bias * scale times the block sums
   int qoff[SG];        // bias * sum(q8): the Hadamard scores and the score export use it
   float sqc = 0.0f;
   {
     RowQ<D> rq;
-    prepare_row_lanes<L, D>(a.q + row_index(a, b, hk, row0 + min(rsel, nvalid - 1)) * D, r, rq);
+    prepare_row_lanes<L, D, FQ>(a.q + row_index(a, b, hk, row0 + min(rsel, nvalid - 1)) * D, r, rq);
+    int qsum[NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) qB[g] = rq.qB[g];
+    for (int g = 0; g < NG; ++g) {
+      qB[g] = rq.qB[g];
+      qBl[g] = FQ ? rq.qBl[g] : 0;
+      qsum[g] = FQ ? 254 * rq.qsum[g] + rq.qsuml[g] : rq.qsum[g];
+    }
 #pragma unroll
     for (int i = 0; i < NG / 4; ++i) {
-      const int qs = r == 0 ? rq.qsum[4 * i] : r == 1 ? rq.qsum[4 * i + 1] : r == 2 ? rq.qsum[4 * i + 2] : rq.qsum[4 * i + 3];
+      const int qs = r == 0 ? qsum[4 * i] : r == 1 ? qsum[4 * i + 1] : r == 2 ? qsum[4 * i + 2] : qsum[4 * i + 3];
       qsB[i] = (L == ASYM) ? (float)qs : -(float)BIAS * (float)qs;
     }
 #pragma unroll
@@ -593,13 +624,14 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
       int sum = 0;
       if (L == HAD) {
 #pragma unroll
-        for (int gg = 0; gg < NG; ++gg) sum += rq.qsum[gg];
+        for (int gg = 0; gg < NG; ++gg) sum += qsum[gg];
       } else {
-        sum = rq.qsum[g];
+        sum = qsum[g];
       }
       qoff[g] = BIAS * sum;
     }
     sqc = rq.sq * a.alpha * KVQ_LOG2E;
+    if (FQ) sqc = sqc / 254.0f;
   }
   const int lim = row_limit(a, qs0, row0 + rsel, nrows);
   const long drow = (DBG && rsel < nvalid) ? (long)row_index(a, b, hk, row0 + rsel) : -1;   // score export only
@@ -645,16 +677,18 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR>::MIN_WAVES)) void atte
     const bool full = T + 32 <= t_end && T + 31 <= lim_min;
     if (TR == 8) {
       if (full)
-        attend_step8<L, D, ST, DBG, true>(a, kbuf, vbuf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic,
-                                          m_run, l_run, oacc, mid);
+        attend_step8<L, D, ST, DBG, true, FQ>(a, kbuf, vbuf, T, t_end, lim, drow, col, r, qB, qBl, qsB, qoff, sqc,
+                                              magic, m_run, l_run, oacc, mid);
       else
-        attend_step8<L, D, ST, DBG, false>(a, kbuf, vbuf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic,
-                                           m_run, l_run, oacc, mid);
+        attend_step8<L, D, ST, DBG, false, FQ>(a, kbuf, vbuf, T, t_end, lim, drow, col, r, qB, qBl, qsB, qoff, sqc,
+                                               magic, m_run, l_run, oacc, mid);
     } else {
       if (full)
-        attend_step<L, D, ST, DBG, true>(a, kbuf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic, m_run, l_run, oacc);
+        attend_step<L, D, ST, DBG, true, FQ>(a, kbuf, T, t_end, lim, drow, col, r, qB, qBl, qsB, qoff, sqc, magic,
+                                             m_run, l_run, oacc);
       else
-        attend_step<L, D, ST, DBG, false>(a, kbuf, T, t_end, lim, drow, col, r, qB, qsB, qoff, sqc, magic, m_run, l_run, oacc);
+        attend_step<L, D, ST, DBG, false, FQ>(a, kbuf, T, t_end, lim, drow, col, r, qB, qBl, qsB, qoff, sqc, magic,
+                                              m_run, l_run, oacc);
     }
   };
 
@@ -874,13 +908,14 @@ __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out
   for (int e = 0; e < E; ++e) out[(size_t)row * D + lane * E + e] = x[e];
 }
 
-template <int L, int D, bool DBG, int TR>
+template <int L, int D, bool DBG, int TR, bool FQ>
 static void launch_partial(const AttendArgs& a, dim3 grid, int n_recent, hipStream_t st) {
-  size_t lds = PartialShape<L, D, TR>::LDS;
+  size_t lds = PartialShape<L, D, TR, FQ>::LDS;
   if (n_recent > 0 && (size_t)window_lds_bytes<D>() > lds) lds = window_lds_bytes<D>();
   if (lds > 65536)
-    (void)hipFuncSetAttribute((const void*)attend_partial<L, D, DBG, TR>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((attend_partial<L, D, DBG, TR>), grid, dim3(256), lds, st, a);
+    (void)hipFuncSetAttribute((const void*)attend_partial<L, D, DBG, TR, FQ>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+  hipLaunchKernelGGL((attend_partial<L, D, DBG, TR, FQ>), grid, dim3(256), lds, st, a);
 }
 
 typedef void (*partial_fn)(const AttendArgs&, dim3, int, hipStream_t);
@@ -888,21 +923,15 @@ typedef void (*partial_fn)(const AttendArgs&, dim3, int, hipStream_t);
 // Rows per tile of the decode kernel: 8 when a (batch row, kv head) has at most 8 query rows.
 static inline int tile_rows(const AttendArgs& a) { return a.n_q * a.G <= 8 ? 8 : 16; }
 
-template <bool DBG>
+template <bool DBG, bool FQ = false>
 static partial_fn pick_partial(int layout, int D, int tr) {
   const int di = (D == 256 ? 1 : 0) + (tr == 8 ? 2 : 0);
-  static const partial_fn tab[kNumLayouts][4] = {
-      {launch_partial<HAD, 128, DBG, 16>, launch_partial<HAD, 256, DBG, 16>, launch_partial<HAD, 128, DBG, 8>,
-       launch_partial<HAD, 256, DBG, 8>},
-      {launch_partial<Q40, 128, DBG, 16>, launch_partial<Q40, 256, DBG, 16>, launch_partial<Q40, 128, DBG, 8>,
-       launch_partial<Q40, 256, DBG, 8>},
-      {launch_partial<Q60, 128, DBG, 16>, launch_partial<Q60, 256, DBG, 16>, launch_partial<Q60, 128, DBG, 8>,
-       launch_partial<Q60, 256, DBG, 8>},
-      {launch_partial<ASYM, 128, DBG, 16>, launch_partial<ASYM, 256, DBG, 16>, launch_partial<ASYM, 128, DBG, 8>,
-       launch_partial<ASYM, 256, DBG, 8>},
-      {launch_partial<Q80, 128, DBG, 16>, launch_partial<Q80, 256, DBG, 16>, launch_partial<Q80, 128, DBG, 8>,
-       launch_partial<Q80, 256, DBG, 8>},
-  };
+#define KVQ_PARTIALS(L)                                                                                       \
+  { launch_partial<L, 128, DBG, 16, FQ>, launch_partial<L, 256, DBG, 16, FQ>, launch_partial<L, 128, DBG, 8, FQ>, \
+    launch_partial<L, 256, DBG, 8, FQ> }
+  static const partial_fn tab[kNumLayouts][4] = {KVQ_PARTIALS(HAD), KVQ_PARTIALS(Q40), KVQ_PARTIALS(Q60),
+                                                 KVQ_PARTIALS(ASYM), KVQ_PARTIALS(Q80)};
+#undef KVQ_PARTIALS
   return tab[layout][di];
 }
 
@@ -987,10 +1016,11 @@ extern "C" size_t kvq_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t 
   return decode_ws_bytes(batch, Hq, D, max_seq_len, chunk);
 }
 
-extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
-                                                float alpha, const int32_t* block_table, int32_t max_pages,
-                                                const int32_t* seq_len, int32_t max_seq_len, int32_t chunk,
-                                                void* workspace, size_t ws_bytes, void* stream) {
+// The split-K phase of decode, in the int8-query mode or (fq) the float-query mode.
+static kvq_status decode_partial(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq, float alpha,
+                                 const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
+                                 int32_t max_seq_len, int32_t chunk, void* workspace, size_t ws_bytes, void* stream,
+                                 bool fq) {
   kvq_status st = check_attend_args(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len);
   if (st != KVQ_OK) return st;
   if ((st = check_chunk(c, chunk)) != KVQ_OK) return st;
@@ -1004,8 +1034,17 @@ extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float*
   if (gx == 0) return KVQ_OK;
   a.batch = batch;
   const dim3 grid((unsigned)gx, c->num_kv_heads, batch);
-  pick_partial<false>(c->layout, c->head_dim, tr)(a, grid, c->n_recent, (hipStream_t)stream);
+  (fq ? pick_partial<false, true> : pick_partial<false, false>)(c->layout, c->head_dim, tr)(a, grid, c->n_recent,
+                                                                                          (hipStream_t)stream);
   return check_launch("decode partial kernel");
+}
+
+extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
+                                                float alpha, const int32_t* block_table, int32_t max_pages,
+                                                const int32_t* seq_len, int32_t max_seq_len, int32_t chunk,
+                                                void* workspace, size_t ws_bytes, void* stream) {
+  return decode_partial(c, q, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace,
+                        ws_bytes, stream, false);
 }
 
 extern "C" kvq_status kvq_attend_decode_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t Hq,
@@ -1030,8 +1069,19 @@ extern "C" kvq_status kvq_attend_decode(const kvq_cache* c, const float* q, floa
                                         const int32_t* seq_len, int32_t max_seq_len, int32_t chunk,
                                         void* workspace, size_t ws_bytes, void* stream) {
   if (!out) return fail(KVQ_ERR_INVALID_ARG, "out must be non-null");
-  kvq_status st = kvq_attend_decode_partial(c, q, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len,
-                                            chunk, workspace, ws_bytes, stream);
+  kvq_status st = decode_partial(c, q, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk,
+                                 workspace, ws_bytes, stream, false);
+  if (st != KVQ_OK) return st;
+  return kvq_attend_decode_reduce(c, out, batch, Hq, seq_len, max_seq_len, chunk, workspace, ws_bytes, stream);
+}
+
+extern "C" kvq_status kvq_attend_decode_float_q(const kvq_cache* c, const float* q, float* out, int32_t batch,
+                                                int32_t Hq, float alpha, const int32_t* block_table,
+                                                int32_t max_pages, const int32_t* seq_len, int32_t max_seq_len,
+                                                int32_t chunk, void* workspace, size_t ws_bytes, void* stream) {
+  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out must be non-null");
+  kvq_status st = decode_partial(c, q, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk,
+                                 workspace, ws_bytes, stream, true);
   if (st != KVQ_OK) return st;
   return kvq_attend_decode_reduce(c, out, batch, Hq, seq_len, max_seq_len, chunk, workspace, ws_bytes, stream);
 }

@@ -140,16 +140,35 @@ __device__ __forceinline__ float butterfly_rows(float v, int swap32, bool upper)
 // the lane, 8 and 16 between lane rows, 32, 64, ... inside the lane again (the ascending stage order
 // of the encoding), each in f32, then f32(1/sqrt(D)); amax over the row, sq = amax / 127 (IEEE
 // division), q8 = rint(x / sq) clamped to [-127, 127]; per-block sums of q8.
+//
+// Float-query mode (FQ): the query also gets a second int8 term, the residual of the first at 254
+// times its resolution, lo = rint(f32(f32(x / sq) - q8) * 254) clamped to [-127, 127], so that
+// sq * (q8 + lo / 254) stands for x to within sq / 508.  The integer dot then runs twice on the same
+// codes, and 254 I(q8) + I(lo) is the block dot with that query (exact in i32).
 template <int D>
 struct RowQ {
   long qB[D / 32];     // B operand of block g: codes [0, 2, 4, 6, 1, 3, 5, 7] of the lane's 8 (the order
                        // in which the A operand unpacks even and odd nibbles); the 8-bit layout, whose
                        // A operand is 8 stored bytes, takes them in element order [0 .. 7]
   int qsum[D / 32];    // sum of q8 over block g (every lane)
+  long qBl[D / 32];    // FQ: the residual term, same order
+  int qsuml[D / 32];   // FQ: its block sums
   float sq;
 };
 
-template <int L, int D>
+// The 8 codes c[0..7] of a lane as the B operand (element order for the 8-bit layout, else even then
+// odd elements).
+template <int L>
+__device__ __forceinline__ long pack_b_operand(const int* c) {
+  const int s1 = L == Q80 ? 1 : 2, s2 = L == Q80 ? 4 : 1;   // element of byte k of lo / hi: s1 * k (+ s2)
+  const uint32_t lo = (uint32_t)(c[0] & 0xFF) | ((uint32_t)(c[s1] & 0xFF) << 8) |
+                      ((uint32_t)(c[2 * s1] & 0xFF) << 16) | ((uint32_t)(c[3 * s1] & 0xFF) << 24);
+  const uint32_t hi = (uint32_t)(c[s2] & 0xFF) | ((uint32_t)(c[s2 + s1] & 0xFF) << 8) |
+                      ((uint32_t)(c[s2 + 2 * s1] & 0xFF) << 16) | ((uint32_t)(c[s2 + 3 * s1] & 0xFF) << 24);
+  return __builtin_bit_cast(long, u32x2{lo, hi});
+}
+
+template <int L, int D, bool FQ = false>
 __device__ __forceinline__ void prepare_row_lanes(const float* qrow, int r, RowQ<D>& out) {
 #pragma clang fp contract(off)
   constexpr int NG = D / 32;
@@ -205,21 +224,28 @@ __device__ __forceinline__ void prepare_row_lanes(const float* qrow, int r, RowQ
   out.sq = s;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    int c[8], sum = 0;
+    int c[8], cl[8], sum = 0, suml = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      c[i] = s != 0.0f ? (int)fminf(fmaxf(rintf(x[g][i] / s), -127.0f), 127.0f) : 0;
+      const float y = s != 0.0f ? x[g][i] / s : 0.0f;
+      const float n = fminf(fmaxf(rintf(y), -127.0f), 127.0f);
+      c[i] = (int)n;
       sum += c[i];
+      if (FQ) {
+        cl[i] = (int)fminf(fmaxf(rintf((y - n) * 254.0f), -127.0f), 127.0f);
+        suml += cl[i];
+      }
     }
-    const int s1 = L == Q80 ? 1 : 2, s2 = L == Q80 ? 4 : 1;   // element of byte k of lo / hi: s1 * k (+ s2)
-    const uint32_t lo = (uint32_t)(c[0] & 0xFF) | ((uint32_t)(c[s1] & 0xFF) << 8) |
-                        ((uint32_t)(c[2 * s1] & 0xFF) << 16) | ((uint32_t)(c[3 * s1] & 0xFF) << 24);
-    const uint32_t hi = (uint32_t)(c[s2] & 0xFF) | ((uint32_t)(c[s2 + s1] & 0xFF) << 8) |
-                        ((uint32_t)(c[s2 + 2 * s1] & 0xFF) << 16) | ((uint32_t)(c[s2 + 3 * s1] & 0xFF) << 24);
-    out.qB[g] = __builtin_bit_cast(long, u32x2{lo, hi});
+    out.qB[g] = pack_b_operand<L>(c);
     sum += __shfl_xor(sum, 16);
     sum += __shfl_xor(sum, 32);
     out.qsum[g] = sum;
+    if (FQ) {
+      out.qBl[g] = pack_b_operand<L>(cl);
+      suml += __shfl_xor(suml, 16);
+      suml += __shfl_xor(suml, 32);
+      out.qsuml[g] = suml;
+    }
   }
 }
 

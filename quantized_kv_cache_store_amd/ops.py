@@ -107,8 +107,11 @@ def decode_workspace_bytes(batch, num_q_heads, head_dim, max_seq_len, chunk_toke
 
 
 def attend_decode(cache, q, block_table, seq_len, max_seq_len, alpha, chunk_tokens=512, out=None,
-                  workspace=None):
-    """kvq_attend_decode: q f32 [B, Hq, D] -> out f32 [B, Hq, D]."""
+                  workspace=None, float_q=False):
+    """kvq_attend_decode: q f32 [B, Hq, D] -> out f32 [B, Hq, D].
+
+    float_q=True calls kvq_attend_decode_float_q (quantised tokens scored with the f32 query).
+    """
     dev = cache.device
     _need(q, "q", torch.float32, dev)
     _need(block_table, "block_table", torch.int32, dev)
@@ -123,10 +126,11 @@ def attend_decode(cache, q, block_table, seq_len, max_seq_len, alpha, chunk_toke
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, dev)
-    st = load().kvq_attend_decode(cache.desc, _ptr(q), _ptr(out), B, Hq, float(alpha), _ptr(block_table),
-                                  block_table.shape[1], _ptr(seq_len), int(max_seq_len), int(chunk_tokens),
-                                  _ptr(workspace), workspace.numel(), _stream(dev))
-    check("kvq_attend_decode", st)
+    name = "kvq_attend_decode_float_q" if float_q else "kvq_attend_decode"
+    st = getattr(load(), name)(cache.desc, _ptr(q), _ptr(out), B, Hq, float(alpha), _ptr(block_table),
+                               block_table.shape[1], _ptr(seq_len), int(max_seq_len), int(chunk_tokens),
+                               _ptr(workspace), workspace.numel(), _stream(dev))
+    check(name, st)
     return out
 
 

@@ -24,7 +24,8 @@ def _rows(rng, lens, Hkv, D, dist="normal"):
     return [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in lens]
 
 
-def _run_case(layout, D, Hkv, G, lens, n_recent=0, chunk=512, page_size=16, seed=0, alpha=None, dist="normal"):
+def _run_case(layout, D, Hkv, G, lens, n_recent=0, chunk=512, page_size=16, seed=0, alpha=None, dist="normal",
+              float_q=False):
     rng = np.random.default_rng(seed)
     rows_k = _rows(rng, lens, Hkv, D, dist)
     rows_v = _rows(rng, lens, Hkv, D, dist)
@@ -33,10 +34,12 @@ def _run_case(layout, D, Hkv, G, lens, n_recent=0, chunk=512, page_size=16, seed
     alpha = alpha if alpha is not None else 1.0 / math.sqrt(D)
     cache, bt, seq, table = U.build_cache(layout, D, Hkv, rows_k, rows_v, page_size=page_size, n_recent=n_recent)
     maxs = max(max(lens), 1)
-    out = kvq.attend_decode(cache, torch.from_numpy(q).to(U.DEV), bt, seq, maxs, alpha, chunk_tokens=chunk)
+    out = kvq.attend_decode(cache, torch.from_numpy(q).to(U.DEV), bt, seq, maxs, alpha, chunk_tokens=chunk,
+                            float_q=float_q)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
-    ref = np.stack([attention.attend_decode(layout, q[b], rows_k[b], rows_v[b], alpha, n_recent=n_recent)
+    ref = np.stack([attention.attend_decode(layout, q[b], rows_k[b], rows_v[b], alpha, n_recent=n_recent,
+                                            float_q=float_q)
                     for b in range(B)])
     return got, ref, (cache, bt, seq, q, rows_k, rows_v)
 
@@ -87,6 +90,31 @@ def test_decode_recent_window(layout, n_recent):
     U.need_gpu()
     got, ref, _ = _run_case(layout, 128, Hkv=2, G=2, lens=[1100, 40, 64, 512], n_recent=n_recent,
                             seed=n_recent + layout)
+    U.assert_close_rel(got, ref)
+
+
+@pytest.mark.parametrize("layout", ALL)
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("G", [2, 8, 12])
+def test_decode_float_q_matches_oracle(layout, D, G):
+    """Float-query mode against the oracle's float-query definition, heavy-tailed values, with a
+    window on one case; the int8 mode lands farther from that definition."""
+    U.need_gpu()
+    n_recent = 16 if G == 2 else 0
+    kw = dict(Hkv=2, G=G, lens=[1500, 129, 33], n_recent=n_recent, seed=7 * G + D + layout, dist="t3")
+    got, ref, _ = _run_case(layout, D, float_q=True, **kw)
+    U.assert_close_rel(got, ref)
+    got8, _, _ = _run_case(layout, D, **kw)
+    err = np.abs(got - ref).max()
+    err8 = np.abs(got8 - ref).max()
+    assert err < 0.5 * err8, (err, err8)
+
+
+@pytest.mark.parametrize("layout", [spec.Q4_0, spec.ASYM_G32])
+@pytest.mark.parametrize("lens", [[1], [31], [0, 300]])
+def test_decode_float_q_edge_lengths(layout, lens):
+    U.need_gpu()
+    got, ref, _ = _run_case(layout, 128, Hkv=1, G=4, lens=lens, seed=sum(lens) + layout, float_q=True)
     U.assert_close_rel(got, ref)
 
 
