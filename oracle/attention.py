@@ -192,6 +192,56 @@ def attend_prefill(layout, q, k, v, alpha, q_start, causal=True, n_recent=0):
     return out
 
 
+# --------------------------------------------------------------------- full-precision prefill
+def attend_prefill_full(layout, q, k, v, alpha, q_start, causal=True, n_recent=0):
+    """Prefill of a chunk in full precision, before the chunk is quantised into the cache.
+
+    [Open-TQ-Metal] prefill/decode selection paragraph: a multi-query step runs
+    attention on the full-precision K, V and only then quantises and stores
+    them; decode reads the packed cache.  Reading taken for a chunk that follows
+    a cached prefix: the chunk's own tokens are read as the exact f32 rows
+    (rotated for the Hadamard layout) scored with the f32 query, and the prefix
+    as the cache held it before the chunk was stored -- quantised, except the
+    newest min(q_start, n_recent) positions, which the window keeps in f32.
+
+    q [Sq, Hq, D], query i at position q_start + i; k, v [q_start + Sq, Hkv, D]:
+    the cached prefix followed by the chunk's rows.  causal: query i sees
+    t <= q_start + i.  Returns [Sq, Hq, D] float64.
+    """
+    q = np.asarray(q)
+    Sq, Hq, D = q.shape
+    S, Hkv, _ = k.shape
+    if S != q_start + Sq:
+        raise ValueError("k, v must hold the prefix and the chunk")
+    G = Hq // Hkv
+    out = np.zeros((Sq, Hq, D), dtype=np.float64)
+    pos = q_start + np.arange(Sq)
+    t = np.arange(S)
+    for hk in range(Hkv):
+        if q_start > 0:
+            cache = encode_cache(layout, k[:q_start, hk, :], v[:q_start, hk, :])
+            Kp, Vp, w0 = _effective_rows(cache, q_start, n_recent)
+        else:
+            Kp, Vp, w0 = np.zeros((0, D)), np.zeros((0, D)), 0
+        if layout == spec.HAD_INT4:
+            kc, vc = fwht_f32(k[q_start:, hk, :]), fwht_f32(v[q_start:, hk, :])
+        else:
+            kc, vc = f32(k[q_start:, hk, :]), f32(v[q_start:, hk, :])
+        K = np.concatenate([Kp, kc])
+        V = np.concatenate([Vp, vc])
+        for h in range(hk * G, (hk + 1) * G):
+            q_quant, q_f = _query_rows(layout, q[:, h, :])
+            s = np.empty((Sq, S), dtype=np.float64)
+            s[:, :w0] = q_quant @ K[:w0].T
+            s[:, w0:] = q_f @ K[w0:].T
+            s = alpha * s
+            if causal:
+                s = np.where(t[None, :] <= pos[:, None], s, -np.inf)
+            o = _softmax_rows(s) @ V
+            out[:, h, :] = hadamard_f64(o) if layout == spec.HAD_INT4 else o
+    return out
+
+
 # --------------------------------------------------------------------- split-K
 def chunk_partial(scores, V):
     """One split-K chunk: (o_c unnormalised, m_c, l_c) of scores [T] and rows V [T, D].

@@ -222,6 +222,54 @@ def test_float_q_equals_int8_mode_for_a_query_on_the_int8_grid(layout, rng):
         np.testing.assert_array_equal(a, b)
 
 
+# ------------------------------------------------------------------ full-precision prefill
+@pytest.mark.parametrize("layout", ALL)
+@pytest.mark.parametrize("q_start,n_recent", [(0, 0), (0, 16), (40, 64), (40, 40)])
+def test_full_prefill_without_quantised_prefix_is_textbook_causal_attention(layout, q_start, n_recent, rng):
+    """A fresh prompt (no prefix), or a prefix that the window holds whole: every token is an exact
+    f32 row, so each query gets textbook attention over t <= its position."""
+    Sq, D = 23, 128
+    _, k, v = _inputs(rng, q_start + Sq, 4, 2, D)
+    q = rng.standard_normal((Sq, 4, D)).astype(np.float32)
+    o = attention.attend_prefill_full(layout, q, k, v, 0.15, q_start, n_recent=n_recent)
+    tol = 1e-5 if layout == spec.HAD_INT4 else 1e-12
+    for i in range(Sq):
+        for h in range(4):
+            ref = _plain_attention(q[i, h], k[:q_start + i + 1, h // 2], v[:q_start + i + 1, h // 2], 0.15)
+            np.testing.assert_allclose(o[i, h], ref, rtol=tol, atol=tol)
+
+
+@pytest.mark.parametrize("layout", [spec.Q4_0, spec.Q6_0, spec.ASYM_G32, spec.Q8_0])
+def test_full_prefill_equals_compressed_prefill_when_nothing_is_lost(layout, rng):
+    """Rows the layout encodes exactly and queries on the int8 grid: quantising loses nothing, so the
+    full-precision prefill equals the compressed-domain prefill over the cache after the append."""
+    q_start, Sq, D = 70, 30, 128
+    k = _exact_block_rows(rng, q_start + Sq, D, layout)[:, None, :]
+    v = _exact_block_rows(rng, q_start + Sq, D, layout)[:, None, :]
+    q8 = rng.integers(-127, 128, size=(Sq, 2, D))
+    q8[..., 0] = 127
+    q = (q8 * 2.0 ** -6).astype(np.float32)
+    for causal in (True, False):
+        a = attention.attend_prefill_full(layout, q, k, v, 0.05, q_start, causal=causal)
+        b = attention.attend_prefill(layout, q, k, v, 0.05, q_start, causal=causal)
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("layout", ALL)
+def test_full_prefill_last_query_not_masked(layout, rng):
+    """The last query of the chunk sees every token, so causal and non-causal agree on it; with the
+    chunk's tokens hidden (a one-token chunk is its own last token) the quantised prefix counts."""
+    q_start, Sq = 50, 9
+    _, k, v = _inputs(rng, q_start + Sq, 2, 1, 128)
+    q = rng.standard_normal((Sq, 2, 128)).astype(np.float32)
+    a = attention.attend_prefill_full(layout, q, k, v, 0.2, q_start, causal=True, n_recent=5)
+    b = attention.attend_prefill_full(layout, q, k, v, 0.2, q_start, causal=False, n_recent=5)
+    np.testing.assert_allclose(a[-1], b[-1], rtol=1e-12, atol=1e-12)
+    assert np.abs(a[0] - b[0]).max() > 1e-6
+    with pytest.raises(ValueError):
+        attention.attend_prefill_full(layout, q, k[:-1], v[:-1], 0.2, q_start)
+
+
 @pytest.mark.parametrize("layout", ALL)
 def test_full_window_is_plain_attention(layout, rng):
     """n_recent >= S keeps every token in f32: the result is plain attention on the inputs."""
