@@ -117,6 +117,21 @@ kvq_status kvq_store(const kvq_cache* cache, const float* k_new, const float* v_
                      int32_t n_tok, const int32_t* slot, const int32_t* batch_idx,
                      const int32_t* pos, const int32_t* seq_len, void* stream);
 
+/* The same quantize-on-append for a chunk of n_q tokens of every batch row,
+ * with the slots taken from the block table: token i of row b goes to position
+ * q_start[b] + i, and the row's length after the append is q_start[b] + n_q
+ * (which decides the window rows, as in kvq_store).
+ *   k_new, v_new  device f32 [batch][n_q][num_kv_heads][head_dim]
+ *   q_start       device int32 [batch]: cached tokens of each row before the chunk
+ *   block_table   device int32 [batch][max_pages_per_seq]
+ *   max_seq_len   host bound on q_start[b] + n_q; max_pages_per_seq * page_size
+ *                 must cover it (a position the table does not cover is skipped)
+ * batch must not exceed max_batch when n_recent > 0.  n_q == 0 is a no-op. */
+kvq_status kvq_store_chunk(const kvq_cache* cache, const float* k_new, const float* v_new,
+                           int32_t batch, int32_t n_q, const int32_t* q_start,
+                           const int32_t* block_table, int32_t max_pages_per_seq,
+                           int32_t max_seq_len, void* stream);
+
 /* Workspace of kvq_attend_decode: room for split-K partials (o_c, m_c, l_c) per
  * (batch, query head, chunk), plus the window partial.  (The decode kernel
  * prepares its int8 queries itself.)  Returns 0 for invalid arguments. */
@@ -187,10 +202,11 @@ kvq_status kvq_attend_decode_reduce(const kvq_cache* cache, float* out, int32_t 
                                     int32_t chunk_tokens, const void* workspace, size_t workspace_bytes,
                                     void* stream);
 
-/* Workspace of kvq_attend_prefill_causal: split-K partials (o_c, m_c, l_c)
- * per (batch, query, query head, 1024-token chunk), plus the window partial,
- * then the prepared queries per (batch, query, query head).  Returns 0 for
- * invalid arguments. */
+/* Workspace of kvq_attend_prefill_causal and kvq_prefill_full_then_store:
+ * split-K partials (o_c, m_c, l_c) per (batch, query, query head, 1024-token
+ * chunk), plus the window partial, then the prepared queries per (batch,
+ * query, query head), then room for the chunk's rotated K and V rows (the
+ * full-precision prefill of HAD_INT4).  Returns 0 for invalid arguments. */
 size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t num_q_heads,
                                    int32_t head_dim, int32_t max_seq_len);
 
@@ -221,6 +237,33 @@ kvq_status kvq_attend_prefill_causal(const kvq_cache* cache, const float* q, flo
                                      const int32_t* block_table, int32_t max_pages_per_seq,
                                      const int32_t* seq_len, int32_t max_seq_len, uint32_t flags,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Full-precision prefill, then quantise-on-store.  [Open-TQ-Metal]
+ * prefill/decode selection paragraph: a multi-query step attends over the
+ * full-precision K, V and only then quantises them into the cache, while decode
+ * reads the packed cache.  Query i of row b (position q_start[b] + i) attends
+ * over the row's cached prefix, read as the cache holds it before this call
+ * (packed tokens, and the window's f32 rows for its newest min(q_start[b],
+ * n_recent) positions), and over the chunk's own tokens as the exact f32 rows
+ * k_new, v_new (rotated for HAD_INT4, like window rows), with the causal limit
+ * q_start[b] + i when causal != 0.  Then the chunk is stored as by
+ * kvq_store_chunk.  The prefix's scores, the window and the merge are those of
+ * kvq_attend_prefill_causal with seq_len = q_start.
+ *   q             device f32 [batch][n_q][num_q_heads][head_dim]
+ *   k_new, v_new  device f32 [batch][n_q][num_kv_heads][head_dim]
+ *   out           device f32 [batch][n_q][num_q_heads][head_dim]
+ *   q_start       device int32 [batch]: cached tokens of each row before the chunk
+ *   max_seq_len   host bound on q_start[b] + n_q
+ *   workspace     kvq_prefill_workspace_bytes(batch, n_q, num_q_heads, head_dim,
+ *                 max_seq_len) bytes of device memory
+ * Errors as for kvq_attend_prefill_causal and kvq_store_chunk; nothing is
+ * launched on an error. */
+kvq_status kvq_prefill_full_then_store(const kvq_cache* cache, const float* q, const float* k_new,
+                                       const float* v_new, float* out, int32_t batch, int32_t n_q,
+                                       int32_t num_q_heads, float alpha, int32_t causal,
+                                       const int32_t* q_start, const int32_t* block_table,
+                                       int32_t max_pages_per_seq, int32_t max_seq_len,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Test exports for the bit-exact gates. */
 

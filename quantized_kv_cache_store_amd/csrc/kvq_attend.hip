@@ -818,10 +818,12 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
 // output elements l * E .. l * E + E - 1; the rotation runs in registers, butterflies inside a
 // lane for strides below E and between lanes above, in the stage order of the encoding
 // (h = 1, 2, ..., D / 2, then 1 / sqrt(D)).
+// win_always: the window slot holds a partial for every row (full-precision prefill: the chunk's
+// own rows), whatever the window.
 template <int D, bool ROT, int W>
 __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out, const int32_t* seq_len,
                                                      int rows_per_b, int nc1, int chunk, int n_recent,
-                                                     long total_rows) {
+                                                     long total_rows, int win_always) {
 #pragma clang fp contract(off)
   constexpr int E = D / 64;
   constexpr int RPB = 4 / W;
@@ -836,7 +838,7 @@ __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out
   const int S = seq_len[b];
   const int Sq = n_recent > 0 ? max(0, S - n_recent) : S;
   const int nq = (Sq + chunk - 1) / chunk;
-  const int cnt = nq + ((n_recent > 0 && S > 0) ? 1 : 0);
+  const int cnt = nq + ((win_always || (n_recent > 0 && S > 0)) ? 1 : 0);
   const int PST = partial_stride(D);
   const float* base = ws + (size_t)rr * nc1 * PST;
   float M = -INFINITY;
@@ -978,29 +980,30 @@ static kvq_status check_chunk(const kvq_cache* c, int32_t chunk) {
 
 template <int D, bool ROT, int W>
 static void launch_reduce_w(float* out, long rows, int rows_per_b, const int32_t* seq_len, int nc1, int chunk,
-                            int n_recent, const float* ws, hipStream_t s) {
+                            int n_recent, const float* ws, hipStream_t s, int win_always) {
   const long blocks = (rows + (4 / W) - 1) / (4 / W);
   hipLaunchKernelGGL((attend_reduce<D, ROT, W>), dim3((unsigned)blocks), dim3(256), 0, s, ws, out, seq_len, rows_per_b,
-                     nc1, chunk, n_recent, rows);
+                     nc1, chunk, n_recent, rows, win_always);
 }
 
 kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b, const int32_t* seq_len,
-                         int nc1, int32_t chunk, const float* ws, hipStream_t s) {
+                         int nc1, int32_t chunk, const float* ws, hipStream_t s, bool win_always) {
+  const int wa = win_always ? 1 : 0;
   const long rows = (long)batch * rows_per_b;
   // one wave per row when there are rows enough to fill the chip, else four waves split each row
   const bool many = rows >= 4096;
   const bool rot = c->layout == HAD;
   const int n = c->n_recent;
   if (c->head_dim == 128) {
-    if (rot) many ? launch_reduce_w<128, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s)
-                  : launch_reduce_w<128, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s);
-    else many ? launch_reduce_w<128, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s)
-              : launch_reduce_w<128, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s);
+    if (rot) many ? launch_reduce_w<128, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa)
+                  : launch_reduce_w<128, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa);
+    else many ? launch_reduce_w<128, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa)
+              : launch_reduce_w<128, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa);
   } else {
-    if (rot) many ? launch_reduce_w<256, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s)
-                  : launch_reduce_w<256, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s);
-    else many ? launch_reduce_w<256, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s)
-              : launch_reduce_w<256, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s);
+    if (rot) many ? launch_reduce_w<256, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa)
+                  : launch_reduce_w<256, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa);
+    else many ? launch_reduce_w<256, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa)
+              : launch_reduce_w<256, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa);
   }
   return check_launch("attention reduce kernel");
 }

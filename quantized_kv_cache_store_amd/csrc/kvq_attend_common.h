@@ -31,6 +31,8 @@ struct AttendArgs {
   const int8_t* q8p;        // prepared rows: int8 query [rows][D]
   const float* sqp;         // prepared rows: its scale [rows]
   const int* qsump;         // prepared rows: sum of q8 per 32-element block [rows][D / 32]
+  const float* kchunk;      // full-precision prefill: the chunk's own K rows f32 [batch][n_q][Hkv][D] (rotated
+  const float* vchunk;      //   for HAD) and V rows, read as exact rows at positions seq_len[b] + i; else null
   int32_t* dbg;
   int Hkv, Hq, G, page_shift, n_recent, max_pages, chunk, nc1, max_seq_len;
   int n_q;       // queries per batch row (1 for decode)
@@ -286,6 +288,11 @@ __device__ __forceinline__ void rotate_quarters(float* x, int r) {
 //     are the rows of the lane's scores, so the online rescale is lane-local.
 // The wave's LDS: the V tile [16][D + 16] f32, rows padded (conflict-free B reads), P in the
 // padding of its rows ([row][D .. D + 15]).
+// Full-precision prefill (a.kchunk set): the chunk's own n_q rows follow the window at positions
+// S .. S + n_q - 1, read from f32 rows [batch][n_q][Hkv][D] (rotated beforehand for HAD), so that
+// tokens t < W come from the ring and t >= W from the chunk, at position w0 + t either way.
+// Tiles past the farthest limit of the wave's rows are not visited: a wholly masked tile would
+// leave m, l and o exactly as they are.
 template <int D>
 __host__ __device__ constexpr int window_wave_lds() { return 16 * (D + 16) * 4; }
 template <int D>
@@ -306,6 +313,8 @@ __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int 
   const int nrows = a.n_q * a.G;
   const int W = min(S, a.n_recent);
   const int w0 = S - W;
+  const int NC = a.kchunk ? a.n_q : 0;      // chunk rows after the window
+  const int NT = W + NC;
   const size_t ring0 = ((size_t)b * a.Hkv + hk) * a.n_recent;
   const float cl = a.alpha * KVQ_LOG2E;
   // the query of row col (prepared rows: rotated for HAD), elements NI r .. NI r + NI - 1
@@ -334,34 +343,51 @@ __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int 
     st.m[j] = -INFINITY;
     st.l[j] = 0.0f;
   }
-  const int ntiles = (W + 15) / 16;
+  int ntiles = (NT + 15) / 16;
+  {
+    const int lmax = nvalid > 0 ? row_limit(a, qs0, row0 + nvalid - 1, nrows) : -1;   // the tile's farthest limit
+    if (lmax < w0) ntiles = 0;
+    else if ((lmax - w0) / 16 + 1 < ntiles) ntiles = (lmax - w0) / 16 + 1;
+  }
   for (int k = k0; k < ntiles; k += kstep) {
     const int t0 = 16 * k;
-    const bool tok_ok = t0 + col < W;
-    int slot = w0 + t0 + col;
-    slot -= (slot / a.n_recent) * a.n_recent;
-    const size_t ro = (ring0 + (size_t)(tok_ok ? slot : 0)) * D + NI * r;
+    const int t = t0 + col;
+    const bool tok_ok = t < NT;
+    const bool in_chunk = t >= W;
+    const float* ksrc;
+    const float* vsrc;
+    if (in_chunk) {
+      const size_t co = (((size_t)b * a.n_q + (tok_ok ? t - W : 0)) * a.Hkv + hk) * D + NI * r;
+      ksrc = a.kchunk + co;
+      vsrc = a.vchunk + co;
+    } else {
+      int slot = w0 + t;
+      slot -= (slot / a.n_recent) * a.n_recent;
+      const size_t ro = (ring0 + (size_t)slot) * D + NI * r;
+      ksrc = a.kring + ro;
+      vsrc = a.vring + ro;
+    }
     // ---- Q K^T
     v4f c = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NI; i += 4) {
-      const float4 kv = tok_ok ? *reinterpret_cast<const float4*>(a.kring + ro + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 kv = tok_ok ? *reinterpret_cast<const float4*>(ksrc + i) : make_float4(0.f, 0.f, 0.f, 0.f);
       c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i], kv.x, c, 0, 0, 0);
       c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 1], kv.y, c, 0, 0, 0);
       c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 2], kv.z, c, 0, 0, 0);
       c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 3], kv.w, c, 0, 0, 0);
     }
-    // ---- V tile to LDS (token col, elements NI r ..), zeros past the window
+    // ---- V tile to LDS (token col, elements NI r ..), zeros past the last token
 #pragma unroll
     for (int i = 0; i < NI; i += 4) {
-      const float4 vv = tok_ok ? *reinterpret_cast<const float4*>(a.vring + ro + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 vv = tok_ok ? *reinterpret_cast<const float4*>(vsrc + i) : make_float4(0.f, 0.f, 0.f, 0.f);
       *reinterpret_cast<float4*>(vt + col * VS + NI * r + i) = vv;
     }
     // ---- online softmax of rows 4 r + j over the tile's 16 tokens (lanes of the 16-lane row)
     float p[4], corr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float x = (tok_ok && w0 + t0 + col <= lim[j]) ? c[j] * cl : -INFINITY;
+      const float x = (tok_ok && w0 + t <= lim[j]) ? c[j] * cl : -INFINITY;
       const float m_new = fmaxf(st.m[j], row16_max(x));
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // a row that sees nothing yet: p = 0
       corr[j] = exp2f(st.m[j] - m_use);
@@ -675,9 +701,11 @@ static inline int64_t grid_x(const AttendArgs& a, int tr) {
 static inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 // Prepared query rows in a workspace, after the partials: [rotated f32 query rows x D] [int8
-// query rows x D] [scale f32 rows] [block sums int32 rows x D / 32], each part 16-byte aligned.
+// query rows x D] [scale f32 rows] [block sums int32 rows x D / 32], then room for the rotated f32
+// K and V rows of a chunk (full-precision prefill, Hadamard layout: at most `rows` rows each, the
+// chunk having n_q * Hkv <= rows of them), each part 16-byte aligned.
 struct RowPrep {
-  size_t qrot, q8, sq, qsum, end;
+  size_t qrot, q8, sq, qsum, kc, vc, end;
 };
 
 static inline RowPrep row_prep_layout(size_t at, size_t rows, int D) {
@@ -686,7 +714,9 @@ static inline RowPrep row_prep_layout(size_t at, size_t rows, int D) {
   w.q8 = w.qrot + align16(rows * D * sizeof(float));
   w.sq = w.q8 + align16(rows * D);
   w.qsum = w.sq + align16(rows * sizeof(float));
-  w.end = w.qsum + align16(rows * (D / 32) * sizeof(int));
+  w.kc = w.qsum + align16(rows * (D / 32) * sizeof(int));
+  w.vc = w.kc + align16(rows * D * sizeof(float));
+  w.end = w.vc + align16(rows * D * sizeof(float));
   return w;
 }
 
@@ -695,8 +725,13 @@ static inline RowPrep row_prep_layout(size_t at, size_t rows, int D) {
 kvq_status launch_prepare_rows(const kvq_cache* c, const float* q, int n_vec, unsigned char* ws, const RowPrep& w,
                                AttendArgs& a, hipStream_t s);
 
-// The online-softmax reduce over the partials of batch * rows_per_b rows (kvq_attend.hip).
+// Hadamard rotation of f32 K and V rows [n_tok][Hkv][D] without storing them (kvq_store.hip).
+kvq_status launch_rotate_rows(const kvq_cache* c, const float* k_new, const float* v_new, int n_tok, float* kr,
+                              float* vr, hipStream_t st);
+
+// The online-softmax reduce over the partials of batch * rows_per_b rows (kvq_attend.hip);
+// win_always: every row has a window-slot partial (full-precision prefill).
 kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b, const int32_t* seq_len,
-                         int nc1, int32_t chunk, const float* ws, hipStream_t s);
+                         int nc1, int32_t chunk, const float* ws, hipStream_t s, bool win_always = false);
 
 }  // namespace kvq

@@ -329,10 +329,11 @@ __global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendA
   const int row0 = 64 * rb;
   const int nblk = min(64, nrows - row0);
   const int qs0 = a.causal ? a.q_start[b] : 0;
-  const int nch = a.n_recent > 0 ? a.ngroups - 1 : a.ngroups;
+  const bool win = a.n_recent > 0 || a.kchunk;    // the last group: f32 rows (window, chunk)
+  const int nch = win ? a.ngroups - 1 : a.ngroups;
   if (c >= nch) {   // window block: wave w takes the 16-row tile 16 w of the 64 rows
     const int w = threadIdx.x >> 6, nv = min(16, nblk - 16 * w);
-    if (S > 0 && nv > 0) {
+    if ((S > 0 || a.kchunk) && nv > 0) {
       WinState<D> st;
       window_wave<L, D>(a, reinterpret_cast<float*>(smem + w * window_wave_lds<D>()), b, hk, S, row0 + 16 * w, nv, qs0, 0, 1,
                         threadIdx.x & 63, st);
@@ -594,4 +595,53 @@ extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float*
   }
   return launch_reduce(c, out, batch, n_q * Hq, seq_len, a.nc1, kPrefillChunk, (const float*)workspace,
                        (hipStream_t)stream);
+}
+
+extern "C" kvq_status kvq_prefill_full_then_store(const kvq_cache* c, const float* q, const float* k_new,
+                                                  const float* v_new, float* out, int32_t batch, int32_t n_q,
+                                                  int32_t Hq, float alpha, int32_t causal, const int32_t* q_start,
+                                                  const int32_t* block_table, int32_t max_pages, int32_t max_seq_len,
+                                                  void* workspace, size_t ws_bytes, void* stream) {
+  // the prefix lengths are q_start: they bound the packed tokens and the window read here
+  kvq_status st = check_attend_args(c, q, batch, Hq, block_table, max_pages, q_start, max_seq_len);
+  if (st != KVQ_OK) return st;
+  if (!out || !k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "out, k_new and v_new must be non-null");
+  if (n_q < 1) return fail(KVQ_ERR_INVALID_ARG, "n_q must be >= 1");
+  if (n_q > max_seq_len) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len must bound q_start + n_q");
+  if (causal != 0 && causal != 1) return fail(KVQ_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (c->n_recent > 0 && batch > c->max_batch) return fail(KVQ_ERR_INVALID_ARG, "batch above the window rings' max_batch");
+  if ((int64_t)batch * n_q * Hq > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "batch * n_q * num_q_heads above 2^31 - 1");
+  if ((int64_t)batch * n_q * c->num_kv_heads * 2 > (int64_t)INT32_MAX)
+    return fail(KVQ_ERR_INVALID_ARG, "too many rows in one store");
+  const size_t need = kvq_prefill_workspace_bytes(batch, n_q, Hq, c->head_dim, max_seq_len);
+  if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  AttendArgs a = make_args(c, q, Hq, n_q, alpha, block_table, max_pages, q_start, max_seq_len, kPrefillChunk,
+                           workspace);
+  a.causal = causal;
+  a.skip = 0;   // every packed token precedes the chunk: nothing to skip
+  a.q_start = causal ? q_start : nullptr;
+  const int nch = chunks_of(max_seq_len, kPrefillChunk);
+  a.ngroups = nch + 1;   // the last group: window and chunk rows
+  const int64_t gx = ((int64_t)n_q * a.G + 63) / 64 * a.ngroups * c->num_kv_heads * batch;
+  if (gx > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
+  const int rows = batch * n_q * Hq;
+  const RowPrep w = prefill_ws((size_t)rows, c->head_dim, max_seq_len);
+  hipStream_t s = (hipStream_t)stream;
+  unsigned char* wsb = (unsigned char*)workspace;
+  if (c->layout == HAD) {   // the chunk's rows in the rotated basis, as the window keeps its rows
+    a.kchunk = (const float*)(wsb + w.kc);
+    a.vchunk = (const float*)(wsb + w.vc);
+    if ((st = launch_rotate_rows(c, k_new, v_new, batch * n_q, (float*)(wsb + w.kc), (float*)(wsb + w.vc), s)) != KVQ_OK)
+      return st;
+  } else {
+    a.kchunk = k_new;
+    a.vchunk = v_new;
+  }
+  if ((st = launch_prepare_rows(c, q, rows, wsb, w, a, s)) != KVQ_OK) return st;
+  pick_prefill(c->layout, c->head_dim)(a, dim3((unsigned)gx), 1 /* the f32-row group runs: its LDS */, s);
+  if ((st = check_launch("prefill partial kernel")) != KVQ_OK) return st;
+  // the store follows the attention on the stream: it rewrites window slots the prefix was read from
+  if ((st = kvq_store_chunk(c, k_new, v_new, batch, n_q, q_start, block_table, max_pages, max_seq_len, stream)) != KVQ_OK)
+    return st;
+  return launch_reduce(c, out, batch, n_q * Hq, q_start, a.nc1, kPrefillChunk, (const float*)workspace, s, true);
 }

@@ -28,6 +28,14 @@ struct StoreArgs {
   int Hkv;
   int page_shift;  // log2(page_size)
   int n_recent;
+  // chunk form (bt set): token tok = b * n_q + i goes to position q_start[b] + i of row b, its slot
+  // read from the block table; the row's length after the append is q_start[b] + n_q
+  const int32_t* bt;
+  const int32_t* q_start;
+  int max_pages, n_q;
+  // rotation only (rot set, Hadamard layout): the rotated f32 rows go to rot[kv] [n_tok][Hkv][D] and
+  // nothing is stored in the cache
+  float* rot[2];
 };
 
 __device__ __forceinline__ uint32_t pack8(const int* n) {
@@ -104,17 +112,39 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
     const float c = hadamard_norm<D>();
 #pragma unroll
     for (int i = 0; i < E; ++i) x[i] = x[i] * c;
+    if (a.rot[0]) {
+      if (active) {
+        float* dst = a.rot[kv] + ((size_t)tok * a.Hkv + h) * D + sub * E;
+#pragma unroll
+        for (int e = 0; e < E; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+      }
+      return;
+    }
   }
 
-  const int s = active ? a.slot[tok] : 0;
+  int s = 0, b = 0, p = 0, len = 0;   // slot; batch row, position and row length (window only)
+  bool ok = active;
+  if (a.bt) {
+    b = tok / a.n_q;
+    p = active ? a.q_start[b] + (tok - b * a.n_q) : 0;
+    const int pg = p >> a.page_shift;
+    ok = ok && p >= 0 && pg < a.max_pages;          // positions the block table does not cover are skipped
+    s = ok ? (a.bt[(size_t)b * a.max_pages + pg] << a.page_shift) | (p & ((1 << a.page_shift) - 1)) : 0;
+    len = active ? a.q_start[b] + a.n_q : 0;
+  } else {
+    s = active ? a.slot[tok] : 0;
+    if (a.n_recent > 0 && active) {
+      b = a.batch_idx[tok];
+      p = a.pos[tok];
+      len = a.seq_len[b];
+    }
+  }
   const size_t prow = ((size_t)(s >> a.page_shift) * a.Hkv + h) * ((size_t)1 << a.page_shift) +
                       (size_t)(s & ((1 << a.page_shift) - 1));
 
   // recent window: exact f32 row (rotated for HAD) at ring slot pos % n_recent
-  if (a.n_recent > 0 && active) {
-    const int b = a.batch_idx[tok];
-    const int p = a.pos[tok];
-    if (p >= a.seq_len[b] - a.n_recent) {
+  if (a.n_recent > 0 && ok) {
+    if (p >= len - a.n_recent) {
       float* dst = a.ring[kv] + (((size_t)b * a.Hkv + h) * a.n_recent + (p % a.n_recent)) * D + sub * E;
 #pragma unroll
       for (int e = 0; e < E; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
@@ -131,7 +161,7 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
     const float sc = m / 8.0f;
 #pragma unroll
     for (int i = 0; i < E; ++i) n[i] = sc == 0.0f ? 0 : (int)fminf(fmaxf(rintf(x[i] / sc), -8.0f), 7.0f);
-    if (active && sub == 0) *reinterpret_cast<float*>(rec) = sc;
+    if (ok && sub == 0) *reinterpret_cast<float*>(rec) = sc;
   } else if (L == Q40 || L == Q60 || L == Q80) {
     constexpr float M = (L == Q40) ? 8.0f : (L == Q60 ? 32.0f : 128.0f);
     constexpr float lo = -M, hi = M - 1.0f;
@@ -144,7 +174,7 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
     const float d = f16_round_sat(d32);
 #pragma unroll
     for (int i = 0; i < E; ++i) n[i] = d == 0.0f ? 0 : (int)fminf(fmaxf(rintf(x[i] / d), lo), hi);
-    if (active && (sub % LPG) == 0) reinterpret_cast<uint16_t*>(rec)[sub / LPG] = f16_bits_sat(d32);
+    if (ok && (sub % LPG) == 0) reinterpret_cast<uint16_t*>(rec)[sub / LPG] = f16_bits_sat(d32);
   } else {
     float mn = x[0], mx = x[0];
 #pragma unroll
@@ -163,11 +193,11 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
       const float t = x[i] - z;
       n[i] = sc == 0.0f ? 0 : (int)fminf(fmaxf(rintf(t / sc), 0.0f), 15.0f);
     }
-    if (active && (sub % LPG) == 0)
+    if (ok && (sub % LPG) == 0)
       reinterpret_cast<uint32_t*>(rec)[sub / LPG] = (uint32_t)f16_bits_sat(s32) | ((uint32_t)f16_bits_sat(mn) << 16);
   }
 
-  if (!active) return;
+  if (!ok) return;
   uint8_t* pay = a.payload[kv] + prow * T::PB;
   if (L == Q80) {
     // one two's-complement byte per code, element order: the lane's E codes at byte sub * E
@@ -256,6 +286,7 @@ extern "C" kvq_status kvq_store(const kvq_cache* c, const float* k_new, const fl
   if ((size_t)n_tok * c->num_kv_heads * 2 > (size_t)INT32_MAX)
     return fail(KVQ_ERR_INVALID_ARG, "too many rows in one store");
   StoreArgs a;
+  memset(&a, 0, sizeof(a));
   a.k_new = k_new;
   a.v_new = v_new;
   a.slot = slot;
@@ -272,6 +303,62 @@ extern "C" kvq_status kvq_store(const kvq_cache* c, const float* k_new, const fl
   a.Hkv = c->num_kv_heads;
   a.page_shift = __builtin_ctz((unsigned)c->page_size);
   a.n_recent = c->n_recent;
+  pick_store(c->layout, c->head_dim)(a, (hipStream_t)stream);
+  return check_launch("store kernel");
+}
+
+namespace kvq {
+// The Hadamard-rotated f32 rows of n_tok tokens of k_new, v_new [n_tok][Hkv][D] into kr, vr (same
+// shape), by the store kernel's own rotation; nothing is stored.  For the full-precision prefill.
+kvq_status launch_rotate_rows(const kvq_cache* c, const float* k_new, const float* v_new, int n_tok, float* kr,
+                              float* vr, hipStream_t st) {
+  StoreArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.n_rows = n_tok * c->num_kv_heads * 2;
+  a.Hkv = c->num_kv_heads;
+  a.page_shift = __builtin_ctz((unsigned)c->page_size);
+  a.rot[0] = kr;
+  a.rot[1] = vr;
+  if (a.n_rows == 0) return KVQ_OK;
+  (c->head_dim == 256 ? launch_store<HAD, 256> : launch_store<HAD, 128>)(a, st);
+  return check_launch("rotation kernel");
+}
+}  // namespace kvq
+
+extern "C" kvq_status kvq_store_chunk(const kvq_cache* c, const float* k_new, const float* v_new, int32_t batch,
+                                      int32_t n_q, const int32_t* q_start, const int32_t* block_table,
+                                      int32_t max_pages, int32_t max_seq_len, void* stream) {
+  kvq_status st = validate_cache(c);
+  if (st != KVQ_OK) return st;
+  if (batch < 1 || n_q < 0) return fail(KVQ_ERR_INVALID_ARG, "batch must be >= 1 and n_q >= 0");
+  if (n_q == 0) return KVQ_OK;
+  if (!k_new || !v_new || !q_start || !block_table)
+    return fail(KVQ_ERR_INVALID_ARG, "k_new, v_new, q_start and block_table must be non-null");
+  if (max_seq_len < n_q || max_pages < 1 || (int64_t)max_pages * c->page_size < max_seq_len)
+    return fail(KVQ_ERR_INVALID_ARG, "max_pages_per_seq * page_size must cover max_seq_len >= n_q");
+  if (c->n_recent > 0 && batch > c->max_batch) return fail(KVQ_ERR_INVALID_ARG, "batch above the window rings' max_batch");
+  if ((int64_t)batch * n_q * c->num_kv_heads * 2 > (int64_t)INT32_MAX)
+    return fail(KVQ_ERR_INVALID_ARG, "too many rows in one store");
+  StoreArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.payload[0] = (uint8_t*)c->k_payload;
+  a.payload[1] = (uint8_t*)c->v_payload;
+  a.record[0] = (uint8_t*)c->k_scale;
+  a.record[1] = (uint8_t*)c->v_scale;
+  a.ring[0] = c->k_recent;
+  a.ring[1] = c->v_recent;
+  a.n_rows = batch * n_q * c->num_kv_heads * 2;
+  a.Hkv = c->num_kv_heads;
+  a.page_shift = __builtin_ctz((unsigned)c->page_size);
+  a.n_recent = c->n_recent;
+  a.bt = block_table;
+  a.q_start = q_start;
+  a.max_pages = max_pages;
+  a.n_q = n_q;
   pick_store(c->layout, c->head_dim)(a, (hipStream_t)stream);
   return check_launch("store kernel");
 }

@@ -192,6 +192,76 @@ def attend_prefill_causal(cache, q, q_start, block_table, seq_len, max_seq_len, 
     return out
 
 
+def _chunk_rows(cache, k_new, v_new, B, n_q):
+    dev = cache.device
+    _need(k_new, "k_new", torch.float32, dev)
+    _need(v_new, "v_new", torch.float32, dev)
+    if k_new.shape != (B, n_q, cache.num_kv_heads, cache.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [B, n_q, Hkv, D]")
+
+
+def store_chunk(cache, k_new, v_new, q_start, block_table, max_seq_len):
+    """kvq_store_chunk: append k_new, v_new f32 [B, n_q, Hkv, D] at positions q_start[b] + i."""
+    dev = cache.device
+    _need(q_start, "q_start", torch.int32, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    B, n_q = k_new.shape[0], k_new.shape[1]
+    _chunk_rows(cache, k_new, v_new, B, n_q)
+    if q_start.shape != (B,) or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("q_start must be [B] and block_table [B, max_pages]")
+    st = load().kvq_store_chunk(cache.desc, _ptr(k_new), _ptr(v_new), B, n_q, _ptr(q_start), _ptr(block_table),
+                                block_table.shape[1], int(max_seq_len), _stream(dev))
+    check("kvq_store_chunk", st)
+
+
+def prefill_full_then_store(cache, q, k_new, v_new, q_start, block_table, max_seq_len, alpha, causal=True,
+                            out=None, workspace=None):
+    """kvq_prefill_full_then_store: the chunk's queries q f32 [B, n_q, Hq, D] attend over the cached
+    prefix and over the chunk's own rows k_new, v_new f32 [B, n_q, Hkv, D] in full precision; then the
+    chunk is stored at positions q_start[b] + i.  Returns out f32 [B, n_q, Hq, D]."""
+    dev = cache.device
+    _need(q, "q", torch.float32, dev)
+    _need(q_start, "q_start", torch.int32, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, n_q, Hq, D]")
+    B, n_q, Hq, D = q.shape
+    _chunk_rows(cache, k_new, v_new, B, n_q)
+    if q_start.shape != (B,) or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("q_start must be [B] and block_table [B, max_pages]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float32, dev)
+    need = prefill_workspace_bytes(B, n_q, Hq, D, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load().kvq_prefill_full_then_store(cache.desc, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), B, n_q, Hq,
+                                            float(alpha), int(bool(causal)), _ptr(q_start), _ptr(block_table),
+                                            block_table.shape[1], int(max_seq_len), _ptr(workspace),
+                                            workspace.numel() if workspace is not None else 0, _stream(dev))
+    check("kvq_prefill_full_then_store", st)
+    return out
+
+
+def attend_step(cache, q, k_new, v_new, q_start, seq_len, block_table, max_seq_len, alpha, cached_tokens,
+                chunk_tokens=512):
+    """One attention step of a model layer with the dispatch rule of [Open-TQ-Metal]'s prefill/decode
+    selection: a single query with at least 32 cached tokens appends its token (kvq_store_chunk) and
+    runs the fused decode over the packed cache; any other step (several queries, or fewer than 32
+    cached tokens) runs the full-precision prefill and then stores the chunk.
+
+    q f32 [B, n_q, Hq, D]; k_new, v_new f32 [B, n_q, Hkv, D]; q_start int32 [B] (cached tokens before
+    the step); seq_len int32 [B] = q_start + n_q; cached_tokens: host int, the fewest cached tokens of
+    any row.  Returns (out f32 [B, n_q, Hq, D], "decode" or "full").
+    """
+    B, n_q = q.shape[0], q.shape[1]
+    if n_q == 1 and cached_tokens >= 32:
+        store_chunk(cache, k_new, v_new, q_start, block_table, max_seq_len)
+        out = attend_decode(cache, q[:, 0], block_table, seq_len, max_seq_len, alpha, chunk_tokens=chunk_tokens)
+        return out[:, None], "decode"
+    return prefill_full_then_store(cache, q, k_new, v_new, q_start, block_table, max_seq_len, alpha), "full"
+
+
 def debug_quantize_q(layout, q):
     """kvq_debug_quantize_q: q f32 [n, D] -> (q8 int8 [n, D], sq f32 [n])."""
     n, D = q.shape
