@@ -127,6 +127,53 @@ def time_prefill(steps, warmup, dev, seed=2):
                 bound="mfma (int8 Q K^T at 5.0 POP/s + f16 P V at 2.5 PFLOP/s)")
 
 
+def time_prefill_full(steps, warmup, dev, q_start, n_q, seed=3):
+    """Full-precision prefill then store, Hadamard workload shape: n_q queries at q_start (the prefix
+    stored first), the chunk's own tokens exact, then the chunk quantised into the cache."""
+    import torch
+    import quantized_kv_cache_store_amd as kvq
+    import workloads as W
+
+    w = W.WORKLOADS["qwen3_1p7b_had_s8k"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    S1 = q_start + n_q
+    ps = w.page_size
+    npages = (S1 + ps - 1) // ps
+    cache = kvq.KvqCache(w.layout, w.D, w.Hkv, npages, ps, n_recent=w.n_recent, max_batch=1, device=dev)
+    table = torch.arange(npages, dtype=torch.int32, device=dev).reshape(1, npages)
+    qs = torch.full((1,), q_start, dtype=torch.int32, device=dev)
+    if q_start > 0:
+        k = W.kv_tokens_device(w, q_start, "k", gen, dev)
+        v = W.kv_tokens_device(w, q_start, "v", gen, dev)
+        pos = torch.arange(q_start, dtype=torch.int32, device=dev)
+        kvq.store(cache, k, v, pos.clone(), torch.zeros(q_start, dtype=torch.int32, device=dev), pos, qs)
+    kc = W.kv_tokens_device(w, n_q, "k", gen, dev).reshape(1, n_q, w.Hkv, w.D)
+    vc = W.kv_tokens_device(w, n_q, "v", gen, dev).reshape(1, n_q, w.Hkv, w.D)
+    q = torch.randn((1, n_q, w.Hq, w.D), generator=gen, device=dev, dtype=torch.float32)
+    out = torch.empty_like(q)
+    ws = torch.empty(kvq.prefill_workspace_bytes(1, n_q, w.Hq, w.D, S1), dtype=torch.uint8, device=dev)
+    # the same chunk is stored at the same positions on every call
+    for _ in range(warmup):
+        kvq.prefill_full_then_store(cache, q, kc, vc, qs, table, S1, w.alpha, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        kvq.prefill_full_then_store(cache, q, kc, vc, qs, table, S1, w.alpha, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    assert torch.isfinite(out).all(), "non-finite prefill output"
+    prefix_pairs = q_start * n_q * w.Hq              # every query sees the whole prefix
+    chunk_pairs = n_q * (n_q + 1) // 2 * w.Hq        # causal within the chunk
+    t_min = (2.0 * prefix_pairs * w.D / 5.0e15 + 2.0 * prefix_pairs * w.D / 2.5e15   # int8 Q K^T + f16 P V
+             + 2.0 * 2.0 * chunk_pairs * w.D / 157.3e12)                              # f32 Q K^T + P V (window MFMA)
+    return dict(workload=w.name, n_q=n_q, q_start=q_start, us=round(us, 2), prefix_pairs=prefix_pairs,
+                chunk_pairs=chunk_pairs, roofline_us=round(t_min * 1e6, 2), frac=round(t_min * 1e6 / us, 4),
+                bound="mfma (prefix: int8 + f16; chunk rows: f32 at 157.3 TFLOP/s)")
+
+
 def time_store(steps, warmup, dev, seed=1):
     """kvq_store of one new token per kv head into the Llama-3-8B-shaped q4_0 cache (32768 slots)."""
     import torch
@@ -297,6 +344,8 @@ def main():
                                partial_us=r1["partial_ms_mean"] * 1e3, layers_walked=r1["layers"])
     if not a.no_prefill:
         extra["prefill"] = time_prefill(max(a.steps, 20), a.warmup, dev)
+        extra["prefill_full_precision"] = [time_prefill_full(max(a.steps, 20), a.warmup, dev, qs, nq)
+                                           for qs, nq in ((8192, 512), (0, 512), (0, 4096))]
         extra["store"] = time_store(max(a.steps, 20), a.warmup, dev)
     gbs = r["bytes_layer"] / (r["ms_per_step"] * 1e-3) / 1e9
     ach = r["bytes_layer"] / (r["partial_ms_mean"] * 1e-3) / 1e9

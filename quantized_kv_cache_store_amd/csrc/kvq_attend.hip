@@ -818,12 +818,13 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
 // output elements l * E .. l * E + E - 1; the rotation runs in registers, butterflies inside a
 // lane for strides below E and between lanes above, in the stage order of the encoding
 // (h = 1, 2, ..., D / 2, then 1 / sqrt(D)).
-// win_always: the window slot holds a partial for every row (full-precision prefill: the chunk's
-// own rows), whatever the window.
+// nwin_always > 0: the last nwin_always slots hold partials of every row (full-precision prefill:
+// the slices of its f32 rows), whatever the window; else the last slot holds the window's partial
+// when there is a window and the row is not empty.
 template <int D, bool ROT, int W>
 __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out, const int32_t* seq_len,
                                                      int rows_per_b, int nc1, int chunk, int n_recent,
-                                                     long total_rows, int win_always) {
+                                                     long total_rows, int nwin_always, int slice, int causal_nq) {
 #pragma clang fp contract(off)
   constexpr int E = D / 64;
   constexpr int RPB = 4 / W;
@@ -838,11 +839,17 @@ __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out
   const int S = seq_len[b];
   const int Sq = n_recent > 0 ? max(0, S - n_recent) : S;
   const int nq = (Sq + chunk - 1) / chunk;
-  const int cnt = nq + ((win_always || (n_recent > 0 && S > 0)) ? 1 : 0);
+  int nw = nwin_always > 0 ? nwin_always : ((n_recent > 0 && S > 0) ? 1 : 0);
+  if (nwin_always > 0 && causal_nq > 0) {   // the slices this query's causal limit reaches
+    const int i = (int)(rr % rows_per_b) / (rows_per_b / causal_nq);
+    nw = min(nw, (min(S, n_recent) + i) / slice + 1);
+  }
+  const int cnt = nq + nw;
+  const int wbase = nc1 - (nwin_always > 0 ? nwin_always : 1) - nq;   // slot of partial i >= nq: wbase + i
   const int PST = partial_stride(D);
   const float* base = ws + (size_t)rr * nc1 * PST;
   float M = -INFINITY;
-  for (int i = sub * 64 + lane; i < cnt; i += 64 * W) M = fmaxf(M, base[(size_t)(i < nq ? i : nc1 - 1) * PST + D]);
+  for (int i = sub * 64 + lane; i < cnt; i += 64 * W) M = fmaxf(M, base[(size_t)(i < nq ? i : wbase + i) * PST + D]);
   for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
   if (W > 1) {
     if (lane == 0) red_m[wave] = M;
@@ -856,7 +863,7 @@ __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out
   for (int e = 0; e < E; ++e) o[e] = 0.0f;
 #pragma unroll 4
   for (int i = sub; i < cnt; i += W) {
-    const float* p = base + (size_t)(i < nq ? i : nc1 - 1) * PST;
+    const float* p = base + (size_t)(i < nq ? i : wbase + i) * PST;
     const float mc = p[D];
     const float w = (mc == -INFINITY) ? 0.0f : exp2f(mc - M);
     l += w * p[D + 1];
@@ -980,30 +987,31 @@ static kvq_status check_chunk(const kvq_cache* c, int32_t chunk) {
 
 template <int D, bool ROT, int W>
 static void launch_reduce_w(float* out, long rows, int rows_per_b, const int32_t* seq_len, int nc1, int chunk,
-                            int n_recent, const float* ws, hipStream_t s, int win_always) {
+                            int n_recent, const float* ws, hipStream_t s, int nwin_always, int slice, int causal_nq) {
   const long blocks = (rows + (4 / W) - 1) / (4 / W);
   hipLaunchKernelGGL((attend_reduce<D, ROT, W>), dim3((unsigned)blocks), dim3(256), 0, s, ws, out, seq_len, rows_per_b,
-                     nc1, chunk, n_recent, rows, win_always);
+                     nc1, chunk, n_recent, rows, nwin_always, slice, causal_nq);
 }
 
 kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b, const int32_t* seq_len,
-                         int nc1, int32_t chunk, const float* ws, hipStream_t s, bool win_always) {
-  const int wa = win_always ? 1 : 0;
+                         int nc1, int32_t chunk, const float* ws, hipStream_t s, int nwin_always, int slice,
+                         int causal_nq) {
+  const int wa = nwin_always;
   const long rows = (long)batch * rows_per_b;
   // one wave per row when there are rows enough to fill the chip, else four waves split each row
   const bool many = rows >= 4096;
   const bool rot = c->layout == HAD;
   const int n = c->n_recent;
   if (c->head_dim == 128) {
-    if (rot) many ? launch_reduce_w<128, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa)
-                  : launch_reduce_w<128, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa);
-    else many ? launch_reduce_w<128, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa)
-              : launch_reduce_w<128, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa);
+    if (rot) many ? launch_reduce_w<128, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq)
+                  : launch_reduce_w<128, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq);
+    else many ? launch_reduce_w<128, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq)
+              : launch_reduce_w<128, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq);
   } else {
-    if (rot) many ? launch_reduce_w<256, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa)
-                  : launch_reduce_w<256, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa);
-    else many ? launch_reduce_w<256, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa)
-              : launch_reduce_w<256, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa);
+    if (rot) many ? launch_reduce_w<256, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq)
+                  : launch_reduce_w<256, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq);
+    else many ? launch_reduce_w<256, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq)
+              : launch_reduce_w<256, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq);
   }
   return check_launch("attention reduce kernel");
 }

@@ -35,6 +35,9 @@ struct AttendArgs {
   const float* vchunk;      //   for HAD) and V rows, read as exact rows at positions seq_len[b] + i; else null
   int32_t* dbg;
   int Hkv, Hq, G, page_shift, n_recent, max_pages, chunk, nc1, max_seq_len;
+  int nwin;      // partial slots of the f32 rows, the last nwin of a row's nc1 (full-precision prefill: one
+                 // per slice of its f32 rows; else 1)
+  int slice;     // full-precision prefill: f32 rows per slice (a multiple of 16)
   int n_q;       // queries per batch row (1 for decode)
   int batch;     // batch rows (decode: the grid is one-dimensional)
   int ngroups;   // blocks per row tile along the sequence: chunk groups of four, + 1 for the window
@@ -306,7 +309,8 @@ struct WinState {
 
 template <int L, int D>
 __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int b, int hk, int S, int row0, int nvalid,
-                                            int qs0, int k0, int kstep, int lane, WinState<D>& st) {
+                                            int qs0, int k0, int kstep, int lane, WinState<D>& st,
+                                            int kend = 0x7fffffff) {
   constexpr int NI = D / 4;           // MFMAs of Q K^T (d = 32 r + i... four lanes groups of D / 4)
   constexpr int VS = D + 16;          // V tile row stride (floats)
   const int col = lane & 15, r = lane >> 4;
@@ -343,7 +347,7 @@ __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int 
     st.m[j] = -INFINITY;
     st.l[j] = 0.0f;
   }
-  int ntiles = (NT + 15) / 16;
+  int ntiles = min((NT + 15) / 16, kend);   // kend: the end of this call's slice of tiles
   {
     const int lmax = nvalid > 0 ? row_limit(a, qs0, row0 + nvalid - 1, nrows) : -1;   // the tile's farthest limit
     if (lmax < w0) ntiles = 0;
@@ -417,15 +421,15 @@ __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int 
   for (int j = 0; j < 4; ++j) st.l[j] = row16_sum(st.l[j]);
 }
 
-// Write a window state as the partial of rows row0 + 4 r + j (< nvalid) in the window slot.
+// Write a window state as the partial of rows row0 + 4 r + j (< nvalid) in partial slot `slot`.
 template <int D>
 __device__ __forceinline__ void window_store(const AttendArgs& a, const WinState<D>& st, int b, int hk, int row0, int nvalid,
-                                             int lane) {
+                                             int lane, int slot) {
   const int col = lane & 15, r = lane >> 4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (4 * r + j >= nvalid) continue;
-    float* dst = a.ws + (row_index(a, b, hk, row0 + 4 * r + j) * a.nc1 + (a.nc1 - 1)) * partial_stride(D);
+    float* dst = a.ws + (row_index(a, b, hk, row0 + 4 * r + j) * a.nc1 + slot) * partial_stride(D);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) dst[16 * dt + col] = st.o[dt][j];
     if (col == 0) {
@@ -683,6 +687,7 @@ static inline AttendArgs make_args(const kvq_cache* c, const float* q, int32_t H
   a.chunk = chunk;
   const int nch = chunks_of(max_seq_len, chunk);
   a.nc1 = nch + 1;
+  a.nwin = 1;
   a.max_seq_len = max_seq_len;
   a.n_q = n_q;
   a.ngroups = (nch + 3) / 4 + (c->n_recent > 0 ? 1 : 0);
@@ -730,8 +735,12 @@ kvq_status launch_rotate_rows(const kvq_cache* c, const float* k_new, const floa
                               float* vr, hipStream_t st);
 
 // The online-softmax reduce over the partials of batch * rows_per_b rows (kvq_attend.hip);
-// win_always: every row has a window-slot partial (full-precision prefill).
+// nwin_always > 0: the rows' f32-row partials are the last nwin_always slots (full-precision
+// prefill, slices of `slice` rows; with causal_nq > 0, the causal limit of query i, i = (row in the
+// batch row) / (rows_per_b / causal_nq), reaches only the first (W + i) / slice + 1 of them, W the
+// row's window); else one window partial when n_recent > 0 and the row is not empty.
 kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b, const int32_t* seq_len,
-                         int nc1, int32_t chunk, const float* ws, hipStream_t s, bool win_always = false);
+                         int nc1, int32_t chunk, const float* ws, hipStream_t s, int nwin_always = 0, int slice = 0,
+                         int causal_nq = 0);
 
 }  // namespace kvq

@@ -34,6 +34,12 @@ namespace kvq {
 
 // Split-K chunk of the prefill (tokens); each (64-row block, chunk) is one block of the grid.
 constexpr int kPrefillChunk = 1024;
+// Full-precision prefill: its f32 rows (the prefix's window and the chunk's own rows) are split into
+// slices of at least this many tokens, one group and one partial slot each.
+constexpr int kRowSlice = 128;
+
+// Slices of the f32 rows of a full-precision prefill of n_q queries (window at most n_recent).
+static inline int row_slices(int n_recent, int n_q) { return (n_recent + n_q + kRowSlice - 1) / kRowSlice; }
 static_assert(kPrefillChunk % 32 == 0 && kPrefillChunk / 16 <= 64, "a chunk's pages (>= 16 tokens each) fit one per lane");
 
 // LDS of one 32-token step:
@@ -329,15 +335,25 @@ __global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendA
   const int row0 = 64 * rb;
   const int nblk = min(64, nrows - row0);
   const int qs0 = a.causal ? a.q_start[b] : 0;
-  const bool win = a.n_recent > 0 || a.kchunk;    // the last group: f32 rows (window, chunk)
-  const int nch = win ? a.ngroups - 1 : a.ngroups;
-  if (c >= nch) {   // window block: wave w takes the 16-row tile 16 w of the 64 rows
+  // the last groups: f32 rows (the window; for the full-precision prefill also the chunk's own rows,
+  // in a.nwin slices of a.slice rows)
+  const int nwg = a.kchunk ? a.nwin : (a.n_recent > 0 ? 1 : 0);
+  const int nch = a.ngroups - nwg;
+  if (c >= nch) {   // f32-row block: wave w takes the 16-row tile 16 w of the 64 rows
     const int w = threadIdx.x >> 6, nv = min(16, nblk - 16 * w);
-    if ((S > 0 || a.kchunk) && nv > 0) {
+    const int j = c - nch;
+    bool run = (S > 0 || a.kchunk) && nv > 0;
+    if (a.kchunk && run) {   // a slice past every limit of the wave's rows: the reduce does not read it
+      const int lmax = row_limit(a, qs0, row0 + 16 * w + nv - 1, nrows);
+      run = j * a.slice <= lmax - (S - min(S, a.n_recent));
+    }
+    if (run) {
+      const int k0 = a.kchunk ? j * (a.slice / 16) : 0;
+      const int kend = a.kchunk ? k0 + a.slice / 16 : 0x7fffffff;
       WinState<D> st;
-      window_wave<L, D>(a, reinterpret_cast<float*>(smem + w * window_wave_lds<D>()), b, hk, S, row0 + 16 * w, nv, qs0, 0, 1,
-                        threadIdx.x & 63, st);
-      window_store<D>(a, st, b, hk, row0 + 16 * w, nv, threadIdx.x & 63);
+      window_wave<L, D>(a, reinterpret_cast<float*>(smem + w * window_wave_lds<D>()), b, hk, S, row0 + 16 * w, nv, qs0, k0, 1,
+                        threadIdx.x & 63, st, kend);
+      window_store<D>(a, st, b, hk, row0 + 16 * w, nv, threadIdx.x & 63, a.nc1 - a.nwin + j);
     }
     return;
   }
@@ -533,10 +549,10 @@ static prefill_fn pick_prefill(int layout, int D) {
 }
 
 
-// Workspace of the prefill: the partials [rows x (chunks + 1) x (D + 4)] f32, then the prepared rows.
-static RowPrep prefill_ws(size_t rows, int D, int max_seq_len) {
-  const size_t nc1 = (size_t)chunks_of(max_seq_len, kPrefillChunk) + 1;
-  return row_prep_layout(rows * nc1 * partial_stride(D) * sizeof(float), rows, D);
+// Workspace of a prefill: the partials [rows x nslots x (D + 4)] f32 (nslots: the chunks and the f32-row
+// slots of that call), then the prepared rows.
+static RowPrep prefill_ws(size_t rows, int D, int nslots) {
+  return row_prep_layout(rows * (size_t)nslots * partial_stride(D) * sizeof(float), rows, D);
 }
 
 kvq_status launch_prepare_rows(const kvq_cache* c, const float* q, int n_vec, unsigned char* ws, const RowPrep& w,
@@ -558,7 +574,10 @@ using namespace kvq;
 extern "C" size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t Hq, int32_t D,
                                               int32_t max_seq_len) {
   if (batch < 1 || n_q < 1 || Hq < 1 || (D != 128 && D != 256) || max_seq_len < 0) return 0;
-  return prefill_ws((size_t)batch * n_q * Hq, D, max_seq_len).end;
+  // the larger of the two prefills' needs: one window slot, or the slices of a full-precision
+  // prefill's f32 rows with the largest window
+  const int nslots = chunks_of(max_seq_len, kPrefillChunk) + row_slices(512, n_q);
+  return prefill_ws((size_t)batch * n_q * Hq, D, nslots).end;
 }
 
 extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float* q, float* out, int32_t batch,
@@ -586,7 +605,7 @@ extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float*
   const int64_t gx = ((int64_t)n_q * a.G + 63) / 64 * a.ngroups * c->num_kv_heads * batch;
   if (gx > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
   const int rows = batch * n_q * Hq;
-  const RowPrep w = prefill_ws((size_t)rows, c->head_dim, max_seq_len);
+  const RowPrep w = prefill_ws((size_t)rows, c->head_dim, a.nc1);
   if ((st = launch_prepare_rows(c, q, rows, (unsigned char*)workspace, w, a, (hipStream_t)stream)) != KVQ_OK) return st;
   if (gx > 0) {
     const dim3 grid((unsigned)gx);
@@ -621,11 +640,21 @@ extern "C" kvq_status kvq_prefill_full_then_store(const kvq_cache* c, const floa
   a.skip = 0;   // every packed token precedes the chunk: nothing to skip
   a.q_start = causal ? q_start : nullptr;
   const int nch = chunks_of(max_seq_len, kPrefillChunk);
-  a.ngroups = nch + 1;   // the last group: window and chunk rows
+  // the last groups: slices of the window and chunk rows, each of at least kRowSlice rows, and as
+  // many as bring the grid to about 4096 blocks
+  const int nf32 = min(c->n_recent, max_seq_len) + n_q;
+  const int64_t row_blocks = ((int64_t)n_q * a.G + 63) / 64 * c->num_kv_heads * batch;
+  const int64_t want = (4096 + row_blocks - 1) / row_blocks;
+  int slice = (int)((nf32 + want - 1) / want);
+  slice = max(kRowSlice, (slice + 15) / 16 * 16);
+  a.slice = slice;
+  a.nwin = (nf32 + slice - 1) / slice;
+  a.nc1 = nch + a.nwin;
+  a.ngroups = nch + a.nwin;
   const int64_t gx = ((int64_t)n_q * a.G + 63) / 64 * a.ngroups * c->num_kv_heads * batch;
   if (gx > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
   const int rows = batch * n_q * Hq;
-  const RowPrep w = prefill_ws((size_t)rows, c->head_dim, max_seq_len);
+  const RowPrep w = prefill_ws((size_t)rows, c->head_dim, a.nc1);
   hipStream_t s = (hipStream_t)stream;
   unsigned char* wsb = (unsigned char*)workspace;
   if (c->layout == HAD) {   // the chunk's rows in the rotated basis, as the window keeps its rows
@@ -643,5 +672,6 @@ extern "C" kvq_status kvq_prefill_full_then_store(const kvq_cache* c, const floa
   // the store follows the attention on the stream: it rewrites window slots the prefix was read from
   if ((st = kvq_store_chunk(c, k_new, v_new, batch, n_q, q_start, block_table, max_pages, max_seq_len, stream)) != KVQ_OK)
     return st;
-  return launch_reduce(c, out, batch, n_q * Hq, q_start, a.nc1, kPrefillChunk, (const float*)workspace, s, true);
+  return launch_reduce(c, out, batch, n_q * Hq, q_start, a.nc1, kPrefillChunk, (const float*)workspace, s, a.nwin,
+                       a.slice, causal ? n_q : 0);
 }

@@ -84,6 +84,24 @@ def test_prefill_full_then_store_matches_oracle(layout, D, prefix, n_q, n_recent
     _check_stored(c)
 
 
+@pytest.mark.parametrize("layout", ALL)
+@pytest.mark.parametrize("prefix,n_q,n_recent,causal", [([200, 30], 300, 64, True), ([0], 333, 0, True),
+                                                        ([90, 500], 260, 128, False)])
+def test_prefill_full_several_row_slices(layout, prefix, n_q, n_recent, causal):
+    """More f32 rows (window + chunk) than one slice of 128: several slice groups and partial slots,
+    rows of different windows in one batch, the causal reach per query in the reduce."""
+    U.need_gpu()
+    c = _setup(layout, 128, 2, 2, prefix, n_q, n_recent, seed=13 * layout + n_q)
+    out = kvq.prefill_full_then_store(c["cache"], c["qt"], c["kc"], c["vc"], c["qs"], c["bt"], max(c["total"]),
+                                      c["alpha"], causal=causal)
+    torch.cuda.synchronize()
+    ref = np.stack([attention.attend_prefill_full(layout, c["q"][b], c["rows_k"][b], c["rows_v"][b], c["alpha"],
+                                                  prefix[b], causal=causal, n_recent=n_recent)
+                    for b in range(len(prefix))])
+    U.assert_close_rel(out.cpu().numpy(), ref)
+    _check_stored(c)
+
+
 @pytest.mark.parametrize("layout", [spec.HAD_INT4, spec.ASYM_G32])
 @pytest.mark.parametrize("G", [1, 8])
 def test_prefill_full_not_causal_and_gqa(layout, G):
