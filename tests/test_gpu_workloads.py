@@ -164,3 +164,59 @@ def test_gemma_q6_0_ragged_b16():
     assert np.isfinite(got).all()
     for b, hk in pairs:
         _check_pair(w, got, q, b, hk, lens[b])
+
+
+def test_qwen3_hadamard_full_precision_prefill_then_store():
+    """The same 512-query chunk at 8192 through the full-precision prefill: the chunk's own rows exact,
+    the prefix as cached (packed, plus the 64-token window), then the chunk stored bit for bit."""
+    U.need_gpu()
+    w = W.WORKLOADS["qwen3_1p7b_had_s8k"]
+    S0, Sq = w.S, w.prefill_q
+    S1 = S0 + Sq
+    cache, table = _cache_for(w, [S1], 1)
+    pairs = [(0, hk) for hk in range(w.Hkv)]
+    _fill(w, cache, table, [S0], cpu_pairs=pairs)
+    k = W.kv_tokens(w, 0, 0, S1, "k")
+    v = W.kv_tokens(w, 0, 0, S1, "v")
+    qp = W.queries(w, 0, n=Sq, tag=1)[None]
+    out = kvq.prefill_full_then_store(cache, torch.from_numpy(qp).to(U.DEV), torch.from_numpy(k[None, S0:]).to(U.DEV),
+                                      torch.from_numpy(v[None, S0:]).to(U.DEV),
+                                      torch.tensor([S0], dtype=torch.int32, device=U.DEV),
+                                      torch.from_numpy(table).to(U.DEV), S1, w.alpha)
+    torch.cuda.synchronize()
+    ref = attention.attend_prefill_full(spec.HAD_INT4, qp[0], k, v, w.alpha, S0, n_recent=w.n_recent)
+    U.assert_close_rel(out[0].cpu().numpy(), ref, what="full-precision prefill")
+    for hk in (0, 5):
+        for which, x in (("k", k), ("v", v)):
+            pay, rec = U.row_bytes(cache, which, table, 0, S0, S1, hk)
+            enc = quant.encode_rows(spec.HAD_INT4, x[S0:, hk, :])
+            np.testing.assert_array_equal(pay, enc["payload"])
+            np.testing.assert_array_equal(rec.reshape(-1), enc["record"].reshape(-1))
+
+
+@pytest.mark.parametrize("mode", ["q8_0", "float_q"])
+def test_llama31_70b_128k_next_modes(mode):
+    """The 128K Llama-3.1-70B shape in the q8_0 layout, and in the float-query mode on its own layout;
+    sampled (batch row, kv head) pairs against the oracle."""
+    import dataclasses
+    U.need_gpu()
+    w = W.WORKLOADS["llama31_70b_asym_s128k"]
+    if mode == "q8_0":
+        w = dataclasses.replace(w, layout="q8_0")
+    B, pairs = 2, [(0, 3), (1, 6)]
+    lens = [w.S] * B
+    cache, table = _cache_for(w, lens, B)
+    seq = _fill(w, cache, table, lens, cpu_pairs=pairs, gen_seed=11)
+    q = np.stack([W.queries(w, b)[0] for b in range(B)])
+    fq = mode == "float_q"
+    out = kvq.attend_decode(cache, torch.from_numpy(q).to(U.DEV), torch.from_numpy(table).to(U.DEV), seq, w.S,
+                            w.alpha, chunk_tokens=w.chunk_tokens, float_q=fq)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    for b, hk in pairs:
+        kk = W.kv_rows(w, b, hk, 0, w.S, "k")[:, None, :]
+        vv = W.kv_rows(w, b, hk, 0, w.S, "v")[:, None, :]
+        hs = slice(hk * w.G, (hk + 1) * w.G)
+        ref = attention.attend_decode(LAYOUT[w.layout], q[b, hs], kk, vv, w.alpha, float_q=fq)
+        U.assert_close_rel(got[b, hs], ref, what=f"{mode} b{b} hk{hk}")
