@@ -289,11 +289,25 @@ def time_decode(w, B, chunk, steps, warmup, layers, dev, seed):
     total_ms = t0.elapsed_time(t1)
     part_ms = [a.elapsed_time(b) for a, b in evs]
     assert torch.isfinite(out).all(), "non-finite attention output"
+    # read probe: the same layers' planes (the algorithmic bytes of one launch) read once each
+    planes = lambda c: (c.k_payload, c.v_payload, c.k_scale, c.v_scale)
+    for i in range(warmup):
+        kvq.debug_stream_read(planes(caches[i % L]))
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record()
+    for i in range(steps):
+        kvq.debug_stream_read(planes(caches[i % L]))
+    p1.record()
+    torch.cuda.synchronize()
+    probe_us = p0.elapsed_time(p1) * 1e3 / steps
     del caches
     torch.cuda.empty_cache()
+    srt = sorted(part_ms)
     return dict(bytes_layer=bytes_layer, layers=L, ms_per_step=total_ms / steps, wall_s=wall,
                 partial_ms_mean=sum(part_ms) / len(part_ms), partial_ms_min=min(part_ms),
-                partial_ms_median=sorted(part_ms)[len(part_ms) // 2])
+                partial_ms_median=srt[len(srt) // 2], partial_ms_p10=srt[len(srt) // 10],
+                partial_ms_p90=srt[min(len(srt) - 1, (9 * len(srt)) // 10)], probe_us=probe_us)
 
 
 def cpu_baseline(w, kv_heads):
@@ -372,8 +386,16 @@ def main():
                      "traffic": measured_traffic() if (a.batch, a.chunk) == (8, 512) else None, "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + "
                      "WRITE_SIZE, copy-calibrated; null if the kernel changed since)",
                      "avg_launch_us": round(r["partial_ms_mean"] * 1e3, 2),
-                     "min_launch_us": round(r["partial_ms_min"] * 1e3, 2)},
+                     "min_launch_us": round(r["partial_ms_min"] * 1e3, 2),
+                     "median_launch_us": round(r["partial_ms_median"] * 1e3, 2),
+                     "p10_launch_us": round(r["partial_ms_p10"] * 1e3, 2),
+                     "p90_launch_us": round(r["partial_ms_p90"] * 1e3, 2)},
     }
+    probe_gbs = r["bytes_layer"] / (r["probe_us"] * 1e-6) / 1e9
+    extra["read_probe"] = dict(gbs=round(probe_gbs, 1), us_per_layer=round(r["probe_us"], 2),
+                               bytes_per_layer=r["bytes_layer"], decode_partial_frac_of_probe=round(ach / probe_gbs, 4),
+                               kernel="kvq_debug_stream_read: the layer's four planes read once, in one launch, "
+                                      "with the decode's direct-to-LDS 16-byte nontemporal loads")
     if extra:
         line["extra"] = extra
     if not a.no_cpu_baseline:

@@ -265,6 +265,15 @@ kvq_status kvq_prefill_full_then_store(const kvq_cache* cache, const float* q, c
                                        int32_t max_pages_per_seq, int32_t max_seq_len,
                                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Read-only streaming probe (measurement, not part of the method): reads n
+ * (1..4) device buffers src[i] of bytes[i] bytes (host arrays) once, in one
+ * launch across the whole device, with the direct-to-LDS 16-byte nontemporal
+ * loads the decode kernel streams with (the data lands in LDS that nothing
+ * reads).  Buffers and sizes must be 16-byte aligned.  The bench times it over
+ * a layer's four planes: the attainable HBM read rate for those bytes, which
+ * the decode kernel's rate is compared with. */
+kvq_status kvq_debug_stream_read(int32_t n, const void* const* src, const size_t* bytes, void* stream);
+
 /* Test exports for the bit-exact gates. */
 
 /* Query preparation of the attention kernels: rotation (HAD_INT4 only) and

@@ -35,6 +35,7 @@ SIGNATURES = {
     "kvq_payload_bytes": (c_size, [c_i32, c_i32]),
     "kvq_scale_bytes": (c_size, [c_i32, c_i32]),
     "kvq_store": (c_i32, [P, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "kvq_debug_stream_read": (c_i32, [c_i32, c_vp, c_vp, c_vp]),
     "kvq_store_chunk": (c_i32, [P, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp]),
     "kvq_prefill_full_then_store": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_f, c_i32, c_vp,
                                             c_vp, c_i32, c_i32, c_vp, c_size, c_vp]),

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkvq.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["kvq_api.hip", "kvq_store.hip", "kvq_attend.hip", "kvq_prefill.hip"]
+SOURCES = ["kvq_api.hip", "kvq_store.hip", "kvq_attend.hip", "kvq_prefill.hip", "kvq_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

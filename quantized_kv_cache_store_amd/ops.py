@@ -274,6 +274,19 @@ def debug_quantize_q(layout, q):
     return q8, sq
 
 
+def debug_stream_read(bufs):
+    """kvq_debug_stream_read: read every byte of up to four contiguous device tensors once, in one
+    launch (the read probe)."""
+    bufs = list(bufs)
+    if not 1 <= len(bufs) <= 4 or any(not b.is_cuda or not b.is_contiguous() for b in bufs):
+        raise ValueError("one to four contiguous device tensors")
+    src = (ctypes.c_void_p * len(bufs))(*[b.data_ptr() for b in bufs])
+    nbytes = (ctypes.c_size_t * len(bufs))(*[b.numel() * b.element_size() for b in bufs])
+    st = load().kvq_debug_stream_read(len(bufs), ctypes.cast(src, ctypes.c_void_p), ctypes.cast(nbytes, ctypes.c_void_p),
+                                      _stream(bufs[0].device))
+    check("kvq_debug_stream_read", st)
+
+
 def debug_qk_i32(cache, q, block_table, seq_len, max_seq_len):
     """kvq_debug_qk_i32: the decode kernel's per-block i32 scores [B, Hq, max_seq_len, n_groups]."""
     dev = cache.device
