@@ -77,7 +77,7 @@ template <int L, int D>
 struct PrefillShape {
   using ST = Step<L, D, true>;
   static constexpr int OPS = 2 * PStep<L, D>::BYTES;        // the two operand buffers
-  static constexpr int BUDGET = D == 128 ? 54613 : 81920;     // three (two) blocks per CU
+  static constexpr int BUDGET = 81920;                          // two blocks per CU
   static constexpr int NR_FIT = (BUDGET - OPS) / (2 * ST::HALF);
   static constexpr int NR = NR_FIT < 2 ? 2 : (NR_FIT > 6 ? 6 : NR_FIT);
   static constexpr int LDS = OPS + NR * 2 * ST::HALF;
@@ -221,108 +221,127 @@ __device__ __forceinline__ void prefill_produce(unsigned char* buf, int tid, con
   if (tid < 8 * SB) *reinterpret_cast<uint32_t*>(buf + PS::KR + 4 * tid) = ld.kr;
 }
 
-// One step of one wave: Q K^T for the wave's 16 rows, online softmax, P V.
-// FULL: all 32 tokens exist and every row of the tile sees them.
-template <int L, int D, bool FULL>
-__device__ __forceinline__ void prefill_consume(const unsigned char* buf, int lane, int T0, int n_tok, int lim,
-                                                const uint32_t (*qb)[2], const float* qsB, int qoff0, float sqc,
-                                                float& m_run, float& l_run, v4f* oacc) {
+// One step of one wave: Q K^T for the wave's TPW tiles of 16 rows, online softmax, P V.  Each V^T
+// operand read from LDS serves every tile of the wave.
+// FULL: all 32 tokens exist and every row of the wave sees them.
+template <int L, int D, bool FULL, int TPW>
+__device__ __forceinline__ void prefill_consume(const unsigned char* buf, int lane, int T0, int n_tok, const int* lim,
+                                                const long (*qb)[D / 32], const float (*qsB)[(D / 32 + 3) / 4],
+                                                const int* qoff0, const float* sqc, float* m_run, float* l_run,
+                                                v4f (*oacc)[D / 16]) {
   using T = Layout<L, D>;
   using PS = PStep<L, D>;
   constexpr int NG = T::NG, SG = T::SG, SB = T::SB;
   const int col = lane & 15, r = lane >> 4;
-  float xs[8];
+  // Q K^T one tile after the other (its accumulators die with the tile's scores); the K codes are
+  // read again for the second tile, which costs less than keeping both tiles' accumulators live
+  float xs[TPW][8];
 #pragma unroll
-  for (int tau = 0; tau < 2; ++tau) {
-    v4i acc[SG];
+  for (int u = 0; u < TPW; ++u) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const uint2 w = *reinterpret_cast<const uint2*>(buf + PS::KC + ((g * 2 + tau) * 64 + lane) * 8);
-      const long A = (long)((uint64_t)w.x | ((uint64_t)w.y << 32));
-      const long B = (long)((uint64_t)qb[g][0] | ((uint64_t)qb[g][1] << 32));
-      if (L == HAD)
-        acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[0], 0, 0, 0);
-      else
-        acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
-    }
-    v4f xo = v4f{0.f, 0.f, 0.f, 0.f};
-    if (L != HAD && L != Q80) {   // the 8-bit K codes carry no offset
-      // offset term sum_g c_g(t) qsum_g: A[t = col][k = r] from the record of token 16 tau + col
-      const unsigned char* orec = buf + PS::KR + (16 * tau + col) * SB;
+    for (int tau = 0; tau < 2; ++tau) {
+      v4i acc[SG];
 #pragma unroll
-      for (int i = 0; i < NG / 4; ++i) {
-        const _Float16* h = reinterpret_cast<const _Float16*>(orec);
-        const float av = (L == ASYM) ? (float)h[2 * (4 * i + r) + 1] : (float)h[4 * i + r];
-        xo = __builtin_amdgcn_mfma_f32_16x16x4f32(av, qsB[i], xo, 0, 0, 0);
+      for (int g = 0; g < NG; ++g) {
+        const uint2 w = *reinterpret_cast<const uint2*>(buf + PS::KC + ((g * 2 + tau) * 64 + lane) * 8);
+        const long A = (long)((uint64_t)w.x | ((uint64_t)w.y << 32));
+        if (L == HAD)
+          acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, qb[u][g], g == 0 ? v4i{0, 0, 0, 0} : acc[0], 0, 0, 0);
+        else
+          acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, qb[u][g], v4i{0, 0, 0, 0}, 0, 0, 0);
       }
-    }
+      v4f xo = v4f{0.f, 0.f, 0.f, 0.f};
+      if (L != HAD && L != Q80) {   // the 8-bit K codes carry no offset
+        // offset term sum_g c_g(t) qsum_g: A[t = col][k = r] from the record of token 16 tau + col
+        const unsigned char* orec = buf + PS::KR + (16 * tau + col) * SB;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tl = 16 * tau + 4 * r + j;
-      const bool vis = FULL || (tl < n_tok && T0 + tl <= lim);
-      const unsigned char* rec = buf + PS::KR + tl * SB;
-      float x;
-      if (L == HAD) {
-        x = (float)(acc[0][j] - qoff0) * *reinterpret_cast<const float*>(rec);
-      } else {
-        x = xo[j];
-#pragma unroll
-        for (int g = 0; g < SG; ++g) {
-          const uint32_t w = reinterpret_cast<const uint32_t*>(rec)[(L == ASYM) ? g : (g >> 1)];
-          const float s = (float)as_h2(w)[(L == ASYM) ? 0 : (g & 1)];
-          x = fmaf(s, (float)acc[g][j], x);
+        for (int i = 0; i < NG / 4; ++i) {
+          const _Float16* h = reinterpret_cast<const _Float16*>(orec);
+          const float av = (L == ASYM) ? (float)h[2 * (4 * i + r) + 1] : (float)h[4 * i + r];
+          xo = __builtin_amdgcn_mfma_f32_16x16x4f32(av, qsB[u][i], xo, 0, 0, 0);
         }
       }
-      xs[tau * 4 + j] = vis ? x * sqc : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tl = 16 * tau + 4 * r + j;
+        const unsigned char* rec = buf + PS::KR + tl * SB;
+        const bool vis = FULL || (tl < n_tok && T0 + tl <= lim[u]);
+        float x;
+        if (L == HAD) {
+          x = (float)(acc[0][j] - qoff0[u]) * *reinterpret_cast<const float*>(rec);
+        } else {
+          x = xo[j];
+#pragma unroll
+          for (int g = 0; g < SG; ++g) {
+            const uint32_t w = reinterpret_cast<const uint32_t*>(rec)[(L == ASYM) ? g : (g >> 1)];
+            const float sc = (float)as_h2(w)[(L == ASYM) ? 0 : (g & 1)];
+            x = fmaf(sc, (float)acc[g][j], x);
+          }
+        }
+        xs[u][tau * 4 + j] = vis ? x * sqc[u] : -INFINITY;
+      }
     }
   }
 
-  float smax = xs[0];
+  v8h pB[TPW];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) smax = fmaxf(smax, xs[i]);
-  smax = max_over_rows(smax);
-  const float m_new = fmaxf(m_run, smax);
-  const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-  if (__any(m_new > m_run)) {
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
-    l_run *= corr;
+  for (int u = 0; u < TPW; ++u) {
+    float smax = xs[u][0];
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) oacc[i] *= corr;
+    for (int i = 1; i < 8; ++i) smax = fmaxf(smax, xs[u][i]);
+    smax = max_over_rows(smax);
+    const float m_new = fmaxf(m_run[u], smax);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    if (__any(m_new > m_run[u])) {
+      const float corr = __builtin_amdgcn_exp2f(m_run[u] - m_use);
+      l_run[u] *= corr;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) oacc[u][i] *= corr;
+    }
+    m_run[u] = m_new;
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = __builtin_amdgcn_exp2f(xs[u][i] - m_use);
+      psum += p;
+      pB[u][i] = (_Float16)p;
+    }
+    l_run[u] += psum;
   }
-  m_run = m_new;
-  float psum = 0.0f;
-  v8h pB;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float p = __builtin_amdgcn_exp2f(xs[i] - m_use);
-    psum += p;
-    pB[i] = (_Float16)p;
-  }
-  l_run += psum;
 
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
     const v8h A = *reinterpret_cast<const v8h*>(buf + PS::VT + (dt * 64 + lane) * 16);
-    oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pB, oacc[dt], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) oacc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pB[u], oacc[u][dt], 0, 0, 0);
   }
 }
 
-// Grid: one block per (batch row, kv head, group, 64-row block), the groups being the chunks of
-// the quantised region and, when n_recent > 0, the window.
+// Grid: one block per (batch row, kv head, group, block of BR rows), the groups being the chunks
+// of the quantised region and, when n_recent > 0, the window.  Each wave takes TPW consecutive
+// 16-row tiles of the block (two at head_dim 128, so that the block's shared unpacking and
+// dequantisation serve 128 rows; one at 256 and for q6_0, where the registers would not hold it).
 // The rows' int8 queries, scales and block sums come prepared by prepare_rows.
 template <int L, int D>
-__global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendArgs a) {
+struct PrefillTiles {
+  static constexpr int TPW = (D == 128 && L != Q60) ? 2 : 1;   // 16-row tiles per wave
+  static constexpr int BR = 64 * TPW;                          // rows per block
+};
+
+template <int L, int D>
+__global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
   using T = Layout<L, D>;
   using PS = PStep<L, D>;
   constexpr int NG = T::NG;
   constexpr int BIAS = CodeBias<L>::k_side;
+  constexpr int TPW = PrefillTiles<L, D>::TPW, BR = PrefillTiles<L, D>::BR;
   extern __shared__ __align__(16) unsigned char smem[];
 
   // One-dimensional grid in an XCD-aware order: the chip hands consecutive blocks round robin to
   // its 8 XCDs (block id runs on XCD id % 8), so virtual index v gives each XCD a contiguous
-  // range, and v puts the 64-row blocks of one (batch row, kv head, chunk) next to each other:
+  // range, and v puts the row blocks of one (batch row, kv head, chunk) next to each other:
   // they read the same K/V, which their XCD's L2 then holds for all of them.
-  const int nrb = (a.n_q * a.G + 63) / 64;
+  const int nrb = (a.n_q * a.G + BR - 1) / BR;
   const int id = (int)blockIdx.x, nblocks = (int)gridDim.x;
   const int v = (nblocks % 8 == 0) ? (id % 8) * (nblocks / 8) + id / 8 : id;
   const int rb = v % nrb;
@@ -332,28 +351,33 @@ __global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendA
   const int S = a.seq_len[b];
   const int Sq = a.n_recent > 0 ? max(0, S - a.n_recent) : S;
   const int nrows = a.n_q * a.G;
-  const int row0 = 64 * rb;
-  const int nblk = min(64, nrows - row0);
+  const int row0 = BR * rb;
+  const int nblk = min(BR, nrows - row0);
   const int qs0 = a.causal ? a.q_start[b] : 0;
   // the last groups: f32 rows (the window; for the full-precision prefill also the chunk's own rows,
   // in a.nwin slices of a.slice rows)
   const int nwg = a.kchunk ? a.nwin : (a.n_recent > 0 ? 1 : 0);
   const int nch = a.ngroups - nwg;
-  if (c >= nch) {   // f32-row block: wave w takes the 16-row tile 16 w of the 64 rows
-    const int w = threadIdx.x >> 6, nv = min(16, nblk - 16 * w);
+  if (c >= nch) {   // f32-row block: wave w takes the 16-row tiles TPW w .. TPW w + TPW - 1
+    const int w = threadIdx.x >> 6;
     const int j = c - nch;
-    bool run = (S > 0 || a.kchunk) && nv > 0;
-    if (a.kchunk && run) {   // a slice past every limit of the wave's rows: the reduce does not read it
-      const int lmax = row_limit(a, qs0, row0 + 16 * w + nv - 1, nrows);
-      run = j * a.slice <= lmax - (S - min(S, a.n_recent));
-    }
-    if (run) {
-      const int k0 = a.kchunk ? j * (a.slice / 16) : 0;
-      const int kend = a.kchunk ? k0 + a.slice / 16 : 0x7fffffff;
-      WinState<D> st;
-      window_wave<L, D>(a, reinterpret_cast<float*>(smem + w * window_wave_lds<D>()), b, hk, S, row0 + 16 * w, nv, qs0, k0, 1,
-                        threadIdx.x & 63, st, kend);
-      window_store<D>(a, st, b, hk, row0 + 16 * w, nv, threadIdx.x & 63, a.nc1 - a.nwin + j);
+#pragma unroll 1
+    for (int u = 0; u < TPW; ++u) {
+      const int trow = row0 + 16 * (TPW * w + u);
+      const int nv = min(16, nblk - 16 * (TPW * w + u));
+      bool run = (S > 0 || a.kchunk) && nv > 0;
+      if (a.kchunk && run) {   // a slice past every limit of the tile's rows: the reduce does not read it
+        const int lmax = row_limit(a, qs0, trow + nv - 1, nrows);
+        run = j * a.slice <= lmax - (S - min(S, a.n_recent));
+      }
+      if (run) {
+        const int k0 = a.kchunk ? j * (a.slice / 16) : 0;
+        const int kend = a.kchunk ? k0 + a.slice / 16 : 0x7fffffff;
+        WinState<D> st;
+        window_wave<L, D>(a, reinterpret_cast<float*>(smem + w * window_wave_lds<D>()), b, hk, S, trow, nv, qs0, k0, 1,
+                          threadIdx.x & 63, st, kend);
+        window_store<D>(a, st, b, hk, trow, nv, threadIdx.x & 63, a.nc1 - a.nwin + j);
+      }
     }
     return;
   }
@@ -368,39 +392,59 @@ __global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendA
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, r = lane >> 4;
-  const int wrow0 = row0 + 16 * wave;
-  const int nval = min(16, max(0, nblk - 16 * wave));
-
-  // ---- prologue: this wave's 16 rows from the prepared rows (int8 query in the B-operand order,
-  // its scale and block sums); the perms consume the loads here, outside the streaming loop
-  uint32_t qb[NG][2] = {};
-  float qsB[NG / 4] = {};
-  int qoff0 = 0;
-  float sqc = 0.0f;
-  if (col < nval) {
-    const size_t fr = row_index(a, b, hk, wrow0 + col);
+  const int wrow0 = row0 + 16 * TPW * wave;            // the wave's first row
+  int nval[TPW];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const uint2 w = *reinterpret_cast<const uint2*>(a.q8p + fr * D + 32 * g + 8 * r);
-      qb[g][0] = L == Q80 ? w.x : __builtin_amdgcn_perm(w.y, w.x, 0x06040200u);
-      qb[g][1] = L == Q80 ? w.y : __builtin_amdgcn_perm(w.y, w.x, 0x07050301u);
+  for (int u = 0; u < TPW; ++u) nval[u] = min(16, max(0, nblk - 16 * (TPW * wave + u)));
+
+  // ---- prologue: this wave's rows from the prepared rows (int8 query in the B-operand order, its
+  // scale and block sums); the perms consume the loads here, outside the streaming loop
+  constexpr int NQ = (NG + 3) / 4;
+  long qb[TPW][NG];
+  float qsB[TPW][NQ];
+  int qoff0[TPW], lim[TPW];
+  float sqc[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int trow = wrow0 + 16 * u;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) qb[u][g] = 0;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) qsB[u][i] = 0.0f;
+    qoff0[u] = 0;
+    sqc[u] = 0.0f;
+    if (col < nval[u]) {
+      const size_t fr = row_index(a, b, hk, trow + col);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const uint2 w = *reinterpret_cast<const uint2*>(a.q8p + fr * D + 32 * g + 8 * r);
+        const uint32_t lo = L == Q80 ? w.x : __builtin_amdgcn_perm(w.y, w.x, 0x06040200u);
+        const uint32_t hi = L == Q80 ? w.y : __builtin_amdgcn_perm(w.y, w.x, 0x07050301u);
+        qb[u][g] = __builtin_bit_cast(long, u32x2{lo, hi});
+      }
+      const int* qs = a.qsump + fr * NG;
+#pragma unroll
+      for (int i = 0; i < NG / 4; ++i)
+        qsB[u][i] = (L == ASYM) ? (float)qs[4 * i + r] : -(float)BIAS * (float)qs[4 * i + r];
+      int tot = 0;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) tot += qs[g];
+      qoff0[u] = BIAS * tot;
+      sqc[u] = a.sqp[fr] * a.alpha * KVQ_LOG2E;
     }
-    const int* qs = a.qsump + fr * NG;
-#pragma unroll
-    for (int i = 0; i < NG / 4; ++i) qsB[i] = (L == ASYM) ? (float)qs[4 * i + r] : -(float)BIAS * (float)qs[4 * i + r];
-    int tot = 0;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) tot += qs[g];
-    qoff0 = BIAS * tot;
-    sqc = a.sqp[fr] * a.alpha * KVQ_LOG2E;
+    lim[u] = row_limit(a, qs0, trow + col, nrows);
   }
-  const int lim = row_limit(a, qs0, wrow0 + col, nrows);
-  const int lim_min = row_limit(a, qs0, wrow0, nrows);   // -1 for a wave without rows
+  const int lim_min = row_limit(a, qs0, wrow0, nrows);   // the wave's smallest limit; -1 without rows
 
-  float m_run = -INFINITY, l_run = 0.0f;
-  v4f oacc[D / 16];
+  float m_run[TPW], l_run[TPW];
+  v4f oacc[TPW][D / 16];
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) oacc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < TPW; ++u) {
+    m_run[u] = -INFINITY;
+    l_run[u] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) oacc[u][i] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
   uint32_t magic;   // fp16 "1024 + code" exponent bits, in a VGPR so v_and_or_b32 can take it
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
@@ -461,26 +505,33 @@ __global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_partial(AttendA
     }
     const unsigned char* buf = smem + (s & 1) * PS::BYTES;
     const int n_tok = min(32, t_end - T0);
-    if (nval > 0) {
+    if (nval[0] > 0) {
       if (n_tok == 32 && T0 + 31 <= lim_min)
-        prefill_consume<L, D, true>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, oacc);
+        prefill_consume<L, D, true, TPW>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, oacc);
       else
-        prefill_consume<L, D, false>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, oacc);
+        prefill_consume<L, D, false, TPW>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, oacc);
     }
   }
 
-  // ---------------- this wave's chunk partial: o[d = 16 dt + 4 r + j] of row col
-  l_run = sum_over_rows(l_run);
-  if (col < nval) {
-    float* dst = a.ws + (row_index(a, b, hk, wrow0 + col) * a.nc1 + c) * partial_stride(D);
+  // ---------------- this wave's chunk partials: o[d = 16 dt + 4 r + j] of row col of each tile
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<v4f*>(dst + 16 * dt + 4 * r) = oacc[dt];
-    if (r == 0) {
-      dst[D] = m_run;
-      dst[D + 1] = l_run;
+  for (int u = 0; u < TPW; ++u) {
+    const float l = sum_over_rows(l_run[u]);
+    if (col < nval[u]) {
+      float* dst = a.ws + (row_index(a, b, hk, wrow0 + 16 * u + col) * a.nc1 + c) * partial_stride(D);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<v4f*>(dst + 16 * dt + 4 * r) = oacc[u][dt];
+      if (r == 0) {
+        dst[D] = m_run[u];
+        dst[D + 1] = l;
+      }
     }
   }
 }
+
+static inline int prefill_rows_per_block(int layout, int D) { return (D == 128 && layout != Q60) ? 128 : 64; }
+static_assert(PrefillTiles<HAD, 128>::BR == 128 && PrefillTiles<Q60, 128>::BR == 64 && PrefillTiles<Q40, 256>::BR == 64,
+              "rows per block as the host computes them");
 
 // Query preparation of every row once (a1), 16 rows per block: int8 query, scale, per-block sums,
 // and for the Hadamard layout the rotated f32 query the window uses.
@@ -602,7 +653,8 @@ extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float*
   a.q_start = causal ? q_start : nullptr;
   const int nch = chunks_of(max_seq_len, kPrefillChunk);
   a.ngroups = nch + (c->n_recent > 0 ? 1 : 0);
-  const int64_t gx = ((int64_t)n_q * a.G + 63) / 64 * a.ngroups * c->num_kv_heads * batch;
+  const int64_t gx = ((int64_t)n_q * a.G + prefill_rows_per_block(c->layout, c->head_dim) - 1) / prefill_rows_per_block(c->layout, c->head_dim) *
+                     a.ngroups * c->num_kv_heads * batch;
   if (gx > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
   const int rows = batch * n_q * Hq;
   const RowPrep w = prefill_ws((size_t)rows, c->head_dim, a.nc1);
@@ -643,7 +695,8 @@ extern "C" kvq_status kvq_prefill_full_then_store(const kvq_cache* c, const floa
   // the last groups: slices of the window and chunk rows, each of at least kRowSlice rows, and as
   // many as bring the grid to about 4096 blocks
   const int nf32 = min(c->n_recent, max_seq_len) + n_q;
-  const int64_t row_blocks = ((int64_t)n_q * a.G + 63) / 64 * c->num_kv_heads * batch;
+  const int64_t row_blocks = ((int64_t)n_q * a.G + prefill_rows_per_block(c->layout, c->head_dim) - 1) /
+                             prefill_rows_per_block(c->layout, c->head_dim) * c->num_kv_heads * batch;
   const int64_t want = (4096 + row_blocks - 1) / row_blocks;
   int slice = (int)((nf32 + want - 1) / want);
   slice = max(kRowSlice, (slice + 15) / 16 * 16);
@@ -651,7 +704,8 @@ extern "C" kvq_status kvq_prefill_full_then_store(const kvq_cache* c, const floa
   a.nwin = (nf32 + slice - 1) / slice;
   a.nc1 = nch + a.nwin;
   a.ngroups = nch + a.nwin;
-  const int64_t gx = ((int64_t)n_q * a.G + 63) / 64 * a.ngroups * c->num_kv_heads * batch;
+  const int64_t gx = ((int64_t)n_q * a.G + prefill_rows_per_block(c->layout, c->head_dim) - 1) / prefill_rows_per_block(c->layout, c->head_dim) *
+                     a.ngroups * c->num_kv_heads * batch;
   if (gx > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
   const int rows = batch * n_q * Hq;
   const RowPrep w = prefill_ws((size_t)rows, c->head_dim, a.nc1);
