@@ -38,6 +38,8 @@ struct AttendArgs {
   int nwin;      // partial slots of the f32 rows, the last nwin of a row's nc1 (full-precision prefill: one
                  // per slice of its f32 rows; else 1)
   int slice;     // full-precision prefill: f32 rows per slice (a multiple of 16)
+  int nwg;       // prefill: groups of f32 rows at the end of the prefill kernel's grid (0: none, or their
+                 // own launch)
   int n_q;       // queries per batch row (1 for decode)
   int batch;     // batch rows (decode: the grid is one-dimensional)
   int ngroups;   // blocks per row tile along the sequence: chunk groups of four, + 1 for the window

@@ -317,8 +317,9 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
   }
 }
 
-// Grid: one block per (batch row, kv head, group, block of BR rows), the groups being the chunks
-// of the quantised region and, when n_recent > 0, the window.  Each wave takes TPW consecutive
+// Grid: one block per (batch row, kv head, group, block of BR rows), the groups being the chunks of
+// the quantised region and then a.nwg groups of f32 rows (window, chunk rows; a prefill without
+// packed chunks runs them through prefill_rows_f32 instead).  Each wave takes TPW consecutive
 // 16-row tiles of the block (two at head_dim 128, so that the block's shared unpacking and
 // dequantisation serve 128 rows; one at 256 and for q6_0, where the registers would not hold it).
 // The rows' int8 queries, scales and block sums come prepared by prepare_rows.
@@ -354,10 +355,9 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
   const int row0 = BR * rb;
   const int nblk = min(BR, nrows - row0);
   const int qs0 = a.causal ? a.q_start[b] : 0;
-  // the last groups: f32 rows (the window; for the full-precision prefill also the chunk's own rows,
-  // in a.nwin slices of a.slice rows)
-  const int nwg = a.kchunk ? a.nwin : (a.n_recent > 0 ? 1 : 0);
-  const int nch = a.ngroups - nwg;
+  // the last a.nwg groups of this grid (if any): f32 rows (the window; for the full-precision prefill
+  // also the chunk's own rows, in a.nwin slices of a.slice rows)
+  const int nch = a.ngroups - a.nwg;
   if (c >= nch) {   // f32-row block: wave w takes the 16-row tiles TPW w .. TPW w + TPW - 1
     const int w = threadIdx.x >> 6;
     const int j = c - nch;
@@ -529,6 +529,43 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
   }
 }
 
+// The f32 rows of a full-precision prefill without a cached prefix: its chunk's own rows in a.nwin
+// slices of a.slice rows.  A launch of its own, which needs fewer registers than prefill_partial and
+// runs at a higher occupancy (with packed chunks to stream, the f32 rows instead share
+// prefill_partial's grid, whose tail they fill).  Grid: one block per (batch row, kv head,
+// slice, block of 64 rows), in the XCD-aware order of prefill_partial; wave w takes the 16-row
+// tile 16 w of the block.
+template <int L, int D>
+__global__ __launch_bounds__(256, D == 128 ? 4 : 2) void prefill_rows_f32(AttendArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nrb = (a.n_q * a.G + 63) / 64;
+  const int id = (int)blockIdx.x, nblocks = (int)gridDim.x;
+  const int v = (nblocks % 8 == 0) ? (id % 8) * (nblocks / 8) + id / 8 : id;
+  const int rb = v % nrb;
+  const int rest = v / nrb;
+  const int j = rest % a.nwin;
+  const int hk = (rest / a.nwin) % a.Hkv, b = rest / a.nwin / a.Hkv;
+  const int S = a.seq_len[b];
+  const int nrows = a.n_q * a.G;
+  const int qs0 = a.causal ? a.q_start[b] : 0;
+  const int w = threadIdx.x >> 6;
+  const int trow = 64 * rb + 16 * w;
+  const int nv = min(16, nrows - trow);
+  bool run = (S > 0 || a.kchunk) && nv > 0;
+  if (a.kchunk && run) {   // a slice past every limit of the tile's rows: the reduce does not read it
+    const int lmax = row_limit(a, qs0, trow + nv - 1, nrows);
+    run = j * a.slice <= lmax - (S - min(S, a.n_recent));
+  }
+  if (run) {
+    const int k0 = a.kchunk ? j * (a.slice / 16) : 0;
+    const int kend = a.kchunk ? k0 + a.slice / 16 : 0x7fffffff;
+    WinState<D> st;
+    window_wave<L, D>(a, reinterpret_cast<float*>(smem + w * window_wave_lds<D>()), b, hk, S, trow, nv, qs0, k0, 1,
+                      threadIdx.x & 63, st, kend);
+    window_store<D>(a, st, b, hk, trow, nv, threadIdx.x & 63, a.nc1 - a.nwin + j);
+  }
+}
+
 static inline int prefill_rows_per_block(int layout, int D) { return (D == 128 && layout != Q60) ? 128 : 64; }
 static_assert(PrefillTiles<HAD, 128>::BR == 128 && PrefillTiles<Q60, 128>::BR == 64 && PrefillTiles<Q40, 256>::BR == 64,
               "rows per block as the host computes them");
@@ -576,16 +613,24 @@ static prepare_fn pick_prepare(int layout, int D) {
                        : (D == 256 ? launch_prepare<Q40, 256> : launch_prepare<Q40, 128>);
 }
 
+// f32 = false: the packed chunks (prefill_partial); f32 = true: the f32 rows (prefill_rows_f32).
 template <int L, int D>
-static void launch_prefill(const AttendArgs& a, dim3 grid, int n_recent, hipStream_t st) {
+static void launch_prefill(const AttendArgs& a, dim3 grid, bool f32, hipStream_t st) {
+  if (f32) {
+    const size_t lds = window_lds_bytes<D>();
+    if (lds > 65536)
+      (void)hipFuncSetAttribute((const void*)prefill_rows_f32<L, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL((prefill_rows_f32<L, D>), grid, dim3(256), lds, st, a);
+    return;
+  }
   size_t lds = PrefillShape<L, D>::LDS;
-  if (n_recent > 0 && (size_t)window_lds_bytes<D>() > lds) lds = window_lds_bytes<D>();
+  if (a.nwg > 0 && (size_t)window_lds_bytes<D>() > lds) lds = window_lds_bytes<D>();
   if (lds > 65536)
     (void)hipFuncSetAttribute((const void*)prefill_partial<L, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL((prefill_partial<L, D>), grid, dim3(256), lds, st, a);
 }
 
-typedef void (*prefill_fn)(const AttendArgs&, dim3, int, hipStream_t);
+typedef void (*prefill_fn)(const AttendArgs&, dim3, bool, hipStream_t);
 
 static prefill_fn pick_prefill(int layout, int D) {
   const int di = D == 256 ? 1 : 0;
@@ -652,16 +697,16 @@ extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float*
   a.skip = causal && !(flags & KVQ_PREFILL_NO_CAUSAL_SKIP);
   a.q_start = causal ? q_start : nullptr;
   const int nch = chunks_of(max_seq_len, kPrefillChunk);
-  a.ngroups = nch + (c->n_recent > 0 ? 1 : 0);
-  const int64_t gx = ((int64_t)n_q * a.G + prefill_rows_per_block(c->layout, c->head_dim) - 1) / prefill_rows_per_block(c->layout, c->head_dim) *
-                     a.ngroups * c->num_kv_heads * batch;
+  a.nwg = c->n_recent > 0 ? 1 : 0;   // the window: one group in the same grid
+  a.ngroups = nch + a.nwg;
+  const int64_t gx = ((int64_t)n_q * a.G + prefill_rows_per_block(c->layout, c->head_dim) - 1) /
+                     prefill_rows_per_block(c->layout, c->head_dim) * a.ngroups * c->num_kv_heads * batch;
   if (gx > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
   const int rows = batch * n_q * Hq;
   const RowPrep w = prefill_ws((size_t)rows, c->head_dim, a.nc1);
   if ((st = launch_prepare_rows(c, q, rows, (unsigned char*)workspace, w, a, (hipStream_t)stream)) != KVQ_OK) return st;
   if (gx > 0) {
-    const dim3 grid((unsigned)gx);
-    pick_prefill(c->layout, c->head_dim)(a, grid, c->n_recent, (hipStream_t)stream);
+    pick_prefill(c->layout, c->head_dim)(a, dim3((unsigned)gx), false, (hipStream_t)stream);
     if ((st = check_launch("prefill partial kernel")) != KVQ_OK) return st;
   }
   return launch_reduce(c, out, batch, n_q * Hq, seq_len, a.nc1, kPrefillChunk, (const float*)workspace,
@@ -692,21 +737,25 @@ extern "C" kvq_status kvq_prefill_full_then_store(const kvq_cache* c, const floa
   a.skip = 0;   // every packed token precedes the chunk: nothing to skip
   a.q_start = causal ? q_start : nullptr;
   const int nch = chunks_of(max_seq_len, kPrefillChunk);
-  // the last groups: slices of the window and chunk rows, each of at least kRowSlice rows, and as
-  // many as bring the grid to about 4096 blocks
+  // slices of the window and chunk rows, each of at least kRowSlice rows, and as many as bring
+  // their blocks to about 4096.  With a possible prefix (max_seq_len > n_q) they are the last groups
+  // of prefill_partial's grid, after the packed chunks; without one they are the whole work and run
+  // in prefill_rows_f32, with 64-row blocks at a higher occupancy.
+  const bool sep = max_seq_len <= n_q;
+  const int rpb = sep ? 64 : prefill_rows_per_block(c->layout, c->head_dim);
   const int nf32 = min(c->n_recent, max_seq_len) + n_q;
-  const int64_t row_blocks = ((int64_t)n_q * a.G + prefill_rows_per_block(c->layout, c->head_dim) - 1) /
-                             prefill_rows_per_block(c->layout, c->head_dim) * c->num_kv_heads * batch;
+  const int64_t row_blocks = ((int64_t)n_q * a.G + rpb - 1) / rpb * c->num_kv_heads * batch;
   const int64_t want = (4096 + row_blocks - 1) / row_blocks;
   int slice = (int)((nf32 + want - 1) / want);
   slice = max(kRowSlice, (slice + 15) / 16 * 16);
   a.slice = slice;
   a.nwin = (nf32 + slice - 1) / slice;
   a.nc1 = nch + a.nwin;
-  a.ngroups = nch + a.nwin;
-  const int64_t gx = ((int64_t)n_q * a.G + prefill_rows_per_block(c->layout, c->head_dim) - 1) / prefill_rows_per_block(c->layout, c->head_dim) *
-                     a.ngroups * c->num_kv_heads * batch;
-  if (gx > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
+  a.nwg = sep ? 0 : a.nwin;
+  a.ngroups = sep ? 0 : nch + a.nwin;
+  const int64_t gx = sep ? 0 : row_blocks * a.ngroups;
+  const int64_t gw = sep ? row_blocks * a.nwin : 0;
+  if (gx > 0x7fffffff || gw > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
   const int rows = batch * n_q * Hq;
   const RowPrep w = prefill_ws((size_t)rows, c->head_dim, a.nc1);
   hipStream_t s = (hipStream_t)stream;
@@ -721,8 +770,14 @@ extern "C" kvq_status kvq_prefill_full_then_store(const kvq_cache* c, const floa
     a.vchunk = v_new;
   }
   if ((st = launch_prepare_rows(c, q, rows, wsb, w, a, s)) != KVQ_OK) return st;
-  pick_prefill(c->layout, c->head_dim)(a, dim3((unsigned)gx), 1 /* the f32-row group runs: its LDS */, s);
-  if ((st = check_launch("prefill partial kernel")) != KVQ_OK) return st;
+  if (gx > 0) {
+    pick_prefill(c->layout, c->head_dim)(a, dim3((unsigned)gx), false, s);
+    if ((st = check_launch("prefill partial kernel")) != KVQ_OK) return st;
+  }
+  if (gw > 0) {
+    pick_prefill(c->layout, c->head_dim)(a, dim3((unsigned)gw), true, s);
+    if ((st = check_launch("prefill f32-row kernel")) != KVQ_OK) return st;
+  }
   // the store follows the attention on the stream: it rewrites window slots the prefix was read from
   if ((st = kvq_store_chunk(c, k_new, v_new, batch, n_q, q_start, block_table, max_pages, max_seq_len, stream)) != KVQ_OK)
     return st;

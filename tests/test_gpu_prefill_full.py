@@ -69,10 +69,11 @@ def _check_stored(c):
 
 @pytest.mark.parametrize("layout", ALL)
 @pytest.mark.parametrize("D", [128, 256])
-@pytest.mark.parametrize("prefix,n_q,n_recent", [([300, 0], 40, 0), ([1100, 77], 33, 16), ([5], 70, 64)])
+@pytest.mark.parametrize("prefix,n_q,n_recent", [([300, 0], 40, 0), ([1100, 77], 33, 16), ([5], 70, 64), ([0, 0], 50, 16)])
 def test_prefill_full_then_store_matches_oracle(layout, D, prefix, n_q, n_recent):
-    """Ragged prefixes (one empty: a fresh prompt), windows shorter and longer than the prefix, a
-    chunk that is not a multiple of the 16-row tile; then the stored chunk, bit for bit."""
+    """Ragged prefixes (one empty: a fresh prompt; all empty: the launch without packed chunks),
+    windows shorter and longer than the prefix, a chunk that is not a multiple of the 16-row tile;
+    then the stored chunk, bit for bit."""
     U.need_gpu()
     c = _setup(layout, D, 2, 2, prefix, n_q, n_recent, seed=31 * layout + D + n_q)
     out = kvq.prefill_full_then_store(c["cache"], c["qt"], c["kc"], c["vc"], c["qs"], c["bt"], max(c["total"]),
