@@ -1,4 +1,4 @@
-"""Quantisers, packers and unpackers of the four cache encodings (float64 + explicit rounding).
+"""Quantisers, packers and unpackers of the five cache encodings (float64 + explicit rounding).
 
 Test infrastructure only (see the package docstring).
 

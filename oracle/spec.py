@@ -1,4 +1,4 @@
-"""Layout constants of the four cache encodings.
+"""Layout constants of the five cache encodings.
 
 Test infrastructure only (see the package docstring).
 
