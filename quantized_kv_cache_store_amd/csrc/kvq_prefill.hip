@@ -32,7 +32,7 @@
 
 namespace kvq {
 
-// Split-K chunk of the prefill (tokens); each (64-row block, chunk) is one block of the grid.
+// Shortest split-K chunk of the prefill (tokens); each (row block, chunk) is one block of the grid.
 constexpr int kPrefillChunk = 1024;
 // Full-precision prefill: its f32 rows (the prefix's window and the chunk's own rows) are split into
 // slices of at least this many tokens, one group and one partial slot each.
@@ -40,7 +40,7 @@ constexpr int kRowSlice = 128;
 
 // Slices of the f32 rows of a full-precision prefill of n_q queries (window at most n_recent).
 static inline int row_slices(int n_recent, int n_q) { return (n_recent + n_q + kRowSlice - 1) / kRowSlice; }
-static_assert(kPrefillChunk % 32 == 0 && kPrefillChunk / 16 <= 64, "a chunk's pages (>= 16 tokens each) fit one per lane");
+static_assert(kPrefillChunk % 32 == 0, "chunks of whole 32-token steps");
 
 // LDS of one 32-token step:
 //   KC  int8 codes (code + bias) in A-operand order: [block g][half tau][lane group r][token
@@ -566,6 +566,33 @@ __global__ __launch_bounds__(256, D == 128 ? 4 : 2) void prefill_rows_f32(Attend
   }
 }
 
+// Split-K chunk of a prefill: 1024 tokens, or longer when that saves a round of the chip's block
+// slots (two per CU): a block's time grows with its chunk, and a grid a little larger than one round
+// of blocks costs nearly two rounds.  The chunk minimises rounds x chunk over multiples of 32 from
+// 1024 (so the partial slots never exceed those of 1024-token chunks).
+static int prefill_chunk(int64_t row_blocks, int max_seq_len, int extra_groups) {
+  static int cus_of[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus_of[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    cus_of[dev] = cus;
+  }
+  const int64_t slots = 2LL * cus_of[dev];
+  int best = kPrefillChunk;
+  int64_t best_cost = -1;
+  for (int c = kPrefillChunk; c == kPrefillChunk || c < max_seq_len + 32; c += 32) {
+    const int64_t blocks = row_blocks * (chunks_of(max_seq_len, c) + extra_groups);
+    const int64_t cost = (blocks + slots - 1) / slots * c;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = c;
+    }
+  }
+  return best;
+}
+
 static inline int prefill_rows_per_block(int layout, int D) { return (D == 128 && layout != Q60) ? 128 : 64; }
 static_assert(PrefillTiles<HAD, 128>::BR == 128 && PrefillTiles<Q60, 128>::BR == 64 && PrefillTiles<Q40, 256>::BR == 64,
               "rows per block as the host computes them");
@@ -691,12 +718,14 @@ extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float*
   if ((int64_t)batch * n_q * Hq > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "batch * n_q * num_q_heads above 2^31 - 1");
   const size_t need = kvq_prefill_workspace_bytes(batch, n_q, Hq, c->head_dim, max_seq_len);
   if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
-  AttendArgs a = make_args(c, q, Hq, n_q, alpha, block_table, max_pages, seq_len, max_seq_len, kPrefillChunk,
-                           workspace);
+  const int64_t rbp = ((int64_t)n_q * (Hq / c->num_kv_heads) + prefill_rows_per_block(c->layout, c->head_dim) - 1) /
+                      prefill_rows_per_block(c->layout, c->head_dim) * c->num_kv_heads * batch;
+  const int chunk = prefill_chunk(rbp, max_seq_len, c->n_recent > 0 ? 1 : 0);
+  AttendArgs a = make_args(c, q, Hq, n_q, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace);
   a.causal = causal;
   a.skip = causal && !(flags & KVQ_PREFILL_NO_CAUSAL_SKIP);
   a.q_start = causal ? q_start : nullptr;
-  const int nch = chunks_of(max_seq_len, kPrefillChunk);
+  const int nch = chunks_of(max_seq_len, chunk);
   a.nwg = c->n_recent > 0 ? 1 : 0;   // the window: one group in the same grid
   a.ngroups = nch + a.nwg;
   const int64_t gx = ((int64_t)n_q * a.G + prefill_rows_per_block(c->layout, c->head_dim) - 1) /
@@ -709,7 +738,7 @@ extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float*
     pick_prefill(c->layout, c->head_dim)(a, dim3((unsigned)gx), false, (hipStream_t)stream);
     if ((st = check_launch("prefill partial kernel")) != KVQ_OK) return st;
   }
-  return launch_reduce(c, out, batch, n_q * Hq, seq_len, a.nc1, kPrefillChunk, (const float*)workspace,
+  return launch_reduce(c, out, batch, n_q * Hq, seq_len, a.nc1, chunk, (const float*)workspace,
                        (hipStream_t)stream);
 }
 
@@ -731,12 +760,6 @@ extern "C" kvq_status kvq_prefill_full_then_store(const kvq_cache* c, const floa
     return fail(KVQ_ERR_INVALID_ARG, "too many rows in one store");
   const size_t need = kvq_prefill_workspace_bytes(batch, n_q, Hq, c->head_dim, max_seq_len);
   if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
-  AttendArgs a = make_args(c, q, Hq, n_q, alpha, block_table, max_pages, q_start, max_seq_len, kPrefillChunk,
-                           workspace);
-  a.causal = causal;
-  a.skip = 0;   // every packed token precedes the chunk: nothing to skip
-  a.q_start = causal ? q_start : nullptr;
-  const int nch = chunks_of(max_seq_len, kPrefillChunk);
   // slices of the window and chunk rows, each of at least kRowSlice rows, and as many as bring
   // their blocks to about 4096.  With a possible prefix (max_seq_len > n_q) they are the last groups
   // of prefill_partial's grid, after the packed chunks; without one they are the whole work and run
@@ -744,17 +767,24 @@ extern "C" kvq_status kvq_prefill_full_then_store(const kvq_cache* c, const floa
   const bool sep = max_seq_len <= n_q;
   const int rpb = sep ? 64 : prefill_rows_per_block(c->layout, c->head_dim);
   const int nf32 = min(c->n_recent, max_seq_len) + n_q;
-  const int64_t row_blocks = ((int64_t)n_q * a.G + rpb - 1) / rpb * c->num_kv_heads * batch;
+  const int64_t row_blocks = ((int64_t)n_q * (Hq / c->num_kv_heads) + rpb - 1) / rpb * c->num_kv_heads * batch;
   const int64_t want = (4096 + row_blocks - 1) / row_blocks;
   int slice = (int)((nf32 + want - 1) / want);
   slice = max(kRowSlice, (slice + 15) / 16 * 16);
+  const int nwin = (nf32 + slice - 1) / slice;
+  const int chunk = sep ? kPrefillChunk : prefill_chunk(row_blocks, max_seq_len, nwin);
+  AttendArgs a = make_args(c, q, Hq, n_q, alpha, block_table, max_pages, q_start, max_seq_len, chunk, workspace);
+  a.causal = causal;
+  a.skip = 0;   // every packed token precedes the chunk: nothing to skip
+  a.q_start = causal ? q_start : nullptr;
+  const int nch = chunks_of(max_seq_len, chunk);
   a.slice = slice;
-  a.nwin = (nf32 + slice - 1) / slice;
-  a.nc1 = nch + a.nwin;
-  a.nwg = sep ? 0 : a.nwin;
-  a.ngroups = sep ? 0 : nch + a.nwin;
+  a.nwin = nwin;
+  a.nc1 = nch + nwin;
+  a.nwg = sep ? 0 : nwin;
+  a.ngroups = sep ? 0 : nch + nwin;
   const int64_t gx = sep ? 0 : row_blocks * a.ngroups;
-  const int64_t gw = sep ? row_blocks * a.nwin : 0;
+  const int64_t gw = sep ? row_blocks * nwin : 0;
   if (gx > 0x7fffffff || gw > 0x7fffffff) return fail(KVQ_ERR_UNSUPPORTED, "prefill grid above 2^31 - 1 blocks");
   const int rows = batch * n_q * Hq;
   const RowPrep w = prefill_ws((size_t)rows, c->head_dim, a.nc1);
@@ -781,6 +811,6 @@ extern "C" kvq_status kvq_prefill_full_then_store(const kvq_cache* c, const floa
   // the store follows the attention on the stream: it rewrites window slots the prefix was read from
   if ((st = kvq_store_chunk(c, k_new, v_new, batch, n_q, q_start, block_table, max_pages, max_seq_len, stream)) != KVQ_OK)
     return st;
-  return launch_reduce(c, out, batch, n_q * Hq, q_start, a.nc1, kPrefillChunk, (const float*)workspace, s, a.nwin,
+  return launch_reduce(c, out, batch, n_q * Hq, q_start, a.nc1, chunk, (const float*)workspace, s, a.nwin,
                        a.slice, causal ? n_q : 0);
 }
