@@ -291,8 +291,10 @@ __device__ __forceinline__ void rotate_quarters(float* x, int r) {
 //     (col, r): P[row col][token 4 q + r]) is P transposed through LDS, the B operand (lane
 //     (col, r): V[token 4 q + r][d]) comes from the V tile staged in LDS.  The output rows 4 r + j
 //     are the rows of the lane's scores, so the online rescale is lane-local.
-// The wave's LDS: the V tile [16][D + 16] f32, rows padded (conflict-free B reads), P in the
-// padding of its rows ([row][D .. D + 15]).
+// The wave's LDS: the V tile [16][D + 16] f32, rows padded (conflict-free B reads), and P in the
+// padding: P[row R][token T] at [T][D + (R ^ ((T >> 2) & 3))], which both the writes (lanes: 16
+// tokens x rows 4 r + j) and the transposing reads (lanes: 16 rows x tokens 4 qq + r) spread over
+// all 64 banks, since a padded row starts 16 banks after the previous one.
 // Full-precision prefill (a.kchunk set): the chunk's own n_q rows follow the window at positions
 // S .. S + n_q - 1, read from f32 rows [batch][n_q][Hkv][D] (rotated beforehand for HAD), so that
 // tokens t < W come from the ring and t >= W from the chunk, at position w0 + t either way.
@@ -400,7 +402,7 @@ __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int 
       p[j] = exp2f(x - m_use);
       st.l[j] = st.l[j] * corr[j] + p[j];
       st.m[j] = m_new;
-      vt[(4 * r + j) * VS + D + col] = p[j];   // P[row][token col] in the row's padding
+      vt[col * VS + D + ((4 * r + j) ^ (col >> 2))] = p[j];   // P[row 4 r + j][token col]
     }
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
@@ -412,7 +414,7 @@ __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int 
     // ---- P V
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
-      const float pa = vt[col * VS + D + 4 * qq + r];   // P[row col][token 4 qq + r]
+      const float pa = vt[(4 * qq + r) * VS + D + (col ^ qq)];   // P[row col][token 4 qq + r]
       const float* vrow = vt + (4 * qq + r) * VS + col;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt)
