@@ -502,10 +502,9 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
   // numerators of this row come from lane col ^ 8
   const uint32_t own0 = as_u32(h2{ph[0], ph[1]}), own1 = as_u32(h2{ph[2], ph[3]});
   const uint32_t oth0 = half_swap_u(own0), oth1 = half_swap_u(own1);
-  const u32x4 pr = hh ? u32x4{oth0, oth1, own0, own1} : u32x4{own0, own1, oth0, oth1};
-  const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-  const v8h pB0 = __builtin_bit_cast(v8h, hh ? zero : pr);
-  const v8h pB1 = __builtin_bit_cast(v8h, hh ? pr : zero);
+  // (pB0 lives in the columns of half 0, pB1 in those of half 1; each is zero in the other half)
+  const v8h pB0 = __builtin_bit_cast(v8h, hh ? u32x4{0u, 0u, 0u, 0u} : u32x4{own0, own1, oth0, oth1});
+  const v8h pB1 = __builtin_bit_cast(v8h, hh ? u32x4{oth0, oth1, own0, own1} : u32x4{0u, 0u, 0u, 0u});
 
   // ---------------- P V: tile pt of octet group o takes elements 2 pt (columns 0..7) and 2 pt + 1
 #pragma unroll
@@ -721,6 +720,11 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
       }
     };
     auto span_count = [](int lo, int hi) { return hi >= lo ? hi - lo + 1 : 0; };
+    // Steps s >= S0 with s + MX < nsteps are the steady part: no count below is clipped by the
+    // chunk's ends, so the K wait counts 2 RK - 1 groups and the V wait 2 RV - 1.  Waits with these
+    // constant counts skip the compare-and-branch ladder that wait_groups compiles to.
+    constexpr int S0 = RK - RV > 0 ? RK - RV : (RV - 1 - RK > 0 ? RV - 1 - RK : 0);
+    static_assert((2 * RK - 1) * G <= 63 && (2 * RV - 1) * G <= 63, "load counter range");
 #pragma unroll
     for (int j = -MX; j < 0; ++j) {
       const int k = j + RK, v = j + RV;
@@ -733,13 +737,20 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
       const HalfRows hk_next = k_next ? rows(s + RK) : HalfRows{0, 0};
       const HalfRows hv_next = v_next ? rows(s + RV) : HalfRows{0, 0};
       // K of step s: then K(s + 1 .. s + RK - 1) and V(s - RK + RV .. s + RV - 1)
-      wait_groups(span_count(s + 1, min(nsteps - 1, s + RK - 1)) +
-                  span_count(max(0, s - RK + RV), min(nsteps - 1, s + RV - 1)));
+      const bool steady = s + MX < nsteps && s >= S0;
+      if (steady)
+        wait_vm<(2 * RK - 1) * G>();
+      else
+        wait_groups(span_count(s + 1, min(nsteps - 1, s + RK - 1)) +
+                    span_count(max(0, s - RK + RV), min(nsteps - 1, s + RV - 1)));
       step(kring + ks * H, vring + vs * H, t_begin + 32 * s, [&]() {
         if (k_next) issue_dma_half<ST, false>(a, hk_next, lane, kr_lds + ks * H);
         // V of step s: then K(s - RV + 1 + RK .. s + RK) and V(s + 1 .. s + RV - 1)
-        wait_groups(span_count(max(0, s - RV + 1 + RK), min(nsteps - 1, s + RK)) +
-                    span_count(s + 1, min(nsteps - 1, s + RV - 1)));
+        if (steady)
+          wait_vm<(2 * RV - 1) * G>();
+        else
+          wait_groups(span_count(max(0, s - RV + 1 + RK), min(nsteps - 1, s + RK)) +
+                      span_count(s + 1, min(nsteps - 1, s + RV - 1)));
       });
       if (v_next) issue_dma_half<ST, true>(a, hv_next, lane, vr_lds + vs * H);
       ks = ks + 1 == RK ? 0 : ks + 1;

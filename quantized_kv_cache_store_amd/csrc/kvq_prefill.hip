@@ -497,7 +497,11 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
     const int T0 = t_begin + 32 * s;
     const bool more = s + 1 < nsteps;
     if (s + NR - 1 < nsteps) issue(s + NR - 1);
-    if (more) wait_steps(min(nsteps - 1, s + NR - 1) - (s + 1));
+    if (s + NR - 1 < nsteps) {   // steady part: a constant count, without wait_steps' branches
+      if (wave < 2) wait_vm<(NR - 2) * G>();
+    } else if (more) {
+      wait_steps(nsteps - 1 - (s + 1));
+    }
     barrier();
     if (more) {
       prefill_fetch<L, D>(raw_k(s + 1), raw_k(s + 1) + H, tid, ld);
