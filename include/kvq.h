@@ -77,7 +77,9 @@ typedef enum kvq_status {
  * The recent window ([tract-RFC] Causality & mixed precision, n_recent) keeps
  * the newest n_recent positions of each batch row as exact f32 rows (rotated
  * for HAD_INT4) in a ring indexed by position % n_recent; may be NULL when
- * n_recent == 0.  page_size is a power of two >= 16; head_dim is 128 or 256. */
+ * n_recent == 0.  page_size is a power of two >= 16; head_dim is 128 or 256;
+ * num_pages * page_size is at most INT32_MAX (slots are int32), while byte
+ * offsets into the planes are 64-bit, so a plane may exceed 4 GiB. */
 typedef struct kvq_cache {
   int32_t layout;       /* kvq_layout */
   int32_t head_dim;

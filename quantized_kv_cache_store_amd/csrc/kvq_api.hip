@@ -31,6 +31,8 @@ kvq_status validate_cache(const kvq_cache* c) {
   if (c->page_size < 16 || (c->page_size & (c->page_size - 1)))
     return fail(KVQ_ERR_INVALID_ARG, "page_size must be a power of two >= 16");
   if (c->num_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "num_pages must be >= 1");
+  if ((int64_t)c->num_pages * c->page_size > (int64_t)INT32_MAX)
+    return fail(KVQ_ERR_INVALID_ARG, "num_pages * page_size must fit the int32 slot index");
   if (c->n_recent < 0) return fail(KVQ_ERR_INVALID_ARG, "n_recent must be >= 0");
   if (c->reserved != 0) return fail(KVQ_ERR_INVALID_ARG, "reserved field must be 0");
   if (!c->k_payload || !c->v_payload || !c->k_scale || !c->v_scale)

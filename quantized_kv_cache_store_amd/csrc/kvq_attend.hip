@@ -724,7 +724,8 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
     // chunk's ends, so the K wait counts 2 RK - 1 groups and the V wait 2 RV - 1.  Waits with these
     // constant counts skip the compare-and-branch ladder that wait_groups compiles to.
     constexpr int S0 = RK - RV > 0 ? RK - RV : (RV - 1 - RK > 0 ? RV - 1 - RK : 0);
-    static_assert((2 * RK - 1) * G <= 63 && (2 * RV - 1) * G <= 63, "load counter range");
+    constexpr int NK = (2 * RK - 1) * G <= 63 ? (2 * RK - 1) * G : 63;   // a smaller count only waits longer
+    constexpr int NV = (2 * RV - 1) * G <= 63 ? (2 * RV - 1) * G : 63;
 #pragma unroll
     for (int j = -MX; j < 0; ++j) {
       const int k = j + RK, v = j + RV;
@@ -739,7 +740,7 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
       // K of step s: then K(s + 1 .. s + RK - 1) and V(s - RK + RV .. s + RV - 1)
       const bool steady = s + MX < nsteps && s >= S0;
       if (steady)
-        wait_vm<(2 * RK - 1) * G>();
+        wait_vm<NK>();
       else
         wait_groups(span_count(s + 1, min(nsteps - 1, s + RK - 1)) +
                     span_count(max(0, s - RK + RV), min(nsteps - 1, s + RV - 1)));
@@ -747,7 +748,7 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
         if (k_next) issue_dma_half<ST, false>(a, hk_next, lane, kr_lds + ks * H);
         // V of step s: then K(s - RV + 1 + RK .. s + RK) and V(s + 1 .. s + RV - 1)
         if (steady)
-          wait_vm<(2 * RV - 1) * G>();
+          wait_vm<NV>();
         else
           wait_groups(span_count(max(0, s - RV + 1 + RK), min(nsteps - 1, s + RK)) +
                       span_count(s + 1, min(nsteps - 1, s + RV - 1)));

@@ -56,6 +56,7 @@ def _desc(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(layout=9), 1), (dict(head_dim=96), 2), (dict(page_size=24), 1), (dict(page_size=8), 1),
     (dict(num_kv_heads=0), 1), (dict(k_payload=None), 1), (dict(n_recent=4), 1), (dict(reserved=3), 1),
+    (dict(num_pages=1 << 27, page_size=16), 1), (dict(num_pages=1 << 20, page_size=4096), 1),
 ])
 def test_store_validates_cache(kw, status):
     lib = kvq.load()
