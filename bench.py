@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--cpu-kv-heads", type=int, default=4, help="kv heads of one row timed on the oracle")
     p.add_argument("--batch1", action="store_true", help="also time batch 1 (reported under extra)")
     p.add_argument("--no-prefill", action="store_true", help="skip the causal prefill timing")
+    p.add_argument("--configs", action="store_true",
+                   help="also time one decode step of each workload at its own shape (reported under extra)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a 1 GiB device-to-device copy 10 times (HBM counter calibration) and exit")
     return p.parse_args()
@@ -310,6 +312,112 @@ def time_decode(w, B, chunk, steps, warmup, layers, dev, seed):
                 partial_ms_p90=srt[min(len(srt) - 1, (9 * len(srt)) // 10)], probe_us=probe_us)
 
 
+# Layer caches walked per configuration so that the walk spans about 1 GiB or more (the tiny case stays
+# cache-resident: it is launch-bound and reported in microseconds only).
+CONFIG_LAYERS = {"tiny_q4_0_s1024": 1, "llama3_8b_q4_0_s32k": 32, "qwen3_1p7b_had_s8k": 128,
+                 "llama31_70b_asym_s128k": 2, "gemma_q6_0_ragged_b16": 2}
+
+
+def time_config(w, steps, warmup, dev, seed=5):
+    """One decode step of a workload at its own shape: store one token per row at its last position,
+    then the split-K partial and the reduce, walking CONFIG_LAYERS[w.name] layer caches."""
+    import numpy as np
+    import torch
+    import quantized_kv_cache_store_amd as kvq
+    import workloads as W
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    lens = [int(n) for n in W.seq_lens(w)]
+    B, S = len(lens), max(lens)
+    table_np, total = W.block_tables(w, lens)
+    for b in range(B):   # unused entries: a page of the row (never read below its length)
+        table_np[b][table_np[b] < 0] = table_np[b, 0]
+    ps = w.page_size
+    table = torch.from_numpy(table_np).to(dev)
+    seq = torch.tensor(lens, dtype=torch.int32, device=dev)
+    lay = kvq.LAYOUT_IDS[w.layout]
+    per_tok = 2 * (kvq.load().kvq_payload_bytes(lay, w.D) + kvq.load().kvq_scale_bytes(lay, w.D))
+    window = sum(min(n, w.n_recent) for n in lens) * w.Hkv * 2 * w.D * 4
+    packed = sum(max(0, n - w.n_recent) if w.n_recent else n for n in lens) * w.Hkv * per_tok
+    L = CONFIG_LAYERS.get(w.name, 2)
+
+    def slots(b, t0, t1):
+        t = torch.arange(t0, t1, device=dev, dtype=torch.int64)
+        return (table[b, t // ps].to(torch.int64) * ps + t % ps).to(torch.int32)
+
+    caches = []
+    fill = 16384
+    for _ in range(L):
+        c = kvq.KvqCache(w.layout, w.D, w.Hkv, total, ps, n_recent=w.n_recent, max_batch=B, device=dev)
+        for b, n in enumerate(lens):
+            for t0 in range(0, n - 1, fill):
+                t1 = min(n - 1, t0 + fill)
+                k = W.kv_tokens_device(w, t1 - t0, "k", gen, dev)
+                v = W.kv_tokens_device(w, t1 - t0, "v", gen, dev)
+                kvq.store(c, k, v, slots(b, t0, t1), torch.full((t1 - t0,), b, dtype=torch.int32, device=dev),
+                          torch.arange(t0, t1, dtype=torch.int32, device=dev), seq)
+        caches.append(c)
+    q = torch.randn((B, w.Hq, w.D), generator=gen, device=dev, dtype=torch.float32)
+    k_new = W.kv_tokens_device(w, B, "k", gen, dev)
+    v_new = W.kv_tokens_device(w, B, "v", gen, dev)
+    slot_new = torch.cat([slots(b, n - 1, n) for b, n in enumerate(lens)])
+    bidx = torch.arange(B, dtype=torch.int32, device=dev)
+    pos_new = (seq - 1).to(torch.int32)
+    out = torch.empty((B, w.Hq, w.D), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.decode_workspace_bytes(B, w.Hq, w.D, S, w.chunk_tokens), dtype=torch.uint8, device=dev)
+
+    def step(i, partial_only=False):
+        c = caches[i % L]
+        if not partial_only:
+            kvq.store(c, k_new, v_new, slot_new, bidx, pos_new, seq)
+        kvq.attend_decode_partial(c, q, table, seq, S, w.alpha, w.chunk_tokens, ws)
+        if not partial_only:
+            kvq.attend_decode_reduce(c, out, seq, S, w.chunk_tokens, ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # The small shapes take less GPU time per step than the binding's host launches, so the steps
+    # are captured into graphs (the decode issues no memset nodes) and the replays are timed: one graph
+    # of whole steps and one of the partial kernel alone, each walking the layer caches.
+    per_graph = max(L, 16)
+
+    def capture(partial_only):
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                for i in range(per_graph):
+                    step(i, partial_only)
+        torch.cuda.current_stream().wait_stream(st)
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def timed(g):
+        reps = max(2, steps // 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
+
+    us = timed(capture(False))
+    assert torch.isfinite(out).all(), "non-finite attention output"
+    part_us = timed(capture(True))
+    del caches
+    torch.cuda.empty_cache()
+    return dict(workload=w.name, layout=w.layout, batch=B, seq_len_max=S, q_heads=w.Hq, kv_heads=w.Hkv,
+                head_dim=w.D, n_recent=w.n_recent, layers_walked=L, bytes_per_layer=packed + window,
+                us_per_layer=round(us, 2), partial_us=round(part_us, 2), timing=f"graphs of {per_graph} steps",
+                gbs=round((packed + window) / (us * 1e-6) / 1e9, 1),
+                ideal_us_at_8tbs=round((packed + window) / 8e12 * 1e6, 2))
+
+
 def cpu_baseline(w, kv_heads):
     """The oracle (as it stands) on one row, ``kv_heads`` kv heads, the full 131072 tokens."""
     import numpy as np
@@ -361,6 +469,8 @@ def main():
         extra["prefill_full_precision"] = [time_prefill_full(max(a.steps, 20), a.warmup, dev, qs, nq)
                                            for qs, nq in ((8192, 512), (0, 512), (0, 4096))]
         extra["store"] = time_store(max(a.steps, 20), a.warmup, dev)
+    if a.configs:
+        extra["configs"] = [time_config(W.WORKLOADS[n], max(a.steps, 20), a.warmup, dev) for n in W.WORKLOADS]
     gbs = r["bytes_layer"] / (r["ms_per_step"] * 1e-3) / 1e9
     ach = r["bytes_layer"] / (r["partial_ms_mean"] * 1e-3) / 1e9
     line = {

@@ -533,7 +533,13 @@ struct PartialShape {
   static constexpr bool DMA = TR == 8;
   using ST = Step<L, D, DMA>;
   static constexpr int NB = (ST::SLOTS <= 5) ? 5 : (D == 128 ? 3 : 2);
-  static constexpr int RK = 2, RV = 2;
+  // Two K and two V slots, unless four slots per wave would leave LDS for less than two blocks per
+  // CU (D = 256 rows of q6_0 and q8_0; those kernels' registers allow two blocks): then one V slot,
+  // and one K slot as well where three slots are still too many.  A single slot is refilled as soon
+  // as its step has read it, and the second block's waves cover the wait.
+  static constexpr int HALF_BYTES = ST::HALF;
+  static constexpr int RK = (TR == 8 && 4 * 3 * HALF_BYTES > 81920) ? 1 : 2;
+  static constexpr int RV = (TR == 8 && 4 * 4 * HALF_BYTES > 81920) ? 1 : 2;
   static constexpr int RING = DMA ? 4 * (RK + RV) * ST::HALF : 4 * ST::BYTES;
   static constexpr int MERGE = 4 * TR * (D + 4) * 4;            // the four waves' chunk partials
   static constexpr int LDS = RING > MERGE ? RING : MERGE;       // per block
@@ -557,10 +563,16 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
   extern __shared__ __align__(16) unsigned char smem[];
 
   // Block numbering: chunk group fastest (measured faster than kv head or batch row fastest: blocks
-  // that run together then stream neighbouring chunks of one (row, kv head)).
+  // that run together then stream neighbouring chunks of one (row, kv head)).  The chip runs block
+  // id on XCD id % 8, and in a ragged batch only the low chunk groups of the short rows hold
+  // tokens, so each (batch row, kv head, tile) rotates its chunk groups by its own index: their
+  // first groups then spread over all XCDs instead of piling onto the same ones.
   const int hk = blockIdx.y, b = blockIdx.z;
   const int tile = (int)blockIdx.x / a.ngroups;
-  const int cg = (int)blockIdx.x - tile * a.ngroups;
+  const int tiles = (int)gridDim.x / a.ngroups;
+  const int rot = (int)((((long)b * gridDim.y + hk) * tiles + tile) % a.ngroups);
+  int cg = (int)blockIdx.x - tile * a.ngroups - rot;
+  if (cg < 0) cg += a.ngroups;
   const int S = a.seq_len[b];
   const int Sq = a.n_recent > 0 ? max(0, S - a.n_recent) : S;   // quantised tokens
   const int nrows = a.n_q * a.G;
@@ -962,8 +974,11 @@ static partial_fn pick_partial(int layout, int D, int tr) {
 // while one round of resident waves (four per SIMD) still has work for all of them: the grid then
 // needs fewer rounds of the chip, each of which ends with the blocks' barriers, merges and partial
 // stores, during which their LDS and wave slots stream nothing (the register-ring kernel also
-// needs the run's pages to fit its page registers).  Half a chunk per wave for small batches,
-// which would fill more wave slots, measured slower (batch 1 at 128K: 42 us against 39).
+// needs the run's pages to fit its page registers).  With few waves the runs get shorter instead,
+// down to a quarter chunk, while the doubled wave count still leaves half the wave slots free: a
+// short context then spreads over more CUs (a wave's run is a serial chain of steps).  Halving the
+// runs where that would fill every slot measured slower (batch 1 at 128K: 42 us against 39).  Every
+// span keeps 4 * span >= chunk, so the partial slots fit the workspace.
 static int decode_span(const kvq_cache* c, int batch, int Hq, int max_seq_len, int chunk) {
   static int cus_of[64];
   int dev = 0;
@@ -979,7 +994,10 @@ static int decode_span(const kvq_cache* c, int batch, int Hq, int max_seq_len, i
   const int64_t resident = (int64_t)cus_of[dev] * 16;
   int cpw = 1;
   while (cpw < 4 && waves >= resident * 2 * cpw && (2 * cpw * chunk) / c->page_size + 1 < 64 * kPageRegs) cpw *= 2;
-  return cpw * chunk;
+  if (cpw > 1) return cpw * chunk;
+  int span = chunk;
+  for (int64_t w = waves; span > chunk / 4 && span % 64 == 0 && 4 * w <= resident; w *= 2) span /= 2;
+  return span;
 }
 
 // Workspace of the decode: room for the partials [B x Hq x (chunks + 1) x (D + 4)] f32 (the decode
