@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--chunk", type=int, default=512)
     p.add_argument("--layers", type=int, default=0, help="layer caches walked (0: enough for >= 2.5 GB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-kv-heads", type=int, default=4, help="kv heads of one row timed on the oracle")
+    p.add_argument("--cpu-kv-heads", type=int, default=8, help="kv heads of one row timed on the oracle")
     p.add_argument("--batch1", action="store_true", help="also time batch 1 (reported under extra)")
     p.add_argument("--no-prefill", action="store_true", help="skip the causal prefill timing")
     p.add_argument("--configs", action="store_true",
