@@ -2,6 +2,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -20,6 +22,18 @@ kvq_status check_launch(const char* what) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return KVQ_OK;
+}
+
+int device_cus() {
+  static std::atomic<int> cus_of[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int cus = cus_of[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    cus_of[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
 }
 
 kvq_status validate_cache(const kvq_cache* c) {

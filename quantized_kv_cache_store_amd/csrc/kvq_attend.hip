@@ -980,18 +980,10 @@ static partial_fn pick_partial(int layout, int D, int tr) {
 // runs where that would fill every slot measured slower (batch 1 at 128K: 42 us against 39).  Every
 // span keeps 4 * span >= chunk, so the partial slots fit the workspace.
 static int decode_span(const kvq_cache* c, int batch, int Hq, int max_seq_len, int chunk) {
-  static int cus_of[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cus_of[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    cus_of[dev] = cus;
-  }
   const int G = Hq / c->num_kv_heads;
   const int tr = G <= 8 ? 8 : 16;
   const int64_t waves = (int64_t)batch * c->num_kv_heads * ((G + tr - 1) / tr) * chunks_of(max_seq_len, chunk);
-  const int64_t resident = (int64_t)cus_of[dev] * 16;
+  const int64_t resident = (int64_t)device_cus() * 16;
   int cpw = 1;
   while (cpw < 4 && waves >= resident * 2 * cpw && (2 * cpw * chunk) / c->page_size + 1 < 64 * kPageRegs) cpw *= 2;
   if (cpw > 1) return cpw * chunk;

@@ -56,6 +56,10 @@ static inline constexpr int partial_stride(int D) { return D + 4; }
 kvq_status fail(kvq_status s, const char* fmt, ...);
 kvq_status check_launch(const char* what);
 kvq_status validate_cache(const kvq_cache* c);
+// Compute units of the current device, cached per device (256 if the query fails).  Safe to call
+// from several host threads: the cache entries are atomics, and racing first calls store the same
+// value.
+int device_cus();
 
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
 // ----------------------------------------------------------------------------- device helpers

@@ -576,15 +576,7 @@ __global__ __launch_bounds__(256, D == 128 ? 4 : 2) void prefill_rows_f32(Attend
 // of blocks costs nearly two rounds.  The chunk minimises rounds x chunk over multiples of 32 from
 // 1024 (so the partial slots never exceed those of 1024-token chunks).
 static int prefill_chunk(int64_t row_blocks, int max_seq_len, int extra_groups) {
-  static int cus_of[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cus_of[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    cus_of[dev] = cus;
-  }
-  const int64_t slots = 2LL * cus_of[dev];
+  const int64_t slots = 2LL * device_cus();
   int best = kPrefillChunk;
   int64_t best_cost = -1;
   for (int c = kPrefillChunk; c == kPrefillChunk || c < max_seq_len + 32; c += 32) {
