@@ -11,7 +11,7 @@ token of every row (kvq_store), then the split-K decode partial and the reduce
 layer caches (L * packed bytes >= 2.5 GB) so the 256 MB Infinity Cache cannot
 serve the reads.  Timed with HIP events on the launch stream after warm-up.
 
-Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
+Prints one JSON line.  ``--gpus`` above 1 is refused: the benchmark runs on one GPU.
 """
 
 import argparse
@@ -449,7 +449,7 @@ def main():
         copy_calibration()
         return
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported",
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus above 1 is not supported",
                           "n_gpus": a.gpus}))
         sys.exit(2)
     import torch
