@@ -28,6 +28,8 @@
 // that are partly visible mask per row.  With the skip off the masked tokens are
 // streamed and contribute exact zeros, so both settings give the same bits.
 
+#include <type_traits>
+
 #include "kvq_attend_common.h"
 
 namespace kvq {
@@ -494,7 +496,14 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
     prefill_fetch<L, D>(raw_k(0), raw_k(0) + H, tid, ld);
     prefill_produce<L, D>(smem, tid, ld, min(32, t_end - t_begin), magic);
   }
-  for (int s = 0; s < nsteps; ++s) {
+  // Steps whose 32 tokens are all present and visible to every row of the wave come first (the
+  // condition only turns from true to false along the chunk): each loop then has one consume form,
+  // and the accumulators stay in place instead of being copied at an if/else join every step.
+  const int nfull_a = (t_end - t_begin) / 32;
+  const int nfull_b = lim_min + 1 - t_begin >= 0 ? (lim_min + 1 - t_begin) / 32 : 0;
+  const int nfull = min(min(nfull_a, nfull_b), nsteps);
+  auto step = [&](int s, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int T0 = t_begin + 32 * s;
     const bool more = s + 1 < nsteps;
     if (s + NR - 1 < nsteps) issue(s + NR - 1);
@@ -510,13 +519,12 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
     }
     const unsigned char* buf = smem + (s & 1) * PS::BYTES;
     const int n_tok = min(32, t_end - T0);
-    if (nval[0] > 0) {
-      if (n_tok == 32 && T0 + 31 <= lim_min)
-        prefill_consume<L, D, true, TPW>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, oacc);
-      else
-        prefill_consume<L, D, false, TPW>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, oacc);
-    }
-  }
+    if (nval[0] > 0)
+      prefill_consume<L, D, FULL, TPW>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, oacc);
+  };
+  int s = 0;
+  for (; s < nfull; ++s) step(s, std::integral_constant<bool, true>{});
+  for (; s < nsteps; ++s) step(s, std::integral_constant<bool, false>{});
 
   // ---------------- this wave's chunk partials: o[d = 16 dt + 4 r + j] of row col of each tile
 #pragma unroll
