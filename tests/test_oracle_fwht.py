@@ -88,3 +88,62 @@ def test_rejects_non_power_of_two():
         fwht.fwht_f32(np.zeros(96, dtype=np.float32))
     with pytest.raises(ValueError):
         fwht.hadamard_matrix(12)
+
+
+# ------------------------------------------------------------------ rounding order, worked by hand
+# A D = 8 row of one-decimal values, none of which is exact in binary, written out stage by stage as
+# f32 bit patterns (each entry worked with one f32 add or subtract of the previous stage's pair,
+# strides 1, 2, 4 in that order, then one f32 multiply by f32(1/sqrt(8)) = 0x3eb504f3).  Running the
+# strides in descending order, or scaling before the butterflies, gives different bits here, so this
+# pins the stage order and the scaling point the encoding reads from [tract-RFC] What's done (CPU).
+_X8 = [0x40966666, 0x40A33333, 0x40F00000, 0x41180000, 0x3ECCCCCD, 0x3FC00000, 0x41033333, 0x41166666]
+_STAGES8 = {
+    1: [0x411CCCCC, 0xBECCCCD0, 0x41880000, 0xC0000000, 0x3FF33333, 0xBF8CCCCD, 0x418CCCCC, 0xBF999998],
+    2: [0x41D66666, 0xC019999A, 0xC0E66668, 0x3FCCCCCC, 0x419BFFFF, 0xC0133332, 0xC17B3332, 0x3DCCCCB0],
+    4: [0x42393332, 0xC0966666, 0xC1B73333, 0x3FD99997, 0x40E9999C, 0xBDCCCD00, 0x4107FFFE, 0x3FC00001],
+}
+_OUT8 = [0x4182F4C7, 0xBFD4B29D, 0xC1018ABE, 0x3F19DDCD, 0x40252E1F, 0xBD10D0E7, 0x4040553F, 0x3F07C3B7]
+
+
+def _bits_to_f32(bits):
+    return np.array(bits, dtype=np.uint32).view(np.float32)
+
+
+def test_stage_table_is_consistent():
+    """Each stage of the worked table is the f32 butterfly of the one before (the table's own check)."""
+    prev = _bits_to_f32(_X8)
+    for h in (1, 2, 4):
+        cur = _bits_to_f32(_STAGES8[h])
+        for i in range(8):
+            if i & h == 0:
+                assert cur[i] == np.float32(prev[i] + prev[i + h])
+                assert cur[i + h] == np.float32(prev[i] - prev[i + h])
+        prev = cur
+    c = np.array([0x3EB504F3], dtype=np.uint32).view(np.float32)[0]
+    np.testing.assert_array_equal((prev * c).astype(np.float32), _bits_to_f32(_OUT8))
+
+
+def test_f32_butterfly_stage_order_and_scale_point():
+    y = fwht.fwht_f32(_bits_to_f32(_X8))
+    np.testing.assert_array_equal(np.asarray(y, dtype=np.float32).view(np.uint32), np.array(_OUT8, dtype=np.uint32))
+
+
+def test_stage_order_and_scale_point_are_visible_in_the_worked_row():
+    """The alternatives differ from the worked row, so a swapped order or scaling point fails above."""
+    def variant(order, scale_first):
+        y = _bits_to_f32(_X8).copy()
+        c = np.float32(fwht.norm_const_f32(8))
+        if scale_first:
+            y = (y * c).astype(np.float32)
+        for h in order:
+            z = y.copy()
+            for i in range(8):
+                if i & h == 0:
+                    z[i] = np.float32(y[i] + y[i + h])
+                    z[i + h] = np.float32(y[i] - y[i + h])
+            y = z
+        return y if scale_first else (y * c).astype(np.float32)
+
+    out = _bits_to_f32(_OUT8)
+    assert not np.array_equal(variant((4, 2, 1), False), out)
+    assert not np.array_equal(variant((1, 2, 4), True), out)

@@ -244,3 +244,75 @@ def test_q8_0_range_ends():
     codes, d = quant.quantize_symmetric_blocks(x, spec.Q8_0)
     assert d[0] == float(np.float16(2.0 / 128.0))
     assert codes[0] == 127 and codes[1] == -128 and codes[2] == 64
+
+
+# ------------------------------------------------------------------ exact ties (round half to even)
+# Quotients that land exactly on k + 1/2 decide the rounding mode: half to even gives the even
+# neighbour (0.5 -> 0, 1.5 -> 2, 2.5 -> 2, -2.5 -> -2), unlike half away from zero, half up or
+# truncation.  Each block below has a scale of exactly 1, so the quotient is the value itself.
+def _tie_block(amax, ties):
+    x = np.zeros(32)
+    x[0] = amax
+    x[1:1 + len(ties)] = ties
+    return x
+
+
+def test_q4_0_ties_round_half_to_even():
+    x = _tie_block(8.0, [0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, -3.5, 6.5, -7.5, 0.75])
+    codes, d = quant.quantize_symmetric_blocks(x[None, :], spec.Q4_0)
+    assert d[0, 0] == 1.0
+    assert list(codes[0, :12]) == [7, 0, 2, 2, 4, 0, -2, -2, -4, 6, -8, 1]
+
+
+def test_q6_0_ties_round_half_to_even():
+    x = _tie_block(32.0, [0.5, 2.5, 30.5, -31.5, -0.5, 5.5, -4.5])
+    codes, d = quant.quantize_symmetric_blocks(x[None, :], spec.Q6_0)
+    assert d[0, 0] == 1.0
+    assert list(codes[0, :8]) == [31, 0, 2, 30, -32, 0, 6, -4]
+
+
+def test_q8_0_ties_round_half_to_even():
+    x = _tie_block(128.0, [126.5, -127.5, 0.5, 1.5, -2.5, 125.5])
+    codes, d = quant.quantize_symmetric_blocks(x[None, :], spec.Q8_0)
+    assert d[0, 0] == 1.0
+    assert list(codes[0, :7]) == [127, 126, -128, 0, 2, -2, 126]
+
+
+def test_asym_ties_round_half_to_even():
+    # min 0, max 15: s = 1, z = 0
+    x = np.zeros(32)
+    x[0], x[1:6] = 15.0, [0.5, 1.5, 2.5, 14.5, 13.5]
+    codes, s, z = quant.quantize_asym_g32(x[None, :])
+    assert (s[0, 0], z[0, 0]) == (1.0, 0.0)
+    assert list(codes[0, :6]) == [15, 0, 2, 2, 14, 14]
+    # min -8, max 7: s = 1, z = -8, so x - z = x + 8 carries the tie
+    y = np.full(32, -8.0)
+    y[0], y[1:4] = 7.0, [-5.5, -7.5, 6.5]
+    codes, s, z = quant.quantize_asym_g32(y[None, :])
+    assert (s[0, 0], z[0, 0]) == (1.0, -8.0)
+    assert list(codes[0, :5]) == [15, 2, 0, 14, 0]
+
+
+def test_int8_query_ties_round_half_to_even():
+    x = np.zeros(128)
+    x[0], x[1:7] = 127.0, [2.5, -0.5, 126.5, -126.5, 1.5, 0.5]
+    q8, sq = quant.quantize_q_int8(x)
+    assert sq == 1.0
+    assert list(q8[:7]) == [127, 2, 0, 126, -126, 2, 0]
+
+
+def test_had_int4_tie_in_the_rotated_basis():
+    """x = 16 h0 + h1 - h2 + 1.5 h3 (rows of the +-1 Sylvester matrix): every butterfly sum is exact,
+    so the rotated row is c * [2048, 128, -128, 192, 0, ...] with c = f32(1/sqrt(128)), where 2048 c
+    and 128 c are exact and 192 c is one f32 rounding.  The scale is 2048 c / 8 = 256 c exactly;
+    the quotients are 8 (clamped to 7), exactly +0.5 and -0.5 (half to even: 0 and 0; half away
+    from zero would give 1 and -1) and about 0.75 (1; truncation would give 0)."""
+    import scipy.linalg
+    H = scipy.linalg.hadamard(128).astype(np.float64)
+    x = 16 * H[0] + H[1] - H[2] + 1.5 * H[3]
+    rot, codes, s = quant.quantize_had_int4(x[None, :])
+    from oracle.fwht import norm_const_f32
+    c = norm_const_f32(128)
+    assert s[0] == 256 * c
+    assert list(codes[0, :5]) == [7, 0, 0, 1, 0]
+    assert not codes[0, 4:].any()
