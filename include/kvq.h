@@ -49,7 +49,12 @@ extern "C" {
  *   Q8_0      [FreeToken-268] Summary and memory table (8-bit block scheme,
  *             1.0625 bytes per element): 32-element blocks, fp16 scale amax/128,
  *             codes [-128, 127] stored one per byte as two's complement, in
- *             element order.  payload D, record 2*D/32. */
+ *             element order.  payload D, record 2*D/32.
+ * Range.  The attention kernels run the P V product on fp16 operands.  For the
+ * layouts with fp16 scales (Q4_0, Q6_0, ASYM_INT4_G32, Q8_0) each dequantised V
+ * element is formed in fp16, so V rows must dequantise to within +-65504 (a
+ * row past that reads as infinite).  HAD_INT4 folds its f32 V scale into the
+ * softmax weights relative to a power of two (no limit short of f32's). */
 typedef enum kvq_layout {
   KVQ_LAYOUT_HAD_INT4 = 0,
   KVQ_LAYOUT_Q4_0 = 1,
@@ -174,10 +179,11 @@ kvq_status kvq_attend_decode(const kvq_cache* cache, const float* q, float* out,
  * into a standard attention) and [Open-TQ-Metal]'s fused kernel (a
  * pre-divided floating-point query against the packed nibbles) read the
  * cache.  The integer dots run on the same packed codes with the query
- * expanded to two int8 terms, sq * (q8 + r8 / 254) with sq = amax|q| / 127,
- * which holds the f32 query to within half a step of sq / 254 (amax|q| / 64516)
- * per element; V, the window, the merge and every argument are those of
- * kvq_attend_decode (same workspace size and errors). */
+ * expanded to three int8 terms, sq * (q8 + r1 / 254 + r2 / 254^2) with
+ * sq = amax|q| / 127, which holds the f32 query to within about amax|q| / 2^24
+ * per element (the resolution of f32 at the vector's largest element); V, the
+ * window, the merge and every argument are those of kvq_attend_decode (same
+ * workspace size and errors). */
 kvq_status kvq_attend_decode_float_q(const kvq_cache* cache, const float* q, float* out,
                                      int32_t batch, int32_t num_q_heads, float alpha,
                                      const int32_t* block_table, int32_t max_pages_per_seq,
@@ -213,16 +219,18 @@ size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t num_q_hea
                                    int32_t head_dim, int32_t max_seq_len);
 
 /* Causal prefill over the packed cache, called after kvq_store of the chunk.
- * [tract-RFC] Architecture (prefill appends the chunk, then attends each
- * position with its causal limit) and Causality & mixed precision (causal
- * skip is bit-identical to compute-then-mask).  Query i of row b sits at
+ * [tract-RFC] Architecture (the prefill path: store the chunk first, then run
+ * attention in which every query is bounded by its own position) and
+ * Causality & mixed precision (skipping the work past a query's bound gives
+ * the same bits as computing it and masking).  Query i of row b sits at
  * position q_start[b] + i and, when causal != 0, sees tokens t <= q_start[b] + i;
  * KV tiles wholly past the limit are skipped unless flags has
  * KVQ_PREFILL_NO_CAUSAL_SKIP (same bits, masked tiles streamed).  The window
  * is the last n_recent positions of the row, the same for every query, masked
  * per query like the packed tokens.  Scores, scales and the HAD_INT4 rotation
  * are those of kvq_attend_decode; a query whose limit covers the whole row
- * gets the decode output exactly.
+ * gets the decode output up to float re-association (the two kernels add the
+ * same terms in different orders; tested to 2e-3 * max|o|).
  *   q          device f32 [batch][n_q][num_q_heads][head_dim]
  *   out        device f32 [batch][n_q][num_q_heads][head_dim]
  *   causal     0 or 1; with 0 every query sees all seq_len[b] tokens

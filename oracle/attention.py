@@ -18,8 +18,8 @@ organization: kv_head = head_idx / gqa_factor):
   the f32 query (reading: the pages report that a full window is exact, which
   only holds with an unquantised query).
 * mask: causal prefill hides t > q_start + i from query i ([tract-RFC]
-  Causality & mixed precision; Architecture: prefill appends the chunk, then
-  attends each position with its causal limit).  Decode is single-query and
+  Causality & mixed precision; Architecture: the chunk is stored first and
+  each query is then bounded by its own position).  Decode is single-query and
   sees every cached token.
 * Hadamard layout: the output is rotated back, o <- H o ([tract-RFC] data
   flow, un-rotate step).

@@ -256,18 +256,77 @@ __device__ __forceinline__ v8h v_operand(const VOctet<L>& v, int e, uint32_t mag
   return A;
 }
 
+// Float-query mode: the scores (before the softmax scale) of the lane's four tokens t0 + j of one
+// 16-token half, with the query in three int8 terms (prepare_row_lanes): per 32-element block, three
+// int8 MFMAs on the same unpacked codes, folded at once into (254 I(q8) + I(r1)) * 254 + I(r2) (the
+// bracket exact in i32) and, for the block layouts, times the block's scale (the offset term is added
+// by the caller); the Hadamard layout sums the three terms over the whole row first and subtracts
+// their offsets qoff[0..2].  Each block's three accumulators die with the block.
+// One16: the 16-row tile's half (A = the half's tokens, B = qB as it is); else the 8-row tile, whose
+// two halves share the MFMA tile (A = half h's tokens, B = the query in the columns of half h, the lane
+// reading half hh).
+template <int L, int D, class ST>
+__device__ __forceinline__ void fq_scores(const unsigned char* kbuf, int arow, int t0, int r, bool one16,
+                                          const long* qB, const long* qBl, const int* qoff, float* xq, int hh = 0) {
+  constexpr int NG = D / 32;
+  constexpr int SB = ST::SB;
+  const int nh = one16 ? 1 : 2;
+  if (L == HAD) {
+    v4i a0 = v4i{0, 0, 0, 0}, a1 = v4i{0, 0, 0, 0}, a2 = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h >= nh) break;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const long A = k_operand<L, ST>(kbuf, one16 ? arow : 16 * h + arow, g, r);
+        const bool on = one16 || hh == h;
+        a0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, on ? qB[g] : 0, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, on ? qBl[g] : 0, a1, 0, 0, 0);
+        a2 = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, on ? qBl[NG + g] : 0, a2, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      xq[j] = fmaf((float)(254 * (a0[j] - qoff[0]) + (a1[j] - qoff[1])), 254.0f, (float)(a2[j] - qoff[2]));
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) xq[j] = 0.0f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    v4i a0 = v4i{0, 0, 0, 0}, a1 = v4i{0, 0, 0, 0}, a2 = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h >= nh) break;
+      const long A = k_operand<L, ST>(kbuf, one16 ? arow : 16 * h + arow, g, r);
+      const bool on = one16 || hh == h;
+      a0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, on ? qB[g] : 0, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, on ? qBl[g] : 0, a1, 0, 0, 0);
+      a2 = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, on ? qBl[NG + g] : 0, a2, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned char* rec = kbuf + ST::KR + (t0 + j) * SB;
+      const uint32_t w = rec_word(rec, (L == ASYM) ? g : (g >> 1));
+      const float sc = (float)as_h2(w)[(L == ASYM) ? 0 : (g & 1)];
+      xq[j] = fmaf(sc, fmaf((float)(254 * a0[j] + a1[j]), 254.0f, (float)a2[j]), xq[j]);
+    }
+  }
+}
+
 // One 32-token step of a wave: Q K^T, online softmax, P V, all from the staged rows in `buf`.
 // FULL: every token of the step is inside the chunk and visible to every row (no masking).
 // Otherwise tokens at or past t_end are dropped (their staged rows may hold anything, so their
 // scales are zeroed too) and tokens past `lim`, the limit of this lane's row, get p = 0.
 // drow: flat row index of this lane's row for the score export (DBG), or -1.
-// FQ: float-query mode; qBl holds the query's residual term, and every block dot becomes
-// 254 I(q8) + I(residual) (qsB, qoff and sqc come scaled to match).
+// FQ: float-query mode; qBl holds the query's two residual terms r1 (blocks 0 .. NG - 1) and r2
+// (NG .. 2 NG - 1), and every block dot becomes (254 I(q8) + I(r1)) * 254 + I(r2) (qsB and sqc come
+// scaled to match; the Hadamard layout's qoff holds the three terms' offsets).
 template <int L, int D, class ST, bool DBG, bool FULL, bool FQ>
 __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned char* buf, int T0, int t_end,
                                             int lim, long drow, int col, int r, const long* qB, const long* qBl,
                                             const float* qsB, const int* qoff, float sqc, uint32_t magic,
-                                            float& m_run, float& l_run, v4f* oacc) {
+                                            float& m_run, float& l_run, int& e_run, v4f* oacc) {
   using T = Layout<L, D>;
   constexpr int NG = T::NG;
   constexpr int SG = T::SG;
@@ -279,24 +338,20 @@ __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned 
   float vs_had[8];
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
-    v4i acc[SG], accl[SG];
+    v4i acc[SG];
+    float xq[4];   // float-query mode: the tokens' scores before the softmax scale
+    if constexpr (FQ) {
+      fq_scores<L, D, ST>(buf, 16 * tau + col, 16 * tau + 4 * r, r, true, qB, qBl, qoff, xq);
+    } else {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const long A = k_operand<L, ST>(buf, 16 * tau + col, g, r);
-      const long B = qB[g];
-      if (L == HAD) {
-        acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[0], 0, 0, 0);
-        if (FQ) accl[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, qBl[g], g == 0 ? v4i{0, 0, 0, 0} : accl[0], 0, 0, 0);
-      } else {
-        acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
-        if (FQ) accl[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, qBl[g], v4i{0, 0, 0, 0}, 0, 0, 0);
+      for (int g = 0; g < NG; ++g) {
+        const long A = k_operand<L, ST>(buf, 16 * tau + col, g, r);
+        const long B = qB[g];
+        if (L == HAD)
+          acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[0], 0, 0, 0);
+        else
+          acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
       }
-    }
-    if (FQ) {
-#pragma unroll
-      for (int g = 0; g < SG; ++g)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[g][j] = 254 * acc[g][j] + accl[g][j];
     }
     // offset term: A[t = col][k = r] from the record of token 16*tau + col
     v4f xo = v4f{0.f, 0.f, 0.f, 0.f};
@@ -316,15 +371,15 @@ __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned 
       const unsigned char* rec = buf + ST::KR + tl * SB;
       float x;
       if (L == HAD) {
-        const int I = acc[0][j] - qoff[0];
-        x = *reinterpret_cast<const float*>(rec) * (float)I;
+        const int I = FQ ? 0 : acc[0][j] - qoff[0];
+        x = *reinterpret_cast<const float*>(rec) * (FQ ? xq[j] : (float)I);
         if (DBG && ok && drow >= 0) a.dbg[(size_t)drow * a.max_seq_len + T0 + tl] = I;
         const float vsc = *reinterpret_cast<const float*>(buf + ST::VR + tl * SB);
         vs_had[tau * 4 + j] = ok ? vsc : 0.0f;
       } else {
-        x = xo[j];
+        x = FQ ? xo[j] + xq[j] : xo[j];
 #pragma unroll
-        for (int g = 0; g < SG; ++g) {
+        for (int g = 0; g < (FQ ? 0 : SG); ++g) {
           // scale of block g: low half of word g (asym: scale|zero), or half g of the packed fp16 scales
           const uint32_t w = rec_word(rec, (L == ASYM) ? g : (g >> 1));
           const float s = (float)as_h2(w)[(L == ASYM) ? 0 : (g & 1)];
@@ -345,21 +400,33 @@ __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned 
   smax = max_over_rows(smax);
   const float m_new = fmaxf(m_run, smax);
   const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-  // rescale the running sums only when some lane's maximum moved (rare after the first steps)
-  if (__any(m_new > m_run)) {
+  // Hadamard layout: the exponent of the largest V scale so far (a lane's 8 tokens, then the four
+  // lane rows: all 32 tokens of the step)
+  int e_new = e_run;
+  if (L == HAD) {
+    float vmax = vs_had[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) vmax = fmaxf(vmax, vs_had[i]);
+    e_new = max(e_run, vscale_exp(max_over_rows(vmax)));
+  }
+  // rescale the running sums only when some lane's maximum (or the V exponent) moved (rare after the
+  // first steps)
+  if (__any(m_new > m_run || e_new > e_run)) {
     const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
     l_run *= corr;
+    const float ocorr = L == HAD ? __builtin_amdgcn_ldexpf(corr, e_run - e_new) : corr;
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) oacc[i] *= corr;
+    for (int i = 0; i < D / 16; ++i) oacc[i] *= ocorr;
   }
   m_run = m_new;
+  e_run = e_new;
   float psum = 0.0f;
   v8h pB;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float p = __builtin_amdgcn_exp2f(xs[i] - m_use);
     psum += p;
-    pB[i] = (_Float16)(L == HAD ? p * vs_had[i] : p);
+    pB[i] = (_Float16)(L == HAD ? p * __builtin_amdgcn_ldexpf(vs_had[i], -e_new) : p);
   }
   l_run += psum;
 
@@ -397,7 +464,8 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
                                              int T0, int t_end,
                                              int lim, long drow, int col, int r, const long* qB, const long* qBl,
                                              const float* qsB, const int* qoff, float sqc,
-                                             uint32_t magic, float& m_run, float& l_run, v4f* oacc, MID&& mid) {
+                                             uint32_t magic, float& m_run, float& l_run, int& e_run, v4f* oacc,
+                                             MID&& mid) {
   using T = Layout<L, D>;
   constexpr int NG = T::NG;
   constexpr int SG = T::SG;
@@ -407,28 +475,23 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
 
   // ---------------- Q K^T: both halves into one tile
   constexpr int NACC = SG == 1 ? 2 : SG;
-  v4i acc[NACC], accl[NACC];
+  v4i acc[NACC];
+  float xq[4];   // float-query mode: the tokens' scores before the softmax scale
+  if constexpr (FQ) {
+    fq_scores<L, D, ST>(kbuf, col, 16 * hh + 4 * r, r, false, qB, qBl, qoff, xq, hh);
+  } else {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const long A = k_operand<L, ST>(kbuf, 16 * h + col, g, r);
-      const long B = (hh == h) ? qB[g] : 0;   // the rows' queries in the columns of half h
-      const long Bl = FQ && hh == h ? qBl[g] : 0;
-      if (L == HAD) {
-        acc[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[h], 0, 0, 0);
-        if (FQ) accl[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, Bl, g == 0 ? v4i{0, 0, 0, 0} : accl[h], 0, 0, 0);
-      } else {
-        acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, h == 0 ? v4i{0, 0, 0, 0} : acc[g], 0, 0, 0);
-        if (FQ) accl[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, Bl, h == 0 ? v4i{0, 0, 0, 0} : accl[g], 0, 0, 0);
+      for (int g = 0; g < NG; ++g) {
+        const long A = k_operand<L, ST>(kbuf, 16 * h + col, g, r);
+        const long B = (hh == h) ? qB[g] : 0;   // the rows' queries in the columns of half h
+        if (L == HAD)
+          acc[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, g == 0 ? v4i{0, 0, 0, 0} : acc[h], 0, 0, 0);
+        else
+          acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, h == 0 ? v4i{0, 0, 0, 0} : acc[g], 0, 0, 0);
       }
     }
-  }
-  if (FQ) {
-#pragma unroll
-    for (int i = 0; i < NACC; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = 254 * acc[i][j] + accl[i][j];
   }
   v4f xo = v4f{0.f, 0.f, 0.f, 0.f};
   if (L != HAD && L != Q80) {   // the 8-bit K codes carry no offset
@@ -451,13 +514,13 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
     const unsigned char* rec = kbuf + ST::KR + tl * SB;
     float x;
     if (L == HAD) {
-      const int I = acc[0][j] + acc[1][j] - qoff[0];
-      x = *reinterpret_cast<const float*>(rec) * (float)I;
+      const int I = FQ ? 0 : acc[0][j] + acc[1][j] - qoff[0];
+      x = *reinterpret_cast<const float*>(rec) * (FQ ? xq[j] : (float)I);
       if (DBG && ok && drow >= 0) a.dbg[(size_t)drow * a.max_seq_len + T0 + tl] = I;
     } else {
-      x = xo[j];
+      x = FQ ? xo[j] + xq[j] : xo[j];
 #pragma unroll
-      for (int g = 0; g < SG; ++g) {
+      for (int g = 0; g < (FQ ? 0 : SG); ++g) {
         const uint32_t w = rec_word(rec, (L == ASYM) ? g : (g >> 1));
         const float s = (float)as_h2(w)[(L == ASYM) ? 0 : (g & 1)];
         x = fmaf(s, (float)acc[g][j], x);
@@ -476,26 +539,38 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
   smax = fmaxf(smax, half_swap(smax));
   const float m_new = fmaxf(m_run, smax);
   const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-  if (__any(m_new > m_run)) {
+  // Hadamard layout: the V scales of the lane's 4 tokens (V side: read after the V half has landed;
+  // zero past the chunk's end) and the exponent of the largest so far (the four lane rows and the
+  // two halves: all 32 tokens of the step)
+  float vsc[4];
+  int e_new = e_run;
+  if (L == HAD) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tl = 16 * hh + 4 * r + j;
+      const float v = *reinterpret_cast<const float*>(vbuf + ST::VR + tl * SB);
+      vsc[j] = (FULL || T0 + tl < t_end) ? v : 0.0f;
+    }
+    float vmax = max_over_rows(fmaxf(fmaxf(vsc[0], vsc[1]), fmaxf(vsc[2], vsc[3])));
+    vmax = fmaxf(vmax, half_swap(vmax));
+    e_new = max(e_run, vscale_exp(vmax));
+  }
+  if (__any(m_new > m_run || e_new > e_run)) {
     const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
     l_run *= corr;
+    const float ocorr = L == HAD ? __builtin_amdgcn_ldexpf(corr, e_run - e_new) : corr;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) oacc[i] *= corr;
+    for (int i = 0; i < D / 32; ++i) oacc[i] *= ocorr;
   }
   m_run = m_new;
+  e_run = e_new;
   float psum = 0.0f;
   _Float16 ph[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float p = __builtin_amdgcn_exp2f(xs[j] - m_use);
     psum += p;
-    float pv = p;
-    if (L == HAD) {   // the token's V scale (V side: read after the V half has landed)
-      const int tl = 16 * hh + 4 * r + j;
-      const float vsc = *reinterpret_cast<const float*>(vbuf + ST::VR + tl * SB);
-      pv = (FULL || T0 + tl < t_end) ? p * vsc : 0.0f;
-    }
-    ph[j] = (_Float16)pv;
+    ph[j] = (_Float16)(L == HAD ? p * __builtin_amdgcn_ldexpf(vsc[j], -e_new) : p);
   }
   l_run += psum;
   // B operand of P V: k-slots 0..3 hold half 0's tokens, 4..7 half 1's; the other half's
@@ -603,52 +678,58 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
   const int nsteps = active ? (t_end - t_begin + 31) / 32 : 0;
 
   // ---- prologue: this lane's row of the tile, prepared in the wave (int8 query in the B-operand
-  // order, its scale and block sums; float-query mode: also the residual term, with the block sums
-  // and the scale taken for 254 I(q8) + I(residual)).  With 8-row tiles lane column col serves row
-  // col & 7, and its operands are zero outside its half.
+  // order, its scale and block sums; float-query mode: also the two residual terms, with the block
+  // sums and the scale taken for (254 I(q8) + I(r1)) * 254 + I(r2)).  With 8-row tiles lane column
+  // col serves row col & 7, and its operands are zero outside its half.
   const int col = lane & 15;
   const int r = lane >> 4;
   const int rsel = TR == 8 ? (col & 7) : col;   // this lane's row within the tile
   const int hh = col >> 3;
   long qB[NG];          // B operands (int8 query of the tile's rows), one aligned register pair each
-  long qBl[NG];         // float-query mode: the residual term's B operands
+  long qBl[2 * NG];     // float-query mode: the residual terms' B operands (r1, then r2)
   float qsB[NG / 4];    // offset-term operand: zero point (asym) or -bias * scale times the block sums
-  int qoff[SG];        // bias * sum(q8): the Hadamard scores and the score export use it
+  // bias * sum(q8): the Hadamard scores and the score export use it (float-query mode, Hadamard
+  // layout: the offsets of q8, r1 and r2)
+  int qoff[SG < 3 ? 3 : SG];
   float sqc = 0.0f;
   {
     RowQ<D> rq;
     prepare_row_lanes<L, D, FQ>(a.q + row_index(a, b, hk, row0 + min(rsel, nvalid - 1)) * D, r, rq);
-    int qsum[NG];
+    float qsf[NG];   // each block's sum as the offset term takes it
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       qB[g] = rq.qB[g];
       qBl[g] = FQ ? rq.qBl[g] : 0;
-      qsum[g] = FQ ? 254 * rq.qsum[g] + rq.qsuml[g] : rq.qsum[g];
+      qBl[NG + g] = FQ ? rq.qBl[NG + g] : 0;
+      qsf[g] = FQ ? fmaf((float)(254 * rq.qsum[g] + rq.qsuml[g]), 254.0f, (float)rq.qsuml[NG + g]) : (float)rq.qsum[g];
     }
 #pragma unroll
     for (int i = 0; i < NG / 4; ++i) {
-      const int qs = r == 0 ? qsum[4 * i] : r == 1 ? qsum[4 * i + 1] : r == 2 ? qsum[4 * i + 2] : qsum[4 * i + 3];
-      qsB[i] = (L == ASYM) ? (float)qs : -(float)BIAS * (float)qs;
+      const float qs = r == 0 ? qsf[4 * i] : r == 1 ? qsf[4 * i + 1] : r == 2 ? qsf[4 * i + 2] : qsf[4 * i + 3];
+      qsB[i] = (L == ASYM) ? qs : -(float)BIAS * qs;
     }
 #pragma unroll
-    for (int g = 0; g < SG; ++g) {
+    for (int t = 0; t < (SG < 3 ? 3 : SG); ++t) {
+      // term t of the Hadamard float-query mode, else block t
+      const int* src = t == 0 || !FQ || L != HAD ? rq.qsum : rq.qsuml + (t - 1) * NG;
       int sum = 0;
       if (L == HAD) {
 #pragma unroll
-        for (int gg = 0; gg < NG; ++gg) sum += qsum[gg];
+        for (int gg = 0; gg < NG; ++gg) sum += src[gg];
       } else {
-        sum = qsum[g];
+        sum = t < NG ? rq.qsum[t] : 0;
       }
-      qoff[g] = BIAS * sum;
+      qoff[t] = BIAS * sum;
     }
     sqc = rq.sq * a.alpha * KVQ_LOG2E;
-    if (FQ) sqc = sqc / 254.0f;
+    if (FQ) sqc = sqc / 64516.0f;
   }
   const int lim = row_limit(a, qs0, row0 + rsel, nrows);
   const long drow = (DBG && rsel < nvalid) ? (long)row_index(a, b, hk, row0 + rsel) : -1;   // score export only
   if (DBG && !has_chunk) return;
 
   float m_run = -INFINITY, l_run = 0.0f;
+  int e_run = kNoExp;   // Hadamard layout: the accumulators are in units of 2^e_run
   constexpr int NACC = TR == 8 ? D / 32 : D / 16;
   v4f oacc[NACC];
 #pragma unroll
@@ -663,20 +744,21 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
     float l = sum_over_rows(l_run);
     if (TR == 8) l += half_swap(l);   // the row's other half of the tokens
     float* dst = mo + rsel * partial_stride(D);
+    const float us = L == HAD ? __builtin_amdgcn_ldexpf(1.0f, e_run) : 1.0f;   // the accumulators' unit
     if (TR == 8) {
 #pragma unroll
       for (int o = 0; o < NO; ++o)
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + 2 * pt + hh] = oacc[o * 4 + pt][j];
+          for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + 2 * pt + hh] = oacc[o * 4 + pt][j] * us;
     } else {
 #pragma unroll
       for (int o = 0; o < NO; ++o)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + e] = oacc[o * 8 + e][j];
+          for (int j = 0; j < 4; ++j) dst[8 * (4 * r + j + 16 * o) + e] = oacc[o * 8 + e][j] * us;
     }
     if (r == 0 && (TR == 16 || hh == 0)) {
       dst[D] = m_run;
@@ -689,17 +771,17 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
     if (TR == 8) {
       if (full)
         attend_step8<L, D, ST, DBG, true, FQ>(a, kbuf, vbuf, T, t_end, lim, drow, col, r, qB, qBl, qsB, qoff, sqc,
-                                              magic, m_run, l_run, oacc, mid);
+                                              magic, m_run, l_run, e_run, oacc, mid);
       else
         attend_step8<L, D, ST, DBG, false, FQ>(a, kbuf, vbuf, T, t_end, lim, drow, col, r, qB, qBl, qsB, qoff, sqc,
-                                               magic, m_run, l_run, oacc, mid);
+                                               magic, m_run, l_run, e_run, oacc, mid);
     } else {
       if (full)
         attend_step<L, D, ST, DBG, true, FQ>(a, kbuf, T, t_end, lim, drow, col, r, qB, qBl, qsB, qoff, sqc, magic,
-                                             m_run, l_run, oacc);
+                                             m_run, l_run, e_run, oacc);
       else
         attend_step<L, D, ST, DBG, false, FQ>(a, kbuf, T, t_end, lim, drow, col, r, qB, qBl, qsB, qoff, sqc, magic,
-                                              m_run, l_run, oacc);
+                                              m_run, l_run, e_run, oacc);
     }
   };
 

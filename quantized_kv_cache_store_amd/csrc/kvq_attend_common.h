@@ -92,6 +92,17 @@ __device__ __forceinline__ float sum_over_rows(float v) {
   return a + b;
 }
 
+// The Hadamard layout keeps one f32 V scale per token, which the f16 P V product cannot carry at
+// every magnitude.  A wave keeps e, the binary exponent of the largest V scale it has seen
+// (s = m * 2^e with m in [0.5, 1), v_frexp_exp), and feeds the f16 P operand p * s / 2^e, which lies in
+// [0, 1] for every token so far; its accumulators are in units of 2^e, rescaled (exactly, by a power of
+// two) when e grows, and multiplied by 2^e in f32 when the partial is written.  The operands, and so
+// the accumulated bits, are the same for V scaled by any power of two.  kNoExp: nothing seen yet.
+constexpr int kNoExp = -(1 << 20);
+__device__ __forceinline__ int vscale_exp(float vmax) {
+  return vmax > 0.0f ? __builtin_amdgcn_frexp_expf(vmax) : kNoExp;
+}
+
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
@@ -148,18 +159,20 @@ __device__ __forceinline__ float butterfly_rows(float v, int swap32, bool upper)
 // of the encoding), each in f32, then f32(1/sqrt(D)); amax over the row, sq = amax / 127 (IEEE
 // division), q8 = rint(x / sq) clamped to [-127, 127]; per-block sums of q8.
 //
-// Float-query mode (FQ): the query also gets a second int8 term, the residual of the first at 254
-// times its resolution, lo = rint(f32(f32(x / sq) - q8) * 254) clamped to [-127, 127], so that
-// sq * (q8 + lo / 254) stands for x to within sq / 508.  The integer dot then runs twice on the same
-// codes, and 254 I(q8) + I(lo) is the block dot with that query (exact in i32).
+// Float-query mode (FQ): the query also gets two more int8 terms, each the residual of the terms
+// before it at 254 times their resolution: t1 = f32(f32(x / sq) - q8) * 254, r1 = rint(t1),
+// r2 = rint(f32(t1 - r1) * 254), all within [-127, 127], so that sq * (q8 + r1 / 254 + r2 / 254^2)
+// stands for x to within about sq / 129032 (f32 resolution at the vector's largest element).  The
+// integer dot then runs three times on the same codes, and (254 I(q8) + I(r1)) * 254 + I(r2) is
+// the block dot with that query (the bracket exact in i32, the rest one f32 rounding).
 template <int D>
 struct RowQ {
   long qB[D / 32];     // B operand of block g: codes [0, 2, 4, 6, 1, 3, 5, 7] of the lane's 8 (the order
                        // in which the A operand unpacks even and odd nibbles); the 8-bit layout, whose
                        // A operand is 8 stored bytes, takes them in element order [0 .. 7]
   int qsum[D / 32];    // sum of q8 over block g (every lane)
-  long qBl[D / 32];    // FQ: the residual term, same order
-  int qsuml[D / 32];   // FQ: its block sums
+  long qBl[2 * (D / 32)];    // FQ: the residual terms r1 (blocks 0 .. NG - 1) and r2 (NG .. 2 NG - 1), same order
+  int qsuml[2 * (D / 32)];   // FQ: their block sums
   float sq;
 };
 
@@ -231,7 +244,7 @@ __device__ __forceinline__ void prepare_row_lanes(const float* qrow, int r, RowQ
   out.sq = s;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    int c[8], cl[8], sum = 0, suml = 0;
+    int c[8], cl[8], cm[8], sum = 0, suml = 0, summ = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float y = s != 0.0f ? x[g][i] / s : 0.0f;
@@ -239,8 +252,12 @@ __device__ __forceinline__ void prepare_row_lanes(const float* qrow, int r, RowQ
       c[i] = (int)n;
       sum += c[i];
       if (FQ) {
-        cl[i] = (int)fminf(fmaxf(rintf((y - n) * 254.0f), -127.0f), 127.0f);
+        const float t1 = (y - n) * 254.0f;
+        const float r1 = fminf(fmaxf(rintf(t1), -127.0f), 127.0f);
+        cl[i] = (int)r1;
         suml += cl[i];
+        cm[i] = (int)fminf(fmaxf(rintf((t1 - r1) * 254.0f), -127.0f), 127.0f);
+        summ += cm[i];
       }
     }
     out.qB[g] = pack_b_operand<L>(c);
@@ -249,9 +266,13 @@ __device__ __forceinline__ void prepare_row_lanes(const float* qrow, int r, RowQ
     out.qsum[g] = sum;
     if (FQ) {
       out.qBl[g] = pack_b_operand<L>(cl);
+      out.qBl[NG + g] = pack_b_operand<L>(cm);
       suml += __shfl_xor(suml, 16);
       suml += __shfl_xor(suml, 32);
       out.qsuml[g] = suml;
+      summ += __shfl_xor(summ, 16);
+      summ += __shfl_xor(summ, 32);
+      out.qsuml[NG + g] = summ;
     }
   }
 }

@@ -1,9 +1,8 @@
 // Causal prefill over the packed cache.
 //
-// [tract-RFC] Architecture (prefill appends the chunk to the cache, then every
-// query position attends with its own causal limit) and Causality & mixed
-// precision (work wholly past the limit is skipped; the result equals
-// compute-then-mask).  The scores are the same int8(Q) . code(K) -> i32 block
+// [tract-RFC] Architecture (the prefill path stores the chunk first; attention
+// then bounds each query by its own position) and Causality & mixed precision
+// (skipping the work past a query's bound changes no bit of the result).  The scores are the same int8(Q) . code(K) -> i32 block
 // dots as decode, and the window and merge are those of decode.
 //
 // Rows and tiles as in the decode kernel: row R of (batch b, kv head hk) is query
@@ -50,14 +49,17 @@ static_assert(kPrefillChunk % 32 == 0, "chunks of whole 32-token steps");
 //       of block g (8-bit layout: the signed codes 8r .. 8r+7 in order);
 //   VT  dequantised V (fp16) in A-operand order of V^T: [d / 16][lane group r][d % 16][slot k],
 //       slot k holding token 16 (k / 4) + 4r + k % 4 (the same token order as the lane's P);
-//   KR  the raw K records of the 32 tokens.
+//   KR  the raw K records of the 32 tokens;
+//   VR  Hadamard layout: the f32 V scales of the 32 tokens (zero past the chunk's end), which its
+//       consumers fold into P (VT then holds the bare codes).
 template <int L, int D>
 struct PStep {
   using T = Layout<L, D>;
   static constexpr int KC = 0;
   static constexpr int VT = KC + T::NG * 1024;
   static constexpr int KR = VT + D * 64;
-  static constexpr int BYTES = KR + 32 * T::SB;
+  static constexpr int VR = KR + 32 * T::SB;
+  static constexpr int BYTES = VR + (L == HAD ? 32 * 4 : 0);
   static constexpr int KU = T::NG / 2;        // K units (token, block, lane group) per thread
   static constexpr int VU = D / 128;          // V units (element pair, lane group) per thread
 };
@@ -71,6 +73,7 @@ struct PLoad {
   uint32_t vh[PStep<L, D>::VU][8];  // q6_0: the byte of top-bit pairs of (d, d+1)
   uint32_t vs[PStep<L, D>::VU][8];  // V record word of the group of d (zeroed past the end)
   uint32_t kr;                      // one dword of the K records
+  uint32_t vr;                      // Hadamard layout: the V scale of token tid (tid < 32)
 };
 
 // Raw steps reach LDS by direct loads (the decode's staging layout: a K slot and a V slot per
@@ -132,17 +135,19 @@ __device__ __forceinline__ void prefill_fetch(const unsigned char* kslot, const 
         ld.vb[k][s] = (w >> (8 * ((d >> 1) & 3))) & 0xFFu;
       }
       const unsigned char* rec = vslot + ST::VR + t * SB;
-      if (L == HAD) ld.vs[k][s] = *reinterpret_cast<const uint32_t*>(rec);
+      if (L == HAD) ld.vs[k][s] = 0u;   // its scales go to VR (ld.vr)
       else if (L == ASYM) ld.vs[k][s] = *reinterpret_cast<const uint32_t*>(rec + 4 * g);
       else ld.vs[k][s] = *reinterpret_cast<const uint16_t*>(rec + 2 * g);
     }
   }
   ld.kr = *reinterpret_cast<const uint32_t*>(kslot + ST::KR + 4 * (tid < 8 * SB ? tid : 0));
+  if (L == HAD) ld.vr = *reinterpret_cast<const uint32_t*>(vslot + ST::VR + 4 * (tid & 31));
 }
 
 // Unpack and dequantise the loaded step into the LDS buffer.
 // n_tok: tokens of the step inside the chunk; the V scales of the others are zeroed so that their
-// (stale) rows contribute exact zeros.
+// (stale) rows contribute exact zeros.  The Hadamard layout's V^T holds the codes themselves (exact
+// in fp16) and its f32 scales go to VR for the consumers.
 template <int L, int D>
 __device__ __forceinline__ void prefill_produce(unsigned char* buf, int tid, const PLoad<L, D>& ld, int n_tok,
                                                 uint32_t magic) {
@@ -197,11 +202,7 @@ __device__ __forceinline__ void prefill_produce(unsigned char* buf, int tid, con
       const int t0 = 16 * (i >> 1) + r4 + 2 * (i & 1);     // tokens of slots 2i and 2i + 1
       const uint32_t w0 = t0 < n_tok ? ld.vs[k][2 * i] : 0u;
       const uint32_t w1 = t0 + 1 < n_tok ? ld.vs[k][2 * i + 1] : 0u;
-      if (L == HAD) {
-        const h2 s2 = h2{(_Float16)__builtin_bit_cast(float, w0), (_Float16)__builtin_bit_cast(float, w1)};
-        v0 = v0 * s2;
-        v1 = v1 * s2;
-      } else {
+      if (L != HAD) {
         const h2 s2 = as_h2(__builtin_amdgcn_perm(w1, w0, 0x05040100u));
         if (L == ASYM) {
           const h2 z2 = as_h2(__builtin_amdgcn_perm(w1, w0, 0x07060302u));
@@ -221,16 +222,19 @@ __device__ __forceinline__ void prefill_produce(unsigned char* buf, int tid, con
         u32x4{as_u32(highv[0]), as_u32(highv[1]), as_u32(highv[2]), as_u32(highv[3])};
   }
   if (tid < 8 * SB) *reinterpret_cast<uint32_t*>(buf + PS::KR + 4 * tid) = ld.kr;
+  if (L == HAD && tid < 32) *reinterpret_cast<uint32_t*>(buf + PS::VR + 4 * tid) = tid < n_tok ? ld.vr : 0u;
 }
 
 // One step of one wave: Q K^T for the wave's TPW tiles of 16 rows, online softmax, P V.  Each V^T
 // operand read from LDS serves every tile of the wave.
 // FULL: all 32 tokens exist and every row of the wave sees them.
+// e_run: Hadamard layout, the wave's V-scale exponent (vscale_exp); the accumulators are in units of
+// 2^e_run and P carries p * s_v / 2^e_run.
 template <int L, int D, bool FULL, int TPW>
 __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int lane, int T0, int n_tok, const int* lim,
                                                 const long (*qb)[D / 32], const float (*qsB)[(D / 32 + 3) / 4],
                                                 const int* qoff0, const float* sqc, float* m_run, float* l_run,
-                                                v4f (*oacc)[D / 16]) {
+                                                int& e_run, v4f (*oacc)[D / 16]) {
   using T = Layout<L, D>;
   using PS = PStep<L, D>;
   constexpr int NG = T::NG, SG = T::SG, SB = T::SB;
@@ -285,6 +289,25 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
     }
   }
 
+  // Hadamard layout: the V scales of the lane's 8 tokens (16 tau + 4 r + j) and the exponent of the
+  // largest so far (the four lane rows hold all 32 tokens)
+  float vsc[8];
+  int e_new = e_run;
+  if (L == HAD) {
+    const v4f a0 = *reinterpret_cast<const v4f*>(buf + PS::VR + 16 * r);
+    const v4f a1 = *reinterpret_cast<const v4f*>(buf + PS::VR + 64 + 16 * r);
+    float vmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vmax = fmaxf(vmax, fmaxf(a0[j], a1[j]));
+    }
+    e_new = max(e_run, vscale_exp(max_over_rows(vmax)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vsc[j] = __builtin_amdgcn_ldexpf(a0[j], -e_new);
+      vsc[4 + j] = __builtin_amdgcn_ldexpf(a1[j], -e_new);
+    }
+  }
   v8h pB[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
@@ -298,8 +321,9 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
         // registers into two copies (measured faster than skipping the product when no max moved)
       const float corr = __builtin_amdgcn_exp2f(m_run[u] - m_use);
       l_run[u] *= corr;
+      const float ocorr = L == HAD ? __builtin_amdgcn_ldexpf(corr, e_run - e_new) : corr;
 #pragma unroll
-      for (int i = 0; i < D / 16; ++i) oacc[u][i] *= corr;
+      for (int i = 0; i < D / 16; ++i) oacc[u][i] *= ocorr;
     }
     m_run[u] = m_new;
     float psum = 0.0f;
@@ -307,10 +331,11 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
     for (int i = 0; i < 8; ++i) {
       const float p = __builtin_amdgcn_exp2f(xs[u][i] - m_use);
       psum += p;
-      pB[u][i] = (_Float16)p;
+      pB[u][i] = (_Float16)(L == HAD ? p * vsc[i] : p);
     }
     l_run[u] += psum;
   }
+  e_run = e_new;
 
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
@@ -440,6 +465,7 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
   const int lim_min = row_limit(a, qs0, wrow0, nrows);   // the wave's smallest limit; -1 without rows
 
   float m_run[TPW], l_run[TPW];
+  int e_run = kNoExp;   // Hadamard layout: the accumulators are in units of 2^e_run
   v4f oacc[TPW][D / 16];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
@@ -520,7 +546,7 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
     const unsigned char* buf = smem + (s & 1) * PS::BYTES;
     const int n_tok = min(32, t_end - T0);
     if (nval[0] > 0)
-      prefill_consume<L, D, FULL, TPW>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, oacc);
+      prefill_consume<L, D, FULL, TPW>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, e_run, oacc);
   };
   int s = 0;
   for (; s < nfull; ++s) step(s, std::integral_constant<bool, true>{});
@@ -532,8 +558,9 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
     const float l = sum_over_rows(l_run[u]);
     if (col < nval[u]) {
       float* dst = a.ws + (row_index(a, b, hk, wrow0 + 16 * u + col) * a.nc1 + c) * partial_stride(D);
+      const float us = L == HAD ? __builtin_amdgcn_ldexpf(1.0f, e_run) : 1.0f;   // the accumulators' unit
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<v4f*>(dst + 16 * dt + 4 * r) = oacc[u][dt];
+      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<v4f*>(dst + 16 * dt + 4 * r) = oacc[u][dt] * us;
       if (r == 0) {
         dst[D] = m_run[u];
         dst[D + 1] = l;
