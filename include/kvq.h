@@ -191,6 +191,28 @@ kvq_status kvq_attend_decode_float_q(const kvq_cache* cache, const float* q, flo
                                      int32_t chunk_tokens, void* workspace, size_t workspace_bytes,
                                      void* stream);
 
+/* kvq_attend_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same kernels, with the split-K partials in a device scratch array of
+ * the library instead of a caller's workspace.  Every argument and result is
+ * that of kvq_attend_decode (int8-query mode).  No memory is allocated or
+ * freed, by the library or any routine it calls; each device holds one
+ * scratch array of KVQ_DECODE_NOALLOC_SCRATCH_BYTES from the library's load
+ * until the process ends.  A call needs batch * num_q_heads * (head_dim + 4)
+ * * 4 bytes per split-K group of the call (plus one group for the window);
+ * a call needing more than the scratch returns KVQ_ERR_WORKSPACE and launches
+ * nothing.  Calls on one device share its array: calls that overlap on that
+ * device (concurrent streams or host threads) race and give wrong results,
+ * so the caller orders them (one stream, or events).  Stream-ordered calls
+ * are independent: each overwrites every partial its own reduce reads.  The
+ * calling thread's current device must be the stream's device. */
+#define KVQ_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+kvq_status kvq_attend_decode_noalloc(const kvq_cache* cache, const float* q, float* out,
+                                     int32_t batch, int32_t num_q_heads, float alpha,
+                                     const int32_t* block_table, int32_t max_pages_per_seq,
+                                     const int32_t* seq_len, int32_t max_seq_len,
+                                     int32_t chunk_tokens, void* stream);
+
 /* The two phases of kvq_attend_decode as separate calls, for callers that time
  * or schedule them apart ([Open-TQ-Metal] split-K paragraphs: a partial phase
  * and a reduce phase ordered by their data dependency; here by stream order).

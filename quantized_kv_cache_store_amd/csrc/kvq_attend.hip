@@ -37,6 +37,8 @@
 // Steps that are partly visible mask per row.  With the skip off, the masked
 // tokens are streamed and contribute exact zeros, so both give the same bits.
 
+#include <atomic>
+
 #include "kvq_attend_common.h"
 
 namespace kvq {
@@ -1075,11 +1077,20 @@ static int decode_span(const kvq_cache* c, int batch, int Hq, int max_seq_len, i
 }
 
 // Workspace of the decode: room for the partials [B x Hq x (chunks + 1) x (D + 4)] f32 (the decode
-// kernel prepares its query rows itself).
+// kernel prepares its query rows itself).  A call writes fewer: one partial per group of a block's
+// four wave runs (decode_span) and the window's, so its partial slots per row are
+// decode_slots(...) <= chunks + 1, and decode_partials_bytes(...) is what it touches.
 static size_t decode_ws_bytes(int batch, int Hq, int D, int max_seq_len, int chunk) {
   const size_t rows = (size_t)batch * Hq;
   const size_t nc1 = (size_t)chunks_of(max_seq_len, chunk) + 1;
   return rows * nc1 * partial_stride(D) * sizeof(float);
+}
+
+static int decode_slots(int max_seq_len, int span) { return chunks_of(max_seq_len, 4 * span) + 1; }
+
+static size_t decode_partials_bytes(const kvq_cache* c, int batch, int Hq, int max_seq_len, int chunk) {
+  const int span = decode_span(c, batch, Hq, max_seq_len, chunk);
+  return (size_t)batch * Hq * decode_slots(max_seq_len, span) * partial_stride(c->head_dim) * sizeof(float);
 }
 
 static kvq_status check_chunk(const kvq_cache* c, int32_t chunk) {
@@ -1131,20 +1142,16 @@ extern "C" size_t kvq_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t 
   return decode_ws_bytes(batch, Hq, D, max_seq_len, chunk);
 }
 
-// The split-K phase of decode, in the int8-query mode or (fq) the float-query mode.
-static kvq_status decode_partial(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq, float alpha,
-                                 const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
-                                 int32_t max_seq_len, int32_t chunk, void* workspace, size_t ws_bytes, void* stream,
-                                 bool fq) {
-  kvq_status st = check_attend_args(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len);
-  if (st != KVQ_OK) return st;
-  if ((st = check_chunk(c, chunk)) != KVQ_OK) return st;
-  const size_t need = kvq_decode_workspace_bytes(batch, Hq, c->head_dim, max_seq_len, chunk);
-  if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+// The split-K phase of decode, in the int8-query mode or (fq) the float-query mode, after the
+// arguments were checked (decode_check) and with a workspace of at least decode_partials_bytes.
+static kvq_status decode_partial_ws(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq, float alpha,
+                                    const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
+                                    int32_t max_seq_len, int32_t chunk, void* workspace, void* stream, bool fq) {
   AttendArgs a = make_args(c, q, Hq, 1, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace);
   const int tr = tile_rows(a);
   a.span = decode_span(c, batch, Hq, max_seq_len, chunk);
   a.ngroups = chunks_of(max_seq_len, 4 * a.span) + (c->n_recent > 0 ? 1 : 0);
+  a.nc1 = decode_slots(max_seq_len, a.span);   // the window's slot is the last
   const int64_t gx = grid_x(a, tr);
   if (gx == 0) return KVQ_OK;
   a.batch = batch;
@@ -1154,12 +1161,40 @@ static kvq_status decode_partial(const kvq_cache* c, const float* q, int32_t bat
   return check_launch("decode partial kernel");
 }
 
+// The reduce phase over the partials decode_partial_ws wrote for the same arguments: each partial
+// slot holds a block's four wave runs of `span` tokens (merged by the partial kernel), the window's
+// partial the last slot.
+static kvq_status decode_reduce_ws(const kvq_cache* c, float* out, int32_t batch, int32_t Hq, const int32_t* seq_len,
+                                   int32_t max_seq_len, int32_t chunk, const void* workspace, void* stream) {
+  const int span = decode_span(c, batch, Hq, max_seq_len, chunk);
+  return launch_reduce(c, out, batch, Hq, seq_len, decode_slots(max_seq_len, span), 4 * span, (const float*)workspace,
+                       (hipStream_t)stream);
+}
+
+static kvq_status check_decode_workspace(const kvq_cache* c, int32_t batch, int32_t Hq, int32_t max_seq_len,
+                                         int32_t chunk, const void* workspace, size_t ws_bytes) {
+  const size_t need = kvq_decode_workspace_bytes(batch, Hq, c->head_dim, max_seq_len, chunk);
+  if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  return KVQ_OK;
+}
+
+static kvq_status decode_check(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
+                               const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
+                               int32_t max_seq_len, int32_t chunk) {
+  kvq_status st = check_attend_args(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len);
+  if (st != KVQ_OK) return st;
+  return check_chunk(c, chunk);
+}
+
 extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
                                                 float alpha, const int32_t* block_table, int32_t max_pages,
                                                 const int32_t* seq_len, int32_t max_seq_len, int32_t chunk,
                                                 void* workspace, size_t ws_bytes, void* stream) {
-  return decode_partial(c, q, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace,
-                        ws_bytes, stream, false);
+  kvq_status st = decode_check(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len, chunk);
+  if (st == KVQ_OK) st = check_decode_workspace(c, batch, Hq, max_seq_len, chunk, workspace, ws_bytes);
+  if (st != KVQ_OK) return st;
+  return decode_partial_ws(c, q, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace,
+                           stream, false);
 }
 
 extern "C" kvq_status kvq_attend_decode_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t Hq,
@@ -1171,34 +1206,86 @@ extern "C" kvq_status kvq_attend_decode_reduce(const kvq_cache* c, float* out, i
   if (batch < 1 || Hq < 1 || Hq % c->num_kv_heads) return fail(KVQ_ERR_INVALID_ARG, "bad batch or num_q_heads");
   if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len must be >= 0");
   if (chunk < 128 || chunk % 128) return fail(KVQ_ERR_INVALID_ARG, "chunk_tokens must be a positive multiple of 128");
-  const size_t need = kvq_decode_workspace_bytes(batch, Hq, c->head_dim, max_seq_len, chunk);
-  if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
-  // each partial slot holds a block's four waves of `span` tokens each (merged by the partial kernel)
-  const int span = decode_span(c, batch, Hq, max_seq_len, chunk);
-  return launch_reduce(c, out, batch, Hq, seq_len, chunks_of(max_seq_len, chunk) + 1, 4 * span, (const float*)workspace,
-                       (hipStream_t)stream);
+  if ((st = check_decode_workspace(c, batch, Hq, max_seq_len, chunk, workspace, ws_bytes)) != KVQ_OK) return st;
+  return decode_reduce_ws(c, out, batch, Hq, seq_len, max_seq_len, chunk, workspace, stream);
+}
+
+// Both phases, int8-query (fq = false) or float-query mode.
+static kvq_status decode_both(const kvq_cache* c, const float* q, float* out, int32_t batch, int32_t Hq, float alpha,
+                              const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
+                              int32_t max_seq_len, int32_t chunk, void* workspace, size_t ws_bytes, void* stream,
+                              bool fq) {
+  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out must be non-null");
+  kvq_status st = decode_check(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len, chunk);
+  if (st == KVQ_OK) st = check_decode_workspace(c, batch, Hq, max_seq_len, chunk, workspace, ws_bytes);
+  if (st != KVQ_OK) return st;
+  if ((st = decode_partial_ws(c, q, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace,
+                              stream, fq)) != KVQ_OK)
+    return st;
+  return decode_reduce_ws(c, out, batch, Hq, seq_len, max_seq_len, chunk, workspace, stream);
 }
 
 extern "C" kvq_status kvq_attend_decode(const kvq_cache* c, const float* q, float* out, int32_t batch, int32_t Hq,
                                         float alpha, const int32_t* block_table, int32_t max_pages,
                                         const int32_t* seq_len, int32_t max_seq_len, int32_t chunk,
                                         void* workspace, size_t ws_bytes, void* stream) {
-  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out must be non-null");
-  kvq_status st = decode_partial(c, q, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk,
-                                 workspace, ws_bytes, stream, false);
-  if (st != KVQ_OK) return st;
-  return kvq_attend_decode_reduce(c, out, batch, Hq, seq_len, max_seq_len, chunk, workspace, ws_bytes, stream);
+  return decode_both(c, q, out, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace,
+                     ws_bytes, stream, false);
 }
 
 extern "C" kvq_status kvq_attend_decode_float_q(const kvq_cache* c, const float* q, float* out, int32_t batch,
                                                 int32_t Hq, float alpha, const int32_t* block_table,
                                                 int32_t max_pages, const int32_t* seq_len, int32_t max_seq_len,
                                                 int32_t chunk, void* workspace, size_t ws_bytes, void* stream) {
+  return decode_both(c, q, out, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace,
+                     ws_bytes, stream, true);
+}
+
+// ----------------------------------------------------------------------------- decode without a workspace
+// The split-K partials of kvq_attend_decode_noalloc live in this file-scope device array, one copy
+// per device, held from the library's load until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it stands for a host-side shadow, not device memory): the
+// device address comes from hipGetSymbolAddress, once per device, with that device current.  The
+// kernels overwrite every slot the reduce reads, so nothing in it needs clearing between calls.
+namespace {
+constexpr size_t kNoAllocScratchBytes = KVQ_DECODE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+kvq_status scratch_address(void** out) {
+  static std::atomic<void*> addr_of[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(KVQ_ERR_HIP, "no current device below %d for the decode scratch", kMaxDevices);
+  void* p = addr_of[dev].load(std::memory_order_acquire);
+  if (!p) {
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KVQ_ERR_HIP, "hipGetSymbolAddress of the decode scratch on device %d: %s", dev, hipGetErrorString(e));
+    addr_of[dev].store(p, std::memory_order_release);   // racing first calls store the same address
+  }
+  *out = p;
+  return KVQ_OK;
+}
+}  // namespace
+
+extern "C" kvq_status kvq_attend_decode_noalloc(const kvq_cache* c, const float* q, float* out, int32_t batch,
+                                                int32_t Hq, float alpha, const int32_t* block_table,
+                                                int32_t max_pages, const int32_t* seq_len, int32_t max_seq_len,
+                                                int32_t chunk, void* stream) {
   if (!out) return fail(KVQ_ERR_INVALID_ARG, "out must be non-null");
-  kvq_status st = decode_partial(c, q, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk,
-                                 workspace, ws_bytes, stream, true);
+  kvq_status st = decode_check(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len, chunk);
   if (st != KVQ_OK) return st;
-  return kvq_attend_decode_reduce(c, out, batch, Hq, seq_len, max_seq_len, chunk, workspace, ws_bytes, stream);
+  const size_t need = decode_partials_bytes(c, batch, Hq, max_seq_len, chunk);
+  if (need > kNoAllocScratchBytes)
+    return fail(KVQ_ERR_WORKSPACE, "this decode needs %zu bytes of partials, above the %zu-byte scratch of "
+                "kvq_attend_decode_noalloc (use kvq_attend_decode with a workspace)", need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != KVQ_OK) return st;
+  if ((st = decode_partial_ws(c, q, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, ws, stream,
+                              false)) != KVQ_OK)
+    return st;
+  return decode_reduce_ws(c, out, batch, Hq, seq_len, max_seq_len, chunk, ws, stream);
 }
 
 extern "C" kvq_status kvq_debug_qk_i32(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,

@@ -134,6 +134,26 @@ def attend_decode(cache, q, block_table, seq_len, max_seq_len, alpha, chunk_toke
     return out
 
 
+def attend_decode_noalloc(cache, q, block_table, seq_len, max_seq_len, alpha, chunk_tokens=512, out=None):
+    """kvq_attend_decode_noalloc: attend_decode with the partials in the library's device scratch
+    (no workspace; calls that overlap on one device race)."""
+    dev = cache.device
+    _need(q, "q", torch.float32, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(seq_len, "seq_len", torch.int32, dev)
+    B, Hq, D = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_len.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_len [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float32, dev)
+    st = load().kvq_attend_decode_noalloc(cache.desc, _ptr(q), _ptr(out), B, Hq, float(alpha), _ptr(block_table),
+                                          block_table.shape[1], _ptr(seq_len), int(max_seq_len), int(chunk_tokens),
+                                          _stream(dev))
+    check("kvq_attend_decode_noalloc", st)
+    return out
+
+
 def attend_decode_partial(cache, q, block_table, seq_len, max_seq_len, alpha, chunk_tokens, workspace):
     """kvq_attend_decode_partial: the split-K phase; partials go to ``workspace``."""
     dev = cache.device

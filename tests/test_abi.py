@@ -107,3 +107,14 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libkvq.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load()
+
+
+def test_noalloc_decode_refuses_oversized_calls_on_the_host():
+    """kvq_attend_decode_noalloc checks its partials against the fixed scratch before any launch."""
+    lib = kvq.load()
+    d = ctypes.byref(_desc(layout=_lib.Q4_0, head_dim=128, num_kv_heads=1, page_size=16, num_pages=4))
+    # 64 rows x 64 query heads at 2^20 tokens: far above KVQ_DECODE_NOALLOC_SCRATCH_BYTES (32 MiB)
+    st = lib.kvq_attend_decode_noalloc(d, 16, 16, 64, 64, 1.0, 16, 1 << 16, 16, 1 << 20, 512, None)
+    assert st == 3
+    assert b"scratch" in lib.kvq_last_error()
+    assert lib.kvq_attend_decode_noalloc(d, 16, None, 1, 4, 1.0, 16, 4, 16, 64, 512, None) == 1   # out
