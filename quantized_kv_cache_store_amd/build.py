@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkvq.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["kvq_api.hip", "kvq_store.hip", "kvq_attend.hip", "kvq_prefill.hip", "kvq_probe.hip"]
+SOURCES = ["kvq_api.hip", "kvq_store.hip", "kvq_attend.hip", "kvq_prefill.hip", "kvq_probe.hip", "kvq_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -39,7 +39,7 @@ def _compile(src):
 
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         results = list(ex.map(_compile, SOURCES))
     for obj, msg in results:
         if verbose and msg.strip():

@@ -37,8 +37,6 @@
 // Steps that are partly visible mask per row.  With the skip off, the masked
 // tokens are streamed and contribute exact zeros, so both give the same bits.
 
-#include <atomic>
-
 #include "kvq_attend_common.h"
 
 namespace kvq {
@@ -460,14 +458,16 @@ __device__ __forceinline__ float half_swap(float v) { return __builtin_bit_cast(
 // numerators and the accumulated products are the same as in attend_step (the idle half adds
 // exact zeros); only the row sum l is added up in another order.
 // `mid` runs between the K side (Q K^T, scores) and the V side (softmax, P V): the direct-load
-// ring refills the K half of the slot there and waits for the V half.
-template <int L, int D, class ST, bool DBG, bool FULL, bool FQ, class MID>
+// ring refills the K half of the slot there and waits for the V half.  `vdone` runs as soon as
+// every read of the V half is done (the codes and scales held in registers), before the softmax and
+// the P V work on them: the ring refills the V half there.
+template <int L, int D, class ST, bool DBG, bool FULL, bool FQ, class MID, class VDONE>
 __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned char* kbuf, const unsigned char* vbuf,
                                              int T0, int t_end,
                                              int lim, long drow, int col, int r, const long* qB, const long* qBl,
                                              const float* qsB, const int* qoff, float sqc,
                                              uint32_t magic, float& m_run, float& l_run, int& e_run, v4f* oacc,
-                                             MID&& mid) {
+                                             MID&& mid, VDONE&& vdone) {
   using T = Layout<L, D>;
   constexpr int NG = T::NG;
   constexpr int SG = T::SG;
@@ -533,19 +533,18 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
     xs[j] = vis ? x * sqc : -INFINITY;
   }
   mid();
-  if (DBG) return;
+  if (DBG) {   // the score export: the V half is not read, but the ring's load counts expect its refill
+    vdone();
+    return;
+  }
 
-  // ---------------- online softmax (base 2): a row's 32 scores sit in lanes (col, r), (col ^ 8, r)
-  float smax = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
-  smax = max_over_rows(smax);
-  smax = fmaxf(smax, half_swap(smax));
-  const float m_new = fmaxf(m_run, smax);
-  const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-  // Hadamard layout: the V scales of the lane's 4 tokens (V side: read after the V half has landed;
-  // zero past the chunk's end) and the exponent of the largest so far (the four lane rows and the
-  // two halves: all 32 tokens of the step)
+  // ---------------- the V half into registers: per octet group the codes and scale (zero) pairs of
+  // the lane's 8 tokens; the Hadamard layout's per-token V scales of the lane's 4 tokens (zero past
+  // the chunk's end).  Then the slot is free.
+  VOctet<L> vo[NO];
+#pragma unroll
+  for (int o = 0; o < NO; ++o) load_voctet<L, ST, FULL>(vbuf, T0, t_end, col + 16 * o, r, vo[o]);
   float vsc[4];
-  int e_new = e_run;
   if (L == HAD) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -553,6 +552,19 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
       const float v = *reinterpret_cast<const float*>(vbuf + ST::VR + tl * SB);
       vsc[j] = (FULL || T0 + tl < t_end) ? v : 0.0f;
     }
+  }
+  vdone();
+
+  // ---------------- online softmax (base 2): a row's 32 scores sit in lanes (col, r), (col ^ 8, r)
+  float smax = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
+  smax = max_over_rows(smax);
+  smax = fmaxf(smax, half_swap(smax));
+  const float m_new = fmaxf(m_run, smax);
+  const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+  // Hadamard layout: the exponent of the largest V scale so far (the four lane rows and the two
+  // halves: all 32 tokens of the step)
+  int e_new = e_run;
+  if (L == HAD) {
     float vmax = max_over_rows(fmaxf(fmaxf(vsc[0], vsc[1]), fmaxf(vsc[2], vsc[3])));
     vmax = fmaxf(vmax, half_swap(vmax));
     e_new = max(e_run, vscale_exp(vmax));
@@ -586,12 +598,10 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
   // ---------------- P V: tile pt of octet group o takes elements 2 pt (columns 0..7) and 2 pt + 1
 #pragma unroll
   for (int o = 0; o < NO; ++o) {
-    VOctet<L> v;
-    load_voctet<L, ST, FULL>(vbuf, T0, t_end, col + 16 * o, r, v);
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
-      oacc[o * 4 + pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand<L>(v, 2 * pt, magic), pB0, oacc[o * 4 + pt], 0, 0, 0);
-      oacc[o * 4 + pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand<L>(v, 2 * pt + 1, magic), pB1, oacc[o * 4 + pt], 0, 0, 0);
+      oacc[o * 4 + pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand<L>(vo[o], 2 * pt, magic), pB0, oacc[o * 4 + pt], 0, 0, 0);
+      oacc[o * 4 + pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand<L>(vo[o], 2 * pt + 1, magic), pB1, oacc[o * 4 + pt], 0, 0, 0);
     }
   }
 }
@@ -682,11 +692,39 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
   // ---- prologue: this lane's row of the tile, prepared in the wave (int8 query in the B-operand
   // order, its scale and block sums; float-query mode: also the two residual terms, with the block
   // sums and the scale taken for (254 I(q8) + I(r1)) * 254 + I(r2)).  With 8-row tiles lane column
-  // col serves row col & 7, and its operands are zero outside its half.
+  // col serves row col & 7, and its operands are zero outside its half.  The row's elements are
+  // loaded first and the direct-load ring's first steps issued right after them, so that the HBM
+  // latency of both passes once, under the preparation's arithmetic.
   const int col = lane & 15;
   const int r = lane >> 4;
   const int rsel = TR == 8 ? (col & 7) : col;   // this lane's row within the tile
   const int hh = col >> 3;
+  float qx[NG][8];
+  load_row_lanes<D>(a.q + row_index(a, b, hk, row0 + min(rsel, nvalid - 1)) * D, r, qx);
+
+  // LDS rings of RK K slots and RV V slots per wave (step s in K slot s % RK and V slot s % RV).
+  // The K half of step s + RK is issued as soon as the K side of step s has read its slot, the
+  // V half of step s + RV as soon as the V side has read its slot, so the issue order is K(j + RK),
+  // V(j + RV) for j = ..., s - 1, s (the prologue issues the same order for negative j), and each
+  // half is waited for only where it is first read.  Loads complete in issue order, so the count of
+  // the groups issued after a half bounds the wait for it (stores in the loop, and the query row's
+  // loads issued before the prologue's, only make such a wait longer).
+  constexpr int RK = PS::RK, RV = PS::RV, MX = RK > RV ? RK : RV;
+  constexpr int G = ST::GROUP, H = ST::HALF;
+  static_assert(!PS::DMA || (2 * MX) * G <= 63, "load counter range");
+  unsigned char* kring = smem + wave * (RK + RV) * H;
+  unsigned char* vring = kring + RK * H;
+  const uint32_t kr_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)kring);
+  const uint32_t vr_lds = kr_lds + RK * H;
+  auto rows = [&](int st) { return half_rows_s(a, b, hk, t_begin + 32 * st, t_end); };
+  if constexpr (PS::DMA) {
+#pragma unroll
+    for (int j = -MX; j < 0; ++j) {
+      const int k = j + RK, v = j + RV;
+      if (k >= 0 && k < nsteps) issue_dma_half<ST, false>(a, rows(k), lane, kr_lds + k * H);
+      if (v >= 0 && v < nsteps) issue_dma_half<ST, true>(a, rows(v), lane, vr_lds + v * H);
+    }
+  }
   long qB[NG];          // B operands (int8 query of the tile's rows), one aligned register pair each
   long qBl[2 * NG];     // float-query mode: the residual terms' B operands (r1, then r2)
   float qsB[NG / 4];    // offset-term operand: zero point (asym) or -bias * scale times the block sums
@@ -696,7 +734,7 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
   float sqc = 0.0f;
   {
     RowQ<D> rq;
-    prepare_row_lanes<L, D, FQ>(a.q + row_index(a, b, hk, row0 + min(rsel, nvalid - 1)) * D, r, rq);
+    prepare_row_lanes<L, D, FQ>(qx, r, rq);
     float qsf[NG];   // each block's sum as the offset term takes it
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -768,15 +806,15 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
     }
   };
 
-  auto step = [&](const unsigned char* kbuf, const unsigned char* vbuf, int T, auto&& mid) {
+  auto step = [&](const unsigned char* kbuf, const unsigned char* vbuf, int T, auto&& mid, auto&& vdone) {
     const bool full = T + 32 <= t_end && T + 31 <= lim_min;
     if (TR == 8) {
       if (full)
         attend_step8<L, D, ST, DBG, true, FQ>(a, kbuf, vbuf, T, t_end, lim, drow, col, r, qB, qBl, qsB, qoff, sqc,
-                                              magic, m_run, l_run, e_run, oacc, mid);
+                                              magic, m_run, l_run, e_run, oacc, mid, vdone);
       else
         attend_step8<L, D, ST, DBG, false, FQ>(a, kbuf, vbuf, T, t_end, lim, drow, col, r, qB, qBl, qsB, qoff, sqc,
-                                               magic, m_run, l_run, e_run, oacc, mid);
+                                               magic, m_run, l_run, e_run, oacc, mid, vdone);
     } else {
       if (full)
         attend_step<L, D, ST, DBG, true, FQ>(a, kbuf, T, t_end, lim, drow, col, r, qB, qBl, qsB, qoff, sqc, magic,
@@ -788,21 +826,6 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
   };
 
   if constexpr (PS::DMA) {
-    // LDS rings of RK K slots and RV V slots per wave (step s in K slot s % RK and V slot s % RV).
-    // The K half of step s + RK is issued as soon as the K side of step s has read its slot, the
-    // V half of step s + RV after the V side, so the issue order is K(j + RK), V(j + RV) for
-    // j = ..., s - 1, s (the prologue issues the same order for negative j), and each half is
-    // waited for only where it is first read.  Loads complete in issue order, so the count of the
-    // groups issued after a half bounds the wait for it (stores in the loop only make such a wait
-    // longer).
-    constexpr int RK = PS::RK, RV = PS::RV, MX = RK > RV ? RK : RV;
-    constexpr int G = ST::GROUP, H = ST::HALF;
-    static_assert((2 * MX) * G <= 63, "load counter range");
-    unsigned char* kring = smem + wave * (RK + RV) * H;
-    unsigned char* vring = kring + RK * H;
-    const uint32_t kr_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)kring);
-    const uint32_t vr_lds = kr_lds + RK * H;
-    auto rows = [&](int st) { return half_rows_s(a, b, hk, t_begin + 32 * st, t_end); };
     auto wait_groups = [](int n) {
       switch (n) {
         case 0: wait_vm<0>(); break;
@@ -822,12 +845,6 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
     constexpr int S0 = RK - RV > 0 ? RK - RV : (RV - 1 - RK > 0 ? RV - 1 - RK : 0);
     constexpr int NK = (2 * RK - 1) * G <= 63 ? (2 * RK - 1) * G : 63;   // a smaller count only waits longer
     constexpr int NV = (2 * RV - 1) * G <= 63 ? (2 * RV - 1) * G : 63;
-#pragma unroll
-    for (int j = -MX; j < 0; ++j) {
-      const int k = j + RK, v = j + RV;
-      if (k >= 0 && k < nsteps) issue_dma_half<ST, false>(a, rows(k), lane, kr_lds + k * H);
-      if (v >= 0 && v < nsteps) issue_dma_half<ST, true>(a, rows(v), lane, vr_lds + v * H);
-    }
     int ks = 0, vs = 0;   // slots of step s
     for (int s = 0; s < nsteps; ++s) {
       const bool k_next = s + RK < nsteps, v_next = s + RV < nsteps;
@@ -848,8 +865,9 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
         else
           wait_groups(span_count(max(0, s - RV + 1 + RK), min(nsteps - 1, s + RK)) +
                       span_count(s + 1, min(nsteps - 1, s + RV - 1)));
+      }, [&]() {
+        if (v_next) issue_dma_half<ST, true>(a, hv_next, lane, vr_lds + vs * H);
       });
-      if (v_next) issue_dma_half<ST, true>(a, hv_next, lane, vr_lds + vs * H);
       ks = ks + 1 == RK ? 0 : ks + 1;
       vs = vs + 1 == RV ? 0 : vs + 1;
     }
@@ -871,7 +889,7 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
         const int su = si - (NB - 1);
         if (su >= 0 && su < nsteps) {
           stage_step<L, D>(buf, lane, pre[(k + 1) % NB]);
-          step(buf, buf, t_begin + 32 * su, [] {});
+          step(buf, buf, t_begin + 32 * su, [] {}, [] {});
         }
       }
     }
@@ -1088,7 +1106,7 @@ static size_t decode_ws_bytes(int batch, int Hq, int D, int max_seq_len, int chu
 
 static int decode_slots(int max_seq_len, int span) { return chunks_of(max_seq_len, 4 * span) + 1; }
 
-static size_t decode_partials_bytes(const kvq_cache* c, int batch, int Hq, int max_seq_len, int chunk) {
+size_t decode_partials_bytes(const kvq_cache* c, int batch, int Hq, int max_seq_len, int chunk) {
   const int span = decode_span(c, batch, Hq, max_seq_len, chunk);
   return (size_t)batch * Hq * decode_slots(max_seq_len, span) * partial_stride(c->head_dim) * sizeof(float);
 }
@@ -1144,7 +1162,7 @@ extern "C" size_t kvq_decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t 
 
 // The split-K phase of decode, in the int8-query mode or (fq) the float-query mode, after the
 // arguments were checked (decode_check) and with a workspace of at least decode_partials_bytes.
-static kvq_status decode_partial_ws(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq, float alpha,
+kvq_status kvq::decode_partial_ws(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq, float alpha,
                                     const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
                                     int32_t max_seq_len, int32_t chunk, void* workspace, void* stream, bool fq) {
   AttendArgs a = make_args(c, q, Hq, 1, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace);
@@ -1164,7 +1182,7 @@ static kvq_status decode_partial_ws(const kvq_cache* c, const float* q, int32_t 
 // The reduce phase over the partials decode_partial_ws wrote for the same arguments: each partial
 // slot holds a block's four wave runs of `span` tokens (merged by the partial kernel), the window's
 // partial the last slot.
-static kvq_status decode_reduce_ws(const kvq_cache* c, float* out, int32_t batch, int32_t Hq, const int32_t* seq_len,
+kvq_status kvq::decode_reduce_ws(const kvq_cache* c, float* out, int32_t batch, int32_t Hq, const int32_t* seq_len,
                                    int32_t max_seq_len, int32_t chunk, const void* workspace, void* stream) {
   const int span = decode_span(c, batch, Hq, max_seq_len, chunk);
   return launch_reduce(c, out, batch, Hq, seq_len, decode_slots(max_seq_len, span), 4 * span, (const float*)workspace,
@@ -1178,7 +1196,7 @@ static kvq_status check_decode_workspace(const kvq_cache* c, int32_t batch, int3
   return KVQ_OK;
 }
 
-static kvq_status decode_check(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
+kvq_status kvq::decode_check(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
                                const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
                                int32_t max_seq_len, int32_t chunk) {
   kvq_status st = check_attend_args(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len);
@@ -1239,53 +1257,6 @@ extern "C" kvq_status kvq_attend_decode_float_q(const kvq_cache* c, const float*
                                                 int32_t chunk, void* workspace, size_t ws_bytes, void* stream) {
   return decode_both(c, q, out, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace,
                      ws_bytes, stream, true);
-}
-
-// ----------------------------------------------------------------------------- decode without a workspace
-// The split-K partials of kvq_attend_decode_noalloc live in this file-scope device array, one copy
-// per device, held from the library's load until the process ends.  Host code never passes the
-// array's name to a kernel (on the host it stands for a host-side shadow, not device memory): the
-// device address comes from hipGetSymbolAddress, once per device, with that device current.  The
-// kernels overwrite every slot the reduce reads, so nothing in it needs clearing between calls.
-namespace {
-constexpr size_t kNoAllocScratchBytes = KVQ_DECODE_NOALLOC_SCRATCH_BYTES;
-constexpr int kMaxDevices = 64;
-__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
-
-kvq_status scratch_address(void** out) {
-  static std::atomic<void*> addr_of[kMaxDevices] = {};
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return fail(KVQ_ERR_HIP, "no current device below %d for the decode scratch", kMaxDevices);
-  void* p = addr_of[dev].load(std::memory_order_acquire);
-  if (!p) {
-    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (e != hipSuccess || !p)
-      return fail(KVQ_ERR_HIP, "hipGetSymbolAddress of the decode scratch on device %d: %s", dev, hipGetErrorString(e));
-    addr_of[dev].store(p, std::memory_order_release);   // racing first calls store the same address
-  }
-  *out = p;
-  return KVQ_OK;
-}
-}  // namespace
-
-extern "C" kvq_status kvq_attend_decode_noalloc(const kvq_cache* c, const float* q, float* out, int32_t batch,
-                                                int32_t Hq, float alpha, const int32_t* block_table,
-                                                int32_t max_pages, const int32_t* seq_len, int32_t max_seq_len,
-                                                int32_t chunk, void* stream) {
-  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out must be non-null");
-  kvq_status st = decode_check(c, q, batch, Hq, block_table, max_pages, seq_len, max_seq_len, chunk);
-  if (st != KVQ_OK) return st;
-  const size_t need = decode_partials_bytes(c, batch, Hq, max_seq_len, chunk);
-  if (need > kNoAllocScratchBytes)
-    return fail(KVQ_ERR_WORKSPACE, "this decode needs %zu bytes of partials, above the %zu-byte scratch of "
-                "kvq_attend_decode_noalloc (use kvq_attend_decode with a workspace)", need, kNoAllocScratchBytes);
-  void* ws = nullptr;
-  if ((st = scratch_address(&ws)) != KVQ_OK) return st;
-  if ((st = decode_partial_ws(c, q, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, ws, stream,
-                              false)) != KVQ_OK)
-    return st;
-  return decode_reduce_ws(c, out, batch, Hq, seq_len, max_seq_len, chunk, ws, stream);
 }
 
 extern "C" kvq_status kvq_debug_qk_i32(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,

@@ -188,18 +188,23 @@ __device__ __forceinline__ long pack_b_operand(const int* c) {
   return __builtin_bit_cast(long, u32x2{lo, hi});
 }
 
-template <int L, int D, bool FQ = false>
-__device__ __forceinline__ void prepare_row_lanes(const float* qrow, int r, RowQ<D>& out) {
-#pragma clang fp contract(off)
-  constexpr int NG = D / 32;
-  float x[NG][8];
+// The lane row's elements 32 g + 8 r .. 32 g + 8 r + 7 of every block g of a query row (loaded apart
+// from the preparation, so that a kernel can issue other loads before it waits for these).
+template <int D>
+__device__ __forceinline__ void load_row_lanes(const float* qrow, int r, float (&x)[D / 32][8]) {
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
+  for (int g = 0; g < D / 32; ++g) {
     const float4 u = *reinterpret_cast<const float4*>(qrow + 32 * g + 8 * r);
     const float4 w = *reinterpret_cast<const float4*>(qrow + 32 * g + 8 * r + 4);
     x[g][0] = u.x; x[g][1] = u.y; x[g][2] = u.z; x[g][3] = u.w;
     x[g][4] = w.x; x[g][5] = w.y; x[g][6] = w.z; x[g][7] = w.w;
   }
+}
+
+template <int L, int D, bool FQ = false>
+__device__ __forceinline__ void prepare_row_lanes(float (&x)[D / 32][8], int r, RowQ<D>& out) {
+#pragma clang fp contract(off)
+  constexpr int NG = D / 32;
   if (L == HAD) {
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1)
@@ -767,5 +772,17 @@ kvq_status launch_rotate_rows(const kvq_cache* c, const float* k_new, const floa
 kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b, const int32_t* seq_len,
                          int nc1, int32_t chunk, const float* ws, hipStream_t s, int nwin_always = 0, int slice = 0,
                          int causal_nq = 0);
+
+// The decode's two phases (kvq_attend.hip), for kvq_attend_decode and its variants: decode_check
+// validates the arguments; decode_partial_ws and decode_reduce_ws then run the split-K phase and the
+// merge with the partials in `workspace`, which must hold decode_partials_bytes(...) bytes.
+kvq_status decode_check(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq, const int32_t* block_table,
+                        int32_t max_pages, const int32_t* seq_len, int32_t max_seq_len, int32_t chunk);
+size_t decode_partials_bytes(const kvq_cache* c, int batch, int Hq, int max_seq_len, int chunk);
+kvq_status decode_partial_ws(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq, float alpha,
+                             const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
+                             int32_t max_seq_len, int32_t chunk, void* workspace, void* stream, bool fq);
+kvq_status decode_reduce_ws(const kvq_cache* c, float* out, int32_t batch, int32_t Hq, const int32_t* seq_len,
+                            int32_t max_seq_len, int32_t chunk, const void* workspace, void* stream);
 
 }  // namespace kvq
