@@ -139,6 +139,19 @@ kvq_status kvq_store_chunk(const kvq_cache* cache, const float* k_new, const flo
                            const int32_t* block_table, int32_t max_pages_per_seq,
                            int32_t max_seq_len, void* stream);
 
+/* The split-K work split kvq_attend_decode executes for these arguments (it
+ * depends on the shape and the device's compute-unit count): each wave
+ * streams *wave_tokens consecutive tokens of one (batch row, kv head) as one
+ * run (whole chunk_tokens chunks, or a half or quarter chunk for short
+ * contexts), and a block merges its four waves' runs into one partial of
+ * *partial_tokens tokens, which the reduce then merges.  Every level is the
+ * same online-softmax merge of the chunk partials of [Open-TQ-Metal]'s split-K
+ * paragraphs, so the result matches chunks of chunk_tokens up to float
+ * re-association.  Errors as for kvq_attend_decode's argument checks. */
+kvq_status kvq_decode_split(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
+                            int32_t max_seq_len, int32_t chunk_tokens, int32_t* wave_tokens,
+                            int32_t* partial_tokens);
+
 /* Workspace of kvq_attend_decode: room for split-K partials (o_c, m_c, l_c) per
  * (batch, query head, chunk), plus the window partial.  (The decode kernel
  * prepares its int8 queries itself.)  Returns 0 for invalid arguments. */

@@ -1204,6 +1204,20 @@ kvq_status kvq::decode_check(const kvq_cache* c, const float* q, int32_t batch, 
   return check_chunk(c, chunk);
 }
 
+extern "C" kvq_status kvq_decode_split(const kvq_cache* c, int32_t batch, int32_t Hq, int32_t max_seq_len,
+                                       int32_t chunk, int32_t* wave_tokens, int32_t* partial_tokens) {
+  kvq_status st = validate_cache(c);
+  if (st != KVQ_OK) return st;
+  if (!wave_tokens || !partial_tokens) return fail(KVQ_ERR_INVALID_ARG, "wave_tokens and partial_tokens must be non-null");
+  if (batch < 1 || Hq < 1 || Hq % c->num_kv_heads) return fail(KVQ_ERR_INVALID_ARG, "bad batch or num_q_heads");
+  if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len must be >= 0");
+  if ((st = check_chunk(c, chunk)) != KVQ_OK) return st;
+  const int span = decode_span(c, batch, Hq, max_seq_len, chunk);
+  *wave_tokens = span;
+  *partial_tokens = 4 * span;
+  return KVQ_OK;
+}
+
 extern "C" kvq_status kvq_attend_decode_partial(const kvq_cache* c, const float* q, int32_t batch, int32_t Hq,
                                                 float alpha, const int32_t* block_table, int32_t max_pages,
                                                 const int32_t* seq_len, int32_t max_seq_len, int32_t chunk,

@@ -134,6 +134,15 @@ def attend_decode(cache, q, block_table, seq_len, max_seq_len, alpha, chunk_toke
     return out
 
 
+def decode_split(cache, batch, num_q_heads, max_seq_len, chunk_tokens=512):
+    """kvq_decode_split: (tokens per wave run, tokens per block partial) the decode executes."""
+    w, p = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = load().kvq_decode_split(cache.desc, int(batch), int(num_q_heads), int(max_seq_len), int(chunk_tokens),
+                                 ctypes.byref(w), ctypes.byref(p))
+    check("kvq_decode_split", st)
+    return w.value, p.value
+
+
 def attend_decode_noalloc(cache, q, block_table, seq_len, max_seq_len, alpha, chunk_tokens=512, out=None):
     """kvq_attend_decode_noalloc: attend_decode with the partials in the library's device scratch
     (no workspace; calls that overlap on one device race)."""

@@ -118,3 +118,15 @@ def test_noalloc_decode_refuses_oversized_calls_on_the_host():
     assert st == 3
     assert b"scratch" in lib.kvq_last_error()
     assert lib.kvq_attend_decode_noalloc(d, 16, None, 1, 4, 1.0, 16, 4, 16, 64, 512, None) == 1   # out
+
+
+def test_decode_split_reports_the_executed_runs():
+    """kvq_decode_split: runs are whole chunks (or halves/quarters), partials four runs; bad args refused."""
+    lib = kvq.load()
+    d = ctypes.byref(_desc(layout=_lib.ASYM_INT4_G32, head_dim=128, num_kv_heads=8, page_size=1024, num_pages=4))
+    w, p = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert lib.kvq_decode_split(d, 8, 64, 131072, 512, ctypes.byref(w), ctypes.byref(p)) == 0
+    assert w.value in (128, 256, 512, 1024, 2048) and p.value == 4 * w.value
+    assert lib.kvq_decode_split(d, 8, 63, 131072, 512, ctypes.byref(w), ctypes.byref(p)) == 1
+    assert lib.kvq_decode_split(d, 8, 64, 131072, 100, ctypes.byref(w), ctypes.byref(p)) == 1
+    assert lib.kvq_decode_split(d, 8, 64, 131072, 512, None, ctypes.byref(p)) == 1
