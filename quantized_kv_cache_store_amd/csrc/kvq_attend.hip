@@ -692,9 +692,9 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
   // ---- prologue: this lane's row of the tile, prepared in the wave (int8 query in the B-operand
   // order, its scale and block sums; float-query mode: also the two residual terms, with the block
   // sums and the scale taken for (254 I(q8) + I(r1)) * 254 + I(r2)).  With 8-row tiles lane column
-  // col serves row col & 7, and its operands are zero outside its half.  The row's elements are
-  // loaded first and the direct-load ring's first steps issued right after them, so that the HBM
-  // latency of both passes once, under the preparation's arithmetic.
+  // col serves row col & 7, and its operands are zero outside its half.  The row's elements and
+  // the page entries of the ring's first steps are loaded together, then the ring's first steps
+  // issued, so that the preparation's arithmetic runs while they are in flight.
   const int col = lane & 15;
   const int r = lane >> 4;
   const int rsel = TR == 8 ? (col & 7) : col;   // this lane's row within the tile
@@ -718,11 +718,23 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
   const uint32_t vr_lds = kr_lds + RK * H;
   auto rows = [&](int st) { return half_rows_s(a, b, hk, t_begin + 32 * st, t_end); };
   if constexpr (PS::DMA) {
+    // The page runs of the ring's first steps are read (scalar loads) while the row's loads fly.
+    // The row is then waited for before the ring's loads are issued: the compiler's own wait, at
+    // the row's first use, counts only its loads and would also wait for every ring load issued
+    // after them, so the preparation below would start only once the ring's first steps had
+    // landed instead of running while they are in flight.
+    HalfRows pro[MX];
+#pragma unroll
+    for (int k = 0; k < MX; ++k) pro[k] = k < nsteps ? rows(k) : HalfRows{0, 0};
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" : : "v"(qx[g][i]));
 #pragma unroll
     for (int j = -MX; j < 0; ++j) {
       const int k = j + RK, v = j + RV;
-      if (k >= 0 && k < nsteps) issue_dma_half<ST, false>(a, rows(k), lane, kr_lds + k * H);
-      if (v >= 0 && v < nsteps) issue_dma_half<ST, true>(a, rows(v), lane, vr_lds + v * H);
+      if (k >= 0 && k < nsteps) issue_dma_half<ST, false>(a, pro[k], lane, kr_lds + k * H);
+      if (v >= 0 && v < nsteps) issue_dma_half<ST, true>(a, pro[v], lane, vr_lds + v * H);
     }
   }
   long qB[NG];          // B operands (int8 query of the tile's rows), one aligned register pair each

@@ -247,12 +247,33 @@ __device__ __forceinline__ void prepare_row_lanes(float (&x)[D / 32][8], int r, 
   m = max_over_rows(m);
   const float s = m / 127.0f;
   out.sq = s;
+  // The quotients x / s.  With r = 1 / s correctly rounded (one IEEE division per row), q0 = x r
+  // lies within an ulp of x / s, the residual x - s q0 is exact (an fma), and q0 + (x - s q0) r
+  // rounds to the correctly rounded quotient (Markstein's correction step) whenever that residual
+  // does not underflow, which holds for |x| >= 2^-102.  Rows with s >= 2^-82 take this form: their
+  // smaller elements have quotients below 2^-20, whose codes (all three terms of the float-query
+  // mode) are zero whatever the quotient's last bits.  Rows below 2^-82 take the IEEE division.
+  if (s >= 0x1p-82f) {
+    const float rs = 1.0f / s;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float q0 = x[g][i] * rs;
+        x[g][i] = fmaf(fmaf(-s, q0, x[g][i]), rs, q0);
+      }
+  } else {
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[g][i] = s != 0.0f ? x[g][i] / s : 0.0f;
+  }
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     int c[8], cl[8], cm[8], sum = 0, suml = 0, summ = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float y = s != 0.0f ? x[g][i] / s : 0.0f;
+      const float y = x[g][i];
       const float n = fminf(fmaxf(rintf(y), -127.0f), 127.0f);
       c[i] = (int)n;
       sum += c[i];

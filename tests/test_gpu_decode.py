@@ -63,6 +63,50 @@ def test_qk_i32_bit_exact(layout, D):
             np.testing.assert_array_equal(got[b, h, :n - 5], ref[:n - 5], err_msg=f"b{b} h{h}")
 
 
+# One factor per query head: row scales s = amax / 127 on both sides of 2^-82 (below it the in-wave
+# preparation keeps the IEEE division, above it takes the reciprocal with a residual correction),
+# a row whose elements reach the subnormal range, and an all-zero row.
+Q_FACTORS = np.array([1.0, 1e-30, 3e-25, 1e25, 0.0, 1e-20, 2.0 ** -70, 1e-37], dtype=np.float32)
+
+
+@pytest.mark.parametrize("layout", ALL)
+def test_qk_i32_bit_exact_query_magnitudes(layout):
+    """Rows of very different magnitudes in one tile: the integer scores match the oracle's codes."""
+    U.need_gpu()
+    rng = np.random.default_rng(17 + layout)
+    D, Hkv, G, lens = 128, 2, 4, [300, 77]
+    rows_k = _rows(rng, lens, Hkv, D)
+    rows_v = _rows(rng, lens, Hkv, D)
+    q = (rng.standard_normal((2, Hkv * G, D)).astype(np.float32) * Q_FACTORS[None, :, None]).astype(np.float32)
+    cache, bt, seq, _ = U.build_cache(layout, D, Hkv, rows_k, rows_v)
+    got = kvq.debug_qk_i32(cache, torch.from_numpy(q).to(U.DEV), bt, seq, max(lens)).cpu().numpy()
+    for b, n in enumerate(lens):
+        for h in range(Hkv * G):
+            _, q8, _ = attention.prepare_query(layout, q[b, h])
+            codes = quant.encode_rows(layout, rows_k[b][:, h // G, :])["codes"]
+            np.testing.assert_array_equal(got[b, h, :n], attention.scores_i32(layout, q8, codes)[:n],
+                                          err_msg=f"b{b} h{h} x{Q_FACTORS[h]:g}")
+
+
+@pytest.mark.parametrize("layout", ALL)
+@pytest.mark.parametrize("float_q", [False, True], ids=["int8q", "floatq"])
+def test_decode_query_magnitudes(layout, float_q):
+    """The same mixed-magnitude rows through the decode (both query modes) against the oracle."""
+    U.need_gpu()
+    rng = np.random.default_rng(23 + layout)
+    D, Hkv, G, lens = 128, 2, 4, [600, 45]
+    rows_k = _rows(rng, lens, Hkv, D)
+    rows_v = _rows(rng, lens, Hkv, D)
+    q = (rng.standard_normal((2, Hkv * G, D)).astype(np.float32) * Q_FACTORS[None, :, None]).astype(np.float32)
+    alpha = 1.0 / math.sqrt(D)
+    cache, bt, seq, _ = U.build_cache(layout, D, Hkv, rows_k, rows_v)
+    out = kvq.attend_decode(cache, torch.from_numpy(q).to(U.DEV), bt, seq, max(lens), alpha, float_q=float_q)
+    torch.cuda.synchronize()
+    ref = np.stack([attention.attend_decode(layout, q[b], rows_k[b], rows_v[b], alpha, float_q=float_q)
+                    for b in range(len(lens))])
+    U.assert_close_rel(out.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("layout", ALL)
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("G", [1, 4, 8])
