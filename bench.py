@@ -437,7 +437,7 @@ def time_config(w, steps, warmup, dev, batch=None, seed=5):
     pos_new = (seq - 1).to(torch.int32)
     out = torch.empty((B, w.Hq, w.D), dtype=torch.float32, device=dev)
     ws = torch.empty(kvq.decode_workspace_bytes(B, w.Hq, w.D, S, w.chunk_tokens), dtype=torch.uint8, device=dev)
-    wave_tokens, partial_tokens = kvq.decode_split(caches[0], B, w.Hq, S, w.chunk_tokens)
+    wave_tokens, partial_tokens = kvq.decode_split_lengths(caches[0], w.Hq, lens, S, w.chunk_tokens)
 
     def step(i, partial_only=False):
         c = caches[i % L]

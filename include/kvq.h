@@ -152,6 +152,20 @@ kvq_status kvq_decode_split(const kvq_cache* cache, int32_t batch, int32_t num_q
                             int32_t max_seq_len, int32_t chunk_tokens, int32_t* wave_tokens,
                             int32_t* partial_tokens);
 
+/* The same for rows of the given lengths (host int32 [batch], each in
+ * [0, max_seq_len]).  When even runs of four chunks leave a batch of several
+ * rows more blocks than the device holds at once, the decode kernels choose the
+ * run length per call from seq_len, among 4, 2 and 1.5 chunks, as the one
+ * with the fewest whole rounds of resident blocks times a wave's time (a
+ * start-up of about four 32-token steps plus its run); a ragged batch can then
+ * take shorter runs that fill its last round.  kvq_decode_split reports that
+ * choice for rows of max_seq_len tokens, this call for these lengths (the
+ * int8-query kernels; the float-query kernels hold fewer blocks per CU). */
+kvq_status kvq_decode_split_lengths(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
+                                    const int32_t* seq_len_host, int32_t max_seq_len,
+                                    int32_t chunk_tokens, int32_t* wave_tokens,
+                                    int32_t* partial_tokens);
+
 /* Workspace of kvq_attend_decode: room for split-K partials (o_c, m_c, l_c) per
  * (batch, query head, chunk), plus the window partial.  (The decode kernel
  * prepares its int8 queries itself.)  Returns 0 for invalid arguments. */

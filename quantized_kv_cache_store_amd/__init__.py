@@ -9,5 +9,5 @@ fails loudly if it is not built.
 
 from ._lib import LAYOUT_IDS, KvqError, load  # noqa: F401
 from .ops import (KvqCache, attend_decode, attend_decode_noalloc, attend_decode_partial, attend_decode_reduce, attend_prefill_causal,  # noqa: F401
-                  attend_step, debug_qk_i32, decode_split, debug_quantize_q, debug_stream_read, decode_workspace_bytes, prefill_full_then_store,
+                  attend_step, debug_qk_i32, decode_split, decode_split_lengths, debug_quantize_q, debug_stream_read, decode_workspace_bytes, prefill_full_then_store,
                   prefill_workspace_bytes, store, store_chunk)

@@ -45,6 +45,7 @@ SIGNATURES = {
     "kvq_attend_decode_float_q": (c_i32, [P, c_vp, c_vp, c_i32, c_i32, c_f, c_vp, c_i32, c_vp, c_i32, c_i32,
                                           c_vp, c_size, c_vp]),
     "kvq_decode_split": (c_i32, [P, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "kvq_decode_split_lengths": (c_i32, [P, c_i32, c_i32, c_vp, c_i32, c_i32, c_vp, c_vp]),
     "kvq_attend_decode_noalloc": (c_i32, [P, c_vp, c_vp, c_i32, c_i32, c_f, c_vp, c_i32, c_vp, c_i32, c_i32,
                                           c_vp]),
     "kvq_attend_decode_partial": (c_i32, [P, c_vp, c_i32, c_i32, c_f, c_vp, c_i32, c_vp, c_i32, c_i32,

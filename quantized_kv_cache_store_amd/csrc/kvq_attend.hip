@@ -606,6 +606,54 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
   }
 }
 
+// The decode grid as a flat list of work items (a.rs.on): rows in order; in a row, its units (kv head,
+// then row tile) in order; in a unit, its chunk groups at the run length run_span picks and then, with
+// a window, the window's block.  The items take the first ids of the grid, which is sized for the
+// shortest runs, so the ids past them exit at once after every item has been dispatched (empty blocks
+// interleaved with the work cost 10-20 % in slot time and dispatch order on a uniform batch).
+struct FlatBlock {
+  int b, hk, tile, cg, span;
+  bool window, valid;
+};
+
+__device__ inline FlatBlock flat_block(const AttendArgs& a, unsigned id, int tiles) {
+  FlatBlock f{};
+  auto len = [&](int bb) { return ((const_i32_ptr)a.seq_len)[bb]; };
+  f.span = run_span(a.rs, a.n_recent, len);
+  const unsigned k = (unsigned)(f.span / a.rs.half_chunk);   // 8, 4 or 3
+  const unsigned um = (1u << a.rs.unit_shift) - 1u;
+  const unsigned win = a.n_recent > 0 ? 1u : 0u;
+  unsigned base = 0, local = 0, per_unit = 1;
+  int found = -1;
+  for (int b0 = 0; b0 < a.rs.batch; b0 += 16) {
+    int S[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) S[j] = len(b0 + j < a.rs.batch ? b0 + j : a.rs.batch - 1);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int Sq = a.n_recent > 0 ? (S[j] > a.n_recent ? S[j] - a.n_recent : 0) : S[j];
+      const unsigned q = ((unsigned)Sq + um) >> a.rs.unit_shift;
+      const unsigned groups = k == 8u ? (q + 7u) >> 3 : (k == 4u ? (q + 3u) >> 2 : (q + 2u) / 3u);
+      const unsigned n = b0 + j < a.rs.batch ? (groups + win) * (unsigned)a.rs.units : 0u;
+      if (found < 0 && id < base + n) {
+        found = b0 + j;
+        local = id - base;
+        per_unit = groups + win;
+      }
+      base += n;
+    }
+  }
+  f.valid = found >= 0;
+  if (!f.valid) return f;
+  f.b = found;
+  const unsigned unit = local / per_unit, c = local - unit * per_unit;
+  f.hk = (int)(unit / (unsigned)tiles);
+  f.tile = (int)(unit - (unsigned)f.hk * (unsigned)tiles);
+  f.window = win != 0u && c == per_unit - 1u;
+  f.cg = f.window ? 0 : (int)c;
+  return f;
+}
+
 // Split-K partial kernel.  Block = four waves = four consecutive chunks of one (batch row,
 // kv head, row tile); each wave streams its chunk in 32-token steps with NB - 1 steps of loads
 // in flight and writes the chunk's partial per row (o unnormalised, m in base-2 logits, l).
@@ -654,23 +702,39 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
   // id on XCD id % 8, and in a ragged batch only the low chunk groups of the short rows hold
   // tokens, so each (batch row, kv head, tile) rotates its chunk groups by its own index: their
   // first groups then spread over all XCDs instead of piling onto the same ones.
-  const int hk = blockIdx.y, b = blockIdx.z;
-  const int tile = (int)blockIdx.x / a.ngroups;
-  const int tiles = (int)gridDim.x / a.ngroups;
-  const int rot = (int)((((long)b * gridDim.y + hk) * tiles + tile) % a.ngroups);
-  int cg = (int)blockIdx.x - tile * a.ngroups - rot;
-  if (cg < 0) cg += a.ngroups;
+  // With a run length chosen from the rows' lengths (a.rs.on) the grid is a flat list instead (flat_block).
+  const int nrows = a.n_q * a.G;
+  int hk, b, tile, cg, span;
+  bool window_block;
+  if (!DBG && a.rs.on) {
+    const FlatBlock f = flat_block(a, blockIdx.x, (nrows + TR - 1) / TR);
+    if (!f.valid) return;
+    hk = f.hk;
+    b = f.b;
+    tile = f.tile;
+    cg = f.cg;
+    span = f.span;
+    window_block = f.window;
+  } else {
+    hk = blockIdx.y;
+    b = blockIdx.z;
+    tile = (int)blockIdx.x / a.ngroups;
+    const int tiles = (int)gridDim.x / a.ngroups;
+    const int rot = (int)((((long)b * gridDim.y + hk) * tiles + tile) % a.ngroups);
+    cg = (int)blockIdx.x - tile * a.ngroups - rot;
+    if (cg < 0) cg += a.ngroups;
+    span = a.span;                               // tokens of each wave
+    window_block = !DBG && a.n_recent > 0 && cg == a.ngroups - 1;
+  }
   const int S = a.seq_len[b];
   const int Sq = a.n_recent > 0 ? max(0, S - a.n_recent) : S;   // quantised tokens
-  const int nrows = a.n_q * a.G;
   const int row0 = TR * tile;
   const int nvalid = min(TR, nrows - row0);
   const int qs0 = a.causal ? a.q_start[b] : 0;
-  if (!DBG && a.n_recent > 0 && cg == a.ngroups - 1) {
+  if (window_block) {
     if (S > 0) window_tile_block<L, D>(a, smem, b, hk, S, row0, nvalid, qs0);
     return;
   }
-  const int span = a.span;                      // tokens of each wave
   if (cg * 4 * span >= Sq) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -962,7 +1026,8 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
 template <int D, bool ROT, int W>
 __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out, const int32_t* seq_len,
                                                      int rows_per_b, int nc1, int chunk, int n_recent,
-                                                     long total_rows, int nwin_always, int slice, int causal_nq) {
+                                                     long total_rows, int nwin_always, int slice, int causal_nq,
+                                                     RunSplit rs) {
 #pragma clang fp contract(off)
   constexpr int E = D / 64;
   constexpr int RPB = 4 / W;
@@ -976,6 +1041,7 @@ __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out
   const int b = (int)(rr / rows_per_b);
   const int S = seq_len[b];
   const int Sq = n_recent > 0 ? max(0, S - n_recent) : S;
+  if (rs.on) chunk = 4 * run_span(rs, n_recent, [&](int bb) { return ((const_i32_ptr)seq_len)[bb]; });
   const int nq = (Sq + chunk - 1) / chunk;
   int nw = nwin_always > 0 ? nwin_always : ((n_recent > 0 && S > 0) ? 1 : 0);
   if (nwin_always > 0 && causal_nq > 0) {   // the slices this query's causal limit reaches
@@ -1118,9 +1184,64 @@ static size_t decode_ws_bytes(int batch, int Hq, int D, int max_seq_len, int chu
 
 static int decode_slots(int max_seq_len, int span) { return chunks_of(max_seq_len, 4 * span) + 1; }
 
+// Blocks of the decode partial kernel resident on one CU: a block holds one wave per SIMD, so the
+// kernel's waves per SIMD (its launch bound, which its registers meet), or fewer where fewer blocks'
+// LDS fits in 160 KiB.
+template <int L, int D, int TR, bool FQ>
+static int partial_blocks_per_cu(int n_recent) {
+  size_t lds = PartialShape<L, D, TR, FQ>::LDS;
+  if (n_recent > 0 && (size_t)window_lds_bytes<D>() > lds) lds = window_lds_bytes<D>();
+  const int by_lds = (int)(163840 / lds);
+  const int w = PartialShape<L, D, TR, FQ>::MIN_WAVES;
+  return by_lds < w ? by_lds : w;
+}
+
+static int blocks_per_cu(int layout, int D, int tr, bool fq, int n_recent) {
+  typedef int (*fn)(int);
+  const int di = (D == 256 ? 1 : 0) + (tr == 8 ? 2 : 0) + (fq ? 4 : 0);
+#define KVQ_RES(L)                                                                                               \
+  { partial_blocks_per_cu<L, 128, 16, false>, partial_blocks_per_cu<L, 256, 16, false>,                        \
+    partial_blocks_per_cu<L, 128, 8, false>, partial_blocks_per_cu<L, 256, 8, false>,                          \
+    partial_blocks_per_cu<L, 128, 16, true>, partial_blocks_per_cu<L, 256, 16, true>,                          \
+    partial_blocks_per_cu<L, 128, 8, true>, partial_blocks_per_cu<L, 256, 8, true> }
+  static const fn tab[kNumLayouts][8] = {KVQ_RES(HAD), KVQ_RES(Q40), KVQ_RES(Q60), KVQ_RES(ASYM), KVQ_RES(Q80)};
+#undef KVQ_RES
+  return tab[layout][di](n_recent);
+}
+
+// The decode's split for a call: a fixed run length (decode_span), or, when even runs of four chunks
+// leave more blocks than the chip holds at once (a batch of several rows), the run length chosen per
+// call from the rows' lengths (run_span, on the device), with the grid and the partial slots sized for
+// the shortest candidate, a chunk and a half.  The 16-row kernel keeps a run's page entries in registers, so
+// that choice needs the longest candidate's pages to fit them.
+struct DecodePlan {
+  int span;      // the grid's run length
+  int nc1;       // partial slots per row
+  RunSplit rs;
+};
+
+static DecodePlan decode_plan(const kvq_cache* c, int batch, int Hq, int max_seq_len, int chunk, bool fq) {
+  DecodePlan p{};
+  p.span = decode_span(c, batch, Hq, max_seq_len, chunk);
+  const int G = Hq / c->num_kv_heads;
+  const int tr = G <= 8 ? 8 : 16;
+  const int units = c->num_kv_heads * ((G + tr - 1) / tr);
+  const long slots = (long)device_cus() * blocks_per_cu(c->layout, c->head_dim, tr, fq, c->n_recent);
+  const long longest = (long)batch * units * chunks_of(max_seq_len, 16 * chunk);   // blocks of four-chunk runs
+  const long most = (long)batch * units * chunks_of(max_seq_len, 6 * chunk);       // of the shortest candidate
+  const bool pages_fit = tr == 8 || (4 * chunk) / c->page_size + 1 < 64 * kPageRegs;
+  const bool pow2 = (chunk & (chunk - 1)) == 0;
+  if (batch > 1 && batch <= 4096 && longest > slots && pages_fit && pow2 && slots > 0 && most < (1L << 31)) {
+    p.rs = RunSplit{1, units, (int)slots, chunk / 2, __builtin_ctz((unsigned)(2 * chunk)), batch};
+    p.span = kRunShortest * (chunk / 2);
+  }
+  p.nc1 = decode_slots(max_seq_len, p.span);
+  return p;
+}
+
 size_t decode_partials_bytes(const kvq_cache* c, int batch, int Hq, int max_seq_len, int chunk) {
-  const int span = decode_span(c, batch, Hq, max_seq_len, chunk);
-  return (size_t)batch * Hq * decode_slots(max_seq_len, span) * partial_stride(c->head_dim) * sizeof(float);
+  const DecodePlan p = decode_plan(c, batch, Hq, max_seq_len, chunk, false);
+  return (size_t)batch * Hq * p.nc1 * partial_stride(c->head_dim) * sizeof(float);
 }
 
 static kvq_status check_chunk(const kvq_cache* c, int32_t chunk) {
@@ -1132,15 +1253,16 @@ static kvq_status check_chunk(const kvq_cache* c, int32_t chunk) {
 
 template <int D, bool ROT, int W>
 static void launch_reduce_w(float* out, long rows, int rows_per_b, const int32_t* seq_len, int nc1, int chunk,
-                            int n_recent, const float* ws, hipStream_t s, int nwin_always, int slice, int causal_nq) {
+                            int n_recent, const float* ws, hipStream_t s, int nwin_always, int slice, int causal_nq,
+                            RunSplit rs) {
   const long blocks = (rows + (4 / W) - 1) / (4 / W);
   hipLaunchKernelGGL((attend_reduce<D, ROT, W>), dim3((unsigned)blocks), dim3(256), 0, s, ws, out, seq_len, rows_per_b,
-                     nc1, chunk, n_recent, rows, nwin_always, slice, causal_nq);
+                     nc1, chunk, n_recent, rows, nwin_always, slice, causal_nq, rs);
 }
 
 kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b, const int32_t* seq_len,
                          int nc1, int32_t chunk, const float* ws, hipStream_t s, int nwin_always, int slice,
-                         int causal_nq) {
+                         int causal_nq, RunSplit rs) {
   const int wa = nwin_always;
   const long rows = (long)batch * rows_per_b;
   // one wave per row when there are rows enough to fill the chip, else four waves split each row
@@ -1148,15 +1270,15 @@ kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t 
   const bool rot = c->layout == HAD;
   const int n = c->n_recent;
   if (c->head_dim == 128) {
-    if (rot) many ? launch_reduce_w<128, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq)
-                  : launch_reduce_w<128, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq);
-    else many ? launch_reduce_w<128, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq)
-              : launch_reduce_w<128, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq);
+    if (rot) many ? launch_reduce_w<128, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs)
+                  : launch_reduce_w<128, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs);
+    else many ? launch_reduce_w<128, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs)
+              : launch_reduce_w<128, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs);
   } else {
-    if (rot) many ? launch_reduce_w<256, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq)
-                  : launch_reduce_w<256, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq);
-    else many ? launch_reduce_w<256, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq)
-              : launch_reduce_w<256, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq);
+    if (rot) many ? launch_reduce_w<256, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs)
+                  : launch_reduce_w<256, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs);
+    else many ? launch_reduce_w<256, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs)
+              : launch_reduce_w<256, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs);
   }
   return check_launch("attention reduce kernel");
 }
@@ -1179,13 +1301,17 @@ kvq_status kvq::decode_partial_ws(const kvq_cache* c, const float* q, int32_t ba
                                     int32_t max_seq_len, int32_t chunk, void* workspace, void* stream, bool fq) {
   AttendArgs a = make_args(c, q, Hq, 1, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace);
   const int tr = tile_rows(a);
-  a.span = decode_span(c, batch, Hq, max_seq_len, chunk);
+  const DecodePlan p = decode_plan(c, batch, Hq, max_seq_len, chunk, fq);
+  a.span = p.span;
+  a.rs = p.rs;
   a.ngroups = chunks_of(max_seq_len, 4 * a.span) + (c->n_recent > 0 ? 1 : 0);
-  a.nc1 = decode_slots(max_seq_len, a.span);   // the window's slot is the last
+  a.nc1 = p.nc1;   // the window's slot is the last
   const int64_t gx = grid_x(a, tr);
   if (gx == 0) return KVQ_OK;
   a.batch = batch;
-  const dim3 grid((unsigned)gx, c->num_kv_heads, batch);
+  // the flat list (rs.on): every unit of every row, its chunk groups at the shortest runs and the window
+  const dim3 grid = p.rs.on ? dim3((unsigned)((int64_t)batch * c->num_kv_heads * gx), 1, 1)
+                            : dim3((unsigned)gx, c->num_kv_heads, batch);
   (fq ? pick_partial<false, true> : pick_partial<false, false>)(c->layout, c->head_dim, tr)(a, grid, c->n_recent,
                                                                                           (hipStream_t)stream);
   return check_launch("decode partial kernel");
@@ -1195,10 +1321,10 @@ kvq_status kvq::decode_partial_ws(const kvq_cache* c, const float* q, int32_t ba
 // slot holds a block's four wave runs of `span` tokens (merged by the partial kernel), the window's
 // partial the last slot.
 kvq_status kvq::decode_reduce_ws(const kvq_cache* c, float* out, int32_t batch, int32_t Hq, const int32_t* seq_len,
-                                   int32_t max_seq_len, int32_t chunk, const void* workspace, void* stream) {
-  const int span = decode_span(c, batch, Hq, max_seq_len, chunk);
-  return launch_reduce(c, out, batch, Hq, seq_len, decode_slots(max_seq_len, span), 4 * span, (const float*)workspace,
-                       (hipStream_t)stream);
+                                   int32_t max_seq_len, int32_t chunk, const void* workspace, void* stream, bool fq) {
+  const DecodePlan p = decode_plan(c, batch, Hq, max_seq_len, chunk, fq);
+  return launch_reduce(c, out, batch, Hq, seq_len, p.nc1, 4 * p.span, (const float*)workspace, (hipStream_t)stream, 0,
+                       0, 0, p.rs);
 }
 
 static kvq_status check_decode_workspace(const kvq_cache* c, int32_t batch, int32_t Hq, int32_t max_seq_len,
@@ -1224,7 +1350,28 @@ extern "C" kvq_status kvq_decode_split(const kvq_cache* c, int32_t batch, int32_
   if (batch < 1 || Hq < 1 || Hq % c->num_kv_heads) return fail(KVQ_ERR_INVALID_ARG, "bad batch or num_q_heads");
   if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len must be >= 0");
   if ((st = check_chunk(c, chunk)) != KVQ_OK) return st;
-  const int span = decode_span(c, batch, Hq, max_seq_len, chunk);
+  const DecodePlan p = decode_plan(c, batch, Hq, max_seq_len, chunk, false);
+  const int span = p.rs.on ? run_span(p.rs, c->n_recent, [&](int) { return max_seq_len; }) : p.span;
+  *wave_tokens = span;
+  *partial_tokens = 4 * span;
+  return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_decode_split_lengths(const kvq_cache* c, int32_t batch, int32_t Hq,
+                                               const int32_t* seq_len_host, int32_t max_seq_len, int32_t chunk,
+                                               int32_t* wave_tokens, int32_t* partial_tokens) {
+  kvq_status st = validate_cache(c);
+  if (st != KVQ_OK) return st;
+  if (!wave_tokens || !partial_tokens || !seq_len_host)
+    return fail(KVQ_ERR_INVALID_ARG, "seq_len, wave_tokens and partial_tokens must be non-null");
+  if (batch < 1 || Hq < 1 || Hq % c->num_kv_heads) return fail(KVQ_ERR_INVALID_ARG, "bad batch or num_q_heads");
+  if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len must be >= 0");
+  for (int b = 0; b < batch; ++b)
+    if (seq_len_host[b] < 0 || seq_len_host[b] > max_seq_len)
+      return fail(KVQ_ERR_INVALID_ARG, "seq_len[%d] = %d outside [0, max_seq_len]", b, seq_len_host[b]);
+  if ((st = check_chunk(c, chunk)) != KVQ_OK) return st;
+  const DecodePlan p = decode_plan(c, batch, Hq, max_seq_len, chunk, false);
+  const int span = p.rs.on ? run_span(p.rs, c->n_recent, [&](int b) { return seq_len_host[b]; }) : p.span;
   *wave_tokens = span;
   *partial_tokens = 4 * span;
   return KVQ_OK;
@@ -1266,7 +1413,7 @@ static kvq_status decode_both(const kvq_cache* c, const float* q, float* out, in
   if ((st = decode_partial_ws(c, q, batch, Hq, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace,
                               stream, fq)) != KVQ_OK)
     return st;
-  return decode_reduce_ws(c, out, batch, Hq, seq_len, max_seq_len, chunk, workspace, stream);
+  return decode_reduce_ws(c, out, batch, Hq, seq_len, max_seq_len, chunk, workspace, stream, fq);
 }
 
 extern "C" kvq_status kvq_attend_decode(const kvq_cache* c, const float* q, float* out, int32_t batch, int32_t Hq,

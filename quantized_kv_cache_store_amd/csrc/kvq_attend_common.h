@@ -15,6 +15,61 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 #define KVQ_LOG2E 1.4426950408889634f
 
+// The decode's run length for grids that take several rounds of resident blocks, chosen per call from
+// the rows' lengths (on the device by the kernels, on the host by kvq_decode_split_lengths, with the
+// same function): runs of k half chunks, k = 8, 4, 3 (4, 2 and 1.5 chunks), each block four runs.  The
+// cost of k counts whole rounds of blocks, ceil(blocks(k) / slots), times a wave's time in steps,
+// kRunStartSteps of start-up (query load and preparation, first ring loads: measured at about four
+// steps) plus its run's 32-token steps.  A ragged batch's last round is then filled by shorter runs
+// where that pays, while a uniform batch keeps its longest runs.  The host enables it only where every
+// count below fits 32 bits and chunk_tokens is a power of two.
+struct RunSplit {
+  int on;           // 1: the run length comes from run_span; 0: AttendArgs::span
+  int units;        // blocks per chunk group: kv heads x row tiles
+  int slots;        // blocks resident at once: CUs x blocks per CU
+  int half_chunk;   // chunk_tokens / 2
+  int unit_shift;   // log2 of u = 2 chunk_tokens, the tokens of a block of k = 1
+  int batch;
+};
+constexpr int kRunStartSteps = 4;
+constexpr int kRunShortest = 3;   // the shortest candidate, in half chunks (the grid is sized for it)
+
+template <class Len>
+__host__ __device__ inline int run_span(const RunSplit& r, int n_recent, Len len) {
+  // a block of runs of k half chunks covers k u tokens, so a row of Sq quantised tokens takes
+  // ceil(Sq / (k u)) = ceil(ceil(Sq / u) / k) blocks; lengths are read 16 at a time (index clamped)
+  // so that their loads are in flight together
+  const unsigned um = (1u << r.unit_shift) - 1u;
+  unsigned g8 = 0, g4 = 0, g3 = 0;
+  for (int b0 = 0; b0 < r.batch; b0 += 16) {
+    int S[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) S[k] = len(b0 + k < r.batch ? b0 + k : r.batch - 1);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int Sq = n_recent > 0 ? (S[k] > n_recent ? S[k] - n_recent : 0) : S[k];
+      const unsigned q = b0 + k < r.batch ? ((unsigned)Sq + um) >> r.unit_shift : 0u;
+      g8 += (q + 7u) >> 3;
+      g4 += (q + 3u) >> 2;
+      g3 += (q + 2u) / 3u;
+    }
+  }
+  const int ks[3] = {8, 4, kRunShortest};
+  const unsigned gs[3] = {g8, g4, g3};
+  int best = 8;
+  unsigned long long best_cost = 0;
+  for (int i = 0; i < 3; ++i) {
+    const unsigned blocks = gs[i] * (unsigned)r.units;
+    const unsigned rounds = (blocks + (unsigned)r.slots - 1u) / (unsigned)r.slots;
+    const unsigned long long cost = (unsigned long long)rounds * (32u * kRunStartSteps + (unsigned)ks[i] * r.half_chunk);
+    if (i == 0 || cost < best_cost) {
+      best_cost = cost;
+      best = ks[i];
+    }
+  }
+  return best * r.half_chunk;
+}
+
 struct AttendArgs {
   const uint8_t* kp;
   const uint8_t* vp;
@@ -43,7 +98,9 @@ struct AttendArgs {
   int n_q;       // queries per batch row (1 for decode)
   int batch;     // batch rows (decode: the grid is one-dimensional)
   int ngroups;   // blocks per row tile along the sequence: chunk groups of four, + 1 for the window
-  int span;      // tokens each wave of the decode kernel streams (a multiple of 32; chunk elsewhere)
+  int span;      // tokens each wave of the decode kernel streams (a multiple of 32; chunk elsewhere); with
+                 // rs.on the shortest run the call may take (it sizes the grid and the partial slots)
+  RunSplit rs;   // decode: the run length chosen from the rows' lengths, for grids of several rounds
   int causal;    // rows see t <= q_start + i
   int skip;      // causal skip: stop streaming past the tile's last visible token
   float alpha;
@@ -792,7 +849,7 @@ kvq_status launch_rotate_rows(const kvq_cache* c, const float* k_new, const floa
 // row's window); else one window partial when n_recent > 0 and the row is not empty.
 kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b, const int32_t* seq_len,
                          int nc1, int32_t chunk, const float* ws, hipStream_t s, int nwin_always = 0, int slice = 0,
-                         int causal_nq = 0);
+                         int causal_nq = 0, RunSplit rs = RunSplit{});
 
 // The decode's two phases (kvq_attend.hip), for kvq_attend_decode and its variants: decode_check
 // validates the arguments; decode_partial_ws and decode_reduce_ws then run the split-K phase and the
@@ -804,6 +861,6 @@ kvq_status decode_partial_ws(const kvq_cache* c, const float* q, int32_t batch, 
                              const int32_t* block_table, int32_t max_pages, const int32_t* seq_len,
                              int32_t max_seq_len, int32_t chunk, void* workspace, void* stream, bool fq);
 kvq_status decode_reduce_ws(const kvq_cache* c, float* out, int32_t batch, int32_t Hq, const int32_t* seq_len,
-                            int32_t max_seq_len, int32_t chunk, const void* workspace, void* stream);
+                            int32_t max_seq_len, int32_t chunk, const void* workspace, void* stream, bool fq = false);
 
 }  // namespace kvq

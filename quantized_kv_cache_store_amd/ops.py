@@ -143,6 +143,17 @@ def decode_split(cache, batch, num_q_heads, max_seq_len, chunk_tokens=512):
     return w.value, p.value
 
 
+def decode_split_lengths(cache, num_q_heads, seq_lens, max_seq_len, chunk_tokens=512):
+    """kvq_decode_split_lengths: the split the decode executes for rows of these lengths (host ints)."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    w, p = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = load().kvq_decode_split_lengths(cache.desc, int(lens.size), int(num_q_heads), lens.ctypes.data,
+                                         int(max_seq_len), int(chunk_tokens), ctypes.byref(w), ctypes.byref(p))
+    check("kvq_decode_split_lengths", st)
+    return w.value, p.value
+
+
 def attend_decode_noalloc(cache, q, block_table, seq_len, max_seq_len, alpha, chunk_tokens=512, out=None):
     """kvq_attend_decode_noalloc: attend_decode with the partials in the library's device scratch
     (no workspace; calls that overlap on one device race)."""

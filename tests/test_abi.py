@@ -130,3 +130,34 @@ def test_decode_split_reports_the_executed_runs():
     assert lib.kvq_decode_split(d, 8, 63, 131072, 512, ctypes.byref(w), ctypes.byref(p)) == 1
     assert lib.kvq_decode_split(d, 8, 64, 131072, 100, ctypes.byref(w), ctypes.byref(p)) == 1
     assert lib.kvq_decode_split(d, 8, 64, 131072, 512, None, ctypes.byref(p)) == 1
+
+
+def _split_lengths(lib, d, Hq, lens, max_seq_len=None, chunk=512):
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
+    w, p = ctypes.c_int32(0), ctypes.c_int32(0)
+    mx = int(lens.max()) if max_seq_len is None else max_seq_len
+    st = lib.kvq_decode_split_lengths(d, int(lens.size), Hq, lens.ctypes.data, mx, chunk, ctypes.byref(w),
+                                      ctypes.byref(p))
+    return st, w.value, p.value
+
+
+def test_decode_split_lengths_follows_the_rows():
+    """Several rounds of blocks: the run length follows the rows' lengths (a ragged batch takes shorter
+    runs that fill its last round, a uniform one its longest); one round or one row: the fixed split."""
+    import workloads as W
+    lib = kvq.load()
+    g = W.WORKLOADS["gemma_q6_0_ragged_b16"]
+    lens = [int(n) for n in W.seq_lens(g)]
+    q6 = ctypes.byref(_desc(layout=_lib.Q6_0, head_dim=256, num_kv_heads=8, page_size=16, num_pages=4))
+    assert _split_lengths(lib, q6, 16, lens) == (0, 768, 3072)
+    assert _split_lengths(lib, q6, 16, [max(lens)] * 16) == (0, 2048, 8192)
+    w, p = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert lib.kvq_decode_split(q6, 16, 16, max(lens), 512, ctypes.byref(w), ctypes.byref(p)) == 0
+    assert (w.value, p.value) == (2048, 8192)      # rows of max_seq_len
+    asym = ctypes.byref(_desc(layout=_lib.ASYM_INT4_G32, head_dim=128, num_kv_heads=8, page_size=1024, num_pages=4))
+    assert _split_lengths(lib, asym, 64, [131072] * 8) == (0, 2048, 8192)    # one round
+    assert _split_lengths(lib, asym, 64, [131072] * 16) == (0, 2048, 8192)   # two full rounds
+    assert _split_lengths(lib, asym, 64, [131072]) == (0, 512, 2048)         # one row
+    assert _split_lengths(lib, asym, 64, [131072, 200], max_seq_len=100)[0] == 1   # a row past max_seq_len
+    assert lib.kvq_decode_split_lengths(asym, 1, 64, None, 10, 512, ctypes.byref(w), ctypes.byref(p)) == 1
