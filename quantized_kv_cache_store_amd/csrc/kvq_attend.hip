@@ -679,9 +679,10 @@ struct PartialShape {
   static constexpr int MERGE = 4 * TR * (D + 4) * 4;            // the four waves' chunk partials
   static constexpr int LDS = RING > MERGE ? RING : MERGE;       // per block
   // waves per SIMD: as many as four blocks' rings in 160 KiB of LDS allow, registers permitting (the
-  // float-query mode's second query term and accumulators need the registers of three)
+  // float-query mode's second and third query terms and accumulators need the registers of two: at three
+  // its head_dim-128 kernels spilled 10-40 registers inside the loop and ran up to three times slower)
   static constexpr int LDS_WAVES = LDS <= 40960 ? 4 : (LDS <= 54613 ? 3 : 2);
-  static constexpr int MIN_WAVES = DMA ? (FQ && LDS_WAVES > 3 ? 3 : LDS_WAVES) : 2;
+  static constexpr int MIN_WAVES = DMA ? (FQ && LDS_WAVES > 2 ? 2 : LDS_WAVES) : 2;
 };
 
 template <int L, int D, bool DBG, int TR, bool FQ>
