@@ -547,7 +547,21 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
     const int n_tok = min(32, t_end - T0);
     if (nval[0] > 0)
       prefill_consume<L, D, FULL, TPW>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, e_run, oacc);
+    // Issue priority by progress, as in the decode kernel: a SIMD's waves come from different blocks of
+    // equal work and would otherwise finish oldest first (causal prefill 110 -> 106 us).  Not in the
+    // full-precision prefill, whose f32-row blocks at the end of the grid then waited behind the
+    // packed blocks (151 -> 156 us with it).
+    const int q_now = (8 * (s + 1)) / nsteps, q_was = (8 * s) / nsteps;
+    if (!a.kchunk && q_now != q_was) {
+      if (q_now == 4)
+        __builtin_amdgcn_s_setprio(2);
+      else if (q_now == 6)
+        __builtin_amdgcn_s_setprio(1);
+      else if (q_now == 7)
+        __builtin_amdgcn_s_setprio(0);
+    }
   };
+  if (!a.kchunk) __builtin_amdgcn_s_setprio(3);
   int s = 0;
   for (; s < nfull; ++s) step(s, std::integral_constant<bool, true>{});
   for (; s < nsteps; ++s) step(s, std::integral_constant<bool, false>{});
