@@ -260,8 +260,9 @@ kvq_status kvq_attend_decode_reduce(const kvq_cache* cache, float* out, int32_t 
                                     void* stream);
 
 /* Workspace of kvq_attend_prefill_causal and kvq_prefill_full_then_store:
- * split-K partials (o_c, m_c, l_c) per (batch, query, query head, 1024-token
- * chunk), plus the window partial, then the prepared queries per (batch,
+ * split-K partials (o_c, m_c, l_c) per (batch, query, query head, chunk of
+ * the shortest split, 512 tokens; the call picks chunks of at least that
+ * length), plus the window partial, then the prepared queries per (batch,
  * query, query head), then room for the chunk's rotated K and V rows (the
  * full-precision prefill of HAD_INT4).  Returns 0 for invalid arguments. */
 size_t kvq_prefill_workspace_bytes(int32_t batch, int32_t n_q, int32_t num_q_heads,

@@ -27,6 +27,8 @@
 // that are partly visible mask per row.  With the skip off the masked tokens are
 // streamed and contribute exact zeros, so both settings give the same bits.
 
+#include <algorithm>
+#include <map>
 #include <type_traits>
 
 #include "kvq_attend_common.h"
@@ -34,7 +36,7 @@
 namespace kvq {
 
 // Shortest split-K chunk of the prefill (tokens); each (row block, chunk) is one block of the grid.
-constexpr int kPrefillChunk = 1024;
+constexpr int kPrefillChunk = 512;
 // Full-precision prefill: its f32 rows (the prefix's window and the chunk's own rows) are split into
 // slices of at least this many tokens, one group and one partial slot each.
 constexpr int kRowSlice = 128;
@@ -148,9 +150,11 @@ __device__ __forceinline__ void prefill_fetch(const unsigned char* kslot, const 
 // n_tok: tokens of the step inside the chunk; the V scales of the others are zeroed so that their
 // (stale) rows contribute exact zeros.  The Hadamard layout's V^T holds the codes themselves (exact
 // in fp16) and its f32 scales go to VR for the consumers.
+// rsign: XORed into every K record dword (the sign bits of its scales and offsets when the rows'
+// score scale is negative, so that the consumers see the negated scores and scale them by |sqc|).
 template <int L, int D>
 __device__ __forceinline__ void prefill_produce(unsigned char* buf, int tid, const PLoad<L, D>& ld, int n_tok,
-                                                uint32_t magic) {
+                                                uint32_t magic, uint32_t rsign) {
   using T = Layout<L, D>;
   using PS = PStep<L, D>;
   constexpr int SB = T::SB;
@@ -221,19 +225,30 @@ __device__ __forceinline__ void prefill_produce(unsigned char* buf, int tid, con
     *reinterpret_cast<u32x4*>(dst + 16) =
         u32x4{as_u32(highv[0]), as_u32(highv[1]), as_u32(highv[2]), as_u32(highv[3])};
   }
-  if (tid < 8 * SB) *reinterpret_cast<uint32_t*>(buf + PS::KR + 4 * tid) = ld.kr;
+  if (tid < 8 * SB) *reinterpret_cast<uint32_t*>(buf + PS::KR + 4 * tid) = ld.kr ^ rsign;
   if (L == HAD && tid < 32) *reinterpret_cast<uint32_t*>(buf + PS::VR + 4 * tid) = tid < n_tok ? ld.vr : 0u;
 }
+
+// Lazy running maximum: a row's maximum is raised, and its l and accumulators rescaled, only when a
+// step's scores pass it by more than kLazyMax (log2 units).  Until then the row's probabilities lie in
+// [0, 2^kLazyMax], which the f16 P operand holds at its full relative precision; l and the accumulators
+// are all relative to the same maximum, so the partial (m, l, o) is the same up to rounding whichever
+// maximum it carries.  Most steps then skip the rescale of the accumulators.
+constexpr float kLazyMax = 8.0f;
 
 // One step of one wave: Q K^T for the wave's TPW tiles of 16 rows, online softmax, P V.  Each V^T
 // operand read from LDS serves every tile of the wave.
 // FULL: all 32 tokens exist and every row of the wave sees them.
+// Scores: xs holds them unscaled (the i32 dots, less the Hadamard layout's block-sum offset qoff0,
+// times the K scales).  The row's scale sqa = |sqc| > 0 is applied in the
+// exponent, exp2(x sqa - m) in one fma, and scaling the step's maximum by sqa keeps the order; a
+// negative sqc is carried by the K records, whose signs the producer flipped.
 // e_run: Hadamard layout, the wave's V-scale exponent (vscale_exp); the accumulators are in units of
 // 2^e_run and P carries p * s_v / 2^e_run.
 template <int L, int D, bool FULL, int TPW>
 __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int lane, int T0, int n_tok, const int* lim,
                                                 const long (*qb)[D / 32], const float (*qsB)[(D / 32 + 3) / 4],
-                                                const int* qoff0, const float* sqc, float* m_run, float* l_run,
+                                                const int* qoff0, const float* sqa, float* m_run, float* l_run,
                                                 int& e_run, v4f (*oacc)[D / 16]) {
   using T = Layout<L, D>;
   using PS = PStep<L, D>;
@@ -284,7 +299,7 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
             x = fmaf(sc, (float)acc[g][j], x);
           }
         }
-        xs[u][tau * 4 + j] = vis ? x * sqc[u] : -INFINITY;
+        xs[u][tau * 4 + j] = vis ? x : -INFINITY;
       }
     }
   }
@@ -308,34 +323,46 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
       vsc[4 + j] = __builtin_amdgcn_ldexpf(a1[j], -e_new);
     }
   }
-  v8h pB[TPW];
+  // the step's scaled maxima; a rescale only where one passes its row's maximum by kLazyMax, or where
+  // the V-scale exponent grew (one branch for the wave)
+  float sm[TPW];
+  bool up = L == HAD && e_new != e_run;
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     float smax = xs[u][0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) smax = fmaxf(smax, xs[u][i]);
     smax = max_over_rows(smax);
-    const float m_new = fmaxf(m_run[u], smax);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    {   // unconditional: corr is exactly 1 where the max held, and no branch splits the accumulators'
-        // registers into two copies (measured faster than skipping the product when no max moved)
-      const float corr = __builtin_amdgcn_exp2f(m_run[u] - m_use);
+    sm[u] = smax == -INFINITY ? -INFINITY : smax * sqa[u];
+    up = up || sm[u] > m_run[u] + kLazyMax;
+  }
+  if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const float m_new = sm[u] > m_run[u] + kLazyMax ? sm[u] : m_run[u];
+      // exactly 1 where the maximum held; 0 from an empty row (-inf) to a finite maximum
+      const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
       l_run[u] *= corr;
       const float ocorr = L == HAD ? __builtin_amdgcn_ldexpf(corr, e_run - e_new) : corr;
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) oacc[u][i] *= ocorr;
+      m_run[u] = m_new;
     }
-    m_run[u] = m_new;
+  }
+  e_run = e_new;
+  v8h pB[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const float nm = m_run[u] == -INFINITY ? 0.0f : -m_run[u];
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float p = __builtin_amdgcn_exp2f(xs[u][i] - m_use);
+      const float p = __builtin_amdgcn_exp2f(fmaf(xs[u][i], sqa[u], nm));
       psum += p;
       pB[u][i] = (_Float16)(L == HAD ? p * vsc[i] : p);
     }
     l_run[u] += psum;
   }
-  e_run = e_new;
 
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
@@ -355,10 +382,16 @@ template <int L, int D>
 struct PrefillTiles {
   static constexpr int TPW = (D == 128 && L != Q60) ? 2 : 1;   // 16-row tiles per wave
   static constexpr int BR = 64 * TPW;                          // rows per block
+  // blocks per CU: three for the Hadamard layout at head_dim 128, whose registers (168 under this
+  // bound) and LDS allow it, two for the others
+  static constexpr int OCC = (L == HAD && D == 128) ? 3 : 2;
 };
+static_assert(PrefillTiles<HAD, 128>::OCC * PrefillShape<HAD, 128>::LDS <= 160 * 1024 &&
+                  PrefillTiles<HAD, 128>::OCC * window_lds_bytes<128>() <= 160 * 1024,
+              "three Hadamard head_dim-128 prefill blocks per CU");
 
 template <int L, int D>
-__global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
+__global__ __launch_bounds__(256, (PrefillTiles<L, D>::OCC)) void prefill_partial(AttendArgs a) {
   using T = Layout<L, D>;
   using PS = PStep<L, D>;
   constexpr int NG = T::NG;
@@ -431,7 +464,7 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
   long qb[TPW][NG];
   float qsB[TPW][NQ];
   int qoff0[TPW], lim[TPW];
-  float sqc[TPW];
+  float sqa[TPW];   // |score scale| in log2 units, at least FLT_MIN (so that -inf * sqa stays -inf)
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int trow = wrow0 + 16 * u;
@@ -440,7 +473,7 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
 #pragma unroll
     for (int i = 0; i < NQ; ++i) qsB[u][i] = 0.0f;
     qoff0[u] = 0;
-    sqc[u] = 0.0f;
+    float sqc = 0.0f;
     if (col < nval[u]) {
       const size_t fr = row_index(a, b, hk, trow + col);
 #pragma unroll
@@ -458,8 +491,9 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) tot += qs[g];
       qoff0[u] = BIAS * tot;
-      sqc[u] = a.sqp[fr] * a.alpha * KVQ_LOG2E;
+      sqc = a.sqp[fr] * a.alpha * KVQ_LOG2E;
     }
+    sqa[u] = fmaxf(fabsf(sqc), __FLT_MIN__);
     lim[u] = row_limit(a, qs0, trow + col, nrows);
   }
   const int lim_min = row_limit(a, qs0, wrow0, nrows);   // the wave's smallest limit; -1 without rows
@@ -474,6 +508,8 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) oacc[u][i] = v4f{0.f, 0.f, 0.f, 0.f};
   }
+  // a negative score scale (alpha < 0): the K records' signs flipped, so that sqa = |sqc| applies
+  const uint32_t rsign = a.alpha < 0.0f ? (L == HAD ? 0x80000000u : 0x80008000u) : 0u;
   uint32_t magic;   // fp16 "1024 + code" exponent bits, in a VGPR so v_and_or_b32 can take it
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
@@ -520,7 +556,7 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
     wait_steps(min(nsteps - 1, NR - 2));
     barrier();
     prefill_fetch<L, D>(raw_k(0), raw_k(0) + H, tid, ld);
-    prefill_produce<L, D>(smem, tid, ld, min(32, t_end - t_begin), magic);
+    prefill_produce<L, D>(smem, tid, ld, min(32, t_end - t_begin), magic, rsign);
   }
   // Steps whose 32 tokens are all present and visible to every row of the wave come first (the
   // condition only turns from true to false along the chunk): each loop then has one consume form,
@@ -541,12 +577,12 @@ __global__ __launch_bounds__(256, 2) void prefill_partial(AttendArgs a) {
     barrier();
     if (more) {
       prefill_fetch<L, D>(raw_k(s + 1), raw_k(s + 1) + H, tid, ld);
-      prefill_produce<L, D>(smem + ((s + 1) & 1) * PS::BYTES, tid, ld, min(32, t_end - T0 - 32), magic);
+      prefill_produce<L, D>(smem + ((s + 1) & 1) * PS::BYTES, tid, ld, min(32, t_end - T0 - 32), magic, rsign);
     }
     const unsigned char* buf = smem + (s & 1) * PS::BYTES;
     const int n_tok = min(32, t_end - T0);
     if (nval[0] > 0)
-      prefill_consume<L, D, FULL, TPW>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqc, m_run, l_run, e_run, oacc);
+      prefill_consume<L, D, FULL, TPW>(buf, lane, T0, n_tok, lim, qb, qsB, qoff0, sqa, m_run, l_run, e_run, oacc);
     // Issue priority by progress, as in the decode kernel: a SIMD's waves come from different blocks of
     // equal work and would otherwise finish oldest first (causal prefill 110 -> 106 us).  Not in the
     // full-precision prefill, whose f32-row blocks at the end of the grid then waited behind the
@@ -620,17 +656,63 @@ __global__ __launch_bounds__(256, D == 128 ? 4 : 2) void prefill_rows_f32(Attend
   }
 }
 
-// Split-K chunk of a prefill: 1024 tokens, or longer when that saves a round of the chip's block
-// slots (two per CU): a block's time grows with its chunk, and a grid a little larger than one round
-// of blocks costs nearly two rounds.  The chunk minimises rounds x chunk over multiples of 32 from
-// 1024 (so the partial slots never exceed those of 1024-token chunks).
-static int prefill_chunk(int64_t row_blocks, int max_seq_len, int extra_groups) {
-  const int64_t slots = 2LL * device_cus();
+// Finish time of a grid under list scheduling on `slots` identical block slots: n1 blocks of cost w1
+// dispatched first, then n2 of cost w2, each block taking the earliest free slot.  Slots are kept
+// as (free time, count) groups, so the work is one step per group visited.
+static int64_t list_makespan(int64_t slots, int64_t n1, int64_t w1, int64_t n2, int64_t w2) {
+  std::map<int64_t, int64_t> free_at{{0, slots}};
+  int64_t end = 0;
+  auto put = [&](int64_t n, int64_t w) {
+    while (n > 0) {
+      auto it = free_at.begin();
+      const int64_t t = it->first, m = std::min(it->second, n);
+      if (it->second > m) it->second -= m;
+      else free_at.erase(it);
+      free_at[t + w] += m;
+      end = std::max(end, t + w);
+      n -= m;
+    }
+  };
+  put(n1, w1);
+  put(n2, w2);
+  return end;
+}
+
+// Fixed cost of one prefill block, in packed tokens (its prologue, first loads and partial store),
+// and the cost of one f32 row relative to one packed token, for list_makespan.
+constexpr int kBlockFixedTokens = 128;
+constexpr int kF32RowTokens = 4;
+
+// Split-K chunk of a prefill (a multiple of 32 tokens, at least kPrefillChunk), for row_blocks row
+// blocks over `packed` packed tokens (chunks past a row's packed tokens return at once), with
+// extra_groups f32-row groups of f32_rows rows each after the chunks.
+// The packed blocks may take `cap` of the device's blocks_per_cu x CUs slots: all those the f32-row
+// blocks leave when those are light (heavy = false: the causal prefill's window), blocks_per_cu - 1
+// per CU when they are heavy (the full-precision prefill's chunk rows, on the f32 MFMA at a sixteenth
+// of the f16 rate, which then keep one slot per CU).  The chunk is the shortest whose packed blocks
+// fit that cap in one round: on the Hadamard head_dim-128 kernel (three blocks per CU), 512 queries at
+// 8192 measured 92 us with 800-token chunks (11 chunks, the rule's choice) against 95-122 with
+// 672-1248, and the full-precision prefill 119 us with 1024 (the rule's) against 121-158 with
+// 512-2048.  When even one chunk per row block exceeds the cap, the chunk is the one whose grid
+// finishes first under list_makespan.
+static int prefill_chunk(int64_t row_blocks, int packed, int extra_groups, int f32_rows, bool heavy,
+                         int blocks_per_cu) {
+  const int64_t slots = (int64_t)blocks_per_cu * device_cus();
+  const int64_t cap = heavy ? slots - device_cus() : slots - row_blocks * extra_groups;
+  const int kmax = chunks_of(max(packed, 1), kPrefillChunk);
+  const int64_t kfit = cap > 0 ? cap / row_blocks : 0;
+  if (kfit >= 1) {
+    const int k = (int)std::min<int64_t>(kfit, kmax);
+    return max(kPrefillChunk, (packed + k - 1) / k + 31) / 32 * 32;
+  }
   int best = kPrefillChunk;
   int64_t best_cost = -1;
-  for (int c = kPrefillChunk; c == kPrefillChunk || c < max_seq_len + 32; c += 32) {
-    const int64_t blocks = row_blocks * (chunks_of(max_seq_len, c) + extra_groups);
-    const int64_t cost = (blocks + slots - 1) / slots * c;
+  // the shortest chunk for each count of chunks with packed tokens, up to four rounds of packed blocks
+  for (int k = kmax; k >= 1; --k) {
+    const int c = max(kPrefillChunk, (packed + k - 1) / k + 31) / 32 * 32;
+    if (k > 1 && (chunks_of(packed, c) != k || row_blocks * k > 4 * slots)) continue;
+    const int64_t cost = list_makespan(slots, row_blocks * k, c + kBlockFixedTokens, row_blocks * extra_groups,
+                                       (int64_t)kF32RowTokens * f32_rows + kBlockFixedTokens);
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
       best = c;
@@ -640,8 +722,11 @@ static int prefill_chunk(int64_t row_blocks, int max_seq_len, int extra_groups) 
 }
 
 static inline int prefill_rows_per_block(int layout, int D) { return (D == 128 && layout != Q60) ? 128 : 64; }
+static inline int prefill_blocks_per_cu(int layout, int D) { return (layout == HAD && D == 128) ? 3 : 2; }
 static_assert(PrefillTiles<HAD, 128>::BR == 128 && PrefillTiles<Q60, 128>::BR == 64 && PrefillTiles<Q40, 256>::BR == 64,
               "rows per block as the host computes them");
+static_assert(PrefillTiles<HAD, 128>::OCC == 3 && PrefillTiles<HAD, 256>::OCC == 2 && PrefillTiles<Q40, 128>::OCC == 2,
+              "blocks per CU as the host computes them");
 
 // Query preparation of every row once (a1), 16 rows per block: int8 query, scale, per-block sums,
 // and for the Hadamard layout the rotated f32 query the window uses.
@@ -766,7 +851,9 @@ extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float*
   if (!workspace || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
   const int64_t rbp = ((int64_t)n_q * (Hq / c->num_kv_heads) + prefill_rows_per_block(c->layout, c->head_dim) - 1) /
                       prefill_rows_per_block(c->layout, c->head_dim) * c->num_kv_heads * batch;
-  const int chunk = prefill_chunk(rbp, max_seq_len, c->n_recent > 0 ? 1 : 0);
+  // packed tokens of the longest row: all but its window
+  const int chunk = prefill_chunk(rbp, max(0, max_seq_len - c->n_recent), c->n_recent > 0 ? 1 : 0,
+                                  min(c->n_recent, max_seq_len), false, prefill_blocks_per_cu(c->layout, c->head_dim));
   AttendArgs a = make_args(c, q, Hq, n_q, alpha, block_table, max_pages, seq_len, max_seq_len, chunk, workspace);
   a.causal = causal;
   a.skip = causal && !(flags & KVQ_PREFILL_NO_CAUSAL_SKIP);
@@ -818,7 +905,10 @@ extern "C" kvq_status kvq_prefill_full_then_store(const kvq_cache* c, const floa
   int slice = (int)((nf32 + want - 1) / want);
   slice = max(kRowSlice, (slice + 15) / 16 * 16);
   const int nwin = (nf32 + slice - 1) / slice;
-  const int chunk = sep ? kPrefillChunk : prefill_chunk(row_blocks, max_seq_len, nwin);
+  // packed tokens of the longest prefix: q_start <= max_seq_len - n_q, less its window
+  const int chunk = sep ? kPrefillChunk
+                        : prefill_chunk(row_blocks, max(0, max_seq_len - n_q - c->n_recent), nwin, slice, true,
+                                        prefill_blocks_per_cu(c->layout, c->head_dim));
   AttendArgs a = make_args(c, q, Hq, n_q, alpha, block_table, max_pages, q_start, max_seq_len, chunk, workspace);
   a.causal = causal;
   a.skip = 0;   // every packed token precedes the chunk: nothing to skip

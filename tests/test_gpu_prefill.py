@@ -22,9 +22,12 @@ pytestmark = pytest.mark.gpu
 ALL = [spec.HAD_INT4, spec.Q4_0, spec.Q6_0, spec.ASYM_G32, spec.Q8_0]
 
 
-def _case(layout, D, Hkv, G, lens, n_q, q_starts, n_recent=0, page_size=16, seed=0, alpha=None):
+def _case(layout, D, Hkv, G, lens, n_q, q_starts, n_recent=0, page_size=16, seed=0, alpha=None, k_ramp=False):
     rng = np.random.default_rng(seed)
     rows_k = [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in lens]
+    if k_ramp:   # |K| growing along the cache: the rows' running maxima keep moving
+        rows_k = [(k * np.linspace(0.2, 3.0, len(k), dtype=np.float32)[:, None, None]).astype(np.float32)
+                  for k in rows_k]
     rows_v = [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in lens]
     B, Hq = len(lens), Hkv * G
     q = rng.standard_normal((B, n_q, Hq, D)).astype(np.float32)
@@ -89,6 +92,20 @@ def test_prefill_mid_cache_and_ragged_batch(layout):
     U.need_gpu()
     lens = [2100, 600, 33]
     c = _case(layout, 128, 2, 4, lens, 24, [1000, 576, 0], n_recent=8, seed=21 + layout)
+    got = _gpu(c)
+    U.assert_close_rel(got.cpu().numpy(), _ref(c))
+    assert torch.equal(_gpu(c, skip=False), got)
+
+
+@pytest.mark.parametrize("layout", ALL)
+@pytest.mark.parametrize("alpha", [-0.09, 0.0, 0.6], ids=["negative", "zero", "sharp"])
+def test_prefill_score_scale(layout, alpha):
+    """Negative, zero and large attention scales over a cache whose scores grow along it, so that the
+    rows' running maxima are raised many times (and by more than the lazy threshold)."""
+    U.need_gpu()
+    lens, n_q = [1500, 400], 40
+    c = _case(layout, 128, 2, 2, lens, n_q, [n - n_q for n in lens], n_recent=16, seed=71 + layout, alpha=alpha,
+              k_ramp=True)
     got = _gpu(c)
     U.assert_close_rel(got.cpu().numpy(), _ref(c))
     assert torch.equal(_gpu(c, skip=False), got)
