@@ -372,6 +372,169 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
   }
 }
 
+// f32 rows of a prefill (the window's newest positions, and for the full-precision prefill the chunk's
+// own rows after them), by the block's four waves together: each wave holds a tile of 16 rows (rows
+// trow .. trow + nv - 1, run = false when it has none to compute) and the block walks the 16-token
+// tiles k0 .. kend - 1 of the f32 rows once, staging each tile's K and V in LDS for all four waves by
+// direct loads issued one tile ahead (one barrier per tile), instead of every wave reading them for
+// itself.  Per wave the arithmetic is that of window_wave, step for step: the Q K^T MFMAs take K from
+// the staged tile in the same order, P goes through the wave's own LDS tile, and P V reads the staged V.
+// The block's tiles end at the farthest limit of its rows (lmax_blk); a wave computes only up to its
+// own rows'.  Every wave of the block calls this with the same k0, kend and lmax_blk.  The rows come
+// prepared (a.qrot: the f32 query, rotated for the Hadamard layout).
+// Staged tiles, unpadded (direct loads fill 1 KiB runs), in 16-byte chunks swizzled by token t: K chunk x
+// of token t at chunk x ^ (t & 15) of its row (a quarter-wave's float4 reads, 16 tokens, then fall on
+// distinct banks), V chunk x at x ^ 4 (t & 3) (the four token rows of a P V read start 16 banks apart).
+// Tokens past the last f32 row load the last row instead: their scores are masked and their P is 0.
+template <int D>
+struct F32Tiles {
+  static constexpr int TILE = 16 * D;                   // floats of a K (or V) tile
+  static constexpr int K0 = 0, V0 = 2 * TILE, P0 = 4 * TILE;   // float offsets: K, V double buffers, P
+  static constexpr int FLOATS = P0 + 4 * 256;          // and each wave's P tile [16 tokens][16 rows]
+  static constexpr int BYTES = 4 * FLOATS;
+  static constexpr int INSTR = TILE * 4 / 1024 / 4;     // direct loads of a tile per wave
+};
+template <int D>
+__host__ __device__ constexpr int f32_block_lds() { return F32Tiles<D>::BYTES; }
+
+template <int L, int D>
+__device__ __forceinline__ void f32_rows_block(const AttendArgs& a, unsigned char* smem, int b, int hk, int S, int trow,
+                                               int nv, bool run, int qs0, int k0, int kend, int lmax_blk,
+                                               WinState<D>& st) {
+  using FT = F32Tiles<D>;
+  constexpr int NI = D / 4, CH = D / 4;   // MFMAs of Q K^T; 16-byte chunks of a row
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, r = lane >> 4;
+  float* const lds = reinterpret_cast<float*>(smem);
+  float* const pw = lds + FT::P0 + wave * 256;      // this wave's P: [token T][row R ^ ((T >> 2) & 3)]
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+  const int nrows = a.n_q * a.G;
+  const int W = min(S, a.n_recent);
+  const int w0 = S - W;
+  const int NT = W + (a.kchunk ? a.n_q : 0);
+  const size_t ring0 = ((size_t)b * a.Hkv + hk) * a.n_recent;
+  const float cl = a.alpha * KVQ_LOG2E;
+  if (!run) nv = 0;
+  float q[NI];   // the prepared f32 query of row col, elements NI r ..
+  {
+    const bool ok = col < nv;
+    const float* qr = a.qrot + (ok ? row_index(a, b, hk, trow + col) * D : 0) + NI * r;
+#pragma unroll
+    for (int i = 0; i < NI; i += 4) {
+      const float4 v = ok ? *reinterpret_cast<const float4*>(qr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      q[i] = v.x;
+      q[i + 1] = v.y;
+      q[i + 2] = v.z;
+      q[i + 3] = v.w;
+    }
+  }
+  int lim[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lim[j] = 4 * r + j < nv ? row_limit(a, qs0, trow + 4 * r + j, nrows) : -1;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) st.o[i] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    st.m[j] = -INFINITY;
+    st.l[j] = 0.0f;
+  }
+  auto tiles_to = [&](int lmax) {   // tiles up to the farthest limit lmax (none below the first f32 row)
+    int n = min((NT + 15) / 16, kend);
+    if (lmax < w0) n = 0;
+    else if ((lmax - w0) / 16 + 1 < n) n = (lmax - w0) / 16 + 1;
+    return n;
+  };
+  const int nt_wave = tiles_to(nv > 0 ? row_limit(a, qs0, trow + nv - 1, nrows) : -1);
+  const int nt_blk = tiles_to(lmax_blk);
+  // Direct loads of tile k into buffer k & 1: this wave's instructions n = INSTR w .. INSTR w + INSTR - 1
+  // of each of K and V, lane l of instruction n filling chunk position p = 64 n + l (token p / CH).
+  auto issue = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < FT::INSTR; ++i) {
+      const int n = FT::INSTR * wave + i;
+      const int p = 64 * n + lane;
+      const int tok = p / CH, x = p % CH;
+      const int t = min(16 * k + tok, NT - 1);
+      const float* ksrc;
+      const float* vsrc;
+      if (t >= W) {
+        const size_t co = (((size_t)b * a.n_q + (t - W)) * a.Hkv + hk) * D;
+        ksrc = a.kchunk + co;
+        vsrc = a.vchunk + co;
+      } else {
+        int slot = w0 + t;
+        slot -= (slot / a.n_recent) * a.n_recent;
+        const size_t ro = (ring0 + (size_t)slot) * D;
+        ksrc = a.kring + ro;
+        vsrc = a.vring + ro;
+      }
+      const uint32_t kb = lds_base + 4 * (FT::K0 + (k & 1) * FT::TILE) + 1024 * n;
+      const uint32_t vb = lds_base + 4 * (FT::V0 + (k & 1) * FT::TILE) + 1024 * n;
+      dma16(reinterpret_cast<const uint8_t*>(ksrc + 4 * (x ^ (tok & 15))), kb);
+      dma16(reinterpret_cast<const uint8_t*>(vsrc + 4 * (x ^ (4 * (tok & 3)))), vb);
+    }
+  };
+  if (k0 < nt_blk) issue(k0);
+  wait_vm<0>();
+  __syncthreads();
+  for (int k = k0; k < nt_blk; ++k) {
+    if (k + 1 < nt_blk) issue(k + 1);
+    if (k < nt_wave) {
+      const float* kt = lds + FT::K0 + (k & 1) * FT::TILE;
+      const float* vt = lds + FT::V0 + (k & 1) * FT::TILE;
+      const int t = 16 * k + col;
+      const bool tok_ok = t < NT;
+      // ---- Q K^T: lane (col, r) supplies K of token col, elements NI r + i, in MFMA i
+      v4f c = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NI; i += 4) {
+        const int x = (NI * r + i) / 4;
+        const float4 kv = *reinterpret_cast<const float4*>(kt + col * D + 4 * (x ^ col));
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i], kv.x, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 1], kv.y, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 2], kv.z, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 3], kv.w, c, 0, 0, 0);
+      }
+      // ---- online softmax of rows 4 r + j over the tile's 16 tokens
+      float p[4], corr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float xs = (tok_ok && w0 + t <= lim[j]) ? c[j] * cl : -INFINITY;
+        const float m_new = fmaxf(st.m[j], row16_max(xs));
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        corr[j] = exp2f(st.m[j] - m_use);
+        p[j] = exp2f(xs - m_use);
+        st.l[j] = st.l[j] * corr[j] + p[j];
+        st.m[j] = m_new;
+        pw[col * 16 + ((4 * r + j) ^ (col >> 2))] = p[j];   // P[row 4 r + j][token col]
+      }
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        v4f o = st.o[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] *= corr[j];
+        st.o[i] = o;
+      }
+      // ---- P V (the wave's P writes reach its own reads in order)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const float pa = pw[(4 * qq + r) * 16 + (col ^ qq)];   // P[row col][token 4 qq + r]
+        const float* vrow = vt + (4 * qq + r) * D;              // token 4 qq + r: swizzle 4 r
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const int e = col + 16 * dt;
+          st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vrow[4 * ((e >> 2) ^ (4 * r)) + (e & 3)], st.o[dt], 0, 0, 0);
+        }
+      }
+    }
+    wait_vm<0>();        // this wave's loads of tile k + 1 have landed
+    __syncthreads();     // every wave's have, and every wave is done with buffer k & 1
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) st.l[j] = row16_sum(st.l[j]);
+}
+
 // Grid: one block per (batch row, kv head, group, block of BR rows), the groups being the chunks of
 // the quantised region and then a.nwg groups of f32 rows (window, chunk rows; a prefill without
 // packed chunks runs them through prefill_rows_f32 instead).  Each wave takes TPW consecutive
@@ -387,7 +550,7 @@ struct PrefillTiles {
   static constexpr int OCC = (L == HAD && D == 128) ? 3 : 2;
 };
 static_assert(PrefillTiles<HAD, 128>::OCC * PrefillShape<HAD, 128>::LDS <= 160 * 1024 &&
-                  PrefillTiles<HAD, 128>::OCC * window_lds_bytes<128>() <= 160 * 1024,
+                  PrefillTiles<HAD, 128>::OCC * f32_block_lds<128>() <= 160 * 1024,
               "three Hadamard head_dim-128 prefill blocks per CU");
 
 template <int L, int D>
@@ -419,9 +582,12 @@ __global__ __launch_bounds__(256, (PrefillTiles<L, D>::OCC)) void prefill_partia
   // the last a.nwg groups of this grid (if any): f32 rows (the window; for the full-precision prefill
   // also the chunk's own rows, in a.nwin slices of a.slice rows)
   const int nch = a.ngroups - a.nwg;
-  if (c >= nch) {   // f32-row block: wave w takes the 16-row tiles TPW w .. TPW w + TPW - 1
+  if (c >= nch) {   // f32-row block: wave w takes the 16-row tiles TPW w .. TPW w + TPW - 1, one per pass
     const int w = threadIdx.x >> 6;
     const int j = c - nch;
+    const int k0 = a.kchunk ? j * (a.slice / 16) : 0;
+    const int kend = a.kchunk ? k0 + a.slice / 16 : 0x7fffffff;
+    const int lmax_blk = nblk > 0 ? row_limit(a, qs0, row0 + nblk - 1, nrows) : -1;
 #pragma unroll 1
     for (int u = 0; u < TPW; ++u) {
       const int trow = row0 + 16 * (TPW * w + u);
@@ -431,14 +597,9 @@ __global__ __launch_bounds__(256, (PrefillTiles<L, D>::OCC)) void prefill_partia
         const int lmax = row_limit(a, qs0, trow + nv - 1, nrows);
         run = j * a.slice <= lmax - (S - min(S, a.n_recent));
       }
-      if (run) {
-        const int k0 = a.kchunk ? j * (a.slice / 16) : 0;
-        const int kend = a.kchunk ? k0 + a.slice / 16 : 0x7fffffff;
-        WinState<D> st;
-        window_wave<L, D>(a, reinterpret_cast<float*>(smem + w * window_wave_lds<D>()), b, hk, S, trow, nv, qs0, k0, 1,
-                          threadIdx.x & 63, st, kend);
-        window_store<D>(a, st, b, hk, trow, nv, threadIdx.x & 63, a.nc1 - a.nwin + j);
-      }
+      WinState<D> st;
+      f32_rows_block<L, D>(a, smem, b, hk, S, trow, nv, run, qs0, k0, kend, lmax_blk, st);   // every wave
+      if (run) window_store<D>(a, st, b, hk, trow, nv, threadIdx.x & 63, a.nc1 - a.nwin + j);
     }
     return;
   }
@@ -626,7 +787,7 @@ __global__ __launch_bounds__(256, (PrefillTiles<L, D>::OCC)) void prefill_partia
 // slice, block of 64 rows), in the XCD-aware order of prefill_partial; wave w takes the 16-row
 // tile 16 w of the block.
 template <int L, int D>
-__global__ __launch_bounds__(256, D == 128 ? 4 : 2) void prefill_rows_f32(AttendArgs a) {
+__global__ __launch_bounds__(256, D == 128 ? 3 : 2) void prefill_rows_f32(AttendArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int nrb = (a.n_q * a.G + 63) / 64;
   const int id = (int)blockIdx.x, nblocks = (int)gridDim.x;
@@ -646,14 +807,13 @@ __global__ __launch_bounds__(256, D == 128 ? 4 : 2) void prefill_rows_f32(Attend
     const int lmax = row_limit(a, qs0, trow + nv - 1, nrows);
     run = j * a.slice <= lmax - (S - min(S, a.n_recent));
   }
-  if (run) {
-    const int k0 = a.kchunk ? j * (a.slice / 16) : 0;
-    const int kend = a.kchunk ? k0 + a.slice / 16 : 0x7fffffff;
-    WinState<D> st;
-    window_wave<L, D>(a, reinterpret_cast<float*>(smem + w * window_wave_lds<D>()), b, hk, S, trow, nv, qs0, k0, 1,
-                      threadIdx.x & 63, st, kend);
-    window_store<D>(a, st, b, hk, trow, nv, threadIdx.x & 63, a.nc1 - a.nwin + j);
-  }
+  const int k0 = a.kchunk ? j * (a.slice / 16) : 0;
+  const int kend = a.kchunk ? k0 + a.slice / 16 : 0x7fffffff;
+  const int nblk = min(64, nrows - 64 * rb);
+  const int lmax_blk = nblk > 0 ? row_limit(a, qs0, 64 * rb + nblk - 1, nrows) : -1;
+  WinState<D> st;
+  f32_rows_block<L, D>(a, smem, b, hk, S, trow, nv, run, qs0, k0, kend, lmax_blk, st);   // every wave
+  if (run) window_store<D>(a, st, b, hk, trow, nv, threadIdx.x & 63, a.nc1 - a.nwin + j);
 }
 
 // Finish time of a grid under list scheduling on `slots` identical block slots: n1 blocks of cost w1
@@ -775,14 +935,14 @@ static prepare_fn pick_prepare(int layout, int D) {
 template <int L, int D>
 static void launch_prefill(const AttendArgs& a, dim3 grid, bool f32, hipStream_t st) {
   if (f32) {
-    const size_t lds = window_lds_bytes<D>();
+    const size_t lds = f32_block_lds<D>();
     if (lds > 65536)
       (void)hipFuncSetAttribute((const void*)prefill_rows_f32<L, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL((prefill_rows_f32<L, D>), grid, dim3(256), lds, st, a);
     return;
   }
   size_t lds = PrefillShape<L, D>::LDS;
-  if (a.nwg > 0 && (size_t)window_lds_bytes<D>() > lds) lds = window_lds_bytes<D>();
+  if (a.nwg > 0 && (size_t)f32_block_lds<D>() > lds) lds = f32_block_lds<D>();
   if (lds > 65536)
     (void)hipFuncSetAttribute((const void*)prefill_partial<L, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL((prefill_partial<L, D>), grid, dim3(256), lds, st, a);
