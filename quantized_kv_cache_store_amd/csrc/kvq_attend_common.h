@@ -399,11 +399,9 @@ __device__ __forceinline__ void rotate_quarters(float* x, int r) {
 // padding: P[row R][token T] at [T][D + (R ^ ((T >> 2) & 3))], which both the writes (lanes: 16
 // tokens x rows 4 r + j) and the transposing reads (lanes: 16 rows x tokens 4 qq + r) spread over
 // all 64 banks, since a padded row starts 16 banks after the previous one.
-// Full-precision prefill (a.kchunk set): the chunk's own n_q rows follow the window at positions
-// S .. S + n_q - 1, read from f32 rows [batch][n_q][Hkv][D] (rotated beforehand for HAD), so that
-// tokens t < W come from the ring and t >= W from the chunk, at position w0 + t either way.
 // Tiles past the farthest limit of the wave's rows are not visited: a wholly masked tile would
-// leave m, l and o exactly as they are.
+// leave m, l and o exactly as they are.  (The prefill's f32 rows, which also include a chunk's own
+// rows, go through f32_rows_block, which stages each tile once for a block's four waves.)
 template <int D>
 __host__ __device__ constexpr int window_wave_lds() { return 16 * (D + 16) * 4; }
 template <int D>
@@ -417,16 +415,14 @@ struct WinState {
 
 template <int L, int D>
 __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int b, int hk, int S, int row0, int nvalid,
-                                            int qs0, int k0, int kstep, int lane, WinState<D>& st,
-                                            int kend = 0x7fffffff) {
+                                            int qs0, int k0, int kstep, int lane, WinState<D>& st) {
   constexpr int NI = D / 4;           // MFMAs of Q K^T (d = 32 r + i... four lanes groups of D / 4)
   constexpr int VS = D + 16;          // V tile row stride (floats)
   const int col = lane & 15, r = lane >> 4;
   const int nrows = a.n_q * a.G;
   const int W = min(S, a.n_recent);
   const int w0 = S - W;
-  const int NC = a.kchunk ? a.n_q : 0;      // chunk rows after the window
-  const int NT = W + NC;
+  const int NT = W;
   const size_t ring0 = ((size_t)b * a.Hkv + hk) * a.n_recent;
   const float cl = a.alpha * KVQ_LOG2E;
   // the query of row col (prepared rows: rotated for HAD), elements NI r .. NI r + NI - 1
@@ -455,7 +451,7 @@ __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int 
     st.m[j] = -INFINITY;
     st.l[j] = 0.0f;
   }
-  int ntiles = min((NT + 15) / 16, kend);   // kend: the end of this call's slice of tiles
+  int ntiles = (NT + 15) / 16;
   {
     const int lmax = nvalid > 0 ? row_limit(a, qs0, row0 + nvalid - 1, nrows) : -1;   // the tile's farthest limit
     if (lmax < w0) ntiles = 0;
@@ -465,20 +461,11 @@ __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int 
     const int t0 = 16 * k;
     const int t = t0 + col;
     const bool tok_ok = t < NT;
-    const bool in_chunk = t >= W;
-    const float* ksrc;
-    const float* vsrc;
-    if (in_chunk) {
-      const size_t co = (((size_t)b * a.n_q + (tok_ok ? t - W : 0)) * a.Hkv + hk) * D + NI * r;
-      ksrc = a.kchunk + co;
-      vsrc = a.vchunk + co;
-    } else {
-      int slot = w0 + t;
-      slot -= (slot / a.n_recent) * a.n_recent;
-      const size_t ro = (ring0 + (size_t)slot) * D + NI * r;
-      ksrc = a.kring + ro;
-      vsrc = a.vring + ro;
-    }
+    int slot = w0 + (tok_ok ? t : 0);
+    slot -= (slot / a.n_recent) * a.n_recent;
+    const size_t ro = (ring0 + (size_t)slot) * D + NI * r;
+    const float* ksrc = a.kring + ro;
+    const float* vsrc = a.vring + ro;
     // ---- Q K^T
     v4f c = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
