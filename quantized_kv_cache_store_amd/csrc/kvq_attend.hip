@@ -916,7 +916,9 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
       }
     };
     auto span_count = [](int lo, int hi) { return hi >= lo ? hi - lo + 1 : 0; };
-    __builtin_amdgcn_s_setprio(3);   // lowered by progress in the loop below
+    __builtin_amdgcn_s_setprio(3);   // lowered by progress in the loop below, after the steps
+    // p2, p1, p0: the first s with 8 (s + 1) >= 4, 6, 7 nsteps (computed once: no division per step)
+    const int p2 = (4 * nsteps + 7) / 8 - 1, p1 = (6 * nsteps + 7) / 8 - 1, p0 = (7 * nsteps + 7) / 8 - 1;
     // Steps s >= S0 with s + MX < nsteps are the steady part: no count below is clipped by the
     // chunk's ends, so the K wait counts 2 RK - 1 groups and the V wait 2 RV - 1.  Waits with these
     // constant counts skip the compare-and-branch ladder that wait_groups compiles to.
@@ -954,15 +956,9 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
       // launch).  Each wave starts at 3 and drops to 2, 1 and 0 at 1/2, 3/4 and 7/8 of its run, so
       // waves ahead yield to waves behind and all finish within about 30 us (measured 236-243 ->
       // 224-230 us for that launch).
-      const int q_now = (8 * (s + 1)) / nsteps, q_was = (8 * s) / nsteps;
-      if (q_now != q_was) {
-        if (q_now == 4)
-          __builtin_amdgcn_s_setprio(2);
-        else if (q_now == 6)
-          __builtin_amdgcn_s_setprio(1);
-        else if (q_now == 7)
-          __builtin_amdgcn_s_setprio(0);
-      }
+      if (s == p2) __builtin_amdgcn_s_setprio(2);
+      if (s == p1) __builtin_amdgcn_s_setprio(1);
+      if (s == p0) __builtin_amdgcn_s_setprio(0);
     }
   } else {
     unsigned char* buf = smem + wave * ST::BYTES;

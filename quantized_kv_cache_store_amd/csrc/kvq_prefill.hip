@@ -725,6 +725,8 @@ __global__ __launch_bounds__(256, (PrefillTiles<L, D>::OCC)) void prefill_partia
   const int nfull_a = (t_end - t_begin) / 32;
   const int nfull_b = lim_min + 1 - t_begin >= 0 ? (lim_min + 1 - t_begin) / 32 : 0;
   const int nfull = min(min(nfull_a, nfull_b), nsteps);
+  // the priority drops after steps p2, p1, p0: the first s with 8 (s + 1) >= 4, 6, 7 nsteps
+  const int p2 = (4 * nsteps + 7) / 8 - 1, p1 = (6 * nsteps + 7) / 8 - 1, p0 = (7 * nsteps + 7) / 8 - 1;
   auto step = [&](int s, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int T0 = t_begin + 32 * s;
@@ -748,14 +750,10 @@ __global__ __launch_bounds__(256, (PrefillTiles<L, D>::OCC)) void prefill_partia
     // equal work and would otherwise finish oldest first (causal prefill 110 -> 106 us).  Not in the
     // full-precision prefill, whose f32-row blocks at the end of the grid then waited behind the
     // packed blocks (151 -> 156 us with it).
-    const int q_now = (8 * (s + 1)) / nsteps, q_was = (8 * s) / nsteps;
-    if (!a.kchunk && q_now != q_was) {
-      if (q_now == 4)
-        __builtin_amdgcn_s_setprio(2);
-      else if (q_now == 6)
-        __builtin_amdgcn_s_setprio(1);
-      else if (q_now == 7)
-        __builtin_amdgcn_s_setprio(0);
+    if (!a.kchunk) {
+      if (s == p2) __builtin_amdgcn_s_setprio(2);
+      if (s == p1) __builtin_amdgcn_s_setprio(1);
+      if (s == p0) __builtin_amdgcn_s_setprio(0);
     }
   };
   if (!a.kchunk) __builtin_amdgcn_s_setprio(3);
