@@ -46,7 +46,7 @@ static inline int row_slices(int n_recent, int n_q) { return (n_recent + n_q + k
 static_assert(kPrefillChunk % 32 == 0, "chunks of whole 32-token steps");
 
 // LDS of one 32-token step:
-//   KC  int8 codes (code + bias) in A-operand order: [block g][half tau][lane group r][token
+//   KC  int8 codes (code + bias; the Hadamard layout signed) in A-operand order: [block g][half tau][lane group r][token
 //       16 tau + i][8 bytes], the bytes being codes 8r, 8r+2, 8r+4, 8r+6, 8r+1, 8r+3, 8r+5, 8r+7
 //       of block g (8-bit layout: the signed codes 8r .. 8r+7 in order);
 //   VT  dequantised V (fp16) in A-operand order of V^T: [d / 16][lane group r][d % 16][slot k],
@@ -172,6 +172,11 @@ __device__ __forceinline__ void prefill_produce(unsigned char* buf, int tid, con
       const uint32_t x = BIAS ? (ld.kw[k] ^ 0x88888888u) : ld.kw[k];
       lo = x & 0x0F0F0F0Fu;
       hi = (x >> 4) & 0x0F0F0F0Fu;
+      if (L == HAD) {   // signed codes c = (c + 8) - 8 per byte (+0x78 never carries out of a byte),
+        // so that the Q K^T MFMA needs no block-sum offset
+        lo = (lo + 0x78787878u) ^ 0x80808080u;
+        hi = (hi + 0x78787878u) ^ 0x80808080u;
+      }
     }
     *reinterpret_cast<uint2*>(buf + PS::KC + 8 * u) = make_uint2(lo, hi);
   }
@@ -239,8 +244,8 @@ constexpr float kLazyMax = 8.0f;
 // One step of one wave: Q K^T for the wave's TPW tiles of 16 rows, online softmax, P V.  Each V^T
 // operand read from LDS serves every tile of the wave.
 // FULL: all 32 tokens exist and every row of the wave sees them.
-// Scores: xs holds them unscaled (the i32 dots, less the Hadamard layout's block-sum offset qoff0,
-// times the K scales).  The row's scale sqa = |sqc| > 0 is applied in the
+// Scores: xs holds them unscaled (the i32 dots times the K scales; the Hadamard layout's K codes are
+// staged signed, so its dots carry no block-sum offset).  The row's scale sqa = |sqc| > 0 is applied in the
 // exponent, exp2(x sqa - m) in one fma, and scaling the step's maximum by sqa keeps the order; a
 // negative sqc is carried by the K records, whose signs the producer flipped.
 // e_run: Hadamard layout, the wave's V-scale exponent (vscale_exp); the accumulators are in units of
@@ -289,7 +294,7 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
         const bool vis = FULL || (tl < n_tok && T0 + tl <= lim[u]);
         float x;
         if (L == HAD) {
-          x = (float)(acc[0][j] - qoff0[u]) * *reinterpret_cast<const float*>(rec);
+          x = (float)acc[0][j] * *reinterpret_cast<const float*>(rec);   // signed codes: no offset
         } else {
           x = xo[j];
 #pragma unroll
