@@ -406,7 +406,7 @@ __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned 
   if (L == HAD) {
     float vmax = vs_had[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) vmax = fmaxf(vmax, vs_had[i]);
+    for (int i = 1; i < 8; ++i) vmax = fmax_pos(vmax, vs_had[i]);   // scales >= 0
     e_new = max(e_run, vscale_exp(max_over_rows(vmax)));
   }
   // rescale the running sums only when some lane's maximum (or the V exponent) moved (rare after the
@@ -558,15 +558,15 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
   // ---------------- online softmax (base 2): a row's 32 scores sit in lanes (col, r), (col ^ 8, r)
   float smax = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
   smax = max_over_rows(smax);
-  smax = fmaxf(smax, half_swap(smax));
+  smax = fmax_nc(smax, half_swap(smax));
   const float m_new = fmaxf(m_run, smax);
   const float m_use = m_new == -INFINITY ? 0.0f : m_new;
   // Hadamard layout: the exponent of the largest V scale so far (the four lane rows and the two
   // halves: all 32 tokens of the step)
   int e_new = e_run;
   if (L == HAD) {
-    float vmax = max_over_rows(fmaxf(fmaxf(vsc[0], vsc[1]), fmaxf(vsc[2], vsc[3])));
-    vmax = fmaxf(vmax, half_swap(vmax));
+    float vmax = max_over_rows(fmax_pos(fmax_pos(vsc[0], vsc[1]), fmax_pos(vsc[2], vsc[3])));   // scales >= 0
+    vmax = fmax_nc(vmax, half_swap(vmax));
     e_new = max(e_run, vscale_exp(vmax));
   }
   if (__any(m_new > m_run || e_new > e_run)) {

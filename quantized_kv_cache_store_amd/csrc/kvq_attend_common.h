@@ -138,8 +138,8 @@ __device__ __forceinline__ void row_pair(float v, int swap32, float& lo, float& 
 __device__ __forceinline__ float max_over_rows(float v) {
   float a, b;
   row_pair(v, 0, a, b);
-  row_pair(fmaxf(a, b), 1, a, b);
-  return fmaxf(a, b);
+  row_pair(fmax_nc(a, b), 1, a, b);
+  return fmax_nc(a, b);
 }
 
 __device__ __forceinline__ float sum_over_rows(float v) {
@@ -187,10 +187,10 @@ __device__ __forceinline__ float row16_rot(float v, int n) {
   return __builtin_bit_cast(float, y);
 }
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, row16_rot(v, 1));
-  v = fmaxf(v, row16_rot(v, 2));
-  v = fmaxf(v, row16_rot(v, 4));
-  return fmaxf(v, row16_rot(v, 8));
+  v = fmax_nc(v, row16_rot(v, 1));
+  v = fmax_nc(v, row16_rot(v, 2));
+  v = fmax_nc(v, row16_rot(v, 4));
+  return fmax_nc(v, row16_rot(v, 8));
 }
 __device__ __forceinline__ float row16_sum(float v) {
   v += row16_rot(v, 1);

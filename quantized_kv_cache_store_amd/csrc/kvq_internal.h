@@ -70,6 +70,15 @@ __device__ __forceinline__ float hadamard_norm() {
   return D == 128 ? 0x1.6a09e6p-4f : 0.0625f;
 }
 
+// Maximum of two values that are never NaN.  fmaxf makes the compiler quiet each operand it cannot prove
+// canonical (a value loaded from memory or moved across lanes) with an extra v_max_f32; the median of a,
+// b and +inf is their maximum and takes no such step.
+__device__ __forceinline__ float fmax_nc(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, __builtin_inff()); }
+// Maximum of two non-negative values, by their bit patterns (whose order is that of the values).
+__device__ __forceinline__ float fmax_pos(float a, float b) {
+  return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
+}
+
 __device__ __forceinline__ float wave_max16(float v) {
   // max over the 16-lane row that holds this lane (lanes 16r..16r+15)
   v = fmaxf(v, __shfl_xor(v, 1));

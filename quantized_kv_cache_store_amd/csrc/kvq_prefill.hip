@@ -319,7 +319,7 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
     float vmax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      vmax = fmaxf(vmax, fmaxf(a0[j], a1[j]));
+      vmax = fmax_pos(vmax, fmax_pos(a0[j], a1[j]));   // scales >= 0
     }
     e_new = max(e_run, vscale_exp(max_over_rows(vmax)));
 #pragma unroll
