@@ -398,7 +398,7 @@ __device__ __forceinline__ void attend_step(const AttendArgs& a, const unsigned 
 #pragma unroll
   for (int i = 1; i < 8; ++i) smax = fmaxf(smax, xs[i]);
   smax = max_over_rows(smax);
-  const float m_new = fmaxf(m_run, smax);
+  const float m_new = fmax_nc(m_run, smax);
   const float m_use = m_new == -INFINITY ? 0.0f : m_new;
   // Hadamard layout: the exponent of the largest V scale so far (a lane's 8 tokens, then the four
   // lane rows: all 32 tokens of the step)
@@ -559,7 +559,7 @@ __device__ __forceinline__ void attend_step8(const AttendArgs& a, const unsigned
   float smax = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
   smax = max_over_rows(smax);
   smax = fmax_nc(smax, half_swap(smax));
-  const float m_new = fmaxf(m_run, smax);
+  const float m_new = fmax_nc(m_run, smax);
   const float m_use = m_new == -INFINITY ? 0.0f : m_new;
   // Hadamard layout: the exponent of the largest V scale so far (the four lane rows and the two
   // halves: all 32 tokens of the step)

@@ -186,11 +186,15 @@ __device__ __forceinline__ float row16_rot(float v, int n) {
   }
   return __builtin_bit_cast(float, y);
 }
+// The maximum: each rotation is one DPP max (max of the rotated lane's value and the lane's own, never
+// NaN), which also spares the quieting of the moved operand that fmaxf would add.  s_nop 1: the wait
+// states a DPP read of a VGPR needs after a VALU wrote it.
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmax_nc(v, row16_rot(v, 1));
-  v = fmax_nc(v, row16_rot(v, 2));
-  v = fmax_nc(v, row16_rot(v, 4));
-  return fmax_nc(v, row16_rot(v, 8));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf" : "+v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf" : "+v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf" : "+v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf" : "+v"(v));
+  return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {
   v += row16_rot(v, 1);
@@ -487,7 +491,7 @@ __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float x = (tok_ok && w0 + t <= lim[j]) ? c[j] * cl : -INFINITY;
-      const float m_new = fmaxf(st.m[j], row16_max(x));
+      const float m_new = fmax_nc(st.m[j], row16_max(x));
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // a row that sees nothing yet: p = 0
       corr[j] = exp2f(st.m[j] - m_use);
       p[j] = exp2f(x - m_use);

@@ -70,10 +70,14 @@ __device__ __forceinline__ float hadamard_norm() {
   return D == 128 ? 0x1.6a09e6p-4f : 0.0625f;
 }
 
-// Maximum of two values that are never NaN.  fmaxf makes the compiler quiet each operand it cannot prove
-// canonical (a value loaded from memory or moved across lanes) with an extra v_max_f32; the median of a,
-// b and +inf is their maximum and takes no such step.
-__device__ __forceinline__ float fmax_nc(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, __builtin_inff()); }
+// Maximum of two values that are never NaN, as one v_max_f32.  For fmaxf the compiler quiets each operand
+// it cannot prove canonical (a value loaded from memory or moved across lanes) with an extra v_max_f32,
+// and it folds a median with +inf back into that form; an instruction written out is left as it is.
+__device__ __forceinline__ float fmax_nc(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 // Maximum of two non-negative values, by their bit patterns (whose order is that of the values).
 __device__ __forceinline__ float fmax_pos(float a, float b) {
   return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));

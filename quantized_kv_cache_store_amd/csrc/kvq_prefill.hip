@@ -506,7 +506,7 @@ __device__ __forceinline__ void f32_rows_block(const AttendArgs& a, unsigned cha
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float xs = (tok_ok && w0 + t <= lim[j]) ? c[j] * cl : -INFINITY;
-        const float m_new = fmaxf(st.m[j], row16_max(xs));
+        const float m_new = fmax_nc(st.m[j], row16_max(xs));
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
         corr[j] = exp2f(st.m[j] - m_use);
         p[j] = exp2f(xs - m_use);
