@@ -493,8 +493,8 @@ __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int 
       const float x = (tok_ok && w0 + t <= lim[j]) ? c[j] * cl : -INFINITY;
       const float m_new = fmax_nc(st.m[j], row16_max(x));
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // a row that sees nothing yet: p = 0
-      corr[j] = exp2f(st.m[j] - m_use);
-      p[j] = exp2f(x - m_use);
+      corr[j] = __builtin_amdgcn_exp2f(st.m[j] - m_use);   // results below 2^-126 (against a maximum of 1)
+      p[j] = __builtin_amdgcn_exp2f(x - m_use);            // may flush: they change no sum
       st.l[j] = st.l[j] * corr[j] + p[j];
       st.m[j] = m_new;
       vt[col * VS + D + ((4 * r + j) ^ (col >> 2))] = p[j];   // P[row 4 r + j][token col]

@@ -419,6 +419,11 @@ __device__ __forceinline__ void f32_rows_block(const AttendArgs& a, unsigned cha
   const int w0 = S - W;
   const int NT = W + (a.kchunk ? a.n_q : 0);
   const size_t ring0 = ((size_t)b * a.Hkv + hk) * a.n_recent;
+  // chunk row t - W at cbase + (t - W) cstride floats; ring slot of token t < W: (w0 + t) mod n_recent,
+  // the window's positions being consecutive: wr0 + t, less n_recent once it wraps
+  const size_t cbase = ((size_t)b * a.n_q * a.Hkv + hk) * D;
+  const size_t cstride = (size_t)a.Hkv * D;
+  const int wr0 = a.n_recent > 0 ? w0 % a.n_recent : 0;
   const float cl = a.alpha * KVQ_LOG2E;
   if (!run) nv = 0;
   float q[NI];   // the prepared f32 query of row col, elements NI r ..
@@ -464,12 +469,11 @@ __device__ __forceinline__ void f32_rows_block(const AttendArgs& a, unsigned cha
       const float* ksrc;
       const float* vsrc;
       if (t >= W) {
-        const size_t co = (((size_t)b * a.n_q + (t - W)) * a.Hkv + hk) * D;
+        const size_t co = cbase + (size_t)(uint32_t)(t - W) * cstride;
         ksrc = a.kchunk + co;
         vsrc = a.vchunk + co;
       } else {
-        int slot = w0 + t;
-        slot -= (slot / a.n_recent) * a.n_recent;
+        const int slot = wr0 + t >= a.n_recent ? wr0 + t - a.n_recent : wr0 + t;
         const size_t ro = (ring0 + (size_t)slot) * D;
         ksrc = a.kring + ro;
         vsrc = a.vring + ro;
@@ -508,8 +512,8 @@ __device__ __forceinline__ void f32_rows_block(const AttendArgs& a, unsigned cha
         const float xs = (tok_ok && w0 + t <= lim[j]) ? c[j] * cl : -INFINITY;
         const float m_new = fmax_nc(st.m[j], row16_max(xs));
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        corr[j] = exp2f(st.m[j] - m_use);
-        p[j] = exp2f(xs - m_use);
+        corr[j] = __builtin_amdgcn_exp2f(st.m[j] - m_use);   // results below 2^-126 (against a maximum of 1)
+        p[j] = __builtin_amdgcn_exp2f(xs - m_use);          // may flush: they change no sum
         st.l[j] = st.l[j] * corr[j] + p[j];
         st.m[j] = m_new;
         pw[col * 16 + ((4 * r + j) ^ (col >> 2))] = p[j];   // P[row 4 r + j][token col]
