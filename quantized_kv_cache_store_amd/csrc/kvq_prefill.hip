@@ -132,9 +132,8 @@ __device__ __forceinline__ void prefill_fetch(const unsigned char* kslot, const 
         ld.vh[k][s] = vrow[24 * g + 16 + (e >> 2)];
       } else if (L == Q80) {
         ld.vb[k][s] = *reinterpret_cast<const uint16_t*>(vslot + ST::vbytes8(t, d >> 3) + (d & 7));
-      } else {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(vslot + ST::vword(t, d >> 3));
-        ld.vb[k][s] = (w >> (8 * ((d >> 1) & 3))) & 0xFFu;
+      } else {   // the byte of elements (d, d + 1): one byte read, the byte index in the address
+        ld.vb[k][s] = vslot[ST::vword(t, d >> 3) + ((d >> 1) & 3)];
       }
       const unsigned char* rec = vslot + ST::VR + t * SB;
       if (L == HAD) ld.vs[k][s] = 0u;   // its scales go to VR (ld.vr)
