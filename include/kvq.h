@@ -260,7 +260,8 @@ kvq_status kvq_attend_decode_reduce(const kvq_cache* cache, float* out, int32_t 
                                     void* stream);
 
 /* Workspace of kvq_attend_prefill_causal and kvq_prefill_full_then_store:
- * split-K partials (o_c, m_c, l_c) per (batch, query, query head, chunk of
+ * split-K partials (o_c as head_dim f16 values with a power-of-two scale,
+ * m_c, l_c; 2 head_dim + 16 bytes) per (batch, query, query head, chunk of
  * the shortest split, 512 tokens; the call picks chunks of at least that
  * length), plus the window partial, then the prepared queries per (batch,
  * query, query head), then room for the chunk's rotated K and V rows (the

@@ -1035,8 +1035,9 @@ __global__ __launch_bounds__(256, (PartialShape<L, D, TR, FQ>::MIN_WAVES)) void 
 // (h = 1, 2, ..., D / 2, then 1 / sqrt(D)).
 // nwin_always > 0: the last nwin_always slots hold partials of every row (full-precision prefill:
 // the slices of its f32 rows), whatever the window; else the last slot holds the window's partial
-// when there is a window and the row is not empty.
-template <int D, bool ROT, int W>
+// when there is a window and the row is not empty.  NARROW: the prefill's records (narrow_stride:
+// f16 numerators and an exponent), else the decode's f32 ones.
+template <int D, bool ROT, int W, bool NARROW>
 __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out, const int32_t* seq_len,
                                                      int rows_per_b, int nc1, int chunk, int n_recent,
                                                      long total_rows, int nwin_always, int slice, int causal_nq,
@@ -1052,6 +1053,21 @@ __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out
   const bool valid = row < total_rows;              // wave-uniform
   const long rr = valid ? row : total_rows - 1;
   const int b = (int)(rr / rows_per_b);
+  const int PST = NARROW ? narrow_stride(D) : partial_stride(D);
+  constexpr int MO = NARROW ? D / 2 : D;            // the record's m, l (and exponent) after the numerators
+  const float* base = ws + (size_t)rr * nc1 * PST;
+  // Narrow records with one wave per row and at most 64 slots: lane j loads slot j's (m, l, x) together
+  // with the row length, and the numerators of every partial the row uses follow in one batch of up to
+  // 16 loads, so a row costs about two dependent memory round trips instead of one per 4 partials.
+  const bool fast = NARROW && W == 1 && nc1 <= 64;
+  float rm = -INFINITY, rl = 0.0f;
+  int rx = 0;
+  if (fast && lane < nc1) {
+    const float* rec = base + (size_t)lane * PST + MO;
+    rm = rec[0];
+    rl = rec[1];
+    rx = reinterpret_cast<const int*>(rec)[2];
+  }
   const int S = seq_len[b];
   const int Sq = n_recent > 0 ? max(0, S - n_recent) : S;
   if (rs.on) chunk = 4 * run_span(rs, n_recent, [&](int bb) { return ((const_i32_ptr)seq_len)[bb]; });
@@ -1063,29 +1079,83 @@ __global__ __launch_bounds__(256) void attend_reduce(const float* ws, float* out
   }
   const int cnt = nq + nw;
   const int wbase = nc1 - (nwin_always > 0 ? nwin_always : 1) - nq;   // slot of partial i >= nq: wbase + i
-  const int PST = partial_stride(D);
-  const float* base = ws + (size_t)rr * nc1 * PST;
-  float M = -INFINITY;
-  for (int i = sub * 64 + lane; i < cnt; i += 64 * W) M = fmaxf(M, base[(size_t)(i < nq ? i : wbase + i) * PST + D]);
-  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
-  if (W > 1) {
-    if (lane == 0) red_m[wave] = M;
-    __syncthreads();
-    const int w0 = wave - sub;
-    M = red_m[w0];
-    for (int k = 1; k < W; ++k) M = fmaxf(M, red_m[w0 + k]);
-  }
   float o[E], l = 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.0f;
-#pragma unroll 4
-  for (int i = sub; i < cnt; i += W) {
-    const float* p = base + (size_t)(i < nq ? i : wbase + i) * PST;
-    const float mc = p[D];
-    const float w = (mc == -INFINITY) ? 0.0f : exp2f(mc - M);
-    l += w * p[D + 1];
+  if (fast) {
+    // slots in use: [0, nq) and [wbase + nq, wbase + cnt); the others may hold anything
+    const bool used = lane < nq || (lane >= wbase + nq && lane < wbase + cnt);
+    const float mj = used ? rm : -INFINITY;
+    float M = mj;
+    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
+    const float w = mj == -INFINITY ? 0.0f : exp2f(mj - M);
+    float lw = mj == -INFINITY ? 0.0f : w * rl;
+    for (int m = 1; m < 64; m <<= 1) lw += __shfl_xor(lw, m);
+    l = lw;
+    const int wx = __float_as_int(__builtin_amdgcn_ldexpf(w, rx));   // w * 2^x: the numerators' weight
+    for (int i0 = 0; i0 < cnt; i0 += 16) {
+      uint32_t hv[16][E / 2];
+      float wk[16];
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] += w * p[lane * E + e];
+      for (int k = 0; k < 16; ++k) {
+        const int i = i0 + k;
+        if (i < cnt) {
+          const int slot = i < nq ? i : wbase + i;
+          const uint32_t* hw = reinterpret_cast<const uint32_t*>(base + (size_t)slot * PST) + lane * (E / 2);
+          if constexpr (E == 2) {
+            hv[k][0] = hw[0];
+          } else {
+            const u32x2 t = *reinterpret_cast<const u32x2*>(hw);
+            hv[k][0] = t[0];
+            hv[k][1] = t[1];
+          }
+          wk[k] = __int_as_float(__builtin_amdgcn_readlane(wx, slot));
+        } else {
+#pragma unroll
+          for (int q = 0; q < E / 2; ++q) hv[k][q] = 0u;
+          wk[k] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] += wk[k] * (float)as_h2(hv[k][e / 2])[e & 1];
+    }
+  } else {
+    float M = -INFINITY;
+    for (int i = sub * 64 + lane; i < cnt; i += 64 * W) M = fmaxf(M, base[(size_t)(i < nq ? i : wbase + i) * PST + MO]);
+    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
+    if (W > 1) {
+      if (lane == 0) red_m[wave] = M;
+      __syncthreads();
+      const int w0 = wave - sub;
+      M = red_m[w0];
+      for (int k = 1; k < W; ++k) M = fmaxf(M, red_m[w0 + k]);
+    }
+#pragma unroll 4
+    for (int i = sub; i < cnt; i += W) {
+      const float* p = base + (size_t)(i < nq ? i : wbase + i) * PST;
+      const float mc = p[MO];
+      const float w = (mc == -INFINITY) ? 0.0f : exp2f(mc - M);
+      l += w * p[MO + 1];
+      if constexpr (NARROW) {
+        const float wx = __builtin_amdgcn_ldexpf(w, reinterpret_cast<const int*>(p)[MO + 2]);
+        const uint32_t* hw = reinterpret_cast<const uint32_t*>(p) + lane * (E / 2);
+        uint32_t hv[E / 2];
+        if constexpr (E == 2) {
+          hv[0] = hw[0];
+        } else {
+          const u32x2 t = *reinterpret_cast<const u32x2*>(hw);
+          hv[0] = t[0];
+          hv[1] = t[1];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] += wx * (float)as_h2(hv[e / 2])[e & 1];
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] += w * p[lane * E + e];
+      }
+    }
   }
   if (W > 1) {
 #pragma unroll
@@ -1267,15 +1337,19 @@ static kvq_status check_chunk(const kvq_cache* c, int32_t chunk) {
 template <int D, bool ROT, int W>
 static void launch_reduce_w(float* out, long rows, int rows_per_b, const int32_t* seq_len, int nc1, int chunk,
                             int n_recent, const float* ws, hipStream_t s, int nwin_always, int slice, int causal_nq,
-                            RunSplit rs) {
+                            RunSplit rs, bool narrow) {
   const long blocks = (rows + (4 / W) - 1) / (4 / W);
-  hipLaunchKernelGGL((attend_reduce<D, ROT, W>), dim3((unsigned)blocks), dim3(256), 0, s, ws, out, seq_len, rows_per_b,
-                     nc1, chunk, n_recent, rows, nwin_always, slice, causal_nq, rs);
+  if (narrow)
+    hipLaunchKernelGGL((attend_reduce<D, ROT, W, true>), dim3((unsigned)blocks), dim3(256), 0, s, ws, out, seq_len,
+                       rows_per_b, nc1, chunk, n_recent, rows, nwin_always, slice, causal_nq, rs);
+  else
+    hipLaunchKernelGGL((attend_reduce<D, ROT, W, false>), dim3((unsigned)blocks), dim3(256), 0, s, ws, out, seq_len,
+                       rows_per_b, nc1, chunk, n_recent, rows, nwin_always, slice, causal_nq, rs);
 }
 
 kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b, const int32_t* seq_len,
                          int nc1, int32_t chunk, const float* ws, hipStream_t s, int nwin_always, int slice,
-                         int causal_nq, RunSplit rs) {
+                         int causal_nq, RunSplit rs, bool narrow) {
   const int wa = nwin_always;
   const long rows = (long)batch * rows_per_b;
   // one wave per row when there are rows enough to fill the chip, else four waves split each row
@@ -1283,15 +1357,15 @@ kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t 
   const bool rot = c->layout == HAD;
   const int n = c->n_recent;
   if (c->head_dim == 128) {
-    if (rot) many ? launch_reduce_w<128, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs)
-                  : launch_reduce_w<128, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs);
-    else many ? launch_reduce_w<128, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs)
-              : launch_reduce_w<128, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs);
+    if (rot) many ? launch_reduce_w<128, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs, narrow)
+                  : launch_reduce_w<128, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs, narrow);
+    else many ? launch_reduce_w<128, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs, narrow)
+              : launch_reduce_w<128, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs, narrow);
   } else {
-    if (rot) many ? launch_reduce_w<256, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs)
-                  : launch_reduce_w<256, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs);
-    else many ? launch_reduce_w<256, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs)
-              : launch_reduce_w<256, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs);
+    if (rot) many ? launch_reduce_w<256, true, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs, narrow)
+                  : launch_reduce_w<256, true, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs, narrow);
+    else many ? launch_reduce_w<256, false, 1>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs, narrow)
+              : launch_reduce_w<256, false, 4>(out, rows, rows_per_b, seq_len, nc1, chunk, n, ws, s, wa, slice, causal_nq, rs, narrow);
   }
   return check_launch("attention reduce kernel");
 }

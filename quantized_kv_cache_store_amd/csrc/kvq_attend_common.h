@@ -163,6 +163,14 @@ __device__ __forceinline__ int vscale_exp(float vmax) {
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
+// Narrow partial records (narrow_stride): x = frexp exponent of the row's largest |o| (0 when every
+// o is 0), h = o * 2^(15 - x) rounded to f16 (|h| < 2^15, exact scaling by ldexp), and the record's
+// exponent x - 15 plus the accumulators' own unit.
+__device__ __forceinline__ int narrow_exp(float amax) { return __builtin_amdgcn_frexp_expf(amax); }
+__device__ __forceinline__ uint32_t narrow_pk(float a, float b, int x) {
+  return as_u32(h2{(_Float16)__builtin_amdgcn_ldexpf(a, 15 - x), (_Float16)__builtin_amdgcn_ldexpf(b, 15 - x)});
+}
+
 // q6_0 octet (low-nibble dword + 16 bits of top-bit pairs) -> biased 6-bit codes
 // (code + 32) as bytes, even elements [0,2,4,6] in `ev`, odd [1,3,5,7] in `od`.
 __device__ __forceinline__ void q6_octet(uint32_t lo, uint32_t hi16, uint32_t& ev, uint32_t& od) {
@@ -520,20 +528,39 @@ __device__ __forceinline__ void window_wave(const AttendArgs& a, float* vt, int 
   for (int j = 0; j < 4; ++j) st.l[j] = row16_sum(st.l[j]);
 }
 
-// Write a window state as the partial of rows row0 + 4 r + j (< nvalid) in partial slot `slot`.
+// Write a window state as the (narrow) partial of rows row0 + 4 r + j (< nvalid) in partial slot
+// `slot` (prefill).  Lane col holds o[16 dt + col]; lane pairs (col, col ^ 1) swap one value so that
+// each writes a dword of two neighbouring elements: the even lane o[16 dt + col], o[16 dt + col + 1]
+// for even dt, the odd lane the pair at col - 1 for odd dt.
 template <int D>
 __device__ __forceinline__ void window_store(const AttendArgs& a, const WinState<D>& st, int b, int hk, int row0, int nvalid,
                                              int lane, int slot) {
   const int col = lane & 15, r = lane >> 4;
+  const bool odd = (col & 1) != 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if (4 * r + j >= nvalid) continue;
-    float* dst = a.ws + (row_index(a, b, hk, row0 + 4 * r + j) * a.nc1 + slot) * partial_stride(D);
+    float amax = 0.0f;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) dst[16 * dt + col] = st.o[dt][j];
+    for (int dt = 0; dt < D / 16; ++dt) amax = fmax_pos(amax, fabsf(st.o[dt][j]));
+    const int x = narrow_exp(row16_max(amax));
+    uint32_t pk[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; dt += 2) {
+      // even lane: keeps o[dt] (its own element 16 dt + col), sends o[dt + 1]; odd lane the reverse
+      const float keep = odd ? st.o[dt + 1][j] : st.o[dt][j];
+      const float send = odd ? st.o[dt][j] : st.o[dt + 1][j];
+      const float got = __shfl_xor(send, 1);
+      pk[dt / 2] = odd ? narrow_pk(got, keep, x) : narrow_pk(keep, got, x);
+    }
+    if (4 * r + j >= nvalid) continue;
+    float* dst = a.ws + (row_index(a, b, hk, row0 + 4 * r + j) * a.nc1 + slot) * narrow_stride(D);
+    uint32_t* hw = reinterpret_cast<uint32_t*>(dst);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; dt += 2) hw[8 * (dt + (odd ? 1 : 0)) + (col >> 1)] = pk[dt / 2];
     if (col == 0) {
-      dst[D] = st.m[j];
-      dst[D + 1] = st.l[j];
+      dst[D / 2] = st.m[j];
+      dst[D / 2 + 1] = st.l[j];
+      reinterpret_cast<int*>(dst)[D / 2 + 2] = x - 15;
     }
   }
 }
@@ -837,10 +864,11 @@ kvq_status launch_rotate_rows(const kvq_cache* c, const float* k_new, const floa
 // nwin_always > 0: the rows' f32-row partials are the last nwin_always slots (full-precision
 // prefill, slices of `slice` rows; with causal_nq > 0, the causal limit of query i, i = (row in the
 // batch row) / (rows_per_b / causal_nq), reaches only the first (W + i) / slice + 1 of them, W the
-// row's window); else one window partial when n_recent > 0 and the row is not empty.
+// row's window); else one window partial when n_recent > 0 and the row is not empty.  narrow: the
+// records are the prefill's (narrow_stride), else the decode's f32 ones (partial_stride).
 kvq_status launch_reduce(const kvq_cache* c, float* out, int32_t batch, int32_t rows_per_b, const int32_t* seq_len,
                          int nc1, int32_t chunk, const float* ws, hipStream_t s, int nwin_always = 0, int slice = 0,
-                         int causal_nq = 0, RunSplit rs = RunSplit{});
+                         int causal_nq = 0, RunSplit rs = RunSplit{}, bool narrow = false);
 
 // The decode's two phases (kvq_attend.hip), for kvq_attend_decode and its variants: decode_check
 // validates the arguments; decode_partial_ws and decode_reduce_ws then run the split-K phase and the

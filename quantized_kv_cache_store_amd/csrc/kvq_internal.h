@@ -51,6 +51,10 @@ static inline size_t scale_bytes_rt(int layout, int D) {
 
 // Split-K partial record: o[D] (unnormalised), m (base-2 logit max), l, 2 pad.
 static inline constexpr int partial_stride(int D) { return D + 4; }
+// The prefill's partial record, in floats: D f16 values h[d], then m, l (f32) and an int exponent x;
+// the unnormalised o[d] is h[d] * 2^x, the row scaled so that max |h| lies in [2^14, 2^15).  2 D + 16
+// bytes: half the f32 record's, which the prefill's reduce reads and its partial kernels write.
+static inline constexpr int narrow_stride(int D) { return D / 2 + 4; }
 
 // host-side error reporting (kvq_api.hip)
 kvq_status fail(kvq_status s, const char* fmt, ...);

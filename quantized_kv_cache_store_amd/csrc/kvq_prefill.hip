@@ -66,6 +66,18 @@ struct PStep {
   static constexpr int VU = D / 128;          // V units (element pair, lane group) per thread
 };
 
+// K unit k of thread tid: unit u = (g * 2 + h) * 64 + 16 r + i is the dword of 8 codes of block g,
+// lane group r, of token 16 h + i of the step, the A-operand piece of lane 16 r + i for the tokens
+// 16 h .. 16 h + 15 of v_mfma_i32_16x16x32_i8.  The Hadamard layout pairs blocks 2 j and 2 j + 1 in
+// one thread (units k, k + 1), so that its producer writes, and its consumers read, both pieces of a
+// v_mfma_i32_16x16x64_i8 operand as 16 contiguous bytes at (128 j + 64 h + lane) * 16.
+template <int L>
+__device__ __forceinline__ int k_unit(int tid, int k) {
+  if (L != HAD) return tid + 256 * k;
+  const int j = (tid >> 7) + 2 * (k >> 1);
+  return ((2 * j + (k & 1)) * 2 + ((tid >> 6) & 1)) * 64 + (tid & 63);
+}
+
 // Loaded (not yet unpacked) inputs of one step, per thread.
 template <int L, int D>
 struct PLoad {
@@ -101,7 +113,7 @@ __device__ __forceinline__ void prefill_fetch(const unsigned char* kslot, const 
   constexpr int PB = T::PB, SB = T::SB;
 #pragma unroll
   for (int k = 0; k < PS::KU; ++k) {
-    const int u = tid + 256 * k;
+    const int u = k_unit<L>(tid, k);
     const int i = u & 15, r = (u >> 4) & 3, h = (u >> 6) & 1, g = u >> 7;
     const int t = 16 * h + i;
     if (L == Q60) {
@@ -158,8 +170,23 @@ __device__ __forceinline__ void prefill_produce(unsigned char* buf, int tid, con
   using PS = PStep<L, D>;
   constexpr int SB = T::SB;
   constexpr int BIAS = CodeBias<L>::value;
+  if (L == HAD) {   // k_unit: a thread's units k and k + 1 are blocks g, g + 1 of one (half, lane)
 #pragma unroll
-  for (int k = 0; k < PS::KU; ++k) {
+    for (int k = 0; k < PS::KU; k += 2) {
+      uint32_t c[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        // signed codes c = (c + 8) - 8 per byte (+0x78 never carries out of a byte), so that the
+        // Q K^T MFMA needs no block-sum offset
+        const uint32_t x = ld.kw[k + e] ^ 0x88888888u;   // the stored codes carry a bias of 8
+        c[2 * e] = ((x & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+        c[2 * e + 1] = (((x >> 4) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+      }
+      *reinterpret_cast<u32x4*>(buf + PS::KC + 16 * (tid + 128 * k)) = u32x4{c[0], c[1], c[2], c[3]};
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < (L == HAD ? 0 : PS::KU); ++k) {
     const int u = tid + 256 * k;
     uint32_t lo, hi;
     if (L == Q60) {
@@ -171,11 +198,6 @@ __device__ __forceinline__ void prefill_produce(unsigned char* buf, int tid, con
       const uint32_t x = BIAS ? (ld.kw[k] ^ 0x88888888u) : ld.kw[k];
       lo = x & 0x0F0F0F0Fu;
       hi = (x >> 4) & 0x0F0F0F0Fu;
-      if (L == HAD) {   // signed codes c = (c + 8) - 8 per byte (+0x78 never carries out of a byte),
-        // so that the Q K^T MFMA needs no block-sum offset
-        lo = (lo + 0x78787878u) ^ 0x80808080u;
-        hi = (hi + 0x78787878u) ^ 0x80808080u;
-      }
     }
     *reinterpret_cast<uint2*>(buf + PS::KC + 8 * u) = make_uint2(lo, hi);
   }
@@ -251,7 +273,7 @@ constexpr float kLazyMax = 8.0f;
 // 2^e_run and P carries p * s_v / 2^e_run.
 template <int L, int D, bool FULL, int TPW>
 __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int lane, int T0, int n_tok, const int* lim,
-                                                const long (*qb)[D / 32], const float (*qsB)[(D / 32 + 3) / 4],
+                                                const v4i (*qb)[(D / 32 + 1) / 2], const float (*qsB)[(D / 32 + 3) / 4],
                                                 const int* qoff0, const float* sqa, float* m_run, float* l_run,
                                                 int& e_run, v4f (*oacc)[D / 16]) {
   using T = Layout<L, D>;
@@ -266,14 +288,25 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       v4i acc[SG];
+      if (L == HAD) {
+        // one scale per token: two 32-code groups per v_mfma_i32_16x16x64_i8, the groups' 8-byte
+        // operand pieces side by side in A and in B (the same pairing of bytes on both sides, so the
+        // integer sum is that of two 16x16x32 products)
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const uint2 w = *reinterpret_cast<const uint2*>(buf + PS::KC + ((g * 2 + tau) * 64 + lane) * 8);
-        const long A = (long)((uint64_t)w.x | ((uint64_t)w.y << 32));
-        if (L == HAD)
-          acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, qb[u][g], g == 0 ? v4i{0, 0, 0, 0} : acc[0], 0, 0, 0);
-        else
-          acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, qb[u][g], v4i{0, 0, 0, 0}, 0, 0, 0);
+        for (int g = 0; g < NG; g += 2) {
+          const v4i A = *reinterpret_cast<const v4i*>(buf + PS::KC + (((g >> 1) * 2 + tau) * 64 + lane) * 16);
+          acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, qb[u][g / 2], g == 0 ? v4i{0, 0, 0, 0} : acc[0], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const uint2 w = *reinterpret_cast<const uint2*>(buf + PS::KC + ((g * 2 + tau) * 64 + lane) * 8);
+          const long A = (long)((uint64_t)w.x | ((uint64_t)w.y << 32));
+          const v4i q2 = qb[u][g / 2];
+          const long B = __builtin_bit_cast(long, (g & 1) ? u32x2{(unsigned)q2[2], (unsigned)q2[3]}
+                                                          : u32x2{(unsigned)q2[0], (unsigned)q2[1]});
+          acc[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+        }
       }
       v4f xo = v4f{0.f, 0.f, 0.f, 0.f};
       if (L != HAD && L != Q80) {   // the 8-bit K codes carry no offset
@@ -630,7 +663,7 @@ __global__ __launch_bounds__(256, (PrefillTiles<L, D>::OCC)) void prefill_partia
   // ---- prologue: this wave's rows from the prepared rows (int8 query in the B-operand order, its
   // scale and block sums); the perms consume the loads here, outside the streaming loop
   constexpr int NQ = (NG + 3) / 4;
-  long qb[TPW][NG];
+  v4i qb[TPW][(NG + 1) / 2];   // group g's 8 bytes: elements 2 (g & 1), 2 (g & 1) + 1 of qb[u][g / 2]
   float qsB[TPW][NQ];
   int qoff0[TPW], lim[TPW];
   float sqa[TPW];   // |score scale| in log2 units, at least FLT_MIN (so that -inf * sqa stays -inf)
@@ -638,7 +671,7 @@ __global__ __launch_bounds__(256, (PrefillTiles<L, D>::OCC)) void prefill_partia
   for (int u = 0; u < TPW; ++u) {
     const int trow = wrow0 + 16 * u;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) qb[u][g] = 0;
+    for (int g = 0; g < (NG + 1) / 2; ++g) qb[u][g] = v4i{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < NQ; ++i) qsB[u][i] = 0.0f;
     qoff0[u] = 0;
@@ -650,7 +683,8 @@ __global__ __launch_bounds__(256, (PrefillTiles<L, D>::OCC)) void prefill_partia
         const uint2 w = *reinterpret_cast<const uint2*>(a.q8p + fr * D + 32 * g + 8 * r);
         const uint32_t lo = L == Q80 ? w.x : __builtin_amdgcn_perm(w.y, w.x, 0x06040200u);
         const uint32_t hi = L == Q80 ? w.y : __builtin_amdgcn_perm(w.y, w.x, 0x07050301u);
-        qb[u][g] = __builtin_bit_cast(long, u32x2{lo, hi});
+        qb[u][g / 2][2 * (g & 1)] = (int)lo;
+        qb[u][g / 2][2 * (g & 1) + 1] = (int)hi;
       }
       const int* qs = a.qsump + fr * NG;
 #pragma unroll
@@ -769,18 +803,31 @@ __global__ __launch_bounds__(256, (PrefillTiles<L, D>::OCC)) void prefill_partia
   for (; s < nfull; ++s) step(s, std::integral_constant<bool, true>{});
   for (; s < nsteps; ++s) step(s, std::integral_constant<bool, false>{});
 
-  // ---------------- this wave's chunk partials: o[d = 16 dt + 4 r + j] of row col of each tile
+  // ---------------- this wave's chunk partials (narrow records): o[d = 16 dt + 4 r + j] of row col of
+  // each tile, lanes col, col + 16, col + 32 and col + 48 holding the row
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const float l = sum_over_rows(l_run[u]);
-    if (col < nval[u]) {
-      float* dst = a.ws + (row_index(a, b, hk, wrow0 + 16 * u + col) * a.nc1 + c) * partial_stride(D);
-      const float us = L == HAD ? __builtin_amdgcn_ldexpf(1.0f, e_run) : 1.0f;   // the accumulators' unit
+    float amax = 0.0f;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<v4f*>(dst + 16 * dt + 4 * r) = oacc[u][dt] * us;
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) amax = fmax_pos(amax, fabsf(oacc[u][dt][j]));
+    amax = fmax_pos(amax, __shfl_xor(amax, 16));
+    const int x = narrow_exp(fmax_pos(amax, __shfl_xor(amax, 32)));
+    if (col < nval[u]) {
+      float* dst = a.ws + (row_index(a, b, hk, wrow0 + 16 * u + col) * a.nc1 + c) * narrow_stride(D);
+      uint32_t* hw = reinterpret_cast<uint32_t*>(dst);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const v4f o = oacc[u][dt];
+        *reinterpret_cast<u32x2*>(hw + 8 * dt + 2 * r) = u32x2{narrow_pk(o[0], o[1], x), narrow_pk(o[2], o[3], x)};
+      }
       if (r == 0) {
-        dst[D] = m_run[u];
-        dst[D + 1] = l;
+        dst[D / 2] = m_run[u];
+        dst[D / 2 + 1] = l;
+        // the accumulators' unit 2^e_run (Hadamard layout) times the record's scale
+        reinterpret_cast<int*>(dst)[D / 2 + 2] = (L == HAD ? e_run : 0) + x - 15;
       }
     }
   }
@@ -969,10 +1016,10 @@ static prefill_fn pick_prefill(int layout, int D) {
 }
 
 
-// Workspace of a prefill: the partials [rows x nslots x (D + 4)] f32 (nslots: the chunks and the f32-row
-// slots of that call), then the prepared rows.
+// Workspace of a prefill: the narrow partial records [rows x nslots x (D / 2 + 4)] floats (nslots: the
+// chunks and the f32-row slots of that call), then the prepared rows.
 static RowPrep prefill_ws(size_t rows, int D, int nslots) {
-  return row_prep_layout(rows * (size_t)nslots * partial_stride(D) * sizeof(float), rows, D);
+  return row_prep_layout(rows * (size_t)nslots * narrow_stride(D) * sizeof(float), rows, D);
 }
 
 kvq_status launch_prepare_rows(const kvq_cache* c, const float* q, int n_vec, unsigned char* ws, const RowPrep& w,
@@ -1038,7 +1085,7 @@ extern "C" kvq_status kvq_attend_prefill_causal(const kvq_cache* c, const float*
     if ((st = check_launch("prefill partial kernel")) != KVQ_OK) return st;
   }
   return launch_reduce(c, out, batch, n_q * Hq, seq_len, a.nc1, chunk, (const float*)workspace,
-                       (hipStream_t)stream);
+                       (hipStream_t)stream, 0, 0, 0, RunSplit{}, true);
 }
 
 extern "C" kvq_status kvq_prefill_full_then_store(const kvq_cache* c, const float* q, const float* k_new,
@@ -1114,5 +1161,5 @@ extern "C" kvq_status kvq_prefill_full_then_store(const kvq_cache* c, const floa
   if ((st = kvq_store_chunk(c, k_new, v_new, batch, n_q, q_start, block_table, max_pages, max_seq_len, stream)) != KVQ_OK)
     return st;
   return launch_reduce(c, out, batch, n_q * Hq, q_start, a.nc1, chunk, (const float*)workspace, s, a.nwin,
-                       a.slice, causal ? n_q : 0);
+                       a.slice, causal ? n_q : 0, RunSplit{}, true);
 }

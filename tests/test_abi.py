@@ -83,12 +83,13 @@ def test_attend_validates_before_launch():
 def test_prefill_validates_before_launch():
     lib = kvq.load()
     d = ctypes.byref(_desc())
-    # partials [B][n_q][Hq][slots][D + 4] f32, then the prepared rows:
+    # narrow partial records [B][n_q][Hq][slots][D / 2 + 4] floats (D f16 numerators, m, l, exponent),
+    # then the prepared rows:
     # rotated f32 query, int8 query, f32 scale, int32 block sums
     rows = 512 * 16
     # partials (17 chunks of the shortest split, 512 tokens, + 8 slices of 128 f32 rows: a 512-token
     # window and the 512-token chunk) | f32 query | int8 query | scale | block sums | chunk K and V rows
-    assert lib.kvq_prefill_workspace_bytes(1, 512, 16, 128, 8704) == rows * (25 * 132 * 4 + 128 * 4 + 128 + 4 + 4 * 4
+    assert lib.kvq_prefill_workspace_bytes(1, 512, 16, 128, 8704) == rows * (25 * 68 * 4 + 128 * 4 + 128 + 4 + 4 * 4
                                                                              + 2 * 128 * 4)
     assert lib.kvq_prefill_workspace_bytes(1, 0, 16, 128, 8704) == 0
     big = 1 << 30
