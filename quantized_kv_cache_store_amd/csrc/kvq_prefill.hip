@@ -341,42 +341,42 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
     }
   }
 
-  // Hadamard layout: the V scales of the lane's 8 tokens (16 tau + 4 r + j) and the exponent of the
-  // largest so far (the four lane rows hold all 32 tokens)
+  // Hadamard layout: the V scales of the lane's 8 tokens (16 tau + 4 r + j); the exponent of the
+  // largest so far grows only where one of them reaches 2^e_run.  A rescale is needed only where a
+  // step's scaled score passes its row's maximum by kLazyMax or where the exponent grows: each lane
+  // tests its own 8 tokens (a row's maximum passes the bound exactly when the lane holding it does),
+  // and the row maxima and the exponent, which need cross-lane steps, are formed in the wave's one
+  // branch, as they were in every step before.
   float vsc[8];
   int e_new = e_run;
+  float vmax = 0.0f;
+  v4f a0, a1;
+  bool up = false;
   if (L == HAD) {
-    const v4f a0 = *reinterpret_cast<const v4f*>(buf + PS::VR + 16 * r);
-    const v4f a1 = *reinterpret_cast<const v4f*>(buf + PS::VR + 64 + 16 * r);
-    float vmax = 0.0f;
+    a0 = *reinterpret_cast<const v4f*>(buf + PS::VR + 16 * r);
+    a1 = *reinterpret_cast<const v4f*>(buf + PS::VR + 64 + 16 * r);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       vmax = fmax_pos(vmax, fmax_pos(a0[j], a1[j]));   // scales >= 0
     }
-    e_new = max(e_run, vscale_exp(max_over_rows(vmax)));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      vsc[j] = __builtin_amdgcn_ldexpf(a0[j], -e_new);
-      vsc[4 + j] = __builtin_amdgcn_ldexpf(a1[j], -e_new);
-    }
+    up = vscale_exp(vmax) > e_run;
   }
-  // the step's scaled maxima; a rescale only where one passes its row's maximum by kLazyMax, or where
-  // the V-scale exponent grew (one branch for the wave)
-  float sm[TPW];
-  bool up = L == HAD && e_new != e_run;
+  float smx[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     float smax = xs[u][0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) smax = fmaxf(smax, xs[u][i]);
-    smax = max_over_rows(smax);
-    sm[u] = smax == -INFINITY ? -INFINITY : smax * sqa[u];
-    up = up || sm[u] > m_run[u] + kLazyMax;
+    smx[u] = smax;
+    up = up || smax * sqa[u] > m_run[u] + kLazyMax;   // -inf * sqa stays -inf (sqa > 0)
   }
   if (__builtin_amdgcn_ballot_w64(up) != 0) {
+    if (L == HAD) e_new = max(e_run, vscale_exp(max_over_rows(vmax)));
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      const float m_new = sm[u] > m_run[u] + kLazyMax ? sm[u] : m_run[u];
+      const float smax = max_over_rows(smx[u]);
+      const float sm = smax == -INFINITY ? -INFINITY : smax * sqa[u];
+      const float m_new = sm > m_run[u] + kLazyMax ? sm : m_run[u];
       // exactly 1 where the maximum held; 0 from an empty row (-inf) to a finite maximum
       const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
       l_run[u] *= corr;
@@ -387,6 +387,13 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
     }
   }
   e_run = e_new;
+  if (L == HAD) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vsc[j] = __builtin_amdgcn_ldexpf(a0[j], -e_new);
+      vsc[4 + j] = __builtin_amdgcn_ldexpf(a1[j], -e_new);
+    }
+  }
   v8h pB[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
