@@ -421,8 +421,9 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
 // trow .. trow + nv - 1, run = false when it has none to compute) and the block walks the 16-token
 // tiles k0 .. kend - 1 of the f32 rows once, staging each tile's K and V in LDS for all four waves by
 // direct loads issued one tile ahead (one barrier per tile), instead of every wave reading them for
-// itself.  Per wave the arithmetic is that of window_wave, step for step: the Q K^T MFMAs take K from
-// the staged tile in the same order, P goes through the wave's own LDS tile, and P V reads the staged V.
+// itself.  Per wave the arithmetic is that of window_wave but for the softmax's lazy maximum: the Q K^T
+// MFMAs take K from the staged tile in the same order, P goes through the wave's own LDS tile, and P V
+// reads the staged V.
 // The block's tiles end at the farthest limit of its rows (lmax_blk); a wave computes only up to its
 // own rows'.  Every wave of the block calls this with the same k0, kend and lmax_blk.  The rows come
 // prepared (a.qrot: the f32 query, rotated for the Hadamard layout).
@@ -544,25 +545,40 @@ __device__ __forceinline__ void f32_rows_block(const AttendArgs& a, unsigned cha
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 2], kv.z, c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 3], kv.w, c, 0, 0, 0);
       }
-      // ---- online softmax of rows 4 r + j over the tile's 16 tokens
-      float p[4], corr[4];
+      // ---- online softmax of rows 4 r + j over the tile's 16 tokens, with a lazy maximum: a row's
+      // maximum, and its l and accumulators, change only in a tile where one of its scores passes it by
+      // kLazyMax (each lane tests its own token; one branch for the wave), so p lies in [0, 2^8]
+      float xs[4];
+      bool up = false;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float xs = (tok_ok && w0 + t <= lim[j]) ? c[j] * cl : -INFINITY;
-        const float m_new = fmax_nc(st.m[j], row16_max(xs));
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        corr[j] = __builtin_amdgcn_exp2f(st.m[j] - m_use);   // results below 2^-126 (against a maximum of 1)
-        p[j] = __builtin_amdgcn_exp2f(xs - m_use);          // may flush: they change no sum
-        st.l[j] = st.l[j] * corr[j] + p[j];
-        st.m[j] = m_new;
-        pw[col * 16 + ((4 * r + j) ^ (col >> 2))] = p[j];   // P[row 4 r + j][token col]
+        xs[j] = (tok_ok && w0 + t <= lim[j]) ? c[j] * cl : -INFINITY;
+        up = up || xs[j] > st.m[j] + kLazyMax;
+      }
+      if (__builtin_amdgcn_ballot_w64(up) != 0) {
+        float corr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float m_new = fmax_nc(st.m[j], row16_max(xs[j]));
+          const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+          corr[j] = __builtin_amdgcn_exp2f(st.m[j] - m_use);   // results below 2^-126 (against a maximum of 1)
+          st.l[j] *= corr[j];
+          st.m[j] = m_new;
+        }
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) {
+          v4f o = st.o[i];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] *= corr[j];
+          st.o[i] = o;
+        }
       }
 #pragma unroll
-      for (int i = 0; i < D / 16; ++i) {
-        v4f o = st.o[i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] *= corr[j];
-        st.o[i] = o;
+      for (int j = 0; j < 4; ++j) {
+        const float m_use = st.m[j] == -INFINITY ? 0.0f : st.m[j];
+        const float p = __builtin_amdgcn_exp2f(xs[j] - m_use);   // may flush: they change no sum
+        st.l[j] += p;
+        pw[col * 16 + ((4 * r + j) ^ (col >> 2))] = p;   // P[row 4 r + j][token col]
       }
       // ---- P V (the wave's P writes reach its own reads in order)
 #pragma unroll
