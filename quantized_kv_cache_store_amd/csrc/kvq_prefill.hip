@@ -421,21 +421,23 @@ __device__ __forceinline__ void prefill_consume(const unsigned char* buf, int la
 // trow .. trow + nv - 1, run = false when it has none to compute) and the block walks the 16-token
 // tiles k0 .. kend - 1 of the f32 rows once, staging each tile's K and V in LDS for all four waves by
 // direct loads issued one tile ahead (one barrier per tile), instead of every wave reading them for
-// itself.  Per wave the arithmetic is that of window_wave but for the softmax's lazy maximum: the Q K^T
-// MFMAs take K from the staged tile in the same order, P goes through the wave's own LDS tile, and P V
-// reads the staged V.
+// itself.  Per wave the arithmetic is window_wave's with the operands of Q K^T swapped, so that the
+// scores come out as S[token][row] and P stays in registers: lane (col, r) holds row col against tokens
+// 4 r + j, which is the A operand of the P V MFMA that takes tokens 4 r + j (k = r); the softmax keeps a
+// lazy maximum per row.
 // The block's tiles end at the farthest limit of its rows (lmax_blk); a wave computes only up to its
 // own rows'.  Every wave of the block calls this with the same k0, kend and lmax_blk.  The rows come
 // prepared (a.qrot: the f32 query, rotated for the Hadamard layout).
 // Staged tiles, unpadded (direct loads fill 1 KiB runs), in 16-byte chunks swizzled by token t: K chunk x
 // of token t at chunk x ^ (t & 15) of its row (a quarter-wave's float4 reads, 16 tokens, then fall on
-// distinct banks), V chunk x at x ^ 4 (t & 3) (the four token rows of a P V read start 16 banks apart).
+// distinct banks), V chunk x at x ^ 4 ((t >> 2) & 3) (the four token rows 4 r + j of a P V read start 16
+// banks apart).
 // Tokens past the last f32 row load the last row instead: their scores are masked and their P is 0.
 template <int D>
 struct F32Tiles {
   static constexpr int TILE = 16 * D;                   // floats of a K (or V) tile
-  static constexpr int K0 = 0, V0 = 2 * TILE, P0 = 4 * TILE;   // float offsets: K, V double buffers, P
-  static constexpr int FLOATS = P0 + 4 * 256;          // and each wave's P tile [16 tokens][16 rows]
+  static constexpr int K0 = 0, V0 = 2 * TILE;         // float offsets: K, V double buffers
+  static constexpr int FLOATS = 4 * TILE;
   static constexpr int BYTES = 4 * FLOATS;
   static constexpr int INSTR = TILE * 4 / 1024 / 4;     // direct loads of a tile per wave
 };
@@ -452,7 +454,6 @@ __device__ __forceinline__ void f32_rows_block(const AttendArgs& a, unsigned cha
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, r = lane >> 4;
   float* const lds = reinterpret_cast<float*>(smem);
-  float* const pw = lds + FT::P0 + wave * 256;      // this wave's P: [token T][row R ^ ((T >> 2) & 3)]
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
   const int nrows = a.n_q * a.G;
   const int W = min(S, a.n_recent);
@@ -479,16 +480,10 @@ __device__ __forceinline__ void f32_rows_block(const AttendArgs& a, unsigned cha
       q[i + 3] = v.w;
     }
   }
-  int lim[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) lim[j] = 4 * r + j < nv ? row_limit(a, qs0, trow + 4 * r + j, nrows) : -1;
+  const int limc = col < nv ? row_limit(a, qs0, trow + col, nrows) : -1;   // row col's last visible position
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) st.o[i] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    st.m[j] = -INFINITY;
-    st.l[j] = 0.0f;
-  }
+  float mrow = -INFINITY, lrow = 0.0f;   // row col: running maximum, and the sum over this lane's tokens
   auto tiles_to = [&](int lmax) {   // tiles up to the farthest limit lmax (none below the first f32 row)
     int n = min((NT + 15) / 16, kend);
     if (lmax < w0) n = 0;
@@ -521,7 +516,7 @@ __device__ __forceinline__ void f32_rows_block(const AttendArgs& a, unsigned cha
       const uint32_t kb = lds_base + 4 * (FT::K0 + (k & 1) * FT::TILE) + 1024 * n;
       const uint32_t vb = lds_base + 4 * (FT::V0 + (k & 1) * FT::TILE) + 1024 * n;
       dma16(reinterpret_cast<const uint8_t*>(ksrc + 4 * (x ^ (tok & 15))), kb);
-      dma16(reinterpret_cast<const uint8_t*>(vsrc + 4 * (x ^ (4 * (tok & 3)))), vb);
+      dma16(reinterpret_cast<const uint8_t*>(vsrc + 4 * (x ^ (4 * ((tok >> 2) & 3)))), vb);
     }
   };
   if (k0 < nt_blk) issue(k0);
@@ -532,71 +527,80 @@ __device__ __forceinline__ void f32_rows_block(const AttendArgs& a, unsigned cha
     if (k < nt_wave) {
       const float* kt = lds + FT::K0 + (k & 1) * FT::TILE;
       const float* vt = lds + FT::V0 + (k & 1) * FT::TILE;
-      const int t = 16 * k + col;
-      const bool tok_ok = t < NT;
-      // ---- Q K^T: lane (col, r) supplies K of token col, elements NI r + i, in MFMA i
+      // ---- S^T = K Q^T: lane (col, r) supplies K of token col (A) and Q of row col (B), elements NI r + i
+      // in MFMA i; it then holds S[token 4 r + j][row col]
       v4f c = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NI; i += 4) {
         const int x = (NI * r + i) / 4;
         const float4 kv = *reinterpret_cast<const float4*>(kt + col * D + 4 * (x ^ col));
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i], kv.x, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 1], kv.y, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 2], kv.z, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(q[i + 3], kv.w, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.x, q[i], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.y, q[i + 1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.z, q[i + 2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.w, q[i + 3], c, 0, 0, 0);
       }
-      // ---- online softmax of rows 4 r + j over the tile's 16 tokens, with a lazy maximum: a row's
-      // maximum, and its l and accumulators, change only in a tile where one of its scores passes it by
-      // kLazyMax (each lane tests its own token; one branch for the wave), so p lies in [0, 2^8]
+      // ---- online softmax of row col over the tile's 16 tokens (four per lane), with a lazy maximum:
+      // the row's maximum, and its l and accumulators, change only in a tile where one of its scores
+      // passes it by kLazyMax (each lane tests its own tokens; one branch for the wave), so p lies in
+      // [0, 2^8]
       float xs[4];
       bool up = false;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        xs[j] = (tok_ok && w0 + t <= lim[j]) ? c[j] * cl : -INFINITY;
-        up = up || xs[j] > st.m[j] + kLazyMax;
+        const int tj = 16 * k + 4 * r + j;
+        xs[j] = (tj < NT && w0 + tj <= limc) ? c[j] * cl : -INFINITY;
+        up = up || xs[j] > mrow + kLazyMax;
       }
       if (__builtin_amdgcn_ballot_w64(up) != 0) {
-        float corr[4];
+        float mx = fmax_nc(fmax_nc(xs[0], xs[1]), fmax_nc(xs[2], xs[3]));
+        mx = fmax_nc(mx, __shfl_xor(mx, 16));   // the row's four lane groups
+        mx = fmax_nc(mx, __shfl_xor(mx, 32));
+        const float m_new = fmax_nc(mrow, mx);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float corr = __builtin_amdgcn_exp2f(mrow - m_use);   // results below 2^-126 (against a maximum of 1)
+        lrow *= corr;
+        mrow = m_new;
+        // the accumulators hold rows 4 r + j: their corrections come from lanes 4 r + j
+        float cj[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float m_new = fmax_nc(st.m[j], row16_max(xs[j]));
-          const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-          corr[j] = __builtin_amdgcn_exp2f(st.m[j] - m_use);   // results below 2^-126 (against a maximum of 1)
-          st.l[j] *= corr[j];
-          st.m[j] = m_new;
-        }
+        for (int j = 0; j < 4; ++j) cj[j] = __shfl(corr, 4 * r + j);
 #pragma unroll
         for (int i = 0; i < D / 16; ++i) {
           v4f o = st.o[i];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] *= corr[j];
+          for (int j = 0; j < 4; ++j) o[j] *= cj[j];
           st.o[i] = o;
         }
       }
+      const float m_use = mrow == -INFINITY ? 0.0f : mrow;
+      float p[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float m_use = st.m[j] == -INFINITY ? 0.0f : st.m[j];
-        const float p = __builtin_amdgcn_exp2f(xs[j] - m_use);   // may flush: they change no sum
-        st.l[j] += p;
-        pw[col * 16 + ((4 * r + j) ^ (col >> 2))] = p;   // P[row 4 r + j][token col]
+        p[j] = __builtin_amdgcn_exp2f(xs[j] - m_use);   // may flush: they change no sum
+        lrow += p[j];
       }
-      // ---- P V (the wave's P writes reach its own reads in order)
+      // ---- P V: MFMA j takes tokens 4 r + j (k = r), A = P[row col][token 4 r + j] from this lane
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const float pa = pw[(4 * qq + r) * 16 + (col ^ qq)];   // P[row col][token 4 qq + r]
-        const float* vrow = vt + (4 * qq + r) * D;              // token 4 qq + r: swizzle 4 r
+      for (int j = 0; j < 4; ++j) {
+        const float* vrow = vt + (4 * r + j) * D;   // token 4 r + j: swizzle 4 r
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
           const int e = col + 16 * dt;
-          st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vrow[4 * ((e >> 2) ^ (4 * r)) + (e & 3)], st.o[dt], 0, 0, 0);
+          st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[j], vrow[4 * ((e >> 2) ^ (4 * r)) + (e & 3)], st.o[dt], 0, 0, 0);
         }
       }
     }
     wait_vm<0>();        // this wave's loads of tile k + 1 have landed
     __syncthreads();     // every wave's have, and every wave is done with buffer k & 1
   }
+  // the state of rows 4 r + j, as the accumulators hold them: l summed over the row's four lane groups
+  lrow += __shfl_xor(lrow, 16);
+  lrow += __shfl_xor(lrow, 32);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) st.l[j] = row16_sum(st.l[j]);
+  for (int j = 0; j < 4; ++j) {
+    st.m[j] = __shfl(mrow, 4 * r + j);
+    st.l[j] = __shfl(lrow, 4 * r + j);
+  }
 }
 
 // Grid: one block per (batch row, kv head, group, block of BR rows), the groups being the chunks of
