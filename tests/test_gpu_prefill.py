@@ -165,3 +165,18 @@ def test_prefill_validation():
     with pytest.raises(kvq.KvqError, match="workspace"):
         kvq.attend_prefill_causal(c["cache"], c["qt"], c["qs"], c["bt"], c["seq"], c["maxs"], 1.0,
                                   workspace=torch.empty(8, dtype=torch.uint8, device=U.DEV))
+
+
+def test_prefill_many_slots_sampled():
+    """More split-K slots than a wave has lanes (36864 tokens: 72 chunks of the shortest split, 512
+    tokens, and the window) with 4096 query rows, so that the reduce merges the narrow partial records
+    on its general path; queries 200..202 of the chunk against the oracle."""
+    U.need_gpu()
+    L, n_q, Hkv, G, D = 36864, 256, 4, 4, 128
+    c = _case(spec.HAD_INT4, D, Hkv, G, [L], n_q, [L - n_q], n_recent=64, page_size=256, seed=11)
+    assert kvq.prefill_workspace_bytes(1, n_q, Hkv * G, D, L) > 0
+    got = _gpu(c).cpu().numpy()
+    i0 = 200
+    ref = attention.attend_prefill(c["layout"], c["q"][0][i0:i0 + 3], c["rows_k"][0], c["rows_v"][0], c["alpha"],
+                                   c["q_starts"][0] + i0, causal=True, n_recent=c["n_recent"])
+    U.assert_close_rel(got[0, i0:i0 + 3], ref)
