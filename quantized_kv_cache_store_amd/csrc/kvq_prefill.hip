@@ -178,7 +178,7 @@ __device__ __forceinline__ void prefill_produce(unsigned char* buf, int tid, con
       for (int e = 0; e < 2; ++e) {
         // signed codes c = (c + 8) - 8 per byte (+0x78 never carries out of a byte), so that the
         // Q K^T MFMA needs no block-sum offset
-        const uint32_t x = ld.kw[k + e] ^ 0x88888888u;   // the stored codes carry a bias of 8
+        const uint32_t x = ld.kw[k + e] ^ 0x88888888u;   // two's-complement nibbles: top bit flipped, c + 8
         c[2 * e] = ((x & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
         c[2 * e + 1] = (((x >> 4) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
       }
