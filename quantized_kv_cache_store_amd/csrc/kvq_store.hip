@@ -197,8 +197,17 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
       reinterpret_cast<uint32_t*>(rec)[sub / LPG] = (uint32_t)f16_bits_sat(s32) | ((uint32_t)f16_bits_sat(mn) << 16);
   }
 
-  if (!ok) return;
+  // Payload words are gathered so that each write is 16 bytes: the lane's packed words, and those of
+  // the next lanes of its row (DPP row shifts, within the 16 lanes of the row), go out from every
+  // 16 / (bytes per lane)-th lane.  Every lane of a row takes part in the shifts (ok is row-uniform).
   uint8_t* pay = a.payload[kv] + prow * T::PB;
+  auto from = [](uint32_t w, auto dn) {   // the word of lane sub + n of this row (n = 1, 2, 3)
+    constexpr int n = decltype(dn)::value;
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0x100 + n, 0xF, 0xF, false);   // row_shl:n
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
   if (L == Q80) {
     // one two's-complement byte per code, element order: the lane's E codes at byte sub * E
     uint32_t w[E / 4];
@@ -206,15 +215,25 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
     for (int i = 0; i < E / 4; ++i)
       w[i] = (uint32_t)(n[4 * i] & 0xFF) | ((uint32_t)(n[4 * i + 1] & 0xFF) << 8) |
              ((uint32_t)(n[4 * i + 2] & 0xFF) << 16) | ((uint32_t)(n[4 * i + 3] & 0xFF) << 24);
-    if constexpr (E == 8) reinterpret_cast<uint2*>(pay)[sub] = make_uint2(w[0], w[1]);
-    else reinterpret_cast<uint4*>(pay)[sub] = make_uint4(w[0], w[1], w[2], w[3]);
-  } else if (L != Q60) {
-    if (E == 8) {
-      reinterpret_cast<uint32_t*>(pay)[sub] = pack8(n);
+    if constexpr (E == 8) {   // 8 bytes per lane: lane pairs
+      const uint32_t w2 = from(w[0], I1{}), w3 = from(w[1], I1{});
+      if (ok && (sub & 1) == 0) reinterpret_cast<uint4*>(pay)[sub >> 1] = make_uint4(w[0], w[1], w2, w3);
     } else {
-      reinterpret_cast<uint2*>(pay)[sub] = make_uint2(pack8(n), pack8(n + 8));
+      if (ok) reinterpret_cast<uint4*>(pay)[sub] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else if (L != Q60) {
+    if (E == 8) {   // 4 bytes per lane: lane quads
+      const uint32_t w0 = pack8(n);
+      const uint32_t w1 = from(w0, I1{}), w2 = from(w0, I2{}), w3 = from(w0, I3{});
+      if (ok && (sub & 3) == 0) reinterpret_cast<uint4*>(pay)[sub >> 2] = make_uint4(w0, w1, w2, w3);
+    } else {        // 8 bytes per lane: lane pairs
+      const uint32_t w0 = pack8(n), w1 = pack8(n + 8);
+      const uint32_t w2 = from(w0, I1{}), w3 = from(w1, I1{});
+      if (ok && (sub & 1) == 0) reinterpret_cast<uint4*>(pay)[sub >> 1] = make_uint4(w0, w1, w2, w3);
     }
   } else {
+    if (!ok) return;
+    // q6_0: 24-byte blocks (16 bytes of low nibbles, then 8 of top-bit pairs), not 16-byte aligned
     // lane holds octets o = sub*E/8 .. ; octet o lives in block o/4 at slot o%4
     if (E == 8) {
       const int g = sub >> 2, c = sub & 3;
